@@ -1,0 +1,363 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each oracle function is checked against at least one of: a hand-derived
+fixture under tests/golden/, a library routine computing the same definition
+by another route (torch float64 bmm / scaled_dot_product_attention, numpy
+indexing), a closed form, or an invariant of the method (naive = absorbed,
+decode at step t = full recompute at t, split-and-merge = single pass, paged =
+contiguous, softmax rows sum to one). The cases are chosen so a dropped term,
+a wrong sign or index, or a transposed operand fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mla_inputs as mi
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _sdpa_mqa(q, kv, pos, scale, causal, L):
+    """Absorbed attention as one-KV-head attention (K = [c_kv | k_pe],
+    V = c_kv) through torch's float64 scaled_dot_product_attention."""
+    q = torch.from_numpy(np.asarray(q, dtype=np.float64))  # [nq, N, E]
+    kv = torch.from_numpy(np.asarray(kv, dtype=np.float64))  # [T, E]
+    nq, N, E = q.shape
+    T = kv.shape[0]
+    qh = q.permute(1, 0, 2).contiguous()  # [N, nq, E]
+    k = kv.unsqueeze(0).expand(N, T, E).contiguous()
+    v = kv[:, :L].unsqueeze(0).expand(N, T, L).contiguous()
+    j = torch.arange(T).unsqueeze(0)
+    p = torch.as_tensor(np.asarray(pos)).unsqueeze(1)
+    mask = (j <= p) if causal else torch.ones(nq, T, dtype=torch.bool)
+    out = torch.nn.functional.scaled_dot_product_attention(qh, k, v, attn_mask=mask, scale=scale)
+    return out.permute(1, 0, 2).numpy()
+
+
+# --------------------------------------------------------------------- bmm
+
+
+def test_bmm_golden():
+    g = _golden("bmm.json")
+    out = oracle.bmm(np.array(g["a"]), np.array(g["b"]))
+    np.testing.assert_array_equal(out, np.array(g["out"]))
+
+
+def test_bmm_golden_transposed_view():
+    # a stored as [M, G, K]; the oracle reads it through strides as [G, M, K]
+    g = _golden("bmm.json")
+    a = np.array(g["a"])  # [G, M, K]
+    store = np.ascontiguousarray(a.transpose(1, 0, 2))  # [M, G, K]
+    G, M, K = a.shape
+    b = np.array(g["b"])
+    N = b.shape[2]
+    out = oracle.bmm_strided(store, (0, K, G * K, 1), b, (0, K * N, N, 1), (G, M, K, N))
+    np.testing.assert_array_equal(out, np.array(g["out"]))
+
+
+@pytest.mark.parametrize("G,M,K,N", [(16, 7, 128, 512), (5, 6, 9, 4), (3, 1, 512, 128)])
+def test_bmm_vs_torch_float64(G, M, K, N):
+    rng = np.random.default_rng(G * 100 + M)
+    a = rng.uniform(-1, 1, (G, M, K))
+    b = rng.uniform(-1, 1, (G, K, N))
+    want = torch.bmm(torch.from_numpy(a), torch.from_numpy(b)).numpy()
+    np.testing.assert_allclose(oracle.bmm(a, b), want, rtol=1e-12, atol=1e-12)
+
+
+def test_fold_and_vup_vs_einsum_on_transposed_layouts():
+    # the q-side fold reads q_nope [T,N,P] as the [N,T,P] view the upstream
+    # call passes; the un-projection writes [T,N,V] (vllm.cpp transposed-view test)
+    rng = np.random.default_rng(5)
+    T, N, P, L, V = 6, 5, 9, 12, 4
+    q_nope = rng.uniform(-1, 1, (T, N, P))
+    w_uk_t = rng.uniform(-1, 1, (N, P, L))
+    o_lat = rng.uniform(-1, 1, (T, N, L))
+    w_uv = rng.uniform(-1, 1, (N, L, V))
+    np.testing.assert_allclose(oracle.fold_q(q_nope, w_uk_t),
+                               np.einsum("thp,hpl->thl", q_nope, w_uk_t), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(oracle.v_up(o_lat, w_uv),
+                               np.einsum("thl,hlv->thv", o_lat, w_uv), rtol=1e-12, atol=1e-13)
+
+
+def test_bmm_identity_and_zero_weights():
+    rng = np.random.default_rng(9)
+    a = rng.uniform(-1, 1, (3, 4, 5))
+    eye = np.broadcast_to(np.eye(5), (3, 5, 5)).copy()
+    np.testing.assert_array_equal(oracle.bmm(a, eye), a)
+    np.testing.assert_array_equal(oracle.bmm(a, np.zeros((3, 5, 2))), np.zeros((3, 4, 2)))
+
+
+# ------------------------------------------------------------ attention
+
+
+@pytest.mark.parametrize("name", ["attend_basic.json", "attend_rope.json", "attend_causal.json"])
+def test_attend_golden(name):
+    g = _golden(name)
+    o, lse, probs = oracle.attend_seq(np.array(g["q"]), np.array(g["kv"]), g["pos"], g["scale"],
+                                      g["causal"], g["L"], want_probs=True)
+    np.testing.assert_allclose(o, np.array(g["o_lat"]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(lse, np.array(g["lse"]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(probs.sum(-1), 1.0, rtol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,N,L,R,T", [(1, 16, 512, 64, 300), (5, 3, 64, 8, 11), (7, 4, 32, 0, 7)])
+def test_attend_vs_sdpa_float64(nq, N, L, R, T, causal):
+    rng = np.random.default_rng(nq * 7 + T)
+    q = rng.normal(0, 0.3, (nq, N, L + R))
+    kv = rng.normal(0, 1.0, (T, L + R))
+    pos = np.arange(T - nq, T)
+    scale = (L + R) ** -0.5
+    o, lse, _ = oracle.attend_seq(q, kv, pos, scale, causal, L)
+    np.testing.assert_allclose(o, _sdpa_mqa(q, kv, pos, scale, causal, L), rtol=1e-11, atol=1e-12)
+    # lse against scipy-free log-sum-exp of numpy scores
+    s = np.einsum("ihe,je->ihj", q, kv) * scale
+    if causal:
+        s = np.where(np.arange(T)[None, None, :] <= pos[:, None, None], s, -np.inf)
+    m = s.max(-1, keepdims=True)
+    want_lse = (m + np.log(np.exp(s - m).sum(-1, keepdims=True)))[..., 0]
+    np.testing.assert_allclose(lse, want_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_attend_closed_forms():
+    rng = np.random.default_rng(11)
+    L, R, T, N = 16, 4, 9, 3
+    kv = rng.normal(0, 1, (T, L + R))
+    # one visible key: output is that key's c_kv exactly, lse its score
+    q = rng.normal(0, 1, (1, N, L + R))
+    o, lse, _ = oracle.attend_seq(q, kv, [0], 0.7, True, L)
+    np.testing.assert_allclose(o[0], np.broadcast_to(kv[0, :L], (N, L)), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(lse[0], 0.7 * q[0] @ kv[0], rtol=1e-14)
+    # zero query: mean of visible rows, lse = ln(count)
+    z = np.zeros((2, N, L + R))
+    o, lse, _ = oracle.attend_seq(z, kv, [3, T - 1], 1.0, True, L)
+    np.testing.assert_allclose(o[0], np.broadcast_to(kv[:4, :L].mean(0), (N, L)), rtol=1e-13)
+    np.testing.assert_allclose(o[1], np.broadcast_to(kv[:, :L].mean(0), (N, L)), rtol=1e-13)
+    np.testing.assert_allclose(lse[0], math.log(4.0), rtol=1e-15)
+    np.testing.assert_allclose(lse[1], math.log(T), rtol=1e-15)
+    # all keys identical: output is that row whatever q is
+    same = np.broadcast_to(kv[2], (T, L + R)).copy()
+    o, _, _ = oracle.attend_seq(q, same, [T - 1], 0.3, False, L)
+    np.testing.assert_allclose(o[0], np.broadcast_to(kv[2, :L], (N, L)), rtol=1e-13)
+
+
+def test_attend_no_visible_key_and_empty_sequence():
+    q = np.ones((2, 2, 5))
+    kv = np.ones((3, 5))
+    o, lse, _ = oracle.attend_seq(q, kv, [-1, 0], 1.0, True, 4)  # query 0 sees nothing
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.all(np.isfinite(lse[1]))
+    o, lse, _ = oracle.attend_seq(q, np.zeros((0, 5)), [0, 0], 1.0, False, 4)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_attend_softmax_rows_sum_to_one_and_key_permutation():
+    rng = np.random.default_rng(3)
+    q = rng.normal(0, 1, (3, 4, 40))
+    kv = rng.normal(0, 1, (25, 40))
+    o, lse, p = oracle.attend_seq(q, kv, [24, 24, 24], 0.4, False, 32, want_probs=True)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=1e-14)
+    assert np.all(p >= 0)
+    perm = rng.permutation(25)
+    o2, lse2, _ = oracle.attend_seq(q, kv[perm], [24, 24, 24], 0.4, False, 32)
+    np.testing.assert_allclose(o2, o, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-14)
+
+
+def test_causal_rows_ignore_future_keys():
+    # changing keys beyond a query's position must not change its output
+    rng = np.random.default_rng(4)
+    q = rng.normal(0, 1, (1, 2, 12))
+    kv = rng.normal(0, 1, (10, 12))
+    o, _, _ = oracle.attend_seq(q, kv, [5], 0.5, True, 8)
+    kv2 = kv.copy()
+    kv2[6:] = 1e3
+    o2, _, _ = oracle.attend_seq(q, kv2, [5], 0.5, True, 8)
+    np.testing.assert_array_equal(o, o2)
+
+
+# ------------------------------------------------------- naive vs absorbed
+
+SHRUNK = [
+    mi.Dims(n_head=4, d_nope=24, d_rope=8, d_v=32, kv_rank=64),
+    mi.Dims(n_head=3, d_nope=12, d_rope=4, d_v=20, kv_rank=48),
+    mi.Dims(n_head=4, d_nope=32, d_rope=0, d_v=32, kv_rank=64),
+]
+
+
+def test_naive_golden():
+    g = _golden("naive.json")
+    out = oracle.naive(np.array(g["q_nope"]), None, np.array(g["c_kv"]), None,
+                       np.array(g["w_uk_t"]), np.array(g["w_uv"]), g["pos"], g["scale"], g["causal"])
+    np.testing.assert_allclose(out, np.array(g["out"]), rtol=1e-14)
+    out2, *_ = oracle.absorbed(np.array(g["q_nope"]), None, np.array(g["c_kv"]), None,
+                               np.array(g["w_uk_t"]), np.array(g["w_uv"]), g["pos"], g["scale"],
+                               g["causal"])
+    np.testing.assert_allclose(out2, np.array(g["out"]), rtol=1e-14)
+
+
+@pytest.mark.parametrize("d", SHRUNK + [mi.V2_LITE, mi.NOPE64], ids=lambda d: f"N{d.n_head}P{d.d_nope}R{d.d_rope}")
+@pytest.mark.parametrize("t_q,t_kv", [(6, 6), (3, 11)])
+def test_naive_equals_absorbed(d, t_q, t_kv):
+    seed = d.n_head * 31 + t_kv
+    q_nope, q_pe, c_kv, k_pe = mi.mla_activations(seed, d, t_q, t_kv, mi.F32)
+    w_uk_t, w_uv = mi.mla_weights(seed, d, mi.F32)
+    pos = np.arange(t_kv - t_q, t_kv)
+    scale = (d.d_nope + d.d_rope) ** -0.5
+    naive = oracle.naive(q_nope, q_pe if d.d_rope else None, c_kv, k_pe if d.d_rope else None,
+                         w_uk_t, w_uv, pos, scale, True)
+    absorbed, q_lat, o_lat, lse = oracle.absorbed(q_nope, q_pe if d.d_rope else None, c_kv,
+                                                  k_pe if d.d_rope else None, w_uk_t, w_uv,
+                                                  pos, scale, True)
+    mx = max(np.abs(naive).max(), 1e-30)
+    assert np.abs(naive - absorbed).max() <= 1e-12 * max(1.0, mx)
+    assert np.abs(naive).max() > 1e-6
+    # stage outputs agree with the stand-alone stages
+    np.testing.assert_allclose(q_lat, oracle.fold_q(q_nope, w_uk_t), rtol=1e-13, atol=1e-14)
+    kv = np.concatenate([c_kv, k_pe], axis=1) if d.d_rope else c_kv
+    q = np.concatenate([q_lat, q_pe], axis=2) if d.d_rope else q_lat
+    o2, lse2, _ = oracle.attend_seq(q, kv, pos, scale, True, d.kv_rank)
+    np.testing.assert_allclose(o_lat, o2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-13)
+
+
+def test_naive_vs_sdpa_on_decompressed_heads():
+    d = SHRUNK[0]
+    q_nope, q_pe, c_kv, k_pe = mi.mla_activations(77, d, 5, 9, mi.F32)
+    w_uk_t, w_uv = mi.mla_weights(77, d, mi.F32)
+    pos = np.arange(4, 9)
+    scale = 0.25
+    out = oracle.naive(q_nope, q_pe, c_kv, k_pe, w_uk_t, w_uv, pos, scale, True)
+    k_nope = np.einsum("hpl,jl->hjp", w_uk_t.astype(np.float64), c_kv.astype(np.float64))
+    v = np.einsum("hld,jl->hjd", w_uv.astype(np.float64), c_kv.astype(np.float64))
+    k = np.concatenate([k_nope, np.broadcast_to(k_pe, (d.n_head,) + k_pe.shape)], axis=2)
+    q = np.concatenate([q_nope, q_pe], axis=2).transpose(1, 0, 2).astype(np.float64)
+    mask = torch.from_numpy(np.arange(9)[None, :] <= pos[:, None])
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.ascontiguousarray(q)), torch.from_numpy(np.ascontiguousarray(k)),
+        torch.from_numpy(np.ascontiguousarray(v)), attn_mask=mask, scale=scale).numpy()
+    np.testing.assert_allclose(out, want.transpose(1, 0, 2), rtol=1e-11, atol=1e-13)
+
+
+def test_decode_step_equals_full_recompute():
+    # memra gate 2: each decode step (one query at pos against rows 0..pos)
+    # equals the full-sequence causal prefill's row at pos.
+    d = SHRUNK[0]
+    total = 9
+    q_nope, q_pe, c_kv, k_pe = mi.mla_activations(0x57E9, d, total, total, mi.F32)
+    w_uk_t, w_uv = mi.mla_weights(0x57E9, d, mi.F32)
+    scale = (d.d_nope + d.d_rope) ** -0.5
+    full, *_ = oracle.absorbed(q_nope, q_pe, c_kv, k_pe, w_uk_t, w_uv, np.arange(total), scale, True)
+    for pos in range(5, total):
+        step, *_ = oracle.absorbed(q_nope[pos:pos + 1], q_pe[pos:pos + 1], c_kv[:pos + 1],
+                                   k_pe[:pos + 1], w_uk_t, w_uv, [pos], scale, True)
+        assert np.abs(step[0] - full[pos]).max() <= 1e-13 * max(1.0, np.abs(full[pos]).max())
+
+
+# ----------------------------------------------------- paging and splits
+
+
+def test_gather_pages_vs_numpy_indexing():
+    rng = np.random.default_rng(21)
+    NB, PG, E = 10, 4, 6
+    pool = rng.normal(0, 1, (NB, PG, E))
+    bt = np.array([[7, 2, 9, -1], [0, 5, -1, -1]], dtype=np.int32)
+    for b, s in [(0, 11), (1, 8), (1, 0)]:
+        rows = oracle.gather_pages(pool, bt, b, s)
+        j = np.arange(s)
+        np.testing.assert_array_equal(rows, pool[bt[b, j // PG], j % PG])
+    with pytest.raises(ValueError):
+        oracle.gather_pages(pool, bt, 0, 13)  # needs page 3 = -1
+
+
+def test_paged_equals_contiguous():
+    d = mi.Dims(n_head=5, d_nope=8, d_rope=8, d_v=8, kv_rank=32)
+    c = mi.decode_case(3, d, mi.F32, [1, 17, 64, 65, 130], q_len=3, page=16, num_blocks=40,
+                       std=0.5)
+    o, lse = oracle.attend_paged(c.q, c.pool, c.block_table, c.seqlens, c.scale, True, d.kv_rank)
+    for b, s in enumerate(c.seqlens):
+        j = np.arange(s)
+        rows = c.pool[c.block_table[b, j // c.page], j % c.page].astype(np.float64)
+        o2, lse2, _ = oracle.attend_seq(c.q[b], rows, np.arange(s - 3, s), c.scale, True, d.kv_rank)
+        np.testing.assert_array_equal(o[b], o2)
+        np.testing.assert_array_equal(lse[b], lse2)
+    assert np.all(np.isfinite(o))  # NaN page tails never reached
+
+
+def test_split_merge_golden():
+    g = _golden("merge.json")
+    o, lse = oracle.attend_split(np.array(g["q"]), np.array(g["kv"]), g["pos"], g["scale"],
+                                 g["causal"], g["L"], g["bounds"])
+    np.testing.assert_allclose(o, np.array(g["o_lat"]), rtol=1e-14)
+    np.testing.assert_allclose(lse, np.array(g["lse"]), rtol=1e-14)
+
+
+@pytest.mark.parametrize("bounds", [[0, 40], [0, 1, 40], [0, 13, 13, 27, 40], [0, 5, 10, 20, 30, 40]])
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_merge_equals_single_pass(bounds, causal):
+    rng = np.random.default_rng(len(bounds))
+    q = rng.normal(0, 1, (4, 3, 24))
+    kv = rng.normal(0, 1, (40, 24))
+    pos = np.array([2, 15, 28, 39])
+    o1, lse1, _ = oracle.attend_seq(q, kv, pos, 0.3, causal, 16)
+    o2, lse2 = oracle.attend_split(q, kv, pos, 0.3, causal, 16, bounds)
+    np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse1, rtol=1e-13)
+
+
+# -------------------------------------------------------------- cache write
+
+
+def test_cache_write_golden():
+    g = _golden("cache_write.json")
+    buf = np.zeros(g["buf_elems"], dtype=np.float32)
+    out = oracle.cache_write(buf, np.array(g["kv_c"], np.float32), np.array(g["k_pe"], np.float32),
+                             g["slots"], g["offset"], g["num_blocks"], g["page"], g["s0"], g["s1"])
+    np.testing.assert_array_equal(out, np.array(g["buf"], np.float32))
+
+
+@pytest.mark.parametrize("pe", [64, 0])
+def test_cache_write_vs_numpy_view_and_zero_bleed(pe):
+    c = mi.cache_write_case(seed=0, pe=pe)
+    bits = lambda a: torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy()
+    kv_c, k_pe = bits(c["kv_c"]), bits(c["k_pe"])
+    buf = np.zeros(c["buf_shape"], dtype=np.int16)
+    out = oracle.cache_write(buf, kv_c, k_pe if pe else None, c["slots"], c["offset"],
+                             c["num_blocks"], c["page"], c["s0"], c["s1"])
+    # route 2: numpy strided view + fancy-index assignment
+    want = np.zeros(c["buf_shape"], dtype=np.int16)
+    flat = want.reshape(-1)
+    view = np.lib.stride_tricks.as_strided(
+        flat[c["offset"]:], shape=(c["num_blocks"], c["page"], c["entry"]),
+        strides=(c["s0"] * 2, c["s1"] * 2, 2))
+    blk, off = c["slots"] // c["page"], c["slots"] % c["page"]
+    view[blk, off] = np.concatenate([kv_c, k_pe], axis=1) if pe else kv_c
+    np.testing.assert_array_equal(out, want)
+    # zero bleed: the neighbour layers stay zero
+    le = c["page"] * c["entry"]
+    o3 = out.reshape(c["num_blocks"], c["n_layers"], le)
+    assert not o3[:, 0].any() and not o3[:, 2].any()
+    # read-back: every token's row is found at its slot
+    np.testing.assert_array_equal(o3[:, 1].reshape(-1, c["entry"])[c["slots"]][:, :512], kv_c)
+
+
+def test_cache_write_skips_bad_slots_and_copies_bits():
+    kv_c = np.array([[np.nan, -0.0], [1.0, 2.0], [3.0, 4.0]], dtype=np.float32)
+    kv_c_bits = kv_c.view(np.int32).copy()
+    kv_c_bits[0, 0] = 0x7FC01234  # a NaN with a payload
+    k_pe = np.array([[5.0], [6.0], [7.0]], dtype=np.float32).view(np.int32)
+    buf = np.full(2 * 2 * 3, 99, dtype=np.int32)
+    out = oracle.cache_write(buf, kv_c_bits, k_pe, [0, -5, 4], 0, 2, 2, 6, 3)
+    assert out[0] == 0x7FC01234 and out[1] == np.float32(-0.0).view(np.int32)
+    assert out[2] == k_pe[0, 0]
+    assert np.all(out[3:] == 99)  # slot -5 and slot 4 (= NB*page) are skipped
