@@ -1,0 +1,204 @@
+/*
+ * mla.h -- C ABI of libmla: multi-head latent attention (MLA) in
+ * weight-absorbed form, for decode and chunked prefill, on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The four compute calls follow the statement of the method on these pages:
+ *   [P1] vllm.cpp "tests/vt/test_ops_mla_absorb.cpp" -- the batched matmul
+ *        (q-side W_UK fold and W_UV un-projection) and the nope/rope concat;
+ *   [P2] memra-engine 0.124.1 "tests/mla_gpu_forward.rs" -- absorb q,
+ *        absorbed attention over the [c_kv | k_pe] latent cache, decompress v,
+ *        latent append, gates 1 and 2;
+ *   [P3] vLLM "tests/kernels/attention/test_mla_cross_layer_kernel_equivalence.py"
+ *        -- concat_and_cache_mla into a paged, possibly block-major cache view,
+ *        and paged dense decode returning (out, lse).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Tensors are passed as `mla_tensor` descriptors: a pointer to element
+ * [0, 0, ...] (any storage offset already folded in), a dtype, a rank, and
+ * per-dimension sizes and strides counted in ELEMENTS ([P1] keeps its tensor
+ * descriptor the same way). The innermost stride must be 1; the others may be
+ * anything non-negative, so transposed and block-major views are accepted as
+ * they are.
+ *
+ * Memory: every data pointer is a DEVICE pointer on the current HIP device.
+ * The caller owns every buffer, the workspace and the stream. The library
+ * allocates no memory, keeps no pointer after a call returns and never
+ * synchronises; all work is enqueued on `stream` (a hipStream_t, NULL = the
+ * null stream), so results are ready when that stream reaches the call.
+ *
+ * Errors: each call returns MLA_OK (0) or a negative status. Arguments are
+ * validated on the host before anything is launched; on any error nothing is
+ * enqueued and no output is touched. MLA_ERR_HIP reports a failed launch.
+ * mla_status_str() names a status.
+ *
+ * Data types: MLA_BF16 and MLA_F32 for values (all value tensors of one call
+ * share one dtype); MLA_I32 / MLA_I64 for indices. bf16 arithmetic uses fp32
+ * accumulation and rounds outputs to nearest-even; copies move bits.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum {
+  MLA_BF16 = 1,
+  MLA_F32 = 2,
+  MLA_I32 = 3,
+  MLA_I64 = 4
+};
+
+/* status codes */
+enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer or descriptor is NULL */
+  MLA_ERR_DTYPE = -2,       /* wrong or mismatched dtype */
+  MLA_ERR_SHAPE = -3,       /* wrong rank or inconsistent sizes */
+  MLA_ERR_STRIDE = -4,      /* inner stride != 1, or a negative stride */
+  MLA_ERR_UNSUPPORTED = -5, /* a size outside what the kernels implement */
+  MLA_ERR_WORKSPACE = -6,   /* workspace missing or too small */
+  MLA_ERR_HIP = -7          /* the HIP runtime reported an error at launch */
+};
+
+#define MLA_MAX_RANK 4
+
+typedef struct mla_tensor {
+  void* data;                     /* device address of element [0,...,0] */
+  int32_t dtype;                  /* MLA_BF16 / MLA_F32 / MLA_I32 / MLA_I64 */
+  int32_t rank;                   /* 1..MLA_MAX_RANK */
+  int64_t shape[MLA_MAX_RANK];    /* sizes; entries >= rank are ignored */
+  int64_t stride[MLA_MAX_RANK];   /* element strides; stride[rank-1] must be 1 */
+} mla_tensor;
+
+typedef void* mla_stream; /* a hipStream_t */
+
+/*
+ * mla_absorb_q -- fold the no-position part of the query through W_UK and
+ * append the rotary part ([P1] the q-side W_UK fold as a strided batched
+ * matmul whose transposed output feeds the nope/rope concat; [P2]
+ * `mla_absorb_q`).
+ *
+ *   q_out[t, h, 0:L]   = sum_p q_nope[t, h, p] * w_uk_t[h, p, 0:L]
+ *   q_out[t, h, L:L+R] = q_pe[t, h, :]      (bit copy; q_pe may be [T, 1, R],
+ *                                            then its one row is broadcast)
+ *
+ *   q_nope  [T, N, P]     bf16 or f32, any strides (inner 1)
+ *   w_uk_t  [N, P, L]     same dtype, any strides (inner 1)
+ *   q_pe    [T, N, R] or [T, 1, R], same dtype; NULL when R == 0
+ *   q_out   [T, N, L + R] same dtype, any strides (inner 1) -- e.g. a view
+ *           into the attention query buffer
+ * T may be 0 (nothing is launched). Sizes: N, P, L, R >= 1 except R == 0
+ * with q_pe NULL. q_out must not overlap the inputs.
+ */
+int mla_absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_tensor* q_pe,
+                 const mla_tensor* q_out, mla_stream stream);
+
+/*
+ * mla_concat_and_cache -- write each token's latent row [kv_c | k_pe] into a
+ * paged cache through a slot mapping ([P3] concat_and_cache_mla with
+ * kv_cache_dtype "auto" and scale 1, written into the middle layer of a
+ * block-major unified slot; [P2] `mla_append_latent`).
+ *
+ *   for t with 0 <= slot_mapping[t] < NB * PG:
+ *     blk = slot / PG, off = slot % PG
+ *     kv_cache[blk, off, 0:L]   = kv_c[t, :]
+ *     kv_cache[blk, off, L:L+R] = k_pe[t, :]
+ *
+ *   kv_c          [T, L]      bf16 or f32, row stride any (inner 1)
+ *   k_pe          [T, R]      same dtype; NULL when R == 0
+ *   slot_mapping  [T]         MLA_I64 (or MLA_I32), contiguous
+ *   kv_cache      [NB, PG, L + R] same dtype; stride[0] and stride[1] any
+ *                 (a per-layer view of a block-major allocation has stride[0]
+ *                 = n_layers * PG * (L + R) and a non-zero offset)
+ * A copy of bits: every element is reproduced exactly. Tokens whose slot is
+ * negative or >= NB * PG are skipped; nothing outside the written rows is
+ * touched. Duplicate slots race: one of the writers' rows lands.
+ */
+int mla_concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
+                         const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
+                         mla_stream stream);
+
+/*
+ * mla_decode_workspace_size -- bytes of device workspace mla_decode_attend
+ * needs for a call of these sizes (an upper bound that depends only on the
+ * arguments, never on the device or on seqlens' contents).
+ *
+ *   batch B, q_len Sq (query tokens per sequence), n_heads N, kv_rank L,
+ *   max_seqlen (>= every seqlens[b]), page PG, dtype of q.
+ * Writes *bytes; returns MLA_OK or a validation error.
+ */
+int mla_decode_workspace_size(int64_t batch, int64_t q_len, int64_t n_heads, int64_t kv_rank,
+                              int64_t max_seqlen, int64_t page, int32_t dtype, size_t* bytes);
+
+/*
+ * mla_decode_attend -- paged decode / chunked-prefill attention of N query
+ * heads over the shared latent cache, in split-KV form with a log-sum-exp
+ * merge ([P3] flash_mla_with_kvcache: q [B, Sq, N, 576], a paged cache with
+ * block_table and cache_seqlens, head_dim_v 512, softmax scale 576^-0.5,
+ * returning (out, lse); [P2] `mla_attn_absorbed`).
+ *
+ * For sequence b, query i sits at position pos = seqlens[b] - Sq + i (the
+ * queries are the last Sq tokens of the sequence); with causal != 0 it sees
+ * keys 0..pos, otherwise keys 0..seqlens[b]-1. Key j of sequence b is the
+ * cache row kv_cache[block_table[b, j / PG], j % PG, :].
+ *
+ *   s_j      = softmax_scale * sum_e q[b, i, h, e] * key_j[e]   (e < L + R)
+ *   out[...] = sum_j softmax(s)_j * key_j[0:L]    (the value is the c_kv part)
+ *   lse[...] = ln sum_j exp(s_j)                  (-inf, and out = 0, when no
+ *                                                  key is visible)
+ *
+ *   q            [B, Sq, N, L + R]  bf16 or f32, any strides (inner 1)
+ *   kv_cache     [NB, PG, L + R]    same dtype; stride[0] any (block-major
+ *                views allowed), stride[1] a multiple of 8 elements
+ *   block_table  [B, MB]            MLA_I32, row stride any; only entries
+ *                j < ceil(seqlens[b] / PG) are read. An entry outside
+ *                [0, NB) makes that page contribute nothing.
+ *   seqlens      [B]                MLA_I32, contiguous, on the device; values
+ *                are clamped to [0, min(max_seqlen, MB * PG)]
+ *   max_seqlen   host upper bound of seqlens (sizes the launch; no D2H copy)
+ *   out          [B, Sq, N, L]      same dtype as q, any strides (inner 1)
+ *   lse          [B, Sq, N]         MLA_F32, any strides; or NULL
+ *   workspace    device scratch of at least mla_decode_workspace_size()
+ *                bytes (16-byte aligned); may be NULL when that size is 0
+ * Supported: L == 512; R == 0 or 64; PG a multiple of 16; L + R rows 16-byte
+ * aligned (pointer and strides). The result depends only on the inputs'
+ * values and sizes -- not on strides, pointers or the device -- so a
+ * block-major view and a contiguous copy give bit-identical outputs, and so
+ * do repeated calls.
+ */
+int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
+                      const mla_tensor* block_table, const mla_tensor* seqlens,
+                      int64_t max_seqlen, float softmax_scale, int32_t causal,
+                      const mla_tensor* out, const mla_tensor* lse, void* workspace,
+                      size_t workspace_bytes, mla_stream stream);
+
+/*
+ * mla_v_up -- un-project the latent attention output through W_UV ([P1] the
+ * `_v_up_proj` bmm writing into a transposed [B, N, V] view; [P2]
+ * `mla_decompress_v`).
+ *
+ *   out[t, h, :] = sum_l o_lat[t, h, l] * w_uv[h, l, :]
+ *
+ *   o_lat  [T, N, L]  bf16 or f32, any strides (inner 1)
+ *   w_uv   [N, L, V]  same dtype, any strides (inner 1)
+ *   out    [T, N, V]  same dtype, any strides (inner 1)
+ * T may be 0.
+ */
+int mla_v_up(const mla_tensor* o_lat, const mla_tensor* w_uv, const mla_tensor* out,
+             mla_stream stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* mla_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,196 @@
+"""Python binding of libmla: MLA in weight-absorbed form on MI355X (gfx950).
+
+Argument marshalling only. Each function turns torch tensors into the C ABI's
+``mla_tensor`` descriptors (data pointer, dtype, sizes and element strides),
+passes the current HIP stream, and raises ``MlaError`` on a non-zero status.
+Every step of the computation runs in the HIP kernels of ``libmla.so``; there
+is no fallback of any kind, so a missing or unbuilt library raises at the first
+call.
+
+The four compute calls mirror include/mla.h:
+
+* ``mla_absorb_q(q_nope, w_uk_t, q_pe, q_out)``
+* ``mla_concat_and_cache(kv_c, k_pe, slot_mapping, kv_cache)``
+* ``mla_decode_attend(q, kv_cache, block_table, seqlens, max_seqlen,
+  softmax_scale, causal, out, lse=None, workspace=None)``
+* ``mla_v_up(o_lat, w_uv, out)``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = [
+    "MlaError",
+    "mla_absorb_q",
+    "mla_concat_and_cache",
+    "mla_decode_workspace_size",
+    "mla_decode_attend",
+    "mla_v_up",
+    "mla_status_str",
+    "lib_path",
+    "load",
+    "STATUS",
+]
+
+lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+_HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                       "mla.h")
+
+MLA_BF16, MLA_F32, MLA_I32, MLA_I64 = 1, 2, 3, 4
+_DTYPES = {torch.bfloat16: MLA_BF16, torch.float32: MLA_F32, torch.int32: MLA_I32,
+           torch.int64: MLA_I64}
+STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_DTYPE", -3: "MLA_ERR_SHAPE",
+          -4: "MLA_ERR_STRIDE", -5: "MLA_ERR_UNSUPPORTED", -6: "MLA_ERR_WORKSPACE",
+          -7: "MLA_ERR_HIP"}
+
+
+class MlaTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("shape", ctypes.c_int64 * 4),
+        ("stride", ctypes.c_int64 * 4),
+    ]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {mla_status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmla.so (built in-tree by mla_absorbed_decode_amd/build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(
+                f"{lib_path} is not built; run `python -m mla_absorbed_decode_amd.build` "
+                "(hipcc, gfx950) first")
+        lib = ctypes.CDLL(lib_path)
+        P = ctypes.POINTER(MlaTensor)
+        vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                                 ctypes.c_size_t)
+        lib.mla_absorb_q.argtypes = [P, P, P, P, vp]
+        lib.mla_concat_and_cache.argtypes = [P, P, P, P, vp]
+        lib.mla_decode_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i32,
+                                                  ctypes.POINTER(sz)]
+        lib.mla_decode_attend.argtypes = [P, P, P, P, i64, f32, i32, P, P, vp, sz, vp]
+        lib.mla_v_up.argtypes = [P, P, P, vp]
+        for fn in ("mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
+                   "mla_decode_attend", "mla_v_up"):
+            getattr(lib, fn).restype = ctypes.c_int
+        lib.mla_status_str.argtypes = [ctypes.c_int]
+        lib.mla_status_str.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Names of the functions include/mla.h declares."""
+    with open(_HEADER) as f:
+        text = f.read()
+    return re.findall(r"^(?:int|const char\*)\s+(mla_\w+)\s*\(", text, flags=re.M)
+
+
+def mla_status_str(status: int) -> str:
+    return load().mla_status_str(int(status)).decode()
+
+
+def desc(t: torch.Tensor | None):
+    """mla_tensor descriptor of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() < 1 or t.dim() > 4:
+        raise ValueError("rank must be 1..4")
+    d = MlaTensor()
+    d.data = t.data_ptr() if t.numel() else 0
+    d.dtype = _DTYPES[t.dtype]
+    d.rank = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ref(d):
+    return ctypes.byref(d) if d is not None else None
+
+
+def _device_check(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libmla operates on device tensors; got a CPU tensor")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise MlaError(rc, what)
+
+
+def mla_absorb_q(q_nope, w_uk_t, q_pe, q_out):
+    """q_out[t,h,:L] = q_nope[t,h,:] @ w_uk_t[h]; q_out[t,h,L:] = q_pe[t,h|0,:]."""
+    _device_check(q_nope, w_uk_t, q_pe, q_out)
+    lib = load()
+    _check(lib.mla_absorb_q(_ref(desc(q_nope)), _ref(desc(w_uk_t)), _ref(desc(q_pe)),
+                            _ref(desc(q_out)), _stream(q_out)), "mla_absorb_q")
+    return q_out
+
+
+def mla_concat_and_cache(kv_c, k_pe, slot_mapping, kv_cache):
+    """kv_cache[slot // PG, slot % PG, :] = [kv_c[t] | k_pe[t]] for valid slots."""
+    _device_check(kv_c, k_pe, slot_mapping, kv_cache)
+    lib = load()
+    _check(lib.mla_concat_and_cache(_ref(desc(kv_c)), _ref(desc(k_pe)), _ref(desc(slot_mapping)),
+                                    _ref(desc(kv_cache)), _stream(kv_cache)),
+           "mla_concat_and_cache")
+    return kv_cache
+
+
+def mla_decode_workspace_size(batch, q_len, n_heads, kv_rank, max_seqlen, page, dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mla_decode_workspace_size(int(batch), int(q_len), int(n_heads), int(kv_rank),
+                                            int(max_seqlen), int(page), _DTYPES[dtype],
+                                            ctypes.byref(out)), "mla_decode_workspace_size")
+    return int(out.value)
+
+
+def mla_decode_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal, out,
+                      lse=None, workspace=None):
+    """Paged absorbed attention; writes out [B,Sq,N,L] and (optionally) lse [B,Sq,N].
+    ``workspace`` (uint8 device tensor) is allocated here when not given."""
+    _device_check(q, kv_cache, block_table, seqlens, out, lse, workspace)
+    lib = load()
+    if workspace is None:
+        nbytes = mla_decode_workspace_size(q.shape[0], q.shape[1], q.shape[2], out.shape[3],
+                                           max_seqlen, kv_cache.shape[1], q.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.mla_decode_attend(_ref(desc(q)), _ref(desc(kv_cache)), _ref(desc(block_table)),
+                                 _ref(desc(seqlens)), int(max_seqlen), float(softmax_scale),
+                                 int(bool(causal)), _ref(desc(out)), _ref(desc(lse)),
+                                 workspace.data_ptr(), workspace.numel(), _stream(out)),
+           "mla_decode_attend")
+    return out
+
+
+def mla_v_up(o_lat, w_uv, out):
+    """out[t,h,:] = o_lat[t,h,:] @ w_uv[h]."""
+    _device_check(o_lat, w_uv, out)
+    lib = load()
+    _check(lib.mla_v_up(_ref(desc(o_lat)), _ref(desc(w_uv)), _ref(desc(out)), _stream(out)),
+           "mla_v_up")
+    return out

@@ -1,0 +1,53 @@
+// cache_write.hip -- latent-cache write: token t's row [kv_c | k_pe] goes to
+// slot_mapping[t] = block * page + offset of a paged, possibly block-major
+// cache view (vLLM "test_mla_cross_layer_kernel_equivalence.py",
+// test_concat_and_cache_mla_into_unified_slot_view; memra-engine 0.124.1
+// "tests/mla_gpu_forward.rs", gate 2's latent append, checked bit for bit).
+//
+// A copy of bits: nothing is converted, so every value, NaN payload and
+// signed zero arrives unchanged. One thread moves one 16-byte chunk (or one
+// element when rows are not 16-byte aligned); a token whose slot is outside
+// [0, num_blocks * page) is skipped, and nothing but the addressed rows is
+// written, so neighbouring layers of a unified slot are never touched.
+#include "mla_device.h"
+#include "mla_kernels.h"
+
+namespace mla {
+namespace {
+
+template <int VEC>  // bytes moved per thread: 16, or the element size
+__global__ void __launch_bounds__(256) cache_write_kernel(CacheWriteParams p) {
+  const int64_t es = p.esize;
+  const int64_t cl = p.L * es / VEC, cr = p.R * es / VEC, cpr = cl + cr;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= p.T * cpr) return;
+  const int64_t t = idx / cpr, c = idx % cpr;
+  const int64_t slot = p.slot_is_i64 ? ((const int64_t*)p.slots)[t] : (int64_t)((const int32_t*)p.slots)[t];
+  if (slot < 0 || slot >= p.num_blocks * p.page) return;
+  const int64_t blk = slot / p.page, off = slot % p.page;
+  char* dst = (char*)p.cache + (blk * p.cache_s0 + off * p.cache_s1) * es + c * VEC;
+  const char* src = c < cl ? (const char*)p.kv_c + t * p.kv_c_s0 * es + c * VEC
+                           : (const char*)p.k_pe + t * p.k_pe_s0 * es + (c - cl) * VEC;
+  if constexpr (VEC == 16) {
+    *(u32x4_t*)dst = __builtin_nontemporal_load((const u32x4_t*)src);
+  } else if constexpr (VEC == 4) {
+    *(uint32_t*)dst = *(const uint32_t*)src;
+  } else {
+    *(uint16_t*)dst = *(const uint16_t*)src;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  const int vec = p.vec16 ? 16 : p.esize;
+  const int64_t threads = p.T * ((p.L + p.R) * p.esize / vec);
+  const int64_t blocks = (threads + 255) / 256;
+  if (vec == 16) hipLaunchKernelGGL(cache_write_kernel<16>, dim3(blocks), dim3(256), 0, s, p);
+  else if (vec == 4) hipLaunchKernelGGL(cache_write_kernel<4>, dim3(blocks), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(cache_write_kernel<2>, dim3(blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

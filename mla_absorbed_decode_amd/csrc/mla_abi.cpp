@@ -1,0 +1,263 @@
+// mla_abi.cpp -- the extern "C" entry points of libmla (declared in
+// include/mla.h). Each call validates every descriptor on the host, plans the
+// launch from sizes alone and enqueues the kernels on the caller's stream.
+// Validation failures return before anything is launched, so no output is
+// touched ("reject malformed shapes and strides rather than mis-compute", as
+// the batched-matmul tests of vllm.cpp "tests/vt/test_ops_mla_absorb.cpp"
+// require of their op).
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "mla.h"
+#include "mla_kernels.h"
+
+namespace {
+
+int esize_of(int32_t dt) {
+  switch (dt) {
+    case MLA_BF16: return 2;
+    case MLA_F32: return 4;
+    case MLA_I32: return 4;
+    case MLA_I64: return 8;
+  }
+  return 0;
+}
+
+bool is_value_dtype(int32_t dt) { return dt == MLA_BF16 || dt == MLA_F32; }
+
+int64_t numel(const mla_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->rank; ++i) n *= t->shape[i];
+  return n;
+}
+
+// rank, shape sign, inner stride 1, non-negative strides, data pointer present
+int check_desc(const mla_tensor* t, int rank) {
+  if (!t) return MLA_ERR_NULL;
+  if (t->rank != rank || rank < 1 || rank > MLA_MAX_RANK) return MLA_ERR_SHAPE;
+  for (int i = 0; i < rank; ++i) {
+    if (t->shape[i] < 0) return MLA_ERR_SHAPE;
+    if (t->stride[i] < 0) return MLA_ERR_STRIDE;
+  }
+  if (t->stride[rank - 1] != 1) return MLA_ERR_STRIDE;
+  if (esize_of(t->dtype) == 0) return MLA_ERR_DTYPE;
+  if (!t->data && numel(t) > 0) return MLA_ERR_NULL;
+  return MLA_OK;
+}
+
+// every row start (all leading strides and the pointer) 16-byte aligned
+bool rows_aligned16(const mla_tensor* t) {
+  const int64_t es = esize_of(t->dtype);
+  if ((uintptr_t)t->data % 16) return false;
+  for (int i = 0; i + 1 < t->rank; ++i)
+    if ((t->stride[i] * es) % 16) return false;
+  return true;
+}
+
+hipError_t g_last_hip = hipSuccess;
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer or descriptor is NULL";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: wrong or mismatched dtype";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: wrong rank or inconsistent sizes";
+    case MLA_ERR_STRIDE: return "MLA_ERR_STRIDE: inner stride is not 1, or a stride is negative";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: sizes or alignment the kernels do not implement";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime reported an error at launch";
+  }
+  return "unknown mla status";
+}
+
+int mla_absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_tensor* q_pe,
+                 const mla_tensor* q_out, mla_stream stream) {
+  int rc;
+  if ((rc = check_desc(q_nope, 3)) || (rc = check_desc(w_uk_t, 3)) || (rc = check_desc(q_out, 3)))
+    return rc;
+  if (q_pe && (rc = check_desc(q_pe, 3))) return rc;
+  const int32_t dt = q_nope->dtype;
+  if (!is_value_dtype(dt) || w_uk_t->dtype != dt || q_out->dtype != dt ||
+      (q_pe && q_pe->dtype != dt))
+    return MLA_ERR_DTYPE;
+  const int64_t T = q_nope->shape[0], N = q_nope->shape[1], P = q_nope->shape[2];
+  if (w_uk_t->shape[0] != N || w_uk_t->shape[1] != P) return MLA_ERR_SHAPE;
+  const int64_t L = w_uk_t->shape[2];
+  int64_t R = 0;
+  if (q_pe) {
+    if (q_pe->shape[0] != T || (q_pe->shape[1] != N && q_pe->shape[1] != 1)) return MLA_ERR_SHAPE;
+    R = q_pe->shape[2];
+  }
+  if (q_out->shape[0] != T || q_out->shape[1] != N || q_out->shape[2] != L + R) return MLA_ERR_SHAPE;
+  if (P == 0 || L == 0) return MLA_ERR_SHAPE;
+  mla::BmmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = q_nope->data; p.a_st = q_nope->stride[0]; p.a_sh = q_nope->stride[1];
+  p.w = w_uk_t->data; p.w_sh = w_uk_t->stride[0]; p.w_sk = w_uk_t->stride[1];
+  p.out = q_out->data; p.o_st = q_out->stride[0]; p.o_sh = q_out->stride[1];
+  if (q_pe) {
+    p.pe = q_pe->data; p.pe_st = q_pe->stride[0]; p.pe_sh = q_pe->shape[1] == 1 ? 0 : q_pe->stride[1];
+  }
+  p.T = T; p.H = N; p.K = P; p.N = L; p.R = R;
+  p.is_f32 = dt == MLA_F32;
+  return launched(mla::launch_bmm(p, (hipStream_t)stream));
+}
+
+int mla_v_up(const mla_tensor* o_lat, const mla_tensor* w_uv, const mla_tensor* out,
+             mla_stream stream) {
+  int rc;
+  if ((rc = check_desc(o_lat, 3)) || (rc = check_desc(w_uv, 3)) || (rc = check_desc(out, 3)))
+    return rc;
+  const int32_t dt = o_lat->dtype;
+  if (!is_value_dtype(dt) || w_uv->dtype != dt || out->dtype != dt) return MLA_ERR_DTYPE;
+  const int64_t T = o_lat->shape[0], N = o_lat->shape[1], L = o_lat->shape[2];
+  if (w_uv->shape[0] != N || w_uv->shape[1] != L) return MLA_ERR_SHAPE;
+  const int64_t V = w_uv->shape[2];
+  if (out->shape[0] != T || out->shape[1] != N || out->shape[2] != V) return MLA_ERR_SHAPE;
+  if (L == 0 || V == 0) return MLA_ERR_SHAPE;
+  mla::BmmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = o_lat->data; p.a_st = o_lat->stride[0]; p.a_sh = o_lat->stride[1];
+  p.w = w_uv->data; p.w_sh = w_uv->stride[0]; p.w_sk = w_uv->stride[1];
+  p.out = out->data; p.o_st = out->stride[0]; p.o_sh = out->stride[1];
+  p.T = T; p.H = N; p.K = L; p.N = V; p.R = 0;
+  p.is_f32 = dt == MLA_F32;
+  return launched(mla::launch_bmm(p, (hipStream_t)stream));
+}
+
+int mla_concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
+                         const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
+                         mla_stream stream) {
+  int rc;
+  if ((rc = check_desc(kv_c, 2)) || (rc = check_desc(slot_mapping, 1)) ||
+      (rc = check_desc(kv_cache, 3)))
+    return rc;
+  if (k_pe && (rc = check_desc(k_pe, 2))) return rc;
+  const int32_t dt = kv_c->dtype;
+  if (!is_value_dtype(dt) || kv_cache->dtype != dt || (k_pe && k_pe->dtype != dt))
+    return MLA_ERR_DTYPE;
+  if (slot_mapping->dtype != MLA_I64 && slot_mapping->dtype != MLA_I32) return MLA_ERR_DTYPE;
+  const int64_t T = kv_c->shape[0], L = kv_c->shape[1];
+  const int64_t R = k_pe ? k_pe->shape[1] : 0;
+  if (k_pe && k_pe->shape[0] != T) return MLA_ERR_SHAPE;
+  if (slot_mapping->shape[0] != T) return MLA_ERR_SHAPE;
+  if (kv_cache->shape[2] != L + R) return MLA_ERR_SHAPE;
+  const int es = esize_of(dt);
+  mla::CacheWriteParams p;
+  memset(&p, 0, sizeof(p));
+  p.kv_c = kv_c->data; p.kv_c_s0 = kv_c->stride[0];
+  p.k_pe = k_pe ? k_pe->data : nullptr; p.k_pe_s0 = k_pe ? k_pe->stride[0] : 0;
+  p.slots = slot_mapping->data; p.slot_is_i64 = slot_mapping->dtype == MLA_I64;
+  p.cache = kv_cache->data; p.cache_s0 = kv_cache->stride[0]; p.cache_s1 = kv_cache->stride[1];
+  p.num_blocks = kv_cache->shape[0]; p.page = kv_cache->shape[1];
+  p.T = T; p.L = L; p.R = R; p.esize = es;
+  p.vec16 = (L * es) % 16 == 0 && (R * es) % 16 == 0 && rows_aligned16(kv_c) &&
+            (!k_pe || rows_aligned16(k_pe)) && rows_aligned16(kv_cache);
+  if (T == 0 || p.num_blocks == 0 || p.page == 0) return MLA_OK;
+  return launched(mla::launch_cache_write(p, (hipStream_t)stream));
+}
+
+int mla_decode_workspace_size(int64_t batch, int64_t q_len, int64_t n_heads, int64_t kv_rank,
+                              int64_t max_seqlen, int64_t page, int32_t dtype, size_t* bytes) {
+  if (!bytes) return MLA_ERR_NULL;
+  if (batch < 0 || q_len < 0 || n_heads < 0 || max_seqlen < 0 || page <= 0) return MLA_ERR_SHAPE;
+  if (!is_value_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (kv_rank != mla::kKvRank || page % 16) return MLA_ERR_UNSUPPORTED;
+  *bytes = 0;
+  if (batch == 0 || q_len == 0 || n_heads == 0) return MLA_OK;
+  mla::DecodePlan plan;
+  if (mla::plan_decode(batch, q_len, n_heads, 64, max_seqlen, dtype == MLA_F32, &plan))
+    return MLA_ERR_UNSUPPORTED;
+  *bytes = plan.workspace_bytes;
+  return MLA_OK;
+}
+
+int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
+                      const mla_tensor* block_table, const mla_tensor* seqlens,
+                      int64_t max_seqlen, float softmax_scale, int32_t causal,
+                      const mla_tensor* out, const mla_tensor* lse, void* workspace,
+                      size_t workspace_bytes, mla_stream stream) {
+  int rc;
+  if ((rc = check_desc(q, 4)) || (rc = check_desc(kv_cache, 3)) ||
+      (rc = check_desc(block_table, 2)) || (rc = check_desc(seqlens, 1)) ||
+      (rc = check_desc(out, 4)))
+    return rc;
+  if (lse && (rc = check_desc(lse, 3))) return rc;
+  const int32_t dt = q->dtype;
+  if (!is_value_dtype(dt) || kv_cache->dtype != dt || out->dtype != dt) return MLA_ERR_DTYPE;
+  if (block_table->dtype != MLA_I32 || seqlens->dtype != MLA_I32) return MLA_ERR_DTYPE;
+  if (lse && lse->dtype != MLA_F32) return MLA_ERR_DTYPE;
+  const int64_t B = q->shape[0], Sq = q->shape[1], N = q->shape[2], E = q->shape[3];
+  const int64_t L = out->shape[3];
+  if (out->shape[0] != B || out->shape[1] != Sq || out->shape[2] != N) return MLA_ERR_SHAPE;
+  if (kv_cache->shape[2] != E) return MLA_ERR_SHAPE;
+  if (block_table->shape[0] != B || seqlens->shape[0] != B) return MLA_ERR_SHAPE;
+  if (lse && (lse->shape[0] != B || lse->shape[1] != Sq || lse->shape[2] != N)) return MLA_ERR_SHAPE;
+  if (max_seqlen < 0) return MLA_ERR_SHAPE;
+  const int64_t R = E - L;
+  const int64_t PG = kv_cache->shape[1], NB = kv_cache->shape[0], MB = block_table->shape[1];
+  if (L != mla::kKvRank || (R != 0 && R != 64)) return MLA_ERR_UNSUPPORTED;
+  if (PG <= 0 || PG % 16) return MLA_ERR_UNSUPPORTED;
+  if (!rows_aligned16(q) || !rows_aligned16(kv_cache) || !rows_aligned16(out))
+    return MLA_ERR_UNSUPPORTED;
+  if (max_seqlen > INT32_MAX || B > INT32_MAX || Sq * N > INT32_MAX || PG > INT32_MAX ||
+      MB > INT32_MAX)
+    return MLA_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0 || N == 0) return MLA_OK;
+  mla::DecodePlan plan;
+  if (mla::plan_decode(B, Sq, N, R, max_seqlen, dt == MLA_F32, &plan)) return MLA_ERR_UNSUPPORTED;
+  if (plan.workspace_bytes > 0) {
+    if (!workspace) return MLA_ERR_WORKSPACE;
+    if (workspace_bytes < plan.workspace_bytes) return MLA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace % 16) return MLA_ERR_WORKSPACE;
+  }
+  if (NB == 0) {
+    // an empty pool can only serve empty sequences; the kernel never reads it
+  }
+  mla::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q->data; p.q_s0 = q->stride[0]; p.q_s1 = q->stride[1]; p.q_s2 = q->stride[2];
+  p.kv = kv_cache->data; p.kv_s0 = kv_cache->stride[0]; p.kv_s1 = kv_cache->stride[1];
+  p.num_blocks = NB > 0 ? NB : 1;
+  p.page = (int)PG;
+  p.block_table = (const int32_t*)block_table->data; p.bt_s0 = block_table->stride[0];
+  p.max_blocks = (int)MB;
+  p.seqlens = (const int32_t*)seqlens->data;
+  p.batch = (int)B; p.q_len = (int)Sq; p.n_heads = (int)N;
+  int64_t cap = MB * PG;
+  if (NB == 0) cap = 0;
+  p.seq_cap = (int)(max_seqlen < cap ? max_seqlen : cap);
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.causal = causal ? 1 : 0;
+  p.out = out->data; p.o_s0 = out->stride[0]; p.o_s1 = out->stride[1]; p.o_s2 = out->stride[2];
+  if (lse) {
+    p.lse = (float*)lse->data; p.l_s0 = lse->stride[0]; p.l_s1 = lse->stride[1]; p.l_s2 = lse->stride[2];
+  }
+  if (plan.split) {
+    const int64_t slots = (int64_t)plan.grid + plan.num_units;
+    p.part_o = (float*)workspace;
+    p.part_lse = (float*)((char*)workspace + (size_t)slots * plan.rows_per_unit * mla::kKvRank * 4);
+  }
+  p.rows_per_unit = plan.rows_per_unit;
+  p.row_tiles = plan.row_tiles;
+  p.num_units = plan.num_units;
+  p.split = plan.split;
+  p.grid = plan.grid;
+  return launched(mla::launch_decode(plan, p, R, dt == MLA_F32, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// mla_kernels.h -- internal interface between the C-ABI layer (mla_abi.cpp)
+// and the kernel translation units. Plain structs of pointers and sizes; the
+// launchers enqueue on the given stream and return the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kKvRank = 512;     // latent width L the attention kernels implement
+constexpr int kWorkBlock = 64;   // split-plan granularity, tokens
+constexpr int kSplitUnits = 256; // fewer (sequence, row-tile) units than this => split KV
+constexpr int kMaxUnitsSplit = 1024;
+
+// ------------------------------------------------------------ cache write
+struct CacheWriteParams {
+  const void* kv_c;  int64_t kv_c_s0;    // [T, L] row stride (elements)
+  const void* k_pe;  int64_t k_pe_s0;    // [T, R] (NULL when R == 0)
+  const void* slots; int slot_is_i64;    // [T]
+  void* cache;       int64_t cache_s0, cache_s1;  // [NB, PG, L+R]
+  int64_t num_blocks, page;
+  int64_t T, L, R;
+  int esize;         // 2 (bf16) or 4 (f32)
+  int vec16;         // 1 when every row start is 16-byte aligned and L, R are multiples of 16/esize
+};
+hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
+
+// ------------------------------------------------------------- batched matmul
+// out[t, h, n] = sum_k a[t, h, k] * w[h, k, n]  (+ optional bit copy of the
+// rope rows into out[t, h, Nout : Nout + R]).
+struct BmmParams {
+  const void* a; int64_t a_st, a_sh;        // a[t, h, k]: t stride, h stride (k stride 1)
+  const void* w; int64_t w_sh, w_sk;        // w[h, k, n]: h stride, k stride (n stride 1)
+  void* out;     int64_t o_st, o_sh;        // out[t, h, n]
+  const void* pe; int64_t pe_st, pe_sh;     // rope rows [t, h or broadcast, R] (pe_sh 0 = broadcast)
+  int64_t T, H, K, N, R;
+  int is_f32;
+};
+hipError_t launch_bmm(const BmmParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------ decode
+struct DecodeParams {
+  const void* q; int64_t q_s0, q_s1, q_s2;          // q [B, Sq, N, E]
+  const void* kv; int64_t kv_s0, kv_s1;              // cache [NB, PG, E]
+  int64_t num_blocks;
+  int page;
+  const int32_t* block_table; int64_t bt_s0; int max_blocks;
+  const int32_t* seqlens;
+  int batch, q_len, n_heads;
+  int seq_cap;            // min(max_seqlen, max_blocks * page)
+  float scale_log2;       // softmax_scale * log2(e)
+  int causal;
+  void* out; int64_t o_s0, o_s1, o_s2;              // out [B, Sq, N, L]
+  float* lse; int64_t l_s0, l_s1, l_s2;             // lse [B, Sq, N] or NULL
+  float* part_o;          // split partials [slots][rows_per_unit][L]
+  float* part_lse;        // [slots][rows_per_unit] (log2 domain)
+  int rows_per_unit;      // rows of (query, head) per unit
+  int row_tiles;          // units per sequence
+  int num_units;
+  int split;              // 1: split-KV over `grid` workgroups + merge
+  int grid;
+};
+
+// Launch plan chosen on the host from sizes alone (never from seqlens).
+struct DecodePlan {
+  int variant;        // kernel variant id
+  int rows_per_unit;
+  int row_tiles;
+  int num_units;
+  int split;
+  int grid;
+  size_t workspace_bytes;
+};
+int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int64_t max_seqlen,
+                int is_f32, DecodePlan* plan);
+hipError_t launch_decode(const DecodePlan& plan, DecodeParams p, int64_t rope, int is_f32,
+                         hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,199 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every entry point include/mla.h declares, and
+reject malformed arguments with the documented status before it touches any
+memory or launches anything (vllm.cpp "tests/vt/test_ops_mla_absorb.cpp":
+the batched matmul rejects inner-dim, batch and inner-stride mismatches). The
+descriptors below carry fake device addresses: on the error paths nothing may
+dereference them.
+"""
+import ctypes
+
+import pytest
+import torch
+
+import mla_absorbed_decode_amd as mla
+from mla_absorbed_decode_amd import MlaTensor
+
+OK, NULL, DTYPE, SHAPE, STRIDE, UNSUP, WS = 0, -1, -2, -3, -4, -5, -6
+BF16, F32, I32, I64 = 1, 2, 3, 4
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced on error paths
+
+
+def T(shape, dtype=BF16, strides=None, data=FAKE):
+    d = MlaTensor()
+    d.data = data
+    d.dtype = dtype
+    d.rank = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, strides)):
+        d.shape[i] = s
+        d.stride[i] = st
+    return d
+
+
+def R(d):
+    return ctypes.byref(d) if d is not None else None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mla.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = mla.header_symbols()
+    assert set(names) == {"mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
+                          "mla_decode_attend", "mla_v_up", "mla_status_str"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in mla.STATUS.items():
+        assert mla.mla_status_str(code).startswith(name)
+    assert "unknown" in mla.mla_status_str(12345)
+
+
+# ---------------------------------------------------------------- absorb_q
+
+
+def absorb(lib, q_nope, w, q_pe, out):
+    return lib.mla_absorb_q(R(q_nope), R(w), R(q_pe), R(out), None)
+
+
+def test_absorb_q_validation(lib):
+    good = dict(q_nope=T([4, 16, 128]), w=T([16, 128, 512]), q_pe=T([4, 16, 64]),
+                out=T([4, 16, 576]))
+    assert absorb(lib, None, good["w"], good["q_pe"], good["out"]) == NULL
+    assert absorb(lib, T([4, 16, 128], data=0), good["w"], good["q_pe"], good["out"]) == NULL
+    # inner-dim mismatch and head (batch) mismatch
+    assert absorb(lib, good["q_nope"], T([16, 100, 512]), good["q_pe"], good["out"]) == SHAPE
+    assert absorb(lib, good["q_nope"], T([8, 128, 512]), good["q_pe"], good["out"]) == SHAPE
+    # output width must be L + R; q_pe heads must be N or 1
+    assert absorb(lib, good["q_nope"], good["w"], good["q_pe"], T([4, 16, 512])) == SHAPE
+    assert absorb(lib, good["q_nope"], good["w"], T([4, 3, 64]), good["out"]) == SHAPE
+    # rank
+    assert absorb(lib, T([4, 16, 128, 1]), good["w"], good["q_pe"], good["out"]) == SHAPE
+    # innermost stride must be 1; strides must be non-negative
+    assert absorb(lib, T([4, 16, 128], strides=[4096, 256, 2]), good["w"], good["q_pe"],
+                  good["out"]) == STRIDE
+    assert absorb(lib, T([4, 16, 128], strides=[-2048, 128, 1]), good["w"], good["q_pe"],
+                  good["out"]) == STRIDE
+    # dtypes
+    assert absorb(lib, T([4, 16, 128], F32), good["w"], good["q_pe"], good["out"]) == DTYPE
+    assert absorb(lib, T([4, 16, 128], I32), T([16, 128, 512], I32), None,
+                  T([4, 16, 512], I32)) == DTYPE
+
+
+def test_absorb_q_empty_batch_is_a_no_op(lib):
+    # T == 0 launches nothing, so it is safe without a device
+    assert absorb(lib, T([0, 16, 128]), T([16, 128, 512]), T([0, 16, 64]),
+                  T([0, 16, 576])) == OK
+
+
+def test_v_up_validation(lib):
+    f = lambda o, w, out: lib.mla_v_up(R(o), R(w), R(out), None)
+    assert f(T([4, 16, 512]), T([16, 512, 128]), T([4, 16, 64])) == SHAPE
+    assert f(T([4, 16, 512]), T([16, 256, 128]), T([4, 16, 128])) == SHAPE
+    assert f(T([4, 16, 512]), T([16, 512, 128], F32), T([4, 16, 128])) == DTYPE
+    assert f(T([4, 16, 512], strides=[8192, 512, 3]), T([16, 512, 128]), T([4, 16, 128])) == STRIDE
+    assert f(T([0, 16, 512]), T([16, 512, 128]), T([0, 16, 128])) == OK
+
+
+# ------------------------------------------------------------ cache write
+
+
+def test_concat_and_cache_validation(lib):
+    f = lambda kv, pe, sl, c: lib.mla_concat_and_cache(R(kv), R(pe), R(sl), R(c), None)
+    kv, pe, sl, cache = T([200, 512]), T([200, 64]), T([200], I64), T([32, 64, 576])
+    assert f(kv, pe, sl, T([32, 64, 512])) == SHAPE   # entry must be L + R
+    assert f(kv, pe, T([199], I64), cache) == SHAPE
+    assert f(kv, T([100, 64]), sl, cache) == SHAPE
+    assert f(kv, pe, T([200], F32), cache) == DTYPE   # slot mapping must be integer
+    assert f(kv, pe, sl, T([32, 64, 576], F32)) == DTYPE
+    assert f(None, pe, sl, cache) == NULL
+    assert f(kv, pe, sl, T([32, 64, 576], strides=[110592, 576, 2])) == STRIDE
+    assert f(T([0, 512]), T([0, 64]), T([0], I64), cache) == OK
+
+
+# ------------------------------------------------------------------ decode
+
+
+def ws_size(lib, B, Sq, N, L, S, PG, dt=BF16):
+    n = ctypes.c_size_t(0)
+    rc = lib.mla_decode_workspace_size(B, Sq, N, L, S, PG, dt, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size(lib):
+    rc, n = ws_size(lib, 64, 1, 16, 512, 4096, 64)
+    assert rc == OK and n > 0          # few units: split KV, partials needed
+    rc, n2 = ws_size(lib, 64, 1, 16, 512, 4096, 64)
+    assert n2 == n                     # depends on the arguments only
+    rc, n = ws_size(lib, 1, 2048, 64, 512, 2048, 64)
+    assert rc == OK and n == 0         # many prefill units: one workgroup each, no partials
+    assert ws_size(lib, 4, 1, 128, 256, 4096, 64)[0] == UNSUP
+    assert ws_size(lib, 4, 1, 128, 512, 4096, 8)[0] == UNSUP
+    assert ws_size(lib, 4, 1, 128, 512, 4096, 64, I32)[0] == DTYPE
+    assert lib.mla_decode_workspace_size(4, 1, 128, 512, 4096, 64, BF16, None) == NULL
+    assert ws_size(lib, 0, 1, 16, 512, 4096, 64) == (OK, 0)
+
+
+def decode(lib, q, kv, bt, sl, out, lse=None, max_seqlen=128, ws=None, ws_bytes=0, causal=1):
+    return lib.mla_decode_attend(R(q), R(kv), R(bt), R(sl), max_seqlen, ctypes.c_float(0.04),
+                                 causal, R(out), R(lse), ws, ws_bytes, None)
+
+
+def test_decode_validation(lib):
+    B, N = 2, 16
+    q, kv, bt, sl = T([B, 1, N, 576]), T([8, 64, 576]), T([B, 4], I32), T([B], I32)
+    out, lse = T([B, 1, N, 512]), T([B, 1, N], F32)
+    rc, need = ws_size(lib, B, 1, N, 512, 128, 64)
+    assert rc == OK and need > 0
+    # missing or short workspace
+    assert decode(lib, q, kv, bt, sl, out, lse) == WS
+    assert decode(lib, q, kv, bt, sl, out, lse, ws=FAKE, ws_bytes=need - 1) == WS
+    assert decode(lib, q, kv, bt, sl, out, lse, ws=FAKE + 4, ws_bytes=need) == WS
+    # unsupported geometry
+    assert decode(lib, T([B, 1, N, 288]), T([8, 64, 288]), bt, sl, T([B, 1, N, 256])) == UNSUP
+    assert decode(lib, T([B, 1, N, 544]), T([8, 64, 544]), bt, sl, out) == UNSUP   # rope 32
+    assert decode(lib, q, T([8, 8, 576]), bt, sl, out) == UNSUP                    # page 8
+    assert decode(lib, T([B, 1, N, 576], data=FAKE + 2), kv, bt, sl, out) == UNSUP  # misaligned
+    assert decode(lib, q, T([8, 64, 576], strides=[36868, 576, 1]), bt, sl, out) == UNSUP
+    # shapes and dtypes
+    assert decode(lib, q, T([8, 64, 512]), bt, sl, out) == SHAPE
+    assert decode(lib, q, kv, T([3, 4], I32), sl, out) == SHAPE
+    assert decode(lib, q, kv, bt, T([3], I32), out) == SHAPE
+    assert decode(lib, q, kv, bt, sl, out, T([B, 1, 8], F32)) == SHAPE
+    assert decode(lib, q, kv, T([B, 4], I64), sl, out) == DTYPE
+    assert decode(lib, q, kv, bt, sl, out, T([B, 1, N], BF16)) == DTYPE
+    assert decode(lib, q, T([8, 64, 576], F32), bt, sl, out) == DTYPE
+    assert decode(lib, q, kv, bt, sl, out, max_seqlen=-1) == SHAPE
+    assert decode(lib, None, kv, bt, sl, out) == NULL
+    # empty batch: nothing to do
+    assert decode(lib, T([0, 1, N, 576]), kv, T([0, 4], I32), T([0], I32), T([0, 1, N, 512])) == OK
+
+
+# ----------------------------------------------------------- python layer
+
+
+def test_binding_refuses_host_tensors():
+    a = torch.zeros(4, 16, 128, dtype=torch.bfloat16)
+    w = torch.zeros(16, 128, 512, dtype=torch.bfloat16)
+    out = torch.zeros(4, 16, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mla.mla_absorb_q(a, w, None, out)
+
+
+def test_binding_descriptor_matches_view():
+    big = torch.zeros(32, 3 * 64 * 576, dtype=torch.bfloat16)
+    view = torch.as_strided(big, (32, 64, 576), (3 * 64 * 576, 576, 1), 64 * 576)
+    d = mla.desc(view)
+    assert d.rank == 3 and list(d.shape[:3]) == [32, 64, 576]
+    assert list(d.stride[:3]) == [110592, 576, 1]
+    assert d.data == big.data_ptr() + 64 * 576 * 2  # storage offset folded into the pointer
