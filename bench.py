@@ -1,0 +1,324 @@
+"""Benchmark of one absorbed-MLA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-v3]
+
+A step is one pass of the whole hot path over one batch of the V2-Lite decode
+workload (16 heads, kv_rank 512 + rope 64, batch 64, seqlens uniform on
+[512, 4096], 64-token pages, random block table, bf16, values N(0, 0.1^2)):
+
+  1. mla_absorb_q          q_nope [64,16,128] x W_UK_T [16,128,512] -> q[..., :512], q_pe -> q[..., 512:]
+  2. mla_concat_and_cache  each sequence's newest [c_kv | k_pe] row into its page
+  3. mla_decode_attend     split-KV attention over the paged latent cache + log-sum-exp merge
+  4. mla_v_up              o_lat [64,16,512] x W_UV [16,512,128]
+
+Inputs are resident in HBM before timing. The latent cache is held in enough
+copies (rotated per step) that the step's working set exceeds twice the
+256 MB last-level cache, so the cache read is an HBM read. Each step is
+captured once per cache copy as a HIP graph (as a serving decode loop runs
+it) and the graphs are replayed in turn: W warm-up steps, then K timed steps
+between device synchronisations; one JSON line is printed.
+
+value = latent-KV bytes the step must read (sum of seqlens x 576 x 2 B) per
+second of step time. The roofline object covers the attention call (its
+partial and merge kernels): graphs holding only that call are replayed K times
+right after the steps and timed with HIP events on the stream they run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mla_absorbed_decode_amd as mla  # noqa: E402
+import mla_inputs as mi  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+LLC_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SRC = os.path.join(ROOT, "mla_absorbed_decode_amd", "csrc", "decode.hip")
+
+
+def src_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class Step:
+    """Device-resident inputs of one decode step and the four calls."""
+
+    def __init__(self, case: mi.DecodeCase, seed: int, copies: int, dev):
+        d = case.dims
+        self.case = case
+        B, N = case.batch, d.n_head
+        bf = torch.bfloat16
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(bf).to(dev)
+        # query-side activations, new latent rows, weights: N(0, 0.1^2)
+        self.q_nope = t(mi.normal(seed, 50, (B, N, d.d_nope), 0.1, "bf16"))
+        self.q_pe = t(mi.normal(seed, 51, (B, N, d.d_rope), 0.1, "bf16"))
+        self.kv_new = t(mi.normal(seed, 52, (B, d.kv_rank), 0.1, "bf16"))
+        self.pe_new = t(mi.normal(seed, 53, (B, d.d_rope), 0.1, "bf16"))
+        self.w_uk_t = t(mi.normal(seed, 54, (N, d.d_nope, d.kv_rank), 0.1, "bf16"))
+        self.w_uv = t(mi.normal(seed, 55, (N, d.kv_rank, d.d_v), 0.1, "bf16"))
+        # the newest token of sequence b sits at position seqlen_b - 1
+        s = case.seqlens.astype(np.int64)
+        bt = case.block_table
+        slots = np.array([bt[b, (s[b] - 1) // case.page] * case.page + (s[b] - 1) % case.page
+                          for b in range(B)], dtype=np.int64)
+        self.slots = torch.from_numpy(slots).to(dev)
+        base = t(case.pool)
+        self.caches = [base] + [base.clone() for _ in range(copies - 1)]
+        self.bt = torch.from_numpy(bt).to(dev)
+        self.seqlens = torch.from_numpy(case.seqlens).to(dev)
+        self.q = torch.empty(B, 1, N, d.entry, dtype=bf, device=dev)
+        self.o_lat = torch.empty(B, 1, N, d.kv_rank, dtype=bf, device=dev)
+        self.lse = torch.empty(B, 1, N, dtype=torch.float32, device=dev)
+        self.out = torch.empty(B, N, d.d_v, dtype=bf, device=dev)
+        nbytes = mla.mla_decode_workspace_size(B, 1, N, d.kv_rank, case.max_seqlen, case.page, bf)
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        self.max_seqlen = case.max_seqlen
+
+    def attend(self, i: int):
+        c = self.caches[i % len(self.caches)]
+        mla.mla_decode_attend(self.q, c, self.bt, self.seqlens, self.max_seqlen, self.case.scale,
+                              True, self.o_lat, self.lse, workspace=self.ws)
+
+    def run(self, i: int):
+        c = self.caches[i % len(self.caches)]
+        mla.mla_absorb_q(self.q_nope, self.w_uk_t, self.q_pe, self.q[:, 0])
+        mla.mla_concat_and_cache(self.kv_new, self.pe_new, self.slots, c)
+        self.attend(i)
+        mla.mla_v_up(self.o_lat[:, 0], self.w_uv, self.out)
+
+
+def capture(fn, n: int):
+    """One HIP graph per cache copy, each holding fn(i)."""
+    graphs = []
+    for i in range(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def replay(graphs, first: int, count: int):
+    """Replay `count` graphs round-robin between two events; returns elapsed ms."""
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(first, first + count):
+        graphs[i % len(graphs)].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
+def time_steps(step: Step, steps: int, warmup: int):
+    """(ms for `steps` whole steps, host seconds for them, ms per attention call)."""
+    n = len(step.caches)
+    for i in range(n):  # eager pass: one-time kernel attributes are set outside capture
+        step.run(i)
+    torch.cuda.synchronize()
+    step_graphs = capture(step.run, n)
+    attn_graphs = capture(step.attend, n)
+    if warmup:
+        replay(step_graphs, 0, warmup)
+    wall0 = time.perf_counter()
+    total_ms = replay(step_graphs, warmup, steps)
+    wall = time.perf_counter() - wall0
+    attn_ms = replay(attn_graphs, warmup, steps) / steps
+    return total_ms, wall, attn_ms
+
+
+def attention_bytes(case: mi.DecodeCase) -> int:
+    """Algorithmic bytes of one attention call: every visible latent row once,
+    plus q, out and lse."""
+    d = case.dims
+    kv = int(case.seqlens.astype(np.int64).sum()) * d.entry * 2
+    rows = case.batch * case.q_len * d.n_head
+    return kv + rows * (d.entry * 2 + d.kv_rank * 2 + 4)
+
+
+def attention_flops(case: mi.DecodeCase) -> int:
+    d = case.dims
+    pairs = int(case.seqlens.astype(np.int64).sum()) * d.n_head * case.q_len
+    return pairs * 2 * (d.entry + d.kv_rank)
+
+
+def pmc_traffic(kernel_key: str, launches_per_call: int = 1):
+    """HBM bytes per attention call from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{kernel_key}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("decode_src_sha") != src_sha(DECODE_SRC):
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def cpu_baseline(case: mi.DecodeCase, step: Step, budget_s: float = 10.0):
+    """The double-precision oracle on the host: fold, paged attention and
+    un-projection of the full batch, repeated until ~budget_s of CPU work."""
+    import oracle
+
+    f64 = lambda x: np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    q_nope = f64(step.q_nope.float().cpu().numpy())
+    w_uk_t = f64(step.w_uk_t.float().cpu().numpy())
+    w_uv = f64(step.w_uv.float().cpu().numpy())
+    q_pe = f64(step.q_pe.float().cpu().numpy())
+    pool = f64(case.pool)
+    bt, sl = case.block_table, case.seqlens
+    reps, t_used = 0, 0.0
+    while t_used < budget_s and reps < 100:
+        t0 = time.perf_counter()
+        q_lat = oracle.fold_q(q_nope, w_uk_t)
+        q = np.concatenate([q_lat, q_pe], axis=2)[:, None]
+        o_lat, _ = oracle.attend_paged(q, pool, bt, sl, case.scale, True, case.dims.kv_rank)
+        oracle.v_up(o_lat[:, 0], w_uv)
+        t_used += time.perf_counter() - t0
+        reps += 1
+    kv_bytes = int(sl.astype(np.int64).sum()) * case.dims.entry * 2
+    return {
+        "value": round(reps * kv_bytes / t_used / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"full V2-Lite batch (64 sequences, {int(sl.sum())} latent rows) x {reps} "
+                  f"repetitions in {t_used:.1f} s: fold, paged attention, un-projection in fp64 "
+                  "(the 64-row cache write is omitted)",
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def v3_secondary(dev, steps: int, warmup: int):
+    """128-head V3 decode (B=4 x 4096, block-major view): attention call only."""
+    c = mi.v3_decode(seed=0, neighbour_fill=0.0)
+    d = c.dims
+    bf = torch.bfloat16
+    q = torch.from_numpy(c.q).to(bf).to(dev)
+    copies = max(1, math.ceil(2 * LLC_BYTES / (c.pool.nbytes // 2 * 3)))
+    unis = [torch.from_numpy(c.unified()).to(bf).to(dev)]
+    unis += [unis[0].clone() for _ in range(copies - 1)]
+    views = [u[:, 1] for u in unis]
+    bt = torch.from_numpy(c.block_table).to(dev)
+    sl = torch.from_numpy(c.seqlens).to(dev)
+    out = torch.empty(c.batch, 1, d.n_head, d.kv_rank, dtype=bf, device=dev)
+    lse = torch.empty(c.batch, 1, d.n_head, dtype=torch.float32, device=dev)
+    nbytes = mla.mla_decode_workspace_size(c.batch, 1, d.n_head, d.kv_rank, c.max_seqlen,
+                                           c.page, bf)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    run = lambda i: mla.mla_decode_attend(q, views[i % len(views)], bt, sl, c.max_seqlen,
+                                          c.scale, True, out, lse, workspace=ws)
+    for i in range(len(views)):
+        run(i)
+    torch.cuda.synchronize()
+    graphs = capture(run, len(views))
+    if warmup:
+        replay(graphs, 0, warmup)
+    ms = replay(graphs, warmup, steps) / steps
+    byts, flops = attention_bytes(c), attention_flops(c)
+    return {
+        "workload": "V3 decode bf16: 128 heads, entry 576 / v 512, batch 4 x 4096, 64-token "
+                    "pages, middle layer of a 3-layer block-major cache",
+        "attention_us": round(ms * 1e3, 2),
+        "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-v3", action="store_true", help="skip the 128-head secondary line")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this implementation runs on a single MI355X and has "
+              "no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    mla.load()
+
+    case = mi.v2lite_decode(seed=0)
+    touched = int(case.seqlens.astype(np.int64).sum()) * case.dims.entry * 2
+    copies = max(2, math.ceil(2 * LLC_BYTES / touched) + 1)
+    step = Step(case, seed=0, copies=copies, dev=dev)
+    print(f"# V2-Lite decode: B={case.batch} sum(seqlens)={int(case.seqlens.sum())} "
+          f"KV {touched / 1e6:.1f} MB, {copies} cache copies", file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    total_ms, wall, attn_avg_ms = time_steps(step, args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    kv_gbs = touched / (ms_per_step * 1e-3) / 1e9
+    pairs = int(case.seqlens.astype(np.int64).sum()) * case.dims.n_head
+    a_bytes = attention_bytes(case)
+    achieved = a_bytes / (attn_avg_ms * 1e-3) / 1e9
+    roof = {
+        "bound": "hbm",
+        "kernel": "mla_decode_attend (decode_partial + decode_merge)",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": pmc_traffic("decode_v2lite"),
+        "algorithmic_bytes": a_bytes,
+        "avg_us": round(attn_avg_ms * 1e3, 2),
+    }
+    line = {
+        "metric": "MLA decode: latent-KV GB/s + query-heads·tokens/s; % HBM/MFMA roofline",
+        "value": round(kv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "V2-Lite decode bf16: 16 heads, kv_rank 512 + rope 64, W_UK_T [16,128,512], "
+                        "W_UV [16,512,128], batch 64, seqlens U[512,4096], 64-token pages, random "
+                        "block table, N(0,0.1^2)",
+            "global_batch": case.batch,
+            "seq_len": int(case.max_seqlen),
+            "sum_seqlens": int(case.seqlens.sum()),
+            "parallelism": "single GPU",
+        },
+        "query_heads_tokens_per_s": round(pairs / (ms_per_step * 1e-3), 1),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "roofline": roof,
+    }
+    if not args.no_v3:
+        line["v3_decode"] = v3_secondary(dev, max(10, args.steps // 2), args.warmup)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(case, step)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

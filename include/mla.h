@@ -158,15 +158,21 @@ int mla_decode_workspace_size(int64_t batch, int64_t q_len, int64_t n_heads, int
  *   kv_cache     [NB, PG, L + R]    same dtype; stride[0] any (block-major
  *                views allowed), stride[1] a multiple of 8 elements
  *   block_table  [B, MB]            MLA_I32, row stride any; only entries
- *                j < ceil(seqlens[b] / PG) are read. An entry outside
- *                [0, NB) makes that page contribute nothing.
+ *                j < ceil(seqlens[b] / PG) are read. Entries must lie in
+ *                [0, NB); one outside is clamped into that range, so every
+ *                read stays inside the cache, but the rows of that sequence
+ *                are then unspecified.
  *   seqlens      [B]                MLA_I32, contiguous, on the device; values
  *                are clamped to [0, min(max_seqlen, MB * PG)]
  *   max_seqlen   host upper bound of seqlens (sizes the launch; no D2H copy)
  *   out          [B, Sq, N, L]      same dtype as q, any strides (inner 1)
  *   lse          [B, Sq, N]         MLA_F32, any strides; or NULL
  *   workspace    device scratch of at least mla_decode_workspace_size()
- *                bytes (16-byte aligned); may be NULL when that size is 0
+ *                bytes (16-byte aligned); may be NULL when that size is 0.
+ *                Its contents need no initialisation and carry nothing from
+ *                one call to the next, so one buffer serves any sequence of
+ *                calls on one stream; calls that run concurrently need
+ *                separate workspaces.
  * Supported: L == 512; R == 0 or 64; PG a multiple of 16; L + R rows 16-byte
  * aligned (pointer and strides). The result depends only on the inputs'
  * values and sizes -- not on strides, pointers or the device -- so a

@@ -172,7 +172,8 @@ def mla_decode_workspace_size(batch, q_len, n_heads, kv_rank, max_seqlen, page, 
 def mla_decode_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal, out,
                       lse=None, workspace=None):
     """Paged absorbed attention; writes out [B,Sq,N,L] and (optionally) lse [B,Sq,N].
-    ``workspace`` (uint8 device tensor) is allocated here when not given."""
+    ``workspace`` (uint8 device tensor of at least mla_decode_workspace_size()
+    bytes, reusable across calls) is allocated here when not given."""
     _device_check(q, kv_cache, block_table, seqlens, out, lse, workspace)
     lib = load()
     if workspace is None:

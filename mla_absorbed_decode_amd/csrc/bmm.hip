@@ -8,12 +8,15 @@
 // optionally followed (absorb_q) by the bit copy of the rope rows
 //   out[t, h, N + r] = pe[t, h or 0, r].
 //
-// bf16: a 64 (tokens) x 64 (outputs) tile per workgroup of 4 waves, K in steps
-// of 32. The weight tile is streamed global->LDS (two buffers); each wave
-// reads its token rows of `a` straight from memory as the MFMA A operand and
-// the weight tile with ds_read_b64_tr_b16, which turns the n-contiguous weight
-// rows into the k-contiguous B operand of v_mfma_f32_16x16x32_bf16. fp32 uses
-// v_mfma_f32_16x16x4_f32 on the same tiling (one element per lane, no
+// bf16: a 64 (tokens) x TN (outputs) tile per workgroup of 4 waves. The
+// workgroup's whole K x TN weight slab (up to 512 rows of K at a time) is
+// staged global->LDS in one burst, and each wave holds its 16 token rows of
+// `a` for all those k-steps in registers, so the tile costs one memory round
+// trip rather than one per k-step. The slab is read with ds_read_b64_tr_b16,
+// which turns the n-contiguous weight rows into the k-contiguous B operand of
+// v_mfma_f32_16x16x32_bf16. TN is 64, or 16 when 64-wide tiles would leave
+// the chip mostly idle (few heads x few outputs). fp32 uses
+// v_mfma_f32_16x16x4_f32 on a 64 x 64 tiling (one element per lane, no
 // transpose needed). Sizes the MFMA tiling does not cover (K not a multiple of
 // 32, N not a multiple of 16) take a plain one-thread-per-output kernel.
 #include "mla_device.h"
@@ -26,11 +29,43 @@ constexpr int kTM = 64, kTN = 64, kKB = 32;
 
 __device__ __forceinline__ int wswz(int r) { return 2 * (r & 3); }  // bf16 weight-tile chunk swizzle
 
+// out[t, h, N + r] = pe[t, h', r] for the tile's tokens (a bit copy), shared by
+// the workgroups of one (token tile, head): 16-byte pieces when the rows allow
+// it, all of a thread's loads issued before its stores.
 template <class T>
 __device__ __forceinline__ void copy_rope(const BmmParams& p, int t0, int h) {
-  // out[t, h, N + r] = pe[t, h', r] for the tile's tokens (bit copy)
   const int nt = (int)(p.T - t0 < kTM ? p.T - t0 : kTM);
-  for (int e = threadIdx.x; e < nt * p.R; e += blockDim.x) {
+  const int nwg = (int)gridDim.x, tid = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int stride = nwg * (int)blockDim.x;
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte piece
+  const bool vec = p.R % V == 0 && ((uintptr_t)p.pe % 16 == 0) && ((uintptr_t)p.out % 16 == 0) &&
+                   (p.pe_st % V == 0) && (p.pe_sh % V == 0) && (p.o_st % V == 0) &&
+                   (p.o_sh % V == 0) && ((p.N) % V == 0);
+  if (vec) {
+    const int per_row = (int)p.R / V, total = nt * per_row;
+    constexpr int U = 4;
+    for (int e0 = tid; e0 < total; e0 += U * stride) {
+      u32x4_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * stride;
+        if (e < total) {
+          const int t = t0 + e / per_row, r = (e % per_row) * V;
+          v[u] = *(const u32x4_t*)((const T*)p.pe + (int64_t)t * p.pe_st + (int64_t)h * p.pe_sh + r);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * stride;
+        if (e < total) {
+          const int t = t0 + e / per_row, r = (e % per_row) * V;
+          *(u32x4_t*)((T*)p.out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + p.N + r) = v[u];
+        }
+      }
+    }
+    return;
+  }
+  for (int e = tid; e < nt * p.R; e += stride) {
     const int t = t0 + e / (int)p.R, r = e % (int)p.R;
     const T* src = (const T*)p.pe + (int64_t)t * p.pe_st + (int64_t)h * p.pe_sh + r;
     T* dst = (T*)p.out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + p.N + r;
@@ -38,49 +73,82 @@ __device__ __forceinline__ void copy_rope(const BmmParams& p, int t0, int h) {
   }
 }
 
+constexpr int kSlabK = 512;  // weight rows staged per round trip
+
+// LDS position of weight-slab row r and 16-byte chunk c (CW chunks per row).
+// 128-byte rows: chunks are XOR-swizzled by 2*(r%4), so the four rows one
+// transposed read touches fall in different banks. 32-byte rows: rows 8-11
+// and 12-15 of every 16 trade places, so the four lane groups of a read
+// (rows 8g..8g+3) alternate between the two halves of the banks.
+template <int CW>
+__device__ __forceinline__ int slab_off(int r, int c) {
+  if constexpr (CW == 8) return r * 128 + ((c ^ wswz(r)) << 4);
+  else return (r ^ (((r >> 3) & 1) << 2)) * (CW * 16) + (c << 4);
+}
+
+template <int TN>
 __global__ void __launch_bounds__(256) bmm_bf16_mfma(BmmParams p) {
-  __shared__ __attribute__((aligned(16))) char wt[2][kKB * kTN * 2];
+  extern __shared__ __attribute__((aligned(1024))) char slab_raw[];
+  constexpr int CW = TN / 8;     // 16-byte chunks per weight row
+  constexpr int NT = TN / 16;    // 16-column MFMA tiles
+  constexpr int KS = kSlabK / kKB;
+  MLA_LDS char* slab = (MLA_LDS char*)slab_raw;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
-  const int n0 = blockIdx.x * kTN, t0 = blockIdx.y * kTM, h = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(w);
+  const int n0 = blockIdx.x * TN, t0 = blockIdx.y * kTM, h = blockIdx.z;
   const uint16_t* W = (const uint16_t*)p.w + (int64_t)h * p.w_sh;
-  // this thread's 16-byte slot of the LDS weight tile: row wr, position wpos
-  const int wr = threadIdx.x >> 3, wpos = threadIdx.x & 7;
-  int wcol = n0 + 8 * (wpos ^ wswz(wr));
-  if (wcol + 8 > p.N) wcol = (int)p.N - 8;  // columns past N are never stored
   const int t = t0 + 16 * w + li;
   const bool tvalid = t < p.T;
   const uint16_t* arow = (const uint16_t*)p.a + (int64_t)(tvalid ? t : 0) * p.a_st +
                          (int64_t)h * p.a_sh + 8 * g;
-  const int nk = (int)(p.K / kKB);
-  f32x4_t acc[4];
+  f32x4_t acc[NT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  i16x8_t av = tvalid ? *(const i16x8_t*)arow : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-  load_lds_16(W + (int64_t)wr * p.w_sk + wcol, (MLA_LDS char*)&wt[0][w * 1024]);
-  for (int kb = 0; kb < nk; ++kb) {
-    wait_vmcnt<0>();
-    __syncthreads();  // tile kb visible to every wave; all waves are done with kb-1
-    const i16x8_t acur = av;
-    if (kb + 1 < nk) {
-      av = tvalid ? *(const i16x8_t*)(arow + (kb + 1) * kKB) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      load_lds_16(W + (int64_t)((kb + 1) * kKB + wr) * p.w_sk + wcol,
-                  (MLA_LDS char*)&wt[(kb + 1) & 1][w * 1024]);
+  for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < p.K; k0 += kSlabK) {
+    const int kc = p.K - k0 < kSlabK ? (int)(p.K - k0) : kSlabK;  // a multiple of 32
+    if (k0 > 0) __syncthreads();  // every wave is done with the previous slab
+    // stage rows k0 .. k0 + kc: LDS chunk q = inst * 64 + lane holds row q / CW at
+    // chunk position q % CW; that position's source chunk is found by inverting slab_off
+    const int ninst = kc * CW / 64;
+    for (int inst = wave; inst < ninst; inst += 4) {
+      const int q = inst * 64 + lane;
+      const int rp = q / CW, cp = q % CW;
+      int r, c;
+      if constexpr (CW == 8) {
+        r = rp;
+        c = cp ^ wswz(rp);
+      } else {
+        r = rp ^ (((rp >> 3) & 1) << 2);
+        c = cp;
+      }
+      int col = n0 + 8 * c;
+      if (col + 8 > p.N) col = (int)p.N - 8;  // columns past N are never stored
+      load_lds_16(W + (int64_t)(k0 + r) * p.w_sk + col, slab + inst * 1024);
     }
-    const MLA_LDS char* tile = (const MLA_LDS char*)wt[kb & 1];
-    const int rlo = 8 * g + (li >> 2), rhi = rlo + 4;
+    i16x8_t av[KS];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int c = 2 * nt + ((li & 3) >> 1);
-      const i16x4_t b0 = lds_read_tr16(tile + rlo * 128 + ((c ^ wswz(rlo)) << 4) + (li & 1) * 8);
-      const i16x4_t b1 = lds_read_tr16(tile + rhi * 128 + ((c ^ wswz(rhi)) << 4) + (li & 1) * 8);
-      const i16x8_t bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-      acc[nt] = mfma_16x16x32(acur, bv, acc[nt]);
+    for (int ks = 0; ks < KS; ++ks)
+      if (ks * kKB < kc)
+        av[ks] = tvalid ? *(const i16x8_t*)(arow + k0 + ks * kKB) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks * kKB >= kc) break;
+      const int rlo = ks * kKB + 8 * g + (li >> 2), rhi = rlo + 4;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int c = 2 * nt + ((li & 3) >> 1);
+        const i16x4_t b0 = lds_read_tr16(slab + slab_off<CW>(rlo, c) + (li & 1) * 8);
+        const i16x4_t b1 = lds_read_tr16(slab + slab_off<CW>(rhi, c) + (li & 1) * 8);
+        const i16x8_t bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        acc[nt] = mfma_16x16x32(av[ks], bv, acc[nt]);
+      }
     }
   }
   // lane holds out[t0 + 16w + 4g + j][n0 + 16nt + li]
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const int n = n0 + 16 * nt + li;
     if (n >= p.N) continue;
 #pragma unroll
@@ -90,7 +158,7 @@ __global__ void __launch_bounds__(256) bmm_bf16_mfma(BmmParams p) {
         ((uint16_t*)p.out)[(int64_t)tt * p.o_st + (int64_t)h * p.o_sh + n] = f32_to_bf16(acc[nt][j]);
     }
   }
-  if (p.R > 0 && blockIdx.x == 0) copy_rope<uint16_t>(p, t0, h);
+  if (p.R > 0) copy_rope<uint16_t>(p, t0, h);
 }
 
 __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
@@ -151,7 +219,7 @@ __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
       if (tt < p.T) ((float*)p.out)[(int64_t)tt * p.o_st + (int64_t)h * p.o_sh + n] = acc[nt][j];
     }
   }
-  if (p.R > 0 && blockIdx.x == 0) copy_rope<uint32_t>(p, t0, h);
+  if (p.R > 0) copy_rope<uint32_t>(p, t0, h);
 }
 
 // Any sizes: one thread per output element, fp32 accumulation in k order.
@@ -199,10 +267,30 @@ hipError_t launch_bmm(const BmmParams& p, hipStream_t s) {
       ((uintptr_t)p.a % 16 == 0) && ((uintptr_t)p.w % 16 == 0) && (p.a_st * es % 16 == 0) &&
       (p.a_sh * es % 16 == 0) && (p.w_sh * es % 16 == 0) && (p.w_sk * es % 16 == 0);
   const bool mfma_ok = aligned && p.K % kKB == 0 && p.N % 16 == 0 && p.N >= 16;
-  if (mfma_ok) {
+  if (mfma_ok && p.is_f32) {
     dim3 grid((unsigned)((p.N + kTN - 1) / kTN), (unsigned)((p.T + kTM - 1) / kTM), (unsigned)p.H);
-    if (p.is_f32) hipLaunchKernelGGL(bmm_f32_mfma, grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(bmm_bf16_mfma, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(bmm_f32_mfma, grid, dim3(256), 0, s, p);
+  } else if (mfma_ok) {
+    // 64-wide tiles when they give the chip at least 128 workgroups
+    const int64_t tiles_t = (p.T + kTM - 1) / kTM;
+    const bool wide = p.N % 64 == 0 && (p.N / 64) * tiles_t * p.H >= 128;
+    const int tn = wide ? 64 : 16;
+    const int64_t kc = p.K < kSlabK ? p.K : kSlabK;
+    const size_t smem = (size_t)kc * tn * 2;
+    dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)tiles_t, (unsigned)p.H);
+    if (wide) {
+      static bool attr = false;
+      if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)bmm_bf16_mfma<64>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           kSlabK * 64 * 2);
+        if (e != hipSuccess) return e;
+        attr = true;
+      }
+      hipLaunchKernelGGL(bmm_bf16_mfma<64>, grid, dim3(256), smem, s, p);
+    } else {
+      hipLaunchKernelGGL(bmm_bf16_mfma<16>, grid, dim3(256), smem, s, p);
+    }
   } else {
     const int64_t total = p.T * p.H * p.N;
     const int64_t blocks = (total + 255) / 256 + (p.T * p.H * p.R + 255) / 256;

@@ -9,6 +9,8 @@
 // element when rows are not 16-byte aligned); a token whose slot is outside
 // [0, num_blocks * page) is skipped, and nothing but the addressed rows is
 // written, so neighbouring layers of a unified slot are never touched.
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -22,19 +24,16 @@ __global__ void __launch_bounds__(256) cache_write_kernel(CacheWriteParams p) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= p.T * cpr) return;
   const int64_t t = idx / cpr, c = idx % cpr;
+  // the row piece and the slot are independent loads: both go out before either is used
+  const char* src = c < cl ? (const char*)p.kv_c + t * p.kv_c_s0 * es + c * VEC
+                           : (const char*)p.k_pe + t * p.k_pe_s0 * es + (c - cl) * VEC;
+  typedef typename std::conditional<VEC == 16, u32x4_t,
+          typename std::conditional<VEC == 4, uint32_t, uint16_t>::type>::type V;
+  const V v = *(const V*)src;
   const int64_t slot = p.slot_is_i64 ? ((const int64_t*)p.slots)[t] : (int64_t)((const int32_t*)p.slots)[t];
   if (slot < 0 || slot >= p.num_blocks * p.page) return;
   const int64_t blk = slot / p.page, off = slot % p.page;
-  char* dst = (char*)p.cache + (blk * p.cache_s0 + off * p.cache_s1) * es + c * VEC;
-  const char* src = c < cl ? (const char*)p.kv_c + t * p.kv_c_s0 * es + c * VEC
-                           : (const char*)p.k_pe + t * p.k_pe_s0 * es + (c - cl) * VEC;
-  if constexpr (VEC == 16) {
-    *(u32x4_t*)dst = __builtin_nontemporal_load((const u32x4_t*)src);
-  } else if constexpr (VEC == 4) {
-    *(uint32_t*)dst = *(const uint32_t*)src;
-  } else {
-    *(uint16_t*)dst = *(const uint16_t*)src;
-  }
+  *(V*)((char*)p.cache + (blk * p.cache_s0 + off * p.cache_s1) * es + c * VEC) = v;
 }
 
 }  // namespace

@@ -20,9 +20,15 @@
 // chunk and merged by decode_merge in chunk order (deterministic). The plan
 // depends only on seqlens and sizes, never on strides or pointers.
 //
-// Inside a workgroup, keys are staged through LDS in tiles of TT tokens with
-// direct global->LDS 16-byte loads, NSLOT tiles deep. Each wave holds the
-// folded query of its 16*RT rows in registers and computes, per tile,
+// Inside a workgroup
+// ------------------
+// Keys are staged through LDS in tiles of TT tokens with direct global->LDS
+// 16-byte loads, NSLOT tiles deep; every wave loads a quarter of every tile and
+// one barrier per tile publishes it. The four waves split the unit's rows (WR)
+// and the 512 output columns (WC): WR x WC = 4. With few heads (the HBM-bound
+// decode) WC = 4, so each wave keeps a 16-row x 128-column accumulator and the
+// 16 x TT score block is recomputed by each wave; with many rows WR = 4 and
+// nothing is recomputed. Per tile a wave computes
 //   S^T[token, row]  = sum_e K[token, e] * Q[row, e]        (MFMA, bf16 -> f32)
 //   online softmax per row (exp2 domain, lazy rescale when the max grows by
 //   more than 2^8)
@@ -30,16 +36,8 @@
 // where V is the first 512 columns of the staged K rows, read transposed with
 // ds_read_b64_tr_b16. S^T's accumulator layout gives each lane one row and
 // four tokens, which is exactly the B operand layout P^T needs, so P never
-// leaves registers.
-//
-// Two wave layouts:
-//   WR row-waves  x WT token-waves, with WR == 1 or WT == 1.
-//   WT == 4 (few heads, the HBM-bound decode): 4 waves share one 16-row tile
-//     and take alternate key tiles, each wave with its own LDS ring; the four
-//     partial states are merged through LDS at the end.
-//   WR == 4 (many heads or prefill rows): 4 waves take 4 row blocks of the
-//     unit and share every key tile, loading a quarter each; one barrier per
-//     tile.
+// leaves registers. Operand reads from LDS are software-pipelined in
+// double-buffered batches so several are in flight behind each MFMA.
 #include <math.h>
 
 #include <type_traits>
@@ -53,6 +51,10 @@ namespace {
 typedef __attribute__((address_space(4))) const int32_t cint32_t;  // scalar-loadable view
 
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr int kBlkCache = 1024;  // block-table entries a workgroup stages in LDS
+// LDS besides the tile ring and score exchange: the split plan (below) and
+// the staged block table
+constexpr int kStaticLds = 3 * 256 * 4 + kBlkCache * 4;
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kNegInf = -__builtin_inff();
 
@@ -88,97 +90,246 @@ __device__ __forceinline__ int unit_kvlen(const DecodeParams& p, int u) {
   return row_limit(p, s, r_last / p.n_heads);
 }
 
-// Inclusive prefix over units of their work-block counts, for up to 256 units
-// (one per thread of a 256-thread block). Leaves the prefix in sh[0..255].
-__device__ void unit_scan(const DecodeParams& p, int* sh) {
-  const int t = threadIdx.x;
-  int v = t < p.num_units ? ceil_div(unit_kvlen(p, t), kWorkBlock) : 0;
-  sh[t] = v;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int x = t >= off ? sh[t - off] : 0;
-    __syncthreads();
-    sh[t] += x;
-    __syncthreads();
+// The split plan in LDS: per unit, the inclusive prefix of work-block counts,
+// the keys the unit needs and its sequence's length.
+struct PlanLds {
+  int scan[256];
+  int kv[256];
+  int sl[256];
+};
+
+// Split plan shared by the partial and merge kernels: each unit's work-block
+// count and their inclusive prefix over units, computed by wave 0 with
+// register shuffles (up to 256 units, four per lane) and published in
+// sh[0..255] with one barrier; with pl given, the units' key counts and
+// sequence lengths go to pl->kv and pl->sl.
+__device__ void plan_units(const DecodeParams& p, int* sh, PlanLds* pl) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int v[4], run = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = lane * 4 + k;
+      const int n = u < p.num_units ? unit_kvlen(p, u) : 0;
+      if (pl) {
+        pl->kv[u] = n;
+        pl->sl[u] = u < p.num_units ? seq_len(p, u / p.row_tiles) : 0;
+      }
+      run += ceil_div(n, kWorkBlock);
+      v[k] = run;
+    }
+    int x = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    const int excl = x - run;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sh[lane * 4 + k] = excl + v[k];
   }
+  __syncthreads();
 }
 
-template <int R_, int WR_, int WT_, int RT_, int TT_, int NSLOT_, bool F32_>
+// R: rope width; WR x WC compute waves split the unit's rows and the 512
+// output columns; RT row tiles of 16 per wave; TT-token tiles, NSLOT deep;
+// F32 values; XS: the waves sharing rows split the score contraction; NP:
+// dedicated loader waves (0: the compute waves load).
+template <int R_, int WR_, int WC_, int RT_, int TT_, int NSLOT_, bool F32_, bool XS_, int NP_>
 struct Cfg {
-  static constexpr int R = R_, WR = WR_, WT = WT_, RT = RT_, TT = TT_, NSLOT = NSLOT_;
-  static constexpr bool F32 = F32_;
+  static constexpr int R = R_, WR = WR_, WC = WC_, RT = RT_, TT = TT_, NSLOT = NSLOT_;
+  static constexpr bool F32 = F32_, XS = XS_ && WC_ > 1;
+  static constexpr int NP = NP_;
   static constexpr int ES = F32 ? 4 : 2;           // element bytes
   static constexpr int E = kKvRank + R;            // latent row width
   static constexpr int PITCH = E * ES;             // bytes per staged row
   static constexpr int CH = PITCH / 16;            // 16-byte chunks per row
-  static constexpr int NW = WR * WT;
-  static constexpr int NT = 64 * NW;
+  static constexpr int NW = WR * WC;               // compute waves
+  static constexpr int LW = NP > 0 ? NP : NW;       // loader waves
+  static constexpr int NT = 64 * (NW + NP);
   static constexpr int ROWS_W = 16 * RT;
-  static constexpr int RTILE = ROWS_W * WR;
+  static constexpr int RTILE = ROWS_W * WR;        // rows per unit
   static constexpr int TILE_BYTES = TT * PITCH;
   static constexpr int LPT = TT * CH / 64;         // 16-byte loads per tile per 64 lanes
-  static constexpr int LPW = LPT / WR;             // issued by each wave of a token group
-  static constexpr int SUB = TT / 16;
-  static constexpr int KSTEPS = F32 ? E / 16 : E / 32;
-  static constexpr int RING_BYTES = WT * NSLOT * TILE_BYTES;
+  static constexpr int LPW = LPT / LW;             // issued by each loader wave
+  static constexpr int SUB = TT / 16;              // 16-token sub-tiles
+  static constexpr int KSTEPS = F32 ? E / 16 : E / 32;  // 64-byte k-steps of a latent row
   static constexpr int DT = kKvRank / 16;          // 32 output column tiles
+  static constexpr int DW = DT / WC;               // column tiles per wave
+  // With XS the WC waves that share rows split the score contraction: wave
+  // wc takes k-steps wc, wc + WC, wc + 2 WC, ... (at most KW of them) and the
+  // partial scores are summed through LDS in wave order.
+  static constexpr int KW = XS ? (KSTEPS + WC - 1) / WC : KSTEPS;
+  static constexpr int XCHG_BYTES = XS ? NW * SUB * RT * 64 * 16 : 0;
+  static constexpr int RING_BYTES = NSLOT * TILE_BYTES;
+  static constexpr int SMEM_BYTES = RING_BYTES + XCHG_BYTES;
+  // With loader waves the query rows of every segment but the first travel
+  // through the ring as a tile of their own ahead of its key tiles (QI 1 KB
+  // reads); the first segment's are read straight into registers.
+  static constexpr bool QT = NP > 0;
+  static constexpr int QI = RTILE * CH / 64;
+  // operand-read batches (rows not shared): K reads per batch kept at about 6
+  static constexpr int KB = F32 ? (KSTEPS % 6 == 0 ? 6 : 4) : (SUB == 1 ? (KSTEPS % 6 == 0 ? 6 : 4)
+                                                : (KSTEPS % 3 == 0 ? 3 : 4));
+  static constexpr int PB = 4;
+  static_assert(NW == 4, "four compute waves per workgroup");
+  static_assert(NP == 0 || NP == 4, "no loader waves, or four");
+  static_assert(!XS || NP == 0, "the score exchange barrier assumes no loader waves");
+  static_assert(!QT || (RTILE <= TT && QI * 64 == RTILE * CH && QI <= LPT), "query tile fits a slot");
+  static_assert(!XS || WC % 2 == 0, "k-step parity is the wave's when WC is even");
   static_assert(LPT * 64 == TT * CH, "tile chunk count");
-  static_assert(LPW * WR == LPT, "tile loads split evenly over row waves");
-  static_assert(WR == 1 || WT == 1, "rows or tokens are split over waves, not both");
-  static_assert(NT == 256, "the split planner assumes 256-thread workgroups");
+  static_assert(LPW * LW == LPT, "tile loads split evenly over the loader waves");
   static_assert(TT == 16 || TT == 32, "tile size");
-  static_assert(!F32 || TT == 16, "f32 path uses 16-token tiles");
-  static_assert(NSLOT >= 1 && NSLOT <= 4, "ring depth");
-  // the token-split layout merges its waves' states through the same LDS
-  static constexpr int MERGE_BYTES = WT > 1 ? WT * DT * 64 * 16 + 2 * WT * 16 * 4 : 0;
-  static constexpr int SMEM_BYTES = RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES;
-  static_assert(SMEM_BYTES + 1024 <= 160 * 1024, "LDS budget");
+  static_assert(!F32 || TT == 16, "the f32 path uses 16-token tiles");
+  static_assert(NSLOT >= 2 && NSLOT <= 4, "ring depth");
+  static_assert(KSTEPS % KB == 0 && DW % PB == 0, "batching");
+  static_assert(SMEM_BYTES + kStaticLds <= 160 * 1024, "LDS budget");
 };
 
 // Everything a wave carries through one segment.
 template <class C>
 struct WaveState {
-  f32x4_t o[C::RT][C::DT];
+  f32x4_t o[C::RT][C::DW];  // O^T: lane holds row li, columns 16*(dc0+d) + 4*g + j
   float m[C::RT];
   float l[C::RT];
   int lim[C::RT];   // this lane's row: keys [.., lim) visible (already capped by the segment end)
 };
 
 // ---------------------------------------------------------------- one tile
-template <class C, class QReg>
-__device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, int j0, const QReg& qreg,
-                                             WaveState<C>& st, float scale_log2) {
+template <class C, class QReg, class Hook>
+__device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, MLA_LDS f32x4_t* xchg,
+                                             int j0, const QReg& qreg, WaveState<C>& st,
+                                             float scale_log2, int wr, int wc, int dc0,
+                                             const Hook& hook) {
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   f32x4_t s[C::SUB][C::RT];
-#pragma unroll
-  for (int a = 0; a < C::SUB; ++a)
-#pragma unroll
-    for (int rt = 0; rt < C::RT; ++rt) s[a][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // ---- S^T = K . Q^T : lane (token li of sub-tile a, e-group g) x (row li, g)
-  if constexpr (!C::F32) {
+  if constexpr (C::XS) {
+    // ---- partial S^T over this wave's k-steps kg = wc + WC*kk. Chunk 4kg + g
+    // is stored at 8*(kg/2) + ((4*(kg%2) + g) ^ swz); kg%2 = wc%2 and
+    // kg/2 = wc/2 + (WC/2)*kk, so one lane base and immediate offsets.
+    using KV = typename std::conditional<C::F32, f32x4_t, i16x8_t>::type;
+    const MLA_LDS char* kb = tile + li * C::PITCH + 128 * (wc >> 1) +
+                             (((4 * (wc & 1) + g) ^ lds_swz(li)) << 4);
+    const bool has_last = wc + C::WC * (C::KW - 1) < C::KSTEPS;
+    KV kbuf[C::KW][C::SUB];
 #pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+    for (int kk = 0; kk < C::KW; ++kk)
+      if (kk < C::KW - 1 || has_last)
 #pragma unroll
-      for (int a = 0; a < C::SUB; ++a) {
-        const int rr = 16 * a + li;
-        const int c = (g + 4 * kk) ^ lds_swz(li);
-        const i16x8_t k = *(const MLA_LDS i16x8_t*)(tile + rr * C::PITCH + c * 16);
+        for (int a = 0; a < C::SUB; ++a)
+          kbuf[kk][a] = *(const MLA_LDS KV*)(kb + 16 * a * C::PITCH + 64 * C::WC * kk);
+    hook(0);
+    f32x4_t acc[2][C::SUB][C::RT];
 #pragma unroll
-        for (int rt = 0; rt < C::RT; ++rt) s[a][rt] = mfma_16x16x32(k, qreg[rt][kk], s[a][rt]);
-      }
-    }
-  } else {
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      const int c = (g + 4 * kk) ^ lds_swz(li);
-      const f32x4_t k = *(const MLA_LDS f32x4_t*)(tile + li * C::PITCH + c * 16);
+      for (int a = 0; a < C::SUB; ++a)
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+        for (int rt = 0; rt < C::RT; ++rt) acc[e][a][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < C::KW; ++kk)
+      if (kk < C::KW - 1 || has_last)
+#pragma unroll
+        for (int a = 0; a < C::SUB; ++a)
+#pragma unroll
+          for (int rt = 0; rt < C::RT; ++rt) {
+            if constexpr (C::F32) {
+#pragma unroll
+              for (int x = 0; x < 4; ++x)
+                acc[kk & 1][a][rt] =
+                    mfma_16x16x4f32(kbuf[kk][a][x], qreg[rt][kk][x], acc[kk & 1][a][rt]);
+            } else {
+              acc[kk & 1][a][rt] = mfma_16x16x32(kbuf[kk][a], qreg[rt][kk], acc[kk & 1][a][rt]);
+            }
+          }
+    // ---- exchange: partials [wr][wc][a][rt][lane], summed in wave order so
+    // every wave of the row group holds bit-identical scores
+    MLA_LDS f32x4_t* mine = xchg + (wr * C::WC + wc) * (C::SUB * C::RT * 64) + lane;
+#pragma unroll
+    for (int a = 0; a < C::SUB; ++a)
+#pragma unroll
+      for (int rt = 0; rt < C::RT; ++rt) mine[(a * C::RT + rt) * 64] = acc[0][a][rt] + acc[1][a][rt];
+    __syncthreads();
+    const MLA_LDS f32x4_t* grp = xchg + wr * C::WC * (C::SUB * C::RT * 64) + lane;
+    f32x4_t part[C::WC][C::SUB][C::RT];
+#pragma unroll
+    for (int w = 0; w < C::WC; ++w)
+#pragma unroll
+      for (int a = 0; a < C::SUB; ++a)
 #pragma unroll
         for (int rt = 0; rt < C::RT; ++rt)
-          s[0][rt] = mfma_16x16x4f32(k[x], qreg[rt][kk][x], s[0][rt]);
+          part[w][a][rt] = grp[(w * C::SUB * C::RT + a * C::RT + rt) * 64];
+    hook(1);
+#pragma unroll
+    for (int a = 0; a < C::SUB; ++a)
+#pragma unroll
+      for (int rt = 0; rt < C::RT; ++rt) {
+        f32x4_t t = part[0][a][rt];
+#pragma unroll
+        for (int w = 1; w < C::WC; ++w) t += part[w][a][rt];
+        s[a][rt] = t;
+      }
+  } else {
+  // ---- S^T = K . Q^T : lane (token li of sub-tile a, e-group g) x (row li, g).
+  // Chunk (g + 4kk) ^ swz(li) = 8*(kk/2) + ((g + 4*(kk%2)) ^ swz(li)): two lane
+  // bases, the rest is an immediate offset. Two accumulators per block (even
+  // and odd kk) halve the MFMA dependency chain.
+  {
+    const int sw = lds_swz(li);
+    const MLA_LDS char* kb0 = tile + li * C::PITCH + ((g ^ sw) << 4);
+    const MLA_LDS char* kb1 = tile + li * C::PITCH + (((g + 4) ^ sw) << 4);
+    using KV = typename std::conditional<C::F32, f32x4_t, i16x8_t>::type;
+    KV kbuf[2][C::KB][C::SUB];
+    f32x4_t acc[2][C::SUB][C::RT];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int a = 0; a < C::SUB; ++a)
+#pragma unroll
+        for (int rt = 0; rt < C::RT; ++rt) acc[e][a][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto load = [&](int bi, int buf) {
+#pragma unroll
+      for (int k = 0; k < C::KB; ++k) {
+        const int kk = bi * C::KB + k;
+        const MLA_LDS char* kb = (kk & 1) ? kb1 : kb0;
+#pragma unroll
+        for (int a = 0; a < C::SUB; ++a)
+          kbuf[buf][k][a] = *(const MLA_LDS KV*)(kb + 16 * a * C::PITCH + 128 * (kk >> 1));
+      }
+    };
+    constexpr int NB = C::KSTEPS / C::KB;
+    load(0, 0);
+    hook(0);
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) {
+      if (bi + 1 < NB) load(bi + 1, (bi + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < C::KB; ++k) {
+        const int kk = bi * C::KB + k;
+#pragma unroll
+        for (int a = 0; a < C::SUB; ++a)
+#pragma unroll
+          for (int rt = 0; rt < C::RT; ++rt) {
+            if constexpr (C::F32) {
+#pragma unroll
+              for (int x = 0; x < 4; ++x)
+                acc[kk & 1][a][rt] =
+                    mfma_16x16x4f32(kbuf[bi & 1][k][a][x], qreg[rt][kk][x], acc[kk & 1][a][rt]);
+            } else {
+              acc[kk & 1][a][rt] = mfma_16x16x32(kbuf[bi & 1][k][a], qreg[rt][kk], acc[kk & 1][a][rt]);
+            }
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int a = 0; a < C::SUB; ++a)
+#pragma unroll
+      for (int rt = 0; rt < C::RT; ++rt) s[a][rt] = acc[0][a][rt] + acc[1][a][rt];
+    hook(1);
+  }
   }
 
   // ---- online softmax (exp2 domain); lane holds row li, tokens 16a + 4g + j
@@ -203,7 +354,7 @@ __device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, int j0, c
       const float mn = fmaxf(st.m[rt], mt);
       const float alpha = mn == kNegInf ? 1.f : fast_exp2(st.m[rt] - mn);
 #pragma unroll
-      for (int d = 0; d < C::DT; ++d) st.o[rt][d] *= alpha;
+      for (int d = 0; d < C::DW; ++d) st.o[rt][d] *= alpha;
       st.l[rt] *= alpha;
       st.m[rt] = mn;
     }
@@ -224,295 +375,570 @@ __device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, int j0, c
 #pragma unroll
       for (int a = 0; a < C::SUB; ++a)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pb[rt][4 * a + j] = (short)f32_to_bf16(v[a][j]);
+        for (int j = 0; j < 4; j += 2) {
+          const uint32_t w = pack_bf16x2(v[a][j], v[a][j + 1]);
+          pb[rt][4 * a + j] = (short)(w & 0xffffu);
+          pb[rt][4 * a + j + 1] = (short)(w >> 16);
+        }
     }
   }
 
   // ---- O^T += V^T . P^T : A = V^T (d = li, tokens by g), B = P^T (tokens by g, row li)
   if constexpr (!C::F32) {
-    // local lane li points at token row (4g + li/4) [+16], columns 16*d + 4*(li%4)
+    // local lane li points at token row (4g + li/4) [+16], columns 16*d + 4*(li%4);
+    // chunk (2d + cx) ^ swz = 8*(d/4) + ((2*(d%4) + cx) ^ swz): four lane bases
+    // and immediate offsets (rows r and r + 16 share a swizzle)
     const int rr0 = 4 * g + (li >> 2);
-    const int sw0 = lds_swz(rr0 & 15), sw1 = lds_swz((rr0 + 16) & 15);
+    const int sw0 = lds_swz(rr0);
     const int cx = (li & 3) >> 1, half8 = (li & 1) * 8;
+    const MLA_LDS char* vb[4];
 #pragma unroll
-    for (int d = 0; d < C::DT; ++d) {
-      const int c = 2 * d + cx;
-      const i16x4_t v0 = lds_read_tr16(tile + rr0 * C::PITCH + ((c ^ sw0) << 4) + half8);
-      if constexpr (C::TT == 32) {
-        const i16x4_t v1 =
-            lds_read_tr16(tile + (rr0 + 16) * C::PITCH + ((c ^ sw1) << 4) + half8);
-        const i16x8_t vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    for (int x = 0; x < 4; ++x)
+      vb[x] = tile + rr0 * C::PITCH + (((2 * x + cx) ^ sw0) << 4) + half8 + 32 * dc0;
+    i16x4_t vbuf[2][C::PB][C::SUB];
+    auto load = [&](int bj, int buf) {
 #pragma unroll
-        for (int rt = 0; rt < C::RT; ++rt) st.o[rt][d] = mfma_16x16x32(vv, pb[rt], st.o[rt][d]);
-      } else {
+      for (int x = 0; x < C::PB; ++x) {
+        const int d = bj * C::PB + x;
+        const MLA_LDS char* vp = vb[d & 3] + 128 * (d >> 2);
 #pragma unroll
-        for (int rt = 0; rt < C::RT; ++rt) st.o[rt][d] = mfma_16x16x16(v0, pb[rt], st.o[rt][d]);
+        for (int a = 0; a < C::SUB; ++a) vbuf[buf][x][a] = lds_read_tr16(vp + 16 * a * C::PITCH);
       }
+    };
+    constexpr int NB = C::DW / C::PB;
+    load(0, 0);
+    hook(2);
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj) {
+      if (bj + 1 < NB) load(bj + 1, (bj + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 0; x < C::PB; ++x) {
+        const int d = bj * C::PB + x;
+        if constexpr (C::TT == 32) {
+          const i16x4_t v0 = vbuf[bj & 1][x][0], v1 = vbuf[bj & 1][x][1];
+          const i16x8_t vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+          for (int rt = 0; rt < C::RT; ++rt) st.o[rt][d] = mfma_16x16x32(vv, pb[rt], st.o[rt][d]);
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < C::RT; ++rt)
+            st.o[rt][d] = mfma_16x16x16(vbuf[bj & 1][x][0], pb[rt], st.o[rt][d]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
+    // f32: A = V[token 4g + x][16d + li] (one element per lane), MFMA x per token
+    float vbuf[2][C::PB][4];
+    auto load = [&](int bj, int buf) {
 #pragma unroll
-    for (int d = 0; d < C::DT; ++d) {
+      for (int y = 0; y < C::PB; ++y) {
+        const int col = 16 * (dc0 + bj * C::PB + y) + li;  // float column
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int rr = 4 * g + x;
-        const int col = 16 * d + li;  // float index
-        const float vv = *(const MLA_LDS float*)(tile + rr * C::PITCH +
-                                                   (((col >> 2) ^ lds_swz(rr)) << 4) +
-                                                   (col & 3) * 4);
-#pragma unroll
-        for (int rt = 0; rt < C::RT; ++rt) st.o[rt][d] = mfma_16x16x4f32(vv, pf[rt][x], st.o[rt][d]);
+        for (int x = 0; x < 4; ++x) {
+          const int rr = 4 * g + x;
+          vbuf[buf][y][x] = *(const MLA_LDS float*)(tile + rr * C::PITCH +
+                                                      (((col >> 2) ^ lds_swz(rr)) << 4) + (col & 3) * 4);
+        }
       }
+    };
+    constexpr int NB = C::DW / C::PB;
+    load(0, 0);
+    hook(2);
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj) {
+      if (bj + 1 < NB) load(bj + 1, (bj + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int y = 0; y < C::PB; ++y) {
+        const int d = bj * C::PB + y;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int rt = 0; rt < C::RT; ++rt)
+            st.o[rt][d] = mfma_16x16x4f32(vbuf[bj & 1][y][x], pf[rt][x], st.o[rt][d]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
 // ------------------------------------------------------ output of a segment
+// This lane's row (local_row of the unit), columns 16*(dc0 + d) + 4*g + j.
 template <class C>
 __device__ __forceinline__ void store_row(const DecodeParams& p, int b, int unit_row0,
                                           int local_row, int slot, const f32x4_t* o, float inv,
-                                          float lse2) {
-  // o[DT]: this lane's row, columns 16*d + 4*g + j
+                                          float lse2, int dc0, bool write_lse) {
   const int lane = threadIdx.x & 63, g = lane >> 4;
   const int rows_seq = p.q_len * p.n_heads;
   const int r = unit_row0 + local_row;
   if (r >= rows_seq) return;
+  const int c0 = 16 * dc0 + 4 * g;
   if (slot >= 0) {
-    float* dst = p.part_o + ((int64_t)slot * p.rows_per_unit + local_row) * kKvRank + 4 * g;
+    float* dst = p.part_o + ((int64_t)slot * p.rows_per_unit + local_row) * kKvRank + c0;
 #pragma unroll
-    for (int d = 0; d < C::DT; ++d) *(f32x4_t*)(dst + 16 * d) = o[d] * inv;
-    if (g == 0) p.part_lse[(int64_t)slot * p.rows_per_unit + local_row] = lse2;
+    for (int d = 0; d < C::DW; ++d) *(f32x4_t*)(dst + 16 * d) = o[d] * inv;
+    if (write_lse && g == 0) p.part_lse[(int64_t)slot * p.rows_per_unit + local_row] = lse2;
     return;
   }
   const int qi = r / p.n_heads, qh = r % p.n_heads;
-  const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)qh * p.o_s2 + 4 * g;
+  const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)qh * p.o_s2 + c0;
   if constexpr (C::F32) {
     float* dst = (float*)p.out + ooff;
 #pragma unroll
-    for (int d = 0; d < C::DT; ++d) *(f32x4_t*)(dst + 16 * d) = o[d] * inv;
+    for (int d = 0; d < C::DW; ++d) *(f32x4_t*)(dst + 16 * d) = o[d] * inv;
   } else {
     uint16_t* dst = (uint16_t*)p.out + ooff;
 #pragma unroll
-    for (int d = 0; d < C::DT; ++d) {
+    for (int d = 0; d < C::DW; ++d) {
       const f32x4_t x = o[d] * inv;
       *(u32x2_t*)(dst + 16 * d) = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
     }
   }
-  if (g == 0 && p.lse)
+  if (write_lse && g == 0 && p.lse)
     p.lse[(int64_t)b * p.l_s0 + (int64_t)qi * p.l_s1 + (int64_t)qh * p.l_s2] =
         lse2 == kNegInf ? kNegInf : lse2 * kLn2;
 }
 
-// ------------------------------------------------------------- one segment
-// Keys [tok_lo, tok_hi) of unit u; slot < 0 writes the final output.
+// ------------------------------------------------------- a workgroup's keys
+// One contiguous run of a unit's keys handled by this workgroup.
+struct Seg {
+  int u;       // unit
+  int b;       // sequence
+  int s;       // the sequence's length
+  int t_lo;    // first key token
+  int t_hi;    // one past the last key token (capped by the unit's visible keys)
+  int ntiles;  // tiles of TT tokens
+  int slot;    // partial slot, or -1 when this workgroup holds the whole unit
+};
+
 template <class C>
-__device__ void process_segment(const DecodeParams& p, int u, int tok_lo, int tok_hi, int slot,
-                                MLA_LDS char* ring_all) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, li = lane & 15;
-  const int wr = C::WT == 1 ? wave : 0;
-  const int wt = C::WT == 1 ? 0 : wave;
-
-  const int b = u / p.row_tiles, rtu = u % p.row_tiles;
-  const int s = seq_len(p, b);
-  const int kvlen = unit_kvlen(p, u);
-  const int t_lo = tok_lo;
-  const int t_hi = tok_hi < kvlen ? tok_hi : kvlen;
-  const int ntiles = t_hi > t_lo ? ceil_div(t_hi - t_lo, C::TT) : 0;
-  const int rows_seq = p.q_len * p.n_heads;
-  const int unit_row0 = rtu * p.rows_per_unit;
-  const int wrow0 = wr * C::ROWS_W;  // first local row of this wave
-
-  // ---- folded query rows of this wave -> registers (B operand layout)
-  using QV = typename std::conditional<C::F32, f32x4_t, i16x8_t>::type;
-  QV qreg[C::RT][C::KSTEPS];
-  WaveState<C> st;
-#pragma unroll
-  for (int rt = 0; rt < C::RT; ++rt) {
-    const int r = unit_row0 + wrow0 + 16 * rt + li;
-    const bool valid = r < rows_seq;
-    const int qi = valid ? r / p.n_heads : 0, qh = valid ? r % p.n_heads : 0;
-    const int64_t qoff = (int64_t)b * p.q_s0 + (int64_t)qi * p.q_s1 + (int64_t)qh * p.q_s2;
-    if constexpr (C::F32) {
-      const float* qp = (const float*)p.q + qoff + 4 * g;
-#pragma unroll
-      for (int kk = 0; kk < C::KSTEPS; ++kk)
-        qreg[rt][kk] = valid ? *(const f32x4_t*)(qp + 16 * kk) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    } else {
-      const uint16_t* qp = (const uint16_t*)p.q + qoff + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < C::KSTEPS; ++kk)
-        qreg[rt][kk] = valid ? *(const i16x8_t*)(qp + 32 * kk) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-    const int lim = valid ? row_limit(p, s, qi) : 0;
-    st.lim[rt] = lim < t_hi ? lim : t_hi;
-    st.m[rt] = kNegInf;
-    st.l[rt] = 0.f;
-#pragma unroll
-    for (int d = 0; d < C::DT; ++d) st.o[rt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ Seg make_seg(const DecodeParams& p, const PlanLds* pl, int u, int w0,
+                                        int w1, int chunk) {
+  Seg sg;
+  sg.u = u;
+  sg.b = u / p.row_tiles;
+  if (u >= p.num_units) {
+    sg.s = sg.t_lo = sg.t_hi = sg.ntiles = 0;
+    sg.slot = -1;
+    return sg;
   }
+  const int kvlen = p.split ? pl->kv[u] : unit_kvlen(p, u);
+  sg.s = p.split ? pl->sl[u] : seq_len(p, sg.b);
+  if (!p.split) {
+    sg.t_lo = 0;
+    sg.t_hi = kvlen;
+    sg.slot = -1;
+  } else {
+    const int start = u > 0 ? pl->scan[u - 1] : 0, end = pl->scan[u];
+    const int a = (w0 > start ? w0 : start) - start;
+    const int e = (w1 < end ? w1 : end) - start;
+    sg.t_lo = a * kWorkBlock;
+    sg.t_hi = e * kWorkBlock < kvlen ? e * kWorkBlock : kvlen;
+    sg.slot = (start / chunk != (end - 1) / chunk) ? (int)blockIdx.x + u : -1;
+  }
+  sg.ntiles = sg.t_hi > sg.t_lo ? ceil_div(sg.t_hi - sg.t_lo, C::TT) : 0;
+  return sg;
+}
 
-  MLA_LDS char* ring = ring_all + wt * C::NSLOT * C::TILE_BYTES;
-  const int nsteps = ntiles > wt ? ceil_div(ntiles - wt, C::WT) : 0;
+// Pages a segment touches (its block-table entries).
+__device__ __forceinline__ int seg_pages(const DecodeParams& p, const Seg& sg) {
+  return sg.ntiles > 0 ? (sg.t_hi - 1) / p.page - sg.t_lo / p.page + 1 : 0;
+}
+
+
+
+// Next unit with work after u, or num_units.
+__device__ __forceinline__ int next_unit(const DecodeParams& p, const int* sh, int u, int w1) {
+  if (!p.split) return p.num_units;
+  for (++u; u < p.num_units; ++u) {
+    const int start = u > 0 ? sh[u - 1] : 0;
+    if (start >= w1) return p.num_units;
+    if (sh[u] > start) return u;
+  }
+  return p.num_units;
+}
+
+// Stage the block-table entries of the workgroup's segments, in stream order,
+// in LDS (the first kBlkCache of them; the loader reads any beyond that from
+// global memory). Entries are clamped to [0, num_blocks) so every tile read
+// stays inside the cache.
+template <class C>
+__device__ void stage_block_table(const DecodeParams& p, const PlanLds* pl, int u0, int w0, int w1,
+                                  int chunk, int* sh_blk) {
+  constexpr int PER = (kBlkCache + C::NT - 1) / C::NT;
+  int64_t idx[PER];
+  bool need[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) need[k] = false;
+  int off = 0;
+  for (int u = u0; u < p.num_units && off < kBlkCache; u = next_unit(p, pl->scan, u, w1)) {
+    const Seg sg = make_seg<C>(p, pl, u, w0, w1, chunk);
+    const int n = seg_pages(p, sg), pf = sg.t_lo / p.page;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = (int)threadIdx.x + C::NT * k;
+      if (i < kBlkCache && i >= off && i < off + n) {
+        idx[k] = (int64_t)sg.b * p.bt_s0 + pf + (i - off);
+        need[k] = true;
+      }
+    }
+    off += n;
+  }
+  int v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) v[k] = need[k] ? p.block_table[idx[k]] : 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    if (need[k])
+      sh_blk[threadIdx.x + C::NT * k] = v[k] < 0 ? 0 : (v[k] >= p.num_blocks ? (int)p.num_blocks - 1 : v[k]);
+  __syncthreads();
+}
+
+// ------------------------------------------------------ the tile stream
+// All tiles of the workgroup's segments form one stream staged through an LDS
+// ring of NSLOT tiles, with one workgroup barrier per tile: before barrier k
+// tile k has landed and every compute wave is done with tile k-1, whose slot
+// the reads of tile k + NSLOT - 1 then refill. Reads run NSLOT - 1 tiles ahead
+// of the compute, across segment boundaries. At a boundary the compute waves
+// write the finished segment (final output, or a partial for the merge) and
+// load the next segment's query rows. With NP loader waves the compute waves
+// never stall on a full memory queue; without them the compute waves send the
+// next tile's reads in three groups between their own phases.
+template <class C>
+__device__ void process_range(const DecodeParams& p, const PlanLds* pl, int* sh_blk, int u0,
+                              int w0, int w1, int chunk, MLA_LDS char* ring,
+                              MLA_LDS f32x4_t* xchg) {
+  const int* sh = pl->scan;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const bool loader = C::NP == 0 || wave >= C::NW;
+  const bool compute = C::NP == 0 || wave < C::NW;
+  const int lwave = C::NP == 0 ? wave : wave - C::NW;  // index among the loader waves
+  const int g = lane >> 4, li = lane & 15;
+  const int cw = compute ? wave : 0;
+  const int wr = cw / C::WC, wc = cw % C::WC;
+  const int dc0 = wc * C::DW;  // first output column tile of this wave
+  const int wrow0 = wr * C::ROWS_W;
+  const int rows_seq = p.q_len * p.n_heads;
   const char* kvbase = (const char*)p.kv;
   const int64_t pitch_g = p.kv_s1 * C::ES;
 
-  auto issue = [&](int step) {
-    const int j0 = t_lo + (wt + step * C::WT) * C::TT;
-    const int nvalid = t_hi - j0 < C::TT ? t_hi - j0 : C::TT;
-    MLA_LDS char* dst = ring + (step % C::NSLOT) * C::TILE_BYTES;
-    // each 16-token half of the tile lies in one page (page is a multiple of 16)
-    const int pg0 = j0 / p.page;
-    int blk0 = load_scalar_i32(p.block_table, (int64_t)b * p.bt_s0 + pg0);
-    blk0 = blk0 < 0 ? 0 : (blk0 >= p.num_blocks ? (int)p.num_blocks - 1 : blk0);
-    const char* base0 = kvbase + (int64_t)blk0 * p.kv_s0 * C::ES + (int64_t)(j0 - pg0 * p.page) * pitch_g;
-    const char* base1 = base0 + 16 * pitch_g;
-    if constexpr (C::TT == 32) {
-      const int j1 = j0 + 16;
-      if (j1 < t_hi && (j1 / p.page) != pg0) {
-        const int pg1 = j1 / p.page;
-        int blk1 = load_scalar_i32(p.block_table, (int64_t)b * p.bt_s0 + pg1);
-        blk1 = blk1 < 0 ? 0 : (blk1 >= p.num_blocks ? (int)p.num_blocks - 1 : blk1);
-        base1 = kvbase + (int64_t)blk1 * p.kv_s0 * C::ES + (int64_t)(j1 - pg1 * p.page) * pitch_g;
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < C::LPW; ++n) {
-      // this lane's 16-byte slot of the tile: row r, stored chunk position cpos
-      const int idx = (wr + n * C::WR) * 64 + lane;
-      const int r = idx / C::CH, cpos = idx % C::CH;
-      const int chunk = cpos ^ lds_swz(r & 15);
-      const int rr = r < nvalid ? r : nvalid - 1;  // rows past the end repeat the last valid row
-      const char* src = (C::TT == 32 && rr >= 16) ? base1 + (rr - 16) * pitch_g : base0 + rr * pitch_g;
-      load_lds_16(src + chunk * 16, dst + (wr + n * C::WR) * 1024);
-    }
-  };
-
-#pragma unroll
-  for (int k = 0; k < C::NSLOT - 1; ++k)
-    if (k < nsteps) issue(k);
-
-  for (int k = 0; k < nsteps; ++k) {
-    if constexpr (C::NSLOT == 1) {
-      static_assert(C::WR == 1, "a one-slot ring is private to its wave");
-      issue(k);  // the previous tile's reads are complete (compiler-inserted lgkmcnt wait)
-      wait_vmcnt<0>();
-    } else {
-      // tiles k+1 .. k+NSLOT-2 may still be in flight; tile k must have landed
-      int ahead = nsteps - 1 - k;
-      ahead = ahead < C::NSLOT - 2 ? ahead : C::NSLOT - 2;
-      if (ahead <= 0) wait_vmcnt<0>();
-      else if (ahead == 1) wait_vmcnt<C::LPW>();
-      else wait_vmcnt<(C::NSLOT >= 4 ? 2 * C::LPW : 0)>();
-      // row-split: tile k is complete for every wave, and every wave is done
-      // with tile k-1, whose slot the next issue overwrites
-      if constexpr (C::WR > 1) __syncthreads();
-      if (k + C::NSLOT - 1 < nsteps) issue(k + C::NSLOT - 1);
-    }
-    const int j0 = t_lo + (wt + k * C::WT) * C::TT;
-    tile_compute<C>(ring + (k % C::NSLOT) * C::TILE_BYTES, j0, qreg, st, p.scale_log2);
+  // total tiles of the range
+  int nsteps = 0;
+  for (int u = u0; u < p.num_units; u = next_unit(p, sh, u, w1)) {
+    const int nt = make_seg<C>(p, pl, u, w0, w1, chunk).ntiles;
+    nsteps += nt + (C::QT && nt > 0 && u != u0 ? 1 : 0);
   }
 
-  // ---- finish
-  if constexpr (C::WT == 1) {
+  // ---- loader walker: this wave's share of each tile's reads. A full tile
+  // inside one page is read as page base + per-lane offsets computed once
+  // here; other tiles (a segment's last, or pages shorter than a tile) take
+  // the general path.
+  const bool fast_ok = p.page % C::TT == 0 && (int64_t)p.page * pitch_g < ((int64_t)1 << 31);
+  uint32_t loff[C::LPW];
+#pragma unroll
+  for (int n = 0; n < C::LPW; ++n) {
+    const int idx = (lwave + n * C::LW) * 64 + lane;
+    const int r = idx / C::CH, cpos = idx % C::CH;
+    loff[n] = (uint32_t)(r * pitch_g) + (uint32_t)((cpos ^ lds_swz(r & 15)) << 4);
+  }
+  Seg ls = make_seg<C>(p, pl, u0, w0, w1, chunk);
+  int lk = 0;         // tile within ls
+  bool lq = true;     // ls's query tile sent (the first segment has none)
+  int ls_off = 0;     // staged block-table position of ls's first page
+  // cache block of page pg of segment ls (staged entry, or a global read past the stage)
+  auto block_of = [&](int pg) -> int {
+    const int ti = ls_off + pg - ls.t_lo / p.page;
+    int blk;
+    if (ti < kBlkCache) {
+      blk = sh_blk[ti];
+    } else {
+      blk = load_scalar_i32(p.block_table, (int64_t)ls.b * p.bt_s0 + pg);
+      blk = blk < 0 ? 0 : (blk >= p.num_blocks ? (int)p.num_blocks - 1 : blk);
+    }
+    return __builtin_amdgcn_readfirstlane(blk);
+  };
+  struct NextTile {
+    const char* base0 = nullptr;
+    const char* base1 = nullptr;
+    int nvalid = 0;
+    int slot = 0;
+    bool fast = false;
+    bool live = false;
+    bool query = false;  // the query rows of a unit: sequence qb, first row qrow0
+    int qb = 0;
+    int qrow0 = 0;
+  };
+  auto prep_next = [&](int step) -> NextTile {
+    // segments in split mode have tiles; an empty unit (no split) is never reached
+    while (lk >= ls.ntiles && (lq || !C::QT) && ls.u < p.num_units) {
+      ls_off += seg_pages(p, ls);
+      ls = make_seg<C>(p, pl, next_unit(p, sh, ls.u, w1), w0, w1, chunk);
+      lk = 0;
+      lq = false;
+    }
+    NextTile t;
+    t.live = true;
+    t.slot = step % C::NSLOT;
+    if (C::QT && !lq) {
+      lq = true;
+      t.query = true;
+      t.qb = ls.b;
+      t.qrow0 = (ls.u % p.row_tiles) * p.rows_per_unit;
+      return t;
+    }
+    const int j0 = ls.t_lo + lk * C::TT;
+    t.nvalid = ls.t_hi - j0 < C::TT ? ls.t_hi - j0 : C::TT;
+    ++lk;
+    // each 16-token half of the tile lies in one page (page is a multiple of 16)
+    const int pg0 = j0 / p.page;
+    const int blk0 = block_of(pg0);
+    t.base0 = kvbase + (int64_t)blk0 * p.kv_s0 * C::ES + (int64_t)(j0 - pg0 * p.page) * pitch_g;
+    t.fast = fast_ok && t.nvalid == C::TT;
+    t.base1 = t.base0 + 16 * pitch_g;
+    if constexpr (C::TT == 32) {
+      const int j1 = j0 + 16;
+      if (!t.fast && j1 < ls.t_hi && (j1 / p.page) != pg0) {
+        const int pg1 = j1 / p.page;
+        const int blk1 = block_of(pg1);
+        t.base1 = kvbase + (int64_t)blk1 * p.kv_s0 * C::ES + (int64_t)(j1 - pg1 * p.page) * pitch_g;
+      }
+    }
+    return t;
+  };
+  // reads n of this wave's share with n * 3 / LPW == stage
+  auto issue_part = [&](const NextTile& t, int stage) {
+    if (!t.live) return;
+    MLA_LDS char* dst = ring + t.slot * C::TILE_BYTES;
+#pragma unroll
+    for (int n = 0; n < C::LPW; ++n) {
+      if (n * 3 / C::LPW != stage) continue;
+      const int inst = lwave + n * C::LW;
+      if (C::QT && t.query) {
+        // query row i of the unit at row i of the slot, staged like a key row;
+        // reads past QI repeat one (same bytes to the same place), so every
+        // loader wave sends LPW reads for every tile
+        const int qinst = inst % C::QI;
+        const int idx = qinst * 64 + lane;
+        const int i = idx / C::CH, cpos = idx % C::CH;
+        int r = t.qrow0 + i;
+        r = r < rows_seq ? r : rows_seq - 1;  // rows past the end are zeroed by the compute waves
+        const int qi = r / p.n_heads, qh = r % p.n_heads;
+        const char* src = (const char*)p.q +
+                          ((int64_t)t.qb * p.q_s0 + (int64_t)qi * p.q_s1 + (int64_t)qh * p.q_s2) * C::ES +
+                          ((cpos ^ lds_swz(i & 15)) << 4);
+        load_lds_16(src, dst + qinst * 1024);
+      } else if (t.fast) {
+        load_lds_16_sbase(t.base0, loff[n], dst + inst * 1024);
+      } else {
+        // this lane's 16-byte slot of the tile: row r, stored chunk position cpos
+        const int idx = inst * 64 + lane;
+        const int r = idx / C::CH, cpos = idx % C::CH;
+        const int chunk16 = cpos ^ lds_swz(r & 15);
+        const int rr = r < t.nvalid ? r : t.nvalid - 1;  // rows past the end repeat the last valid row
+        const char* src =
+            (C::TT == 32 && rr >= 16) ? t.base1 + (rr - 16) * pitch_g : t.base0 + rr * pitch_g;
+        load_lds_16(src + chunk16 * 16, dst + inst * 1024);
+      }
+    }
+  };
+  // wait until this loader wave's reads of tile k have landed
+  auto wait_tile = [&](int k) {
+    int ahead = nsteps - 1 - k;
+    ahead = ahead < C::NSLOT - 2 ? ahead : C::NSLOT - 2;
+    if (ahead <= 0) wait_vmcnt<0>();
+    else if (ahead == 1) wait_vmcnt<C::LPW>();
+    else wait_vmcnt<(C::NSLOT >= 4 ? 2 * C::LPW : 0)>();
+  };
+
+  // ---- compute walker state
+  using QV = typename std::conditional<C::F32, f32x4_t, i16x8_t>::type;
+  // this wave's k-steps of the query rows: kg = wc + WC*kk (all of them when WC == 1)
+  QV qreg[C::RT][C::KW];
+  bool qvalid[C::RT];
+  WaveState<C> st;
+  Seg cs = make_seg<C>(p, pl, u0, w0, w1, chunk);
+  int ck = 0;
+  // state of a new segment: this lane's row limits, empty softmax state
+  auto begin_state = [&]() {
+    const int unit_row0 = (cs.u % p.row_tiles) * p.rows_per_unit;
+#pragma unroll
+    for (int rt = 0; rt < C::RT; ++rt) {
+      const int r = unit_row0 + wrow0 + 16 * rt + li;
+      qvalid[rt] = r < rows_seq;
+      const int lim = qvalid[rt] ? row_limit(p, cs.s, r / p.n_heads) : 0;
+      st.lim[rt] = lim < cs.t_hi ? lim : cs.t_hi;
+      st.m[rt] = kNegInf;
+      st.l[rt] = 0.f;
+#pragma unroll
+      for (int d = 0; d < C::DW; ++d) st.o[rt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // folded query rows of the segment's unit -> registers (B operand layout),
+  // loaded asynchronously from global memory (no query tiles); rows past the
+  // end load row 0 and are zeroed by settle_q
+  auto load_q = [&]() {
+    const int unit_row0 = (cs.u % p.row_tiles) * p.rows_per_unit;
+#pragma unroll
+    for (int rt = 0; rt < C::RT; ++rt) {
+      const int r = unit_row0 + wrow0 + 16 * rt + li;
+      const int qi = qvalid[rt] ? r / p.n_heads : 0, qh = qvalid[rt] ? r % p.n_heads : 0;
+      const int64_t qoff = (int64_t)cs.b * p.q_s0 + (int64_t)qi * p.q_s1 + (int64_t)qh * p.q_s2;
+      const char* qp = (const char*)p.q + qoff * C::ES + 16 * g;
+#pragma unroll
+      for (int kk = 0; kk < C::KW; ++kk) {
+        // with a split contraction a k-step past the row end (uneven split)
+        // reloads the wave's first one, never used
+        const int kg = !C::XS ? kk : (wc + C::WC * kk < C::KSTEPS ? wc + C::WC * kk : wc);
+        load_16_async(qreg[rt][kk], qp + 64 * kg);
+      }
+    }
+  };
+  // the same from a query tile in the ring (staged like key rows)
+  auto read_q_tile = [&](const MLA_LDS char* slot) {
+#pragma unroll
+    for (int rt = 0; rt < C::RT; ++rt) {
+      const int row = wrow0 + 16 * rt + li;
+      const MLA_LDS char* rb = slot + row * C::PITCH;
+      const int sw = lds_swz(row & 15);
+#pragma unroll
+      for (int kk = 0; kk < C::KW; ++kk) {
+        const int c = 4 * kk + g;  // 16-byte chunk of k-step kk
+        const MLA_LDS QV* qp = (const MLA_LDS QV*)(rb + (((c & ~7) | ((c & 7) ^ sw)) << 4));
+        qreg[rt][kk] = qvalid[rt] ? *qp : QV{};
+      }
+    }
+  };
+  auto settle_q = [&]() {
+#pragma unroll
+    for (int rt = 0; rt < C::RT; ++rt)
+#pragma unroll
+      for (int kk = 0; kk < C::KW; ++kk) {
+        settle(qreg[rt][kk]);
+        if (!qvalid[rt]) qreg[rt][kk] = QV{};
+      }
+  };
+  auto end_seg = [&]() {
+    const int unit_row0 = (cs.u % p.row_tiles) * p.rows_per_unit;
 #pragma unroll
     for (int rt = 0; rt < C::RT; ++rt) {
       const float lt = wave_sum16(st.l[rt]);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const float lse2 = lt > 0.f ? st.m[rt] + fast_log2(lt) : kNegInf;
-      store_row<C>(p, b, unit_row0, wrow0 + 16 * rt + li, slot, st.o[rt], inv, lse2);
+      store_row<C>(p, cs.b, unit_row0, wrow0 + 16 * rt + li, cs.slot, st.o[rt], inv, lse2, dc0,
+                   wc == 0);
     }
-    __syncthreads();  // the ring is reused by the next segment
-  } else {
-    // token-split: merge the WT waves' states for the shared 16 rows via LDS
-    static_assert(C::RT == 1, "token-split layout holds one row tile");
-    __syncthreads();  // every wave is done with its ring
-    const float lt = wave_sum16(st.l[0]);
-    MLA_LDS char* xo = ring_all;  // [WT][DT][64] f32x4
-    MLA_LDS float* xs = (MLA_LDS float*)(ring_all + C::WT * C::DT * 64 * 16);  // m,l [WT][2][16]
+  };
+
+  if (compute) {
+    begin_state();
+    load_q();  // out before the block-table staging waits
+  }
+  stage_block_table<C>(p, pl, u0, w0, w1, chunk, sh_blk);
+  if (loader) {
 #pragma unroll
-    for (int d = 0; d < C::DT; ++d)
-      *(MLA_LDS f32x4_t*)(xo + ((wt * C::DT + d) * 64 + lane) * 16) = st.o[0][d];
-    if (g == 0) {
-      xs[(wt * 2 + 0) * 16 + li] = st.m[0];
-      xs[(wt * 2 + 1) * 16 + li] = lt;
+    for (int k = 0; k < C::NSLOT - 1; ++k)
+      if (k < nsteps) {
+        const NextTile t = prep_next(k);
+#pragma unroll
+        for (int st3 = 0; st3 < 3; ++st3) issue_part(t, st3);
+      }
+  }
+  if (compute) {
+    // retire the query loads (with no loader waves they are older than every tile read in flight)
+    if constexpr (C::NP == 0) {
+      const int pro = nsteps < C::NSLOT - 1 ? nsteps : C::NSLOT - 1;
+      if (pro <= 0) wait_vmcnt<0>();
+      else if (pro == 1) wait_vmcnt<C::LPW>();
+      else if (pro == 2) wait_vmcnt<(C::NSLOT >= 3 ? 2 * C::LPW : 0)>();
+      else wait_vmcnt<(C::NSLOT >= 4 ? 3 * C::LPW : 0)>();
+    } else {
+      wait_vmcnt<0>();
     }
-    __syncthreads();
-    float mw[C::WT], aw[C::WT];
-    float M = kNegInf;
+    settle_q();
+  }
+  if constexpr (C::NP > 0) {
+    // ---- separate roles: each runs its own loop (one barrier per stream item)
+    if (loader) {
+      for (int k = 0; k < nsteps; ++k) {
+        wait_tile(k);
+        __syncthreads();
+        if (k + C::NSLOT - 1 < nsteps) {
+          const NextTile nt = prep_next(k + C::NSLOT - 1);
 #pragma unroll
-    for (int w = 0; w < C::WT; ++w) {
-      mw[w] = xs[(w * 2 + 0) * 16 + li];
-      M = fmaxf(M, mw[w]);
-    }
-    float Lt = 0.f;
-#pragma unroll
-    for (int w = 0; w < C::WT; ++w) {
-      aw[w] = mw[w] == kNegInf ? 0.f : fast_exp2(mw[w] - M);
-      Lt += aw[w] * xs[(w * 2 + 1) * 16 + li];
-    }
-    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-    const float lse2 = Lt > 0.f ? M + fast_log2(Lt) : kNegInf;
-    // wave wt finalises column tiles [wt*DT/WT, (wt+1)*DT/WT)
-    constexpr int DPW = C::DT / C::WT;
-    f32x4_t acc[DPW];
-#pragma unroll
-    for (int d = 0; d < DPW; ++d) acc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dd = 0; dd < DPW; ++dd) {
-      const int d = wt * DPW + dd;
-#pragma unroll
-      for (int w = 0; w < C::WT; ++w)
-        acc[dd] += aw[w] * *(const MLA_LDS f32x4_t*)(xo + ((w * C::DT + d) * 64 + lane) * 16);
-    }
-    // write this wave's quarter: reuse store_row on a shifted column window
-    const int rows_seq2 = p.q_len * p.n_heads;
-    const int r = unit_row0 + li;
-    if (r < rows_seq2) {
-      if (slot >= 0) {
-        float* dst = p.part_o + ((int64_t)slot * p.rows_per_unit + li) * kKvRank + 4 * g;
-#pragma unroll
-        for (int dd = 0; dd < DPW; ++dd)
-          *(f32x4_t*)(dst + 16 * (wt * DPW + dd)) = acc[dd] * inv;
-        if (g == 0 && wt == 0) p.part_lse[(int64_t)slot * p.rows_per_unit + li] = lse2;
-      } else {
-        const int qi = r / p.n_heads, qh = r % p.n_heads;
-        const int64_t ooff =
-            (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)qh * p.o_s2 + 4 * g;
-        if constexpr (C::F32) {
-          float* dst = (float*)p.out + ooff;
-#pragma unroll
-          for (int dd = 0; dd < DPW; ++dd) *(f32x4_t*)(dst + 16 * (wt * DPW + dd)) = acc[dd] * inv;
-        } else {
-          uint16_t* dst = (uint16_t*)p.out + ooff;
-#pragma unroll
-          for (int dd = 0; dd < DPW; ++dd) {
-            const f32x4_t x = acc[dd] * inv;
-            *(u32x2_t*)(dst + 16 * (wt * DPW + dd)) =
-                u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-          }
+          for (int st3 = 0; st3 < 3; ++st3) issue_part(nt, st3);
         }
-        if (g == 0 && wt == 0 && p.lse)
-          p.lse[(int64_t)b * p.l_s0 + (int64_t)qi * p.l_s1 + (int64_t)qh * p.l_s2] =
-              lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+      }
+      return;
+    }
+    bool q_tile = false;  // the next stream item is a segment's query tile
+    for (int k = 0; k < nsteps; ++k) {
+      __syncthreads();
+      const MLA_LDS char* slot = ring + (k % C::NSLOT) * C::TILE_BYTES;
+      if (q_tile) {
+        read_q_tile(slot);
+        q_tile = false;
+        continue;
+      }
+      tile_compute<C>(slot, xchg, cs.t_lo + ck * C::TT, qreg, st, p.scale_log2, wr, wc, dc0,
+                      [](int) {});
+      if (++ck == cs.ntiles && k + 1 < nsteps) {
+        end_seg();
+        cs = make_seg<C>(p, pl, next_unit(p, sh, cs.u, w1), w0, w1, chunk);
+        ck = 0;
+        begin_state();
+        q_tile = true;
       }
     }
-    __syncthreads();
+    end_seg();
+  } else {
+    // ---- every wave loads and computes
+    bool q_pending = false;
+    for (int k = 0; k < nsteps; ++k) {
+      if (q_pending) {
+        // query rows of a new segment were loaded after every tile read in flight
+        wait_vmcnt<0>();
+        settle_q();
+        q_pending = false;
+      } else {
+        wait_tile(k);
+      }
+      __syncthreads();
+      const NextTile nt = k + C::NSLOT - 1 < nsteps ? prep_next(k + C::NSLOT - 1) : NextTile{};
+      tile_compute<C>(ring + (k % C::NSLOT) * C::TILE_BYTES, xchg, cs.t_lo + ck * C::TT, qreg, st,
+                      p.scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); });
+      if (++ck == cs.ntiles && k + 1 < nsteps) {
+        end_seg();
+        cs = make_seg<C>(p, pl, next_unit(p, sh, cs.u, w1), w0, w1, chunk);
+        ck = 0;
+        begin_state();
+        load_q();
+        q_pending = true;
+      }
+    }
+    end_seg();
   }
 }
 
 template <class C>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(C::NT, C::NT),
+                               amdgpu_waves_per_eu(C::NT / 256, C::NT / 256)))
 decode_partial(DecodeParams p) {
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
-  __shared__ int sh_scan[256];
+  __shared__ PlanLds plan;
+  __shared__ int sh_blk[kBlkCache];
   MLA_LDS char* ring = (MLA_LDS char*)smem_raw;
+  MLA_LDS f32x4_t* xchg = (MLA_LDS f32x4_t*)(smem_raw + C::RING_BYTES);
   if (!p.split) {
-    const int u = p.num_units - 1 - (int)blockIdx.x;  // heaviest (latest) row tiles first
-    process_segment<C>(p, u, 0, 0x7fffffff, -1, ring);
+    // one unit per workgroup, heaviest (latest) row tiles first
+    process_range<C>(p, &plan, sh_blk, p.num_units - 1 - (int)blockIdx.x, 0, 0x7fffffff, 1, ring,
+                     xchg);
     return;
   }
-  unit_scan(p, sh_scan);
-  const int total = sh_scan[p.num_units - 1];
+  plan_units(p, plan.scan, &plan);
+  const int total = plan.scan[p.num_units - 1];
   const int chunk = total > 0 ? ceil_div(total, p.grid) : 1;
   const int w0 = (int)blockIdx.x * chunk;
   const int w1 = w0 + chunk < total ? w0 + chunk : total;
@@ -521,30 +947,26 @@ decode_partial(DecodeParams p) {
   int lo = 0, hi = p.num_units - 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (sh_scan[mid] > w0) hi = mid; else lo = mid + 1;
+    if (plan.scan[mid] > w0) hi = mid; else lo = mid + 1;
   }
-  for (int u = lo; u < p.num_units; ++u) {
-    const int end = sh_scan[u];
-    const int start = u > 0 ? sh_scan[u - 1] : 0;
-    if (start >= w1) break;
-    if (end == start) continue;
-    const int a = (w0 > start ? w0 : start) - start;
-    const int e = (w1 < end ? w1 : end) - start;
-    const bool split = (start / chunk) != ((end - 1) / chunk);
-    process_segment<C>(p, u, a * kWorkBlock, e * kWorkBlock, split ? (int)blockIdx.x + u : -1, ring);
-  }
+  process_range<C>(p, &plan, sh_blk, lo, w0, w1, chunk, ring, xchg);
 }
 
 // ------------------------------------------------------------------- merge
-// One workgroup per (unit, 4 rows); 64 threads per row, 8 columns each.
+// Merge of the split partials. One workgroup per
+// (unit, 4 rows), 64 threads per row with 8 columns each. Each row's split
+// lse values are read in one pass (one split per lane) and reduced with lane
+// swaps; weights go through LDS; partial rows are then read in batches of 8.
 template <bool F32>
 __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   __shared__ int sh_scan[256];
-  unit_scan(p, sh_scan);
+  __shared__ float sh_w[4][64];
+  plan_units(p, sh_scan, nullptr);
   const int groups = (p.rows_per_unit + 3) / 4;
   const int u = blockIdx.x / groups;
-  const int row = (blockIdx.x % groups) * 4 + (threadIdx.x >> 6);
-  const int c0 = (threadIdx.x & 63) * 8;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = (blockIdx.x % groups) * 4 + wv;
+  const int c0 = lane * 8;
   if (u >= p.num_units || row >= p.rows_per_unit) return;
   const int total = sh_scan[p.num_units - 1];
   const int chunk = total > 0 ? ceil_div(total, p.grid) : 1;
@@ -552,42 +974,61 @@ __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   const int b = u / p.row_tiles;
   const int r = (u % p.row_tiles) * p.rows_per_unit + row;
   if (r >= p.q_len * p.n_heads) return;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float lse2 = kNegInf;
   if (end > start) {
     const int first = start / chunk, last = (end - 1) / chunk;
     if (first == last) return;  // written directly by its only workgroup
-    float M = kNegInf;
-    for (int w = first; w <= last; ++w)
-      M = fmaxf(M, p.part_lse[(int64_t)(w + u) * p.rows_per_unit + row]);
-    float Lt = 0.f;
-    for (int w = first; w <= last; ++w) {
-      const float ls = p.part_lse[(int64_t)(w + u) * p.rows_per_unit + row];
-      const float a = ls == kNegInf ? 0.f : fast_exp2(ls - M);
-      Lt += a;
-      const float* src = p.part_o + ((int64_t)(w + u) * p.rows_per_unit + row) * kKvRank + c0;
-      const f32x4_t x0 = *(const f32x4_t*)src, x1 = *(const f32x4_t*)(src + 4);
+    const int n = last - first + 1;  // <= 64 (each split is a distinct workgroup of <= 256 + units)
+    const int64_t srow = (int64_t)p.rows_per_unit;
+    float M = kNegInf, Lt = 0.f;
+    for (int w0 = 0; w0 < n; w0 += 64) {
+      const float ls = w0 + lane < n ? p.part_lse[(int64_t)(first + w0 + lane + u) * srow + row] : kNegInf;
+      M = fmaxf(M, ls);
+    }
+    // M over all lanes
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float* op = p.part_o + ((int64_t)(first + u) * srow + row) * kKvRank + c0;
+    const int64_t ostride = srow * kKvRank;
+    for (int w0 = 0; w0 < n; w0 += 64) {
+      const int cnt = n - w0 < 64 ? n - w0 : 64;
+      const float ls = lane < cnt ? p.part_lse[(int64_t)(first + w0 + lane + u) * srow + row] : kNegInf;
+      sh_w[wv][lane] = ls == kNegInf ? 0.f : fast_exp2(ls - M);
+      for (int k0 = 0; k0 < cnt; k0 += 8) {
+        f32x4_t x0[8], x1[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[j] += a * x0[j];
-        acc[4 + j] += a * x1[j];
+        for (int k = 0; k < 8; ++k) {
+          if (k0 + k < cnt) {
+            x0[k] = *(const f32x4_t*)(op + (w0 + k0 + k) * ostride);
+            x1[k] = *(const f32x4_t*)(op + (w0 + k0 + k) * ostride + 4);
+          } else {
+            x0[k] = x1[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float a = k0 + k < cnt ? sh_w[wv][k0 + k] : 0.f;
+          Lt += a;
+          acc0 += a * x0[k];
+          acc1 += a * x1[k];
+        }
       }
     }
     const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] *= inv;
+    acc0 *= inv;
+    acc1 *= inv;
     lse2 = Lt > 0.f ? M + fast_log2(Lt) : kNegInf;
   }
   const int qi = r / p.n_heads, qh = r % p.n_heads;
   const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)qh * p.o_s2 + c0;
   if constexpr (F32) {
     float* dst = (float*)p.out + ooff;
-    *(f32x4_t*)dst = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
-    *(f32x4_t*)(dst + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+    *(f32x4_t*)dst = acc0;
+    *(f32x4_t*)(dst + 4) = acc1;
   } else {
     uint16_t* dst = (uint16_t*)p.out + ooff;
-    *(u32x4_t*)dst = u32x4_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    *(u32x4_t*)dst = u32x4_t{pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
+                             pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
   }
   if (c0 == 0 && p.lse)
     p.lse[(int64_t)b * p.l_s0 + (int64_t)qi * p.l_s1 + (int64_t)qh * p.l_s2] =
@@ -595,15 +1036,17 @@ __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
 }
 
 // ------------------------------------------------------------- variants
-// id: layout (token-split / row-split), rope width, dtype
-using TokSplit64 = Cfg<64, 1, 4, 1, 16, 2, false>;
-using TokSplit0 = Cfg<0, 1, 4, 1, 16, 2, false>;
-using RowSplit64 = Cfg<64, 4, 1, 1, 32, 4, false>;
-using RowSplit0 = Cfg<0, 4, 1, 1, 32, 4, false>;
-using TokSplitF64 = Cfg<64, 1, 4, 1, 16, 1, true>;
-using TokSplitF0 = Cfg<0, 1, 4, 1, 16, 1, true>;
+//                      R   WR WC RT TT NSLOT F32    XS     NP
+using Cols64  = Cfg<64, 1, 4, 1, 32, 4, false, false, 4>;  // <= 16 rows: columns split over waves
+using Cols0   = Cfg<0,  1, 4, 1, 32, 4, false, false, 4>;
+using Mixed64 = Cfg<64, 2, 2, 1, 32, 4, false, true,  0>;  // <= 32 rows
+using Mixed0  = Cfg<0,  2, 2, 1, 32, 4, false, true,  0>;
+using Rows64  = Cfg<64, 4, 1, 1, 32, 4, false, false, 0>;  // many rows: rows split over waves
+using Rows0   = Cfg<0,  4, 1, 1, 32, 4, false, false, 0>;
+using ColsF64 = Cfg<64, 1, 4, 1, 16, 4, true,  true,  0>;  // f32
+using ColsF0  = Cfg<0,  1, 4, 1, 16, 4, true,  true,  0>;
 
-enum Variant { kTok64 = 0, kTok0, kRow64, kRow0, kTokF64, kTokF0 };
+enum Variant { kCols64 = 0, kCols0, kMixed64, kMixed0, kRows64, kRows0, kColsF64, kColsF0 };
 
 template <class C>
 hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStream_t s) {
@@ -615,9 +1058,8 @@ hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStre
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipError_t e;
   hipLaunchKernelGGL(decode_partial<C>, dim3(plan.grid), dim3(C::NT), smem, s, p);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || !plan.split) return e;
   const int groups = (plan.rows_per_unit + 3) / 4;
   hipLaunchKernelGGL(decode_merge<C::F32>, dim3(plan.num_units * groups), dim3(256), 0, s, p);
@@ -629,18 +1071,19 @@ hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStre
 int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int64_t max_seqlen,
                 int is_f32, DecodePlan* plan) {
   const int64_t rows = q_len * n_heads;
-  const bool row_split = !is_f32 && rows > 16;
-  int variant;
-  int rtile;
+  int variant, rtile;
   if (is_f32) {
-    variant = rope ? kTokF64 : kTokF0;
-    rtile = 16;
-  } else if (row_split) {
-    variant = rope ? kRow64 : kRow0;
-    rtile = RowSplit64::RTILE;
+    variant = rope ? kColsF64 : kColsF0;
+    rtile = ColsF64::RTILE;
+  } else if (rows <= 16) {
+    variant = rope ? kCols64 : kCols0;
+    rtile = Cols64::RTILE;
+  } else if (rows <= 32) {
+    variant = rope ? kMixed64 : kMixed0;
+    rtile = Mixed64::RTILE;
   } else {
-    variant = rope ? kTok64 : kTok0;
-    rtile = 16;
+    variant = rope ? kRows64 : kRows0;
+    rtile = Rows64::RTILE;
   }
   const int64_t row_tiles = (rows + rtile - 1) / rtile;
   const int64_t units = batch * row_tiles;
@@ -656,7 +1099,8 @@ int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int
     if (g > wb_bound) g = wb_bound;
     plan->grid = (int)g;
     const int64_t slots = g + units;
-    plan->workspace_bytes = (size_t)(slots * rtile * (kKvRank + 1) * 4 + 256);
+    // partials [slots][rtile][L] f32, then lse [slots][rtile] f32
+    plan->workspace_bytes = (size_t)(slots * rtile * (kKvRank + 1) * 4);
   } else {
     plan->split = 0;
     plan->grid = (int)units;
@@ -671,12 +1115,14 @@ hipError_t launch_decode(const DecodePlan& plan, DecodeParams p, int64_t rope, i
   (void)is_f32;
   if (plan.grid <= 0) return hipSuccess;
   switch (plan.variant) {
-    case kTok64: return launch_variant<TokSplit64>(plan, p, s);
-    case kTok0: return launch_variant<TokSplit0>(plan, p, s);
-    case kRow64: return launch_variant<RowSplit64>(plan, p, s);
-    case kRow0: return launch_variant<RowSplit0>(plan, p, s);
-    case kTokF64: return launch_variant<TokSplitF64>(plan, p, s);
-    case kTokF0: return launch_variant<TokSplitF0>(plan, p, s);
+    case kCols64: return launch_variant<Cols64>(plan, p, s);
+    case kCols0: return launch_variant<Cols0>(plan, p, s);
+    case kMixed64: return launch_variant<Mixed64>(plan, p, s);
+    case kMixed0: return launch_variant<Mixed0>(plan, p, s);
+    case kRows64: return launch_variant<Rows64>(plan, p, s);
+    case kRows0: return launch_variant<Rows0>(plan, p, s);
+    case kColsF64: return launch_variant<ColsF64>(plan, p, s);
+    case kColsF0: return launch_variant<ColsF0>(plan, p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -18,18 +18,18 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 #define MLA_LDS __attribute__((address_space(3)))
 
 // ---------------------------------------------------------------- bf16
-// f32 -> bf16, round to nearest even; NaN stays a quiet NaN of the same sign.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// f32 -> bf16 pairs with gfx950's v_cvt_pk_bf16_f32 (round to nearest even,
+// NaN stays NaN); the compiler selects it for these conversions.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
-}
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
 // ---------------------------------------------------------------- MFMA
@@ -81,20 +81,74 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Global -> LDS 16-byte load: each lane's 16 bytes land at lds_base + 16*lane.
+// Global -> LDS 16-byte load: each lane's 16 bytes land at lds_base + 16*lane
+// (lds_base must be wave-uniform; it goes to M0). Issued as inline assembly so
+// the compiler's wait insertion does not model it: callers wait for these
+// loads themselves with wait_vmcnt<>. The compiler's own vector-memory waits
+// stay correct because vector memory operations complete in issue order.
 __device__ __forceinline__ void load_lds_16(const void* gptr, MLA_LDS void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(m0v)
+               : "memory", "m0");
 }
 
-__device__ __forceinline__ float wave_max16(float v) {  // max over lanes l, l^16, l^32, l^48
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// The same load addressed as a wave-uniform 64-bit base (an SGPR pair) plus a
+// per-lane 32-bit byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void load_lds_16_sbase(const void* sbase, uint32_t voff,
+                                                  MLA_LDS void* lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0v)
+               : "memory", "m0");
+}
+
+// 16-byte global load issued as inline assembly (not modelled by the compiler's
+// wait insertion, like load_lds_16). The result must not be used before a
+// wait_vmcnt<> that retires it followed by settle() on the destination.
+template <class T>
+__device__ __forceinline__ void load_16_async(T& dst, const void* gptr) {
+  static_assert(sizeof(T) == 16, "16-byte register");
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(gptr) : "memory");
+}
+// Tell the compiler a register is (re)defined here: its uses stay after this
+// point. Placed after the wait that retires an asynchronous load into it.
+template <class T>
+__device__ __forceinline__ void settle(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Reductions over lanes {l, l^16, l^32, l^48} with gfx950's permlane swaps:
+// v_permlane32_swap a, b exchanges a's upper 32 lanes with b's lower 32, so
+// with a = b = v it leaves (v[l & ~32], v[l | 32]) in (a, b); v_permlane16_swap
+// does the same for 16-lane halves. Both are plain VALU. They are issued as
+// inline assembly with both registers as in/out operands (the compiler's
+// builtin for them merged the two results into one), with the wait states
+// the instruction needs around it.
+__device__ __forceinline__ void lane_pairs(float v, int width, float& a, float& b) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+  if (width == 32)
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  else
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float wave_max16(float v) {
+  float a, b;
+  lane_pairs(v, 32, a, b);
+  v = fmaxf(a, b);
+  lane_pairs(v, 16, a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float wave_sum16(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  float a, b;
+  lane_pairs(v, 32, a, b);
+  v = a + b;
+  lane_pairs(v, 16, a, b);
+  return a + b;
 }
 
 }  // namespace mla

@@ -185,3 +185,28 @@ def test_v3_full_config_block_major():
     out_v, lse_v = check(c, "V3 decode B=4 x 4096 block-major view", block_major=True)
     out_c, lse_c = run_decode(c, block_major=False)
     assert torch.equal(out_c.view(torch.int16), out_v.view(torch.int16))
+
+
+def test_workspace_reused_across_calls():
+    # one uninitialised workspace serves a sequence of calls of different plans
+    import mla_absorbed_decode_amd as mla
+    from helpers import DeviceCache, dev, to_dev
+
+    cases = [mi.decode_case(s, V2, "bf16", sl, max_blocks=40)
+             for s, sl in ((21, [2500, 90, 700, 1300]), (22, [64, 2000, 2048, 5]),
+                           (21, [2500, 90, 700, 1300]))]
+    nbytes = mla.mla_decode_workspace_size(4, 1, 16, 512, 2560, 64, torch.bfloat16)
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=dev())
+    outs = []
+    for i, c in enumerate(cases):
+        say(f"[decode] workspace reuse call {i}")
+        out = torch.empty(4, 1, 16, 512, dtype=torch.bfloat16, device=dev())
+        mla.mla_decode_attend(to_dev(c.q, "bf16"), DeviceCache(c, False).view,
+                              torch.from_numpy(c.block_table).to(dev()),
+                              torch.from_numpy(c.seqlens).to(dev()), 2560, c.scale, True, out,
+                              None, workspace=ws)
+        torch.cuda.synchronize()
+        want, _ = oracle_of(c)
+        assert_close(to_np(out), want, "bf16", f"workspace reuse call {i}")
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
