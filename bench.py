@@ -127,6 +127,37 @@ def replay(graphs, first: int, count: int):
     return t0.elapsed_time(t1)
 
 
+def time_steps_eager(step: Step, steps: int, warmup: int):
+    """As time_steps, every call launched from the host."""
+    for i in range(warmup):
+        step.run(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(warmup, warmup + steps):
+        step.run(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    t0.record()
+    for i in range(warmup, warmup + steps):
+        step.attend(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return total_ms, wall, t0.elapsed_time(t1) / steps
+
+
+def copy_calibration(dev):
+    """A plain device copy of a known 256 MiB (three times)."""
+    src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def time_steps(step: Step, steps: int, warmup: int):
     """(ms for `steps` whole steps, host seconds for them, ms per attention call)."""
     n = len(step.caches)
@@ -251,6 +282,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-v3", action="store_true", help="skip the 128-head secondary line")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call from the host instead of replaying graphs "
+                         "(for counter collection)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy three times (reference for "
+                         "scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this implementation runs on a single MI355X and has "
@@ -270,7 +307,10 @@ def main():
           f"KV {touched / 1e6:.1f} MB, {copies} cache copies", file=sys.stderr, flush=True)
 
     torch.cuda.synchronize()
-    total_ms, wall, attn_avg_ms = time_steps(step, args.steps, args.warmup)
+    timer = time_steps_eager if args.eager else time_steps
+    total_ms, wall, attn_avg_ms = timer(step, args.steps, args.warmup)
+    if args.copy_calibration:
+        copy_calibration(dev)
     ms_per_step = total_ms / args.steps
     kv_gbs = touched / (ms_per_step * 1e-3) / 1e9
     pairs = int(case.seqlens.astype(np.int64).sum()) * case.dims.n_head
