@@ -90,8 +90,9 @@ __device__ __forceinline__ int unit_kvlen(const DecodeParams& p, int u) {
   return row_limit(p, s, r_last / p.n_heads);
 }
 
-// The split plan in LDS: per unit, the inclusive prefix of work-block counts,
-// the keys the unit needs and its sequence's length.
+// The split plan in LDS: per unit, the inclusive prefix of work-block counts
+// (blocks of p.wb tokens), the keys the unit needs and its sequence's length.
+// Unit u's work block i is plan position scan[u-1] + i.
 struct PlanLds {
   int scan[256];
   int kv[256];
@@ -115,7 +116,7 @@ __device__ void plan_units(const DecodeParams& p, int* sh, PlanLds* pl) {
         pl->kv[u] = n;
         pl->sl[u] = u < p.num_units ? seq_len(p, u / p.row_tiles) : 0;
       }
-      run += ceil_div(n, kWorkBlock);
+      run += ceil_div(n, p.wb);
       v[k] = run;
     }
     int x = run;
@@ -531,12 +532,15 @@ __device__ __forceinline__ Seg make_seg(const DecodeParams& p, const PlanLds* pl
     sg.t_hi = kvlen;
     sg.slot = -1;
   } else {
-    const int start = u > 0 ? pl->scan[u - 1] : 0, end = pl->scan[u];
-    const int a = (w0 > start ? w0 : start) - start;
-    const int e = (w1 < end ? w1 : end) - start;
-    sg.t_lo = a * kWorkBlock;
-    sg.t_hi = e * kWorkBlock < kvlen ? e * kWorkBlock : kvlen;
-    sg.slot = (start / chunk != (end - 1) / chunk) ? (int)blockIdx.x + u : -1;
+    // work blocks [i_lo, i_hi) of the unit lie in this workgroup's positions [w0, w1)
+    const int first = u > 0 ? pl->scan[u - 1] : 0, end = pl->scan[u];
+    const int i_lo = (w0 > first ? w0 : first) - first;
+    const int i_hi = (w1 < end ? w1 : end) - first;
+    sg.t_lo = i_lo * p.wb;
+    sg.t_hi = i_hi * p.wb < kvlen ? i_hi * p.wb : kvlen;
+    if (sg.t_hi < sg.t_lo) sg.t_hi = sg.t_lo;
+    // split when the unit's work blocks reach more than one workgroup
+    sg.slot = (first / chunk != (end - 1) / chunk) ? (int)blockIdx.x + u : -1;
   }
   sg.ntiles = sg.t_hi > sg.t_lo ? ceil_div(sg.t_hi - sg.t_lo, C::TT) : 0;
   return sg;
@@ -549,13 +553,20 @@ __device__ __forceinline__ int seg_pages(const DecodeParams& p, const Seg& sg) {
 
 
 
-// Next unit with work after u, or num_units.
-__device__ __forceinline__ int next_unit(const DecodeParams& p, const int* sh, int u, int w1) {
+// Whether unit u has work blocks among positions [w0, w1).
+__device__ __forceinline__ bool unit_in_range(const DecodeParams& p, const int* sh, int u, int w0,
+                                              int w1) {
+  const int first = u > 0 ? sh[u - 1] : 0, end = sh[u];
+  return (w0 > first ? w0 : first) < (w1 < end ? w1 : end);
+}
+
+// Next unit with work in [w0, w1) after u, or num_units.
+__device__ __forceinline__ int next_unit(const DecodeParams& p, const int* sh, int u, int w0,
+                                         int w1) {
   if (!p.split) return p.num_units;
   for (++u; u < p.num_units; ++u) {
-    const int start = u > 0 ? sh[u - 1] : 0;
-    if (start >= w1) return p.num_units;
-    if (sh[u] > start) return u;
+    if ((u > 0 ? sh[u - 1] : 0) >= w1) return p.num_units;
+    if (unit_in_range(p, sh, u, w0, w1)) return u;
   }
   return p.num_units;
 }
@@ -573,7 +584,7 @@ __device__ void stage_block_table(const DecodeParams& p, const PlanLds* pl, int 
 #pragma unroll
   for (int k = 0; k < PER; ++k) need[k] = false;
   int off = 0;
-  for (int u = u0; u < p.num_units && off < kBlkCache; u = next_unit(p, pl->scan, u, w1)) {
+  for (int u = u0; u < p.num_units && off < kBlkCache; u = next_unit(p, pl->scan, u, w0, w1)) {
     const Seg sg = make_seg<C>(p, pl, u, w0, w1, chunk);
     const int n = seg_pages(p, sg), pf = sg.t_lo / p.page;
 #pragma unroll
@@ -607,7 +618,7 @@ __device__ void stage_block_table(const DecodeParams& p, const PlanLds* pl, int 
 // never stall on a full memory queue; without them the compute waves send the
 // next tile's reads in three groups between their own phases.
 template <class C>
-__device__ void process_range(const DecodeParams& p, const PlanLds* pl, int* sh_blk, int u0,
+__device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl, int* sh_blk, int u0,
                               int w0, int w1, int chunk, MLA_LDS char* ring,
                               MLA_LDS f32x4_t* xchg) {
   const int* sh = pl->scan;
@@ -627,7 +638,7 @@ __device__ void process_range(const DecodeParams& p, const PlanLds* pl, int* sh_
 
   // total tiles of the range
   int nsteps = 0;
-  for (int u = u0; u < p.num_units; u = next_unit(p, sh, u, w1)) {
+  for (int u = u0; u < p.num_units; u = next_unit(p, sh, u, w0, w1)) {
     const int nt = make_seg<C>(p, pl, u, w0, w1, chunk).ntiles;
     nsteps += nt + (C::QT && nt > 0 && u != u0 ? 1 : 0);
   }
@@ -675,7 +686,7 @@ __device__ void process_range(const DecodeParams& p, const PlanLds* pl, int* sh_
     // segments in split mode have tiles; an empty unit (no split) is never reached
     while (lk >= ls.ntiles && (lq || !C::QT) && ls.u < p.num_units) {
       ls_off += seg_pages(p, ls);
-      ls = make_seg<C>(p, pl, next_unit(p, sh, ls.u, w1), w0, w1, chunk);
+      ls = make_seg<C>(p, pl, next_unit(p, sh, ls.u, w0, w1), w0, w1, chunk);
       lk = 0;
       lq = false;
     }
@@ -871,8 +882,7 @@ __device__ void process_range(const DecodeParams& p, const PlanLds* pl, int* sh_
           for (int st3 = 0; st3 < 3; ++st3) issue_part(nt, st3);
         }
       }
-      return;
-    }
+    } else {
     bool q_tile = false;  // the next stream item is a segment's query tile
     for (int k = 0; k < nsteps; ++k) {
       __syncthreads();
@@ -886,13 +896,14 @@ __device__ void process_range(const DecodeParams& p, const PlanLds* pl, int* sh_
                       [](int) {});
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
-        cs = make_seg<C>(p, pl, next_unit(p, sh, cs.u, w1), w0, w1, chunk);
+        cs = make_seg<C>(p, pl, next_unit(p, sh, cs.u, w0, w1), w0, w1, chunk);
         ck = 0;
         begin_state();
         q_tile = true;
       }
     }
     end_seg();
+    }
   } else {
     // ---- every wave loads and computes
     bool q_pending = false;
@@ -911,7 +922,7 @@ __device__ void process_range(const DecodeParams& p, const PlanLds* pl, int* sh_
                       p.scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); });
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
-        cs = make_seg<C>(p, pl, next_unit(p, sh, cs.u, w1), w0, w1, chunk);
+        cs = make_seg<C>(p, pl, next_unit(p, sh, cs.u, w0, w1), w0, w1, chunk);
         ck = 0;
         begin_state();
         load_q();
@@ -931,25 +942,26 @@ decode_partial(DecodeParams p) {
   __shared__ int sh_blk[kBlkCache];
   MLA_LDS char* ring = (MLA_LDS char*)smem_raw;
   MLA_LDS f32x4_t* xchg = (MLA_LDS f32x4_t*)(smem_raw + C::RING_BYTES);
+  // this workgroup's stream: units from u0, plan positions [w0, w1)
+  int u0, w0 = 0, w1 = 0x7fffffff, chunk = 1;
   if (!p.split) {
-    // one unit per workgroup, heaviest (latest) row tiles first
-    process_range<C>(p, &plan, sh_blk, p.num_units - 1 - (int)blockIdx.x, 0, 0x7fffffff, 1, ring,
-                     xchg);
-    return;
+    u0 = p.num_units - 1 - (int)blockIdx.x;  // one unit per workgroup, heaviest row tiles first
+  } else {
+    plan_units(p, plan.scan, &plan);
+    const int total = plan.scan[p.num_units - 1];
+    chunk = total > 0 ? ceil_div(total, p.grid) : 1;
+    w0 = (int)blockIdx.x * chunk;
+    w1 = w0 + chunk < total ? w0 + chunk : total;
+    if (w0 >= w1) return;
+    // first unit whose work blocks end past w0
+    int lo = 0, hi = p.num_units - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (plan.scan[mid] > w0) hi = mid; else lo = mid + 1;
+    }
+    u0 = lo;
   }
-  plan_units(p, plan.scan, &plan);
-  const int total = plan.scan[p.num_units - 1];
-  const int chunk = total > 0 ? ceil_div(total, p.grid) : 1;
-  const int w0 = (int)blockIdx.x * chunk;
-  const int w1 = w0 + chunk < total ? w0 + chunk : total;
-  if (w0 >= w1) return;
-  // first unit whose work ends past w0
-  int lo = 0, hi = p.num_units - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (plan.scan[mid] > w0) hi = mid; else lo = mid + 1;
-  }
-  process_range<C>(p, &plan, sh_blk, lo, w0, w1, chunk, ring, xchg);
+  process_range<C>(p, &plan, sh_blk, u0, w0, w1, chunk, ring, xchg);
 }
 
 // ------------------------------------------------------------------- merge
@@ -1092,7 +1104,9 @@ int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int
   plan->rows_per_unit = rtile;
   plan->row_tiles = (int)row_tiles;
   plan->num_units = (int)units;
-  const int64_t wb_bound = batch * row_tiles * ((max_seqlen + kWorkBlock - 1) / kWorkBlock);
+  // plan granularity: the variant's tile
+  plan->wb = is_f32 ? ColsF64::TT : Cols64::TT;
+  const int64_t wb_bound = batch * row_tiles * ((max_seqlen + plan->wb - 1) / plan->wb);
   if (units < kSplitUnits && wb_bound > units) {
     plan->split = 1;
     int64_t g = 256;

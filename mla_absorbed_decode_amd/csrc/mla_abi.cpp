@@ -252,6 +252,7 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
     p.part_o = (float*)workspace;
     p.part_lse = (float*)((char*)workspace + (size_t)slots * plan.rows_per_unit * mla::kKvRank * 4);
   }
+  p.wb = plan.wb;
   p.rows_per_unit = plan.rows_per_unit;
   p.row_tiles = plan.row_tiles;
   p.num_units = plan.num_units;

@@ -10,7 +10,6 @@
 namespace mla {
 
 constexpr int kKvRank = 512;     // latent width L the attention kernels implement
-constexpr int kWorkBlock = 64;   // split-plan granularity, tokens
 constexpr int kSplitUnits = 256; // fewer (sequence, row-tile) units than this => split KV
 constexpr int kMaxUnitsSplit = 1024;
 
@@ -61,6 +60,7 @@ struct DecodeParams {
   int num_units;
   int split;              // 1: split-KV over `grid` workgroups + merge
   int grid;
+  int wb;                 // plan granularity: tokens per work block (the tile size)
 };
 
 // Launch plan chosen on the host from sizes alone (never from seqlens).
@@ -71,6 +71,7 @@ struct DecodePlan {
   int num_units;
   int split;
   int grid;
+  int wb;
   size_t workspace_bytes;
 };
 int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int64_t max_seqlen,
