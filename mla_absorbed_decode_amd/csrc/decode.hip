@@ -63,6 +63,11 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Page of token j (a shift for power-of-two pages).
+__device__ __forceinline__ int page_of(const DecodeParams& p, int j) {
+  return p.page_shift >= 0 ? j >> p.page_shift : j / p.page;
+}
+
 __device__ __forceinline__ int load_scalar_i32(const int32_t* p, int64_t idx) {
   return ((cint32_t*)(uintptr_t)p)[idx];
 }
@@ -548,7 +553,7 @@ __device__ __forceinline__ Seg make_seg(const DecodeParams& p, const PlanLds* pl
 
 // Pages a segment touches (its block-table entries).
 __device__ __forceinline__ int seg_pages(const DecodeParams& p, const Seg& sg) {
-  return sg.ntiles > 0 ? (sg.t_hi - 1) / p.page - sg.t_lo / p.page + 1 : 0;
+  return sg.ntiles > 0 ? page_of(p, sg.t_hi - 1) - page_of(p, sg.t_lo) + 1 : 0;
 }
 
 
@@ -586,7 +591,7 @@ __device__ void stage_block_table(const DecodeParams& p, const PlanLds* pl, int 
   int off = 0;
   for (int u = u0; u < p.num_units && off < kBlkCache; u = next_unit(p, pl->scan, u, w0, w1)) {
     const Seg sg = make_seg<C>(p, pl, u, w0, w1, chunk);
-    const int n = seg_pages(p, sg), pf = sg.t_lo / p.page;
+    const int n = seg_pages(p, sg), pf = page_of(p, sg.t_lo);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = (int)threadIdx.x + C::NT * k;
@@ -648,11 +653,13 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
   // here; other tiles (a segment's last, or pages shorter than a tile) take
   // the general path.
   const bool fast_ok = p.page % C::TT == 0 && (int64_t)p.page * pitch_g < ((int64_t)1 << 31);
-  uint32_t loff[C::LPW];
+  uint32_t loff[C::LPW];  // full tile: row * pitch + chunk offset
+  int lrow[C::LPW];       // the row; a partial tile clamps it to its last valid row
 #pragma unroll
   for (int n = 0; n < C::LPW; ++n) {
     const int idx = (lwave + n * C::LW) * 64 + lane;
     const int r = idx / C::CH, cpos = idx % C::CH;
+    lrow[n] = r;
     loff[n] = (uint32_t)(r * pitch_g) + (uint32_t)((cpos ^ lds_swz(r & 15)) << 4);
   }
   Seg ls = make_seg<C>(p, pl, u0, w0, w1, chunk);
@@ -661,7 +668,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
   int ls_off = 0;     // staged block-table position of ls's first page
   // cache block of page pg of segment ls (staged entry, or a global read past the stage)
   auto block_of = [&](int pg) -> int {
-    const int ti = ls_off + pg - ls.t_lo / p.page;
+    const int ti = ls_off + pg - page_of(p, ls.t_lo);
     int blk;
     if (ti < kBlkCache) {
       blk = sh_blk[ti];
@@ -704,47 +711,67 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
     t.nvalid = ls.t_hi - j0 < C::TT ? ls.t_hi - j0 : C::TT;
     ++lk;
     // each 16-token half of the tile lies in one page (page is a multiple of 16)
-    const int pg0 = j0 / p.page;
+    const int pg0 = page_of(p, j0);
     const int blk0 = block_of(pg0);
     t.base0 = kvbase + (int64_t)blk0 * p.kv_s0 * C::ES + (int64_t)(j0 - pg0 * p.page) * pitch_g;
-    t.fast = fast_ok && t.nvalid == C::TT;
+    t.fast = fast_ok;  // the whole tile lies in one page
     t.base1 = t.base0 + 16 * pitch_g;
     if constexpr (C::TT == 32) {
       const int j1 = j0 + 16;
-      if (!t.fast && j1 < ls.t_hi && (j1 / p.page) != pg0) {
-        const int pg1 = j1 / p.page;
+      if (!t.fast && j1 < ls.t_hi && page_of(p, j1) != pg0) {
+        const int pg1 = page_of(p, j1);
         const int blk1 = block_of(pg1);
         t.base1 = kvbase + (int64_t)blk1 * p.kv_s0 * C::ES + (int64_t)(j1 - pg1 * p.page) * pitch_g;
       }
     }
     return t;
   };
-  // reads n of this wave's share with n * 3 / LPW == stage
+  // global->LDS reads n of this wave's share (n * 3 / LPW == stage) of tile t
   auto issue_part = [&](const NextTile& t, int stage) {
     if (!t.live) return;
     MLA_LDS char* dst = ring + t.slot * C::TILE_BYTES;
+    if (C::QT && t.query) {
+      // query row i of the unit at row i of the slot, staged like a key row;
+      // reads past QI repeat one (same bytes to the same place), so every
+      // loader wave sends LPW reads for every tile
 #pragma unroll
-    for (int n = 0; n < C::LPW; ++n) {
-      if (n * 3 / C::LPW != stage) continue;
-      const int inst = lwave + n * C::LW;
-      if (C::QT && t.query) {
-        // query row i of the unit at row i of the slot, staged like a key row;
-        // reads past QI repeat one (same bytes to the same place), so every
-        // loader wave sends LPW reads for every tile
-        const int qinst = inst % C::QI;
+      for (int n = 0; n < C::LPW; ++n) {
+        if (n * 3 / C::LPW != stage) continue;
+        const int qinst = (lwave + n * C::LW) % C::QI;
         const int idx = qinst * 64 + lane;
         const int i = idx / C::CH, cpos = idx % C::CH;
         int r = t.qrow0 + i;
         r = r < rows_seq ? r : rows_seq - 1;  // rows past the end are zeroed by the compute waves
-        const int qi = r / p.n_heads, qh = r % p.n_heads;
+        const int qi = p.q_len == 1 ? 0 : r / p.n_heads, qh = p.q_len == 1 ? r : r % p.n_heads;
         const char* src = (const char*)p.q +
                           ((int64_t)t.qb * p.q_s0 + (int64_t)qi * p.q_s1 + (int64_t)qh * p.q_s2) * C::ES +
                           ((cpos ^ lds_swz(i & 15)) << 4);
         load_lds_16(src, dst + qinst * 1024);
-      } else if (t.fast) {
-        load_lds_16_sbase(t.base0, loff[n], dst + inst * 1024);
-      } else {
+      }
+    } else if (t.fast && t.nvalid == C::TT) {
+      // a full tile inside one page: page base + per-lane offsets
+      const uint64_t sb = uniform_ptr(t.base0);
+#pragma unroll
+      for (int n = 0; n < C::LPW; ++n) {
+        if (n * 3 / C::LPW != stage) continue;
+        load_lds_16_sbase(sb, loff[n], dst + (lwave + n * C::LW) * 1024);
+      }
+    } else if (t.fast) {
+      // a partial tile inside one page: rows past its end repeat its last valid row
+      const uint64_t sb = uniform_ptr(t.base0);
+      const int last = t.nvalid - 1;
+#pragma unroll
+      for (int n = 0; n < C::LPW; ++n) {
+        if (n * 3 / C::LPW != stage) continue;
+        const int over = lrow[n] > last ? lrow[n] - last : 0;
+        load_lds_16_sbase(sb, loff[n] - (uint32_t)(over * pitch_g), dst + (lwave + n * C::LW) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < C::LPW; ++n) {
+        if (n * 3 / C::LPW != stage) continue;
         // this lane's 16-byte slot of the tile: row r, stored chunk position cpos
+        const int inst = lwave + n * C::LW;
         const int idx = inst * 64 + lane;
         const int r = idx / C::CH, cpos = idx % C::CH;
         const int chunk16 = cpos ^ lds_swz(r & 15);

@@ -94,20 +94,22 @@ __device__ __forceinline__ void load_lds_16(const void* gptr, MLA_LDS void* lds_
                : "memory", "m0");
 }
 
-// The same load addressed as a wave-uniform 64-bit base (an SGPR pair) plus a
-// per-lane 32-bit byte offset: no per-lane 64-bit address arithmetic.
-__device__ __forceinline__ void load_lds_16_sbase(const void* sbase, uint32_t voff,
+// The same load addressed as a wave-uniform 64-bit base (an SGPR pair, see
+// uniform_ptr) plus a per-lane 32-bit byte offset: no per-lane 64-bit address
+// arithmetic.
+__device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
+  // readfirstlane returns a signed int: widen each half through uint32_t
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+__device__ __forceinline__ void load_lds_16_sbase(uint64_t sbase, uint32_t voff,
                                                   MLA_LDS void* lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  // the base is wave-uniform by contract; readfirstlane lets the compiler keep it in SGPRs
-  const uint64_t bv = (uint64_t)(uintptr_t)sbase;
-  // (readfirstlane returns a signed int: widen each half through uint32_t)
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bv);
-  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sb), "s"(m0v)
+               : "v"(voff), "s"(sbase), "s"(m0v)
                : "memory", "m0");
 }
 

@@ -45,6 +45,7 @@ struct DecodeParams {
   const void* kv; int64_t kv_s0, kv_s1;              // cache [NB, PG, E]
   int64_t num_blocks;
   int page;
+  int page_shift;         // log2(page) when page is a power of two, else -1
   const int32_t* block_table; int64_t bt_s0; int max_blocks;
   const int32_t* seqlens;
   int batch, q_len, n_heads;
