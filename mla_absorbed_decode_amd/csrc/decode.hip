@@ -95,20 +95,22 @@ __device__ __forceinline__ int unit_kvlen(const DecodeParams& p, int u) {
   return row_limit(p, s, r_last / p.n_heads);
 }
 
-// The split plan in LDS: per unit, the inclusive prefix of work-block counts
-// (blocks of p.wb tokens), the keys the unit needs and its sequence's length.
-// Unit u's work block i is plan position scan[u-1] + i.
+// The split plan in LDS: per unit, the inclusive prefix of unit costs (work
+// blocks of p.wb tokens, plus p.alpha for entering the unit), the keys the
+// unit needs and its sequence's length. Unit u occupies plan positions
+// [scan[u-1], scan[u]); the first alpha of them stand for the cost of
+// entering it and hold no keys, position scan[u-1] + alpha + i is work block i.
 struct PlanLds {
   int scan[256];
   int kv[256];
   int sl[256];
 };
 
-// Split plan shared by the partial and merge kernels: each unit's work-block
-// count and their inclusive prefix over units, computed by wave 0 with
-// register shuffles (up to 256 units, four per lane) and published in
-// sh[0..255] with one barrier; with pl given, the units' key counts and
-// sequence lengths go to pl->kv and pl->sl.
+// Split plan shared by the partial and merge kernels: each unit's cost and
+// their inclusive prefix over units, computed by wave 0 with register
+// shuffles (up to 256 units, four per lane) and published in sh[0..255] with
+// one barrier; with pl given, the units' key counts and sequence lengths go to
+// pl->kv and pl->sl. A unit with no keys costs nothing.
 __device__ void plan_units(const DecodeParams& p, int* sh, PlanLds* pl) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -121,7 +123,7 @@ __device__ void plan_units(const DecodeParams& p, int* sh, PlanLds* pl) {
         pl->kv[u] = n;
         pl->sl[u] = u < p.num_units ? seq_len(p, u / p.row_tiles) : 0;
       }
-      run += ceil_div(n, p.wb);
+      run += n > 0 ? ceil_div(n, p.wb) + p.alpha : 0;
       v[k] = run;
     }
     int x = run;
@@ -538,7 +540,7 @@ __device__ __forceinline__ Seg make_seg(const DecodeParams& p, const PlanLds* pl
     sg.slot = -1;
   } else {
     // work blocks [i_lo, i_hi) of the unit lie in this workgroup's positions [w0, w1)
-    const int first = u > 0 ? pl->scan[u - 1] : 0, end = pl->scan[u];
+    const int first = (u > 0 ? pl->scan[u - 1] : 0) + p.alpha, end = pl->scan[u];
     const int i_lo = (w0 > first ? w0 : first) - first;
     const int i_hi = (w1 < end ? w1 : end) - first;
     sg.t_lo = i_lo * p.wb;
@@ -561,7 +563,7 @@ __device__ __forceinline__ int seg_pages(const DecodeParams& p, const Seg& sg) {
 // Whether unit u has work blocks among positions [w0, w1).
 __device__ __forceinline__ bool unit_in_range(const DecodeParams& p, const int* sh, int u, int w0,
                                               int w1) {
-  const int first = u > 0 ? sh[u - 1] : 0, end = sh[u];
+  const int first = (u > 0 ? sh[u - 1] : 0) + p.alpha, end = sh[u];
   return (w0 > first ? w0 : first) < (w1 < end ? w1 : end);
 }
 
@@ -980,31 +982,33 @@ decode_partial(DecodeParams p) {
     w0 = (int)blockIdx.x * chunk;
     w1 = w0 + chunk < total ? w0 + chunk : total;
     if (w0 >= w1) return;
-    // first unit whose work blocks end past w0
+    // first unit whose positions end past w0, or the next one if only its entry cost is in range
     int lo = 0, hi = p.num_units - 1;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (plan.scan[mid] > w0) hi = mid; else lo = mid + 1;
     }
+    if (!unit_in_range(p, plan.scan, lo, w0, w1)) lo = next_unit(p, plan.scan, lo, w0, w1);
+    if (lo >= p.num_units) return;
     u0 = lo;
   }
   process_range<C>(p, &plan, sh_blk, u0, w0, w1, chunk, ring, xchg);
 }
 
 // ------------------------------------------------------------------- merge
-// Merge of the split partials. One workgroup per
-// (unit, 4 rows), 64 threads per row with 8 columns each. Each row's split
-// lse values are read in one pass (one split per lane) and reduced with lane
-// swaps; weights go through LDS; partial rows are then read in batches of 8.
+// Merge of the split partials. One workgroup per (unit, 4 rows), one wave
+// per row, 8 columns per lane. A row's split lse values (one split per lane)
+// and its first 8 partial rows are read together, so the merge costs one
+// memory round trip after the plan; the weights reach every lane by shuffle.
+// Splits are combined in split order (deterministic).
 template <bool F32>
 __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   __shared__ int sh_scan[256];
-  __shared__ float sh_w[4][64];
   plan_units(p, sh_scan, nullptr);
   const int groups = (p.rows_per_unit + 3) / 4;
   const int u = blockIdx.x / groups;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = (blockIdx.x % groups) * 4 + wv;
+  const int lane = threadIdx.x & 63;
+  const int row = (blockIdx.x % groups) * 4 + (threadIdx.x >> 6);
   const int c0 = lane * 8;
   if (u >= p.num_units || row >= p.rows_per_unit) return;
   const int total = sh_scan[p.num_units - 1];
@@ -1016,40 +1020,62 @@ __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float lse2 = kNegInf;
   if (end > start) {
-    const int first = start / chunk, last = (end - 1) / chunk;
+    const int first = (start + p.alpha) / chunk, last = (end - 1) / chunk;
     if (first == last) return;  // written directly by its only workgroup
-    const int n = last - first + 1;  // <= 64 (each split is a distinct workgroup of <= 256 + units)
-    const int64_t srow = (int64_t)p.rows_per_unit;
-    float M = kNegInf, Lt = 0.f;
-    for (int w0 = 0; w0 < n; w0 += 64) {
-      const float ls = w0 + lane < n ? p.part_lse[(int64_t)(first + w0 + lane + u) * srow + row] : kNegInf;
-      M = fmaxf(M, ls);
-    }
-    // M over all lanes
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const int n = last - first + 1;
+    const int64_t srow = p.rows_per_unit;
+    const float* lp = p.part_lse + (int64_t)(first + u) * srow + row;
     const float* op = p.part_o + ((int64_t)(first + u) * srow + row) * kKvRank + c0;
     const int64_t ostride = srow * kKvRank;
+    constexpr int BATCH = 8;
+    float M = kNegInf, Lt = 0.f;
     for (int w0 = 0; w0 < n; w0 += 64) {
+      // this lane's split lse, and the first BATCH partial rows, in one round trip
       const int cnt = n - w0 < 64 ? n - w0 : 64;
-      const float ls = lane < cnt ? p.part_lse[(int64_t)(first + w0 + lane + u) * srow + row] : kNegInf;
-      sh_w[wv][lane] = ls == kNegInf ? 0.f : fast_exp2(ls - M);
-      for (int k0 = 0; k0 < cnt; k0 += 8) {
-        f32x4_t x0[8], x1[8];
+      const float ls = lane < cnt ? lp[(int64_t)(w0 + lane) * srow] : kNegInf;
+      f32x4_t x0[BATCH], x1[BATCH];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          if (k0 + k < cnt) {
-            x0[k] = *(const f32x4_t*)(op + (w0 + k0 + k) * ostride);
-            x1[k] = *(const f32x4_t*)(op + (w0 + k0 + k) * ostride + 4);
-          } else {
-            x0[k] = x1[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < BATCH; ++k) {
+        const bool in = k < cnt;
+        const float* src = op + (int64_t)(w0 + (in ? k : 0)) * ostride;
+        x0[k] = *(const f32x4_t*)src;
+        x1[k] = *(const f32x4_t*)(src + 4);
+      }
+      if (w0 == 0) {
+        M = ls;
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        // splits past the first 64 cannot raise M above what the first pass saw
+        // unless n > 64; then M is refined below before any weight is applied
+        if (n > 64) {
+          for (int w1 = 64; w1 < n; w1 += 64) {
+            const float l2 = w1 + lane < n ? lp[(int64_t)(w1 + lane) * srow] : kNegInf;
+            float m2 = l2;
+            for (int off = 32; off >= 1; off >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, off));
+            M = fmaxf(M, m2);
+          }
+        }
+      }
+      const float a = ls == kNegInf ? 0.f : fast_exp2(ls - M);  // this lane's split weight
+      float lsum = a;
+      for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+      Lt += lsum;
+      for (int k0 = 0; k0 < cnt; k0 += BATCH) {
+        if (k0 > 0) {
+#pragma unroll
+          for (int k = 0; k < BATCH; ++k) {
+            const bool in = k0 + k < cnt;
+            const float* src = op + (int64_t)(w0 + (in ? k0 + k : 0)) * ostride;
+            x0[k] = *(const f32x4_t*)src;
+            x1[k] = *(const f32x4_t*)(src + 4);
           }
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float a = k0 + k < cnt ? sh_w[wv][k0 + k] : 0.f;
-          Lt += a;
-          acc0 += a * x0[k];
-          acc1 += a * x1[k];
+        for (int k = 0; k < BATCH; ++k) {
+          const float wk = __shfl(a, k0 + k);  // weight of split w0 + k0 + k
+          if (k0 + k < cnt) {
+            acc0 += wk * x0[k];
+            acc1 += wk * x1[k];
+          }
         }
       }
     }
@@ -1084,6 +1110,8 @@ using Rows64  = Cfg<64, 4, 1, 1, 32, 4, false, false, 0>;  // many rows: rows sp
 using Rows0   = Cfg<0,  4, 1, 1, 32, 4, false, false, 0>;
 using ColsF64 = Cfg<64, 1, 4, 1, 16, 4, true,  true,  0>;  // f32
 using ColsF0  = Cfg<0,  1, 4, 1, 16, 4, true,  true,  0>;
+
+constexpr int kColsEntryCost = 3;  // work blocks (measured: 3-4 best on V2-Lite)
 
 enum Variant { kCols64 = 0, kCols0, kMixed64, kMixed0, kRows64, kRows0, kColsF64, kColsF0 };
 
@@ -1133,6 +1161,8 @@ int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int
   plan->num_units = (int)units;
   // plan granularity: the variant's tile
   plan->wb = is_f32 ? ColsF64::TT : Cols64::TT;
+  // entering a unit costs the few-head layout a query tile and a partial tile
+  plan->alpha = (variant == kCols64 || variant == kCols0) ? kColsEntryCost : 0;
   const int64_t wb_bound = batch * row_tiles * ((max_seqlen + plan->wb - 1) / plan->wb);
   if (units < kSplitUnits && wb_bound > units) {
     plan->split = 1;

@@ -253,6 +253,7 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
     p.part_lse = (float*)((char*)workspace + (size_t)slots * plan.rows_per_unit * mla::kKvRank * 4);
   }
   p.wb = plan.wb;
+  p.alpha = plan.alpha;
   p.page_shift = -1;
   for (int sh = 0; sh < 31; ++sh)
     if (((int64_t)1 << sh) == p.page) p.page_shift = sh;

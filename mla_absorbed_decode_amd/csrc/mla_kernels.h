@@ -62,6 +62,7 @@ struct DecodeParams {
   int split;              // 1: split-KV over `grid` workgroups + merge
   int grid;
   int wb;                 // plan granularity: tokens per work block (the tile size)
+  int alpha;              // plan cost of entering a unit, in work blocks
 };
 
 // Launch plan chosen on the host from sizes alone (never from seqlens).
@@ -73,6 +74,7 @@ struct DecodePlan {
   int split;
   int grid;
   int wb;
+  int alpha;
   size_t workspace_bytes;
 };
 int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int64_t max_seqlen,
