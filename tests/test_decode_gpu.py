@@ -73,6 +73,32 @@ def test_fewer_heads_than_a_tile():
     check(c, "4 heads x 2 queries")
 
 
+# ------------------------------------------------- 17 to 32 rows per unit
+
+
+@pytest.mark.parametrize("rope", [64, 0])
+def test_32_rows_ragged(rope):
+    # 32 heads x 1 query: units of 32 rows, whose two waves per row group split
+    # the score contraction and add the partial scores through LDS
+    d = mi.Dims(n_head=32, d_nope=128, d_rope=rope, d_v=128, kv_rank=512)
+    c = mi.decode_case(16, d, "bf16", [5, 333, 1200, 64, 2])
+    check(c, f"32 heads ragged rope={rope}")
+
+
+def test_32_rows_from_two_queries():
+    # 16 heads x 2 queries: 32 rows per unit spanning two causal query positions
+    d = mi.Dims(n_head=16, d_nope=128, d_rope=64, d_v=128, kv_rank=512)
+    c = mi.decode_case(17, d, "bf16", [1, 2, 3, 700, 1500], q_len=2)
+    check(c, "16 heads x 2 queries")
+
+
+def test_24_rows_partial_unit():
+    # 24 heads: the unit's last 8 rows are padding
+    d = mi.Dims(n_head=24, d_nope=128, d_rope=64, d_v=128, kv_rank=512)
+    c = mi.decode_case(18, d, "bf16", [100, 2000, 31])
+    check(c, "24 heads")
+
+
 # --------------------------------------------------------------- many heads
 
 
