@@ -12,8 +12,8 @@
 // Work decomposition
 // ------------------
 // Rows (query, head) of one sequence are cut into "units" of rows_per_unit
-// rows that share every key. A unit's visible keys are cut into 64-token work
-// blocks. With many units (prefill) each workgroup takes one unit. With few
+// rows that share every key. A unit's visible keys are cut into work blocks
+// of one tile each. With many units (prefill) each workgroup takes one unit. With few
 // units (decode) the work blocks of all units are laid end to end and cut
 // into `grid` equal chunks, one per workgroup; a unit that lands in more than
 // one chunk is written as normalised fp32 partials plus a log2-domain lse per
@@ -52,13 +52,16 @@ typedef __attribute__((address_space(4))) const int32_t cint32_t;  // scalar-loa
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kBlkCache = 1024;  // block-table entries a workgroup stages in LDS
-// LDS besides the tile ring and score exchange: the split plan (below) and
-// the staged block table
-constexpr int kStaticLds = 3 * 256 * 4 + kBlkCache * 4;
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// n / d for n >= 0 with a FastDiv prepared on the host.
+__device__ __forceinline__ int fdiv(int n, const FastDiv& d) {
+  const uint32_t x = (uint32_t)n, t = __umulhi(x, d.mul);
+  return (int)((t + ((x - t) >> d.sh1)) >> d.sh2);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -87,31 +90,44 @@ __device__ __forceinline__ int row_limit(const DecodeParams& p, int s, int qi) {
 
 // Keys a unit needs: the most any of its rows sees.
 __device__ __forceinline__ int unit_kvlen(const DecodeParams& p, int u) {
-  const int b = u / p.row_tiles, rt = u % p.row_tiles;
+  const int b = fdiv(u, p.div_rt), rt = u - b * p.row_tiles;
   const int s = seq_len(p, b);
   const int rows = p.q_len * p.n_heads;
   int r_last = (rt + 1) * p.rows_per_unit;
   r_last = (r_last > rows ? rows : r_last) - 1;
-  return row_limit(p, s, r_last / p.n_heads);
+  return row_limit(p, s, p.q_len == 1 ? 0 : fdiv(r_last, p.div_nh));
 }
 
-// The split plan in LDS: per unit, the inclusive prefix of unit costs (work
-// blocks of p.wb tokens, plus p.alpha for entering the unit), the keys the
-// unit needs and its sequence's length. Unit u occupies plan positions
-// [scan[u-1], scan[u]); the first alpha of them stand for the cost of
-// entering it and hold no keys, position scan[u-1] + alpha + i is work block i.
-struct PlanLds {
-  int scan[256];
-  int kv[256];
-  int sl[256];
-};
+// Split plan: unit u occupies plan positions [scan[u-1], scan[u]) where scan
+// is the inclusive prefix of unit costs in work blocks of p.wb tokens. A unit
+// with keys costs its work blocks plus p.alpha for entering it; the first
+// alpha of its positions hold no keys, position scan[u-1] + alpha + i is work
+// block i. A unit with no keys costs nothing. The positions are cut into
+// chunks of ceil(total / grid), one per workgroup.
+//
+// The merge's copy of the plan: every unit's scan value, computed by wave 0
+// with register shuffles (up to 256 units, four per lane) and published in
+// sh[0..255] with one barrier.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no
+// LDS round trips): shifts by 1, 2, 4 and 8 within each row of 16 lanes, then
+// lane 15 of rows 0 and 2 added to rows 1 and 3, then lane 31 to rows 2 and 3.
+// Lanes without a source read 0.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, true);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, true);  // row_bcast:31, rows 2 and 3
+  return x;
+}
 
-// Split plan shared by the partial and merge kernels: each unit's cost and
-// their inclusive prefix over units, computed by wave 0 with register
-// shuffles (up to 256 units, four per lane) and published in sh[0..255] with
-// one barrier; with pl given, the units' key counts and sequence lengths go to
-// pl->kv and pl->sl. A unit with no keys costs nothing.
-__device__ void plan_units(const DecodeParams& p, int* sh, PlanLds* pl) {
+// Lane src's value of x, src wave-uniform.
+__device__ __forceinline__ int lane_value(int x, int src) {
+  return __builtin_amdgcn_readlane(x, src);
+}
+
+__device__ void plan_units(const DecodeParams& p, int* sh) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int v[4], run = 0;
@@ -119,22 +135,213 @@ __device__ void plan_units(const DecodeParams& p, int* sh, PlanLds* pl) {
     for (int k = 0; k < 4; ++k) {
       const int u = lane * 4 + k;
       const int n = u < p.num_units ? unit_kvlen(p, u) : 0;
-      if (pl) {
-        pl->kv[u] = n;
-        pl->sl[u] = u < p.num_units ? seq_len(p, u / p.row_tiles) : 0;
-      }
       run += n > 0 ? ceil_div(n, p.wb) + p.alpha : 0;
       v[k] = run;
     }
-    int x = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
-    const int excl = x - run;
+    const int excl = wave_scan_incl(run) - run;
 #pragma unroll
     for (int k = 0; k < 4; ++k) sh[lane * 4 + k] = excl + v[k];
+  }
+  __syncthreads();
+}
+
+// The part of the plan a workgroup walks.
+struct SegHdr {
+  int u0, u1;  // first and last unit with keys in the workgroup's positions (u0 > u1: none)
+  int tlo0;    // first key of u0 (units after it start at key 0)
+  int thi1;    // end key of u1 (units before it end at their last visible key)
+  int nsteps;  // stream items: key tiles, plus a query tile per segment after the first (QT)
+};
+// The same in LDS, with per-unit tables indexed by u in split mode and by 0
+// for the one unit of a workgroup without split: the unit's visible keys, its
+// sequence's length and the staged block-table position of its first page,
+// and bit masks of the units in range and of those whose keys reach other
+// workgroups too (written as partials for the merge).
+struct SegLds {
+  int kv[256];
+  int sl[256];
+  int poff[256];
+  uint64_t live[4];
+  uint64_t part[4];
+  SegHdr hdr;
+};
+// LDS besides the tile ring and score exchange: the workgroup's plan and the
+// staged block table
+constexpr int kStaticLds = (int)sizeof(SegLds) + kBlkCache * 4;
+
+// Block-table entries staged in LDS: entry e of the stage is read by lane
+// e % 64 of wave 0, from block-table index idx[e / 64] (0, always a valid
+// index, where e is past the segments' pages).
+constexpr int kStagePer = kBlkCache / 64;
+struct StageRefs {
+  int64_t idx[kStagePer];
+};
+// Mark the stage entries [po, po + np) as pages pf, pf + 1, ... of sequence b.
+__device__ __forceinline__ void stage_segment(const DecodeParams& p, StageRefs& st, int b, int pf,
+                                              int po, int np) {
+  const int lane = threadIdx.x & 63;
+  const int64_t base = (int64_t)b * p.bt_s0 + pf - po;
+#pragma unroll
+  for (int k = 0; k < kStagePer; ++k) {
+    const int e = 64 * k + lane;
+    const bool in = (uint32_t)(e - po) < (uint32_t)np;  // po <= e < po + np
+    st.idx[k] = in ? base + e : st.idx[k];
+  }
+}
+// Read the first n stage entries (all in one round trip) into sh_blk, clamped
+// to [0, num_blocks) so every tile read stays inside the cache. n is
+// wave-uniform; n > 0 implies a non-empty block table.
+__device__ __forceinline__ void stage_read(const DecodeParams& p, const StageRefs& st, int n,
+                                           int* sh_blk) {
+  const int lane = threadIdx.x & 63;
+  int v[kStagePer];
+#pragma unroll
+  for (int k = 0; k < kStagePer; ++k)
+    if (64 * k < n) v[k] = p.block_table[st.idx[k]];
+#pragma unroll
+  for (int k = 0; k < kStagePer; ++k)
+    if (64 * k < n)
+      sh_blk[64 * k + lane] = v[k] < 0 ? 0 : (v[k] >= p.num_blocks ? (int)p.num_blocks - 1 : v[k]);
+}
+
+// Build the workgroup's SegLds and stage its block-table entries in one pass
+// of wave 0, then one barrier. In split mode lane l holds units l, l + 64,
+// l + 128, l + 192, so that a ballot over the lanes is one 64-unit word of a
+// mask; every unit's cost, plan positions, overlap with this workgroup's
+// chunk, key range, tiles and pages are computed side by side rather than
+// walked unit by unit. Without split the workgroup's one unit is the whole
+// table. The stage holds the first kBlkCache pages of the segments in stream
+// order; the loader reads any beyond that from global memory.
+template <class C>
+__device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    StageRefs st;
+#pragma unroll
+    for (int k = 0; k < kStagePer; ++k) st.idx[k] = 0;
+    if (!p.split) {
+      const int u = p.num_units - 1 - (int)blockIdx.x;  // heaviest row tiles first
+      const int b = fdiv(u, p.div_rt);
+      const int n = unit_kvlen(p, u);
+      const int np = n > 0 ? page_of(p, n - 1) + 1 : 0;
+      stage_segment(p, st, b, 0, 0, np);
+      stage_read(p, st, np < kBlkCache ? np : kBlkCache, sh_blk);
+      if (lane == 0) {
+        tab->kv[0] = n;
+        tab->sl[0] = seq_len(p, b);
+        tab->poff[0] = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          tab->live[w] = w == 0 ? 1ull : 0ull;
+          tab->part[w] = 0ull;
+        }
+        tab->hdr.u0 = tab->hdr.u1 = u;
+        tab->hdr.tlo0 = 0;
+        tab->hdr.thi1 = n;
+        tab->hdr.nsteps = n > 0 ? ceil_div(n, C::TT) : 0;
+      }
+    } else {
+      int n[4], sl[4], cost[4], incl[4];
+      int run = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int u = lane + 64 * k;
+        n[k] = u < p.num_units ? unit_kvlen(p, u) : 0;
+        sl[k] = u < p.num_units ? seq_len(p, fdiv(u, p.div_rt)) : 0;
+        cost[k] = n[k] > 0 ? ceil_div(n[k], C::TT) + p.alpha : 0;  // work blocks are tiles
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int x = wave_scan_incl(cost[k]);
+        incl[k] = x + run;
+        run += lane_value(x, 63);
+      }
+      const int total = run;
+      const int chunk = total > 0 ? ceil_div(total, p.grid) : 1;
+      const int w0 = (int)blockIdx.x * chunk;
+      const int w1 = w0 + chunk < total ? w0 + chunk : total;
+      uint64_t live[4], part[4];
+      int tlo[4], thi[4], pages[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int first = incl[k] - cost[k] + p.alpha, end = incl[k];
+        const int lo = w0 > first ? w0 : first, hi = w1 < end ? w1 : end;
+        const bool in = cost[k] > 0 && lo < hi;
+        tlo[k] = (lo - first) * C::TT;
+        thi[k] = (hi - first) * C::TT < n[k] ? (hi - first) * C::TT : n[k];
+        pages[k] = in ? page_of(p, thi[k] - 1) - page_of(p, tlo[k]) + 1 : 0;
+        live[k] = __ballot(in);
+        // whole in this workgroup only if it starts and ends inside its chunk
+        part[k] = __ballot(in && !(first >= w0 && end <= w0 + chunk));
+      }
+      int u0 = 256, u1 = -1;
+#pragma unroll
+      for (int k = 3; k >= 0; --k)
+        if (live[k]) u0 = 64 * k + __builtin_ctzll(live[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (live[k]) u1 = 64 * k + 63 - __builtin_clzll(live[k]);
+      int steps = 0, prun = 0, poff[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bool in = (live[k] >> lane) & 1;
+        const int nt = in ? ceil_div(thi[k] - tlo[k], C::TT) : 0;
+        steps += nt + (C::QT && in && lane + 64 * k != u0 ? 1 : 0);
+        const int x = wave_scan_incl(pages[k]);
+        poff[k] = x - pages[k] + prun;
+        prun += lane_value(x, 63);
+      }
+      // key range ends of the first and last units, from the lanes holding them
+      int a = 0, z = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (k == (u0 >> 6)) a = tlo[k];
+        if (k == (u1 >> 6)) z = thi[k];
+      }
+      a = lane_value(a, u0 & 63);
+      z = lane_value(z, u1 & 63);
+      steps = lane_value(wave_scan_incl(steps), 63);
+      // stage the pages of every unit in range, in unit order: one pass per
+      // segment, the unit's values read from the lane holding it
+      for (int u = u0; u <= u1;) {
+        const int k = u >> 6, src = u & 63;
+        const int tl = k == 0 ? tlo[0] : k == 1 ? tlo[1] : k == 2 ? tlo[2] : tlo[3];
+        const int po = k == 0 ? poff[0] : k == 1 ? poff[1] : k == 2 ? poff[2] : poff[3];
+        const int np = k == 0 ? pages[0] : k == 1 ? pages[1] : k == 2 ? pages[2] : pages[3];
+        stage_segment(p, st, fdiv(u, p.div_rt), page_of(p, lane_value(tl, src)),
+                      lane_value(po, src), lane_value(np, src));
+        // next unit in range
+        int nu = 256;
+        for (int w = (u + 1) >> 6; w < 4; ++w) {
+          const uint64_t lw = w == 0 ? live[0] : w == 1 ? live[1] : w == 2 ? live[2] : live[3];
+          const uint64_t m = w == ((u + 1) >> 6) ? lw & (~0ull << ((u + 1) & 63)) : lw;
+          if (m) {
+            nu = 64 * w + __builtin_ctzll(m);
+            break;
+          }
+        }
+        u = nu;
+      }
+      stage_read(p, st, prun < kBlkCache ? prun : kBlkCache, sh_blk);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        tab->kv[lane + 64 * k] = n[k];
+        tab->sl[lane + 64 * k] = sl[k];
+        tab->poff[lane + 64 * k] = poff[k];
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          tab->live[k] = live[k];
+          tab->part[k] = part[k];
+        }
+        tab->hdr.u0 = u0;
+        tab->hdr.u1 = u1;
+        tab->hdr.tlo0 = a;
+        tab->hdr.thi1 = z;
+        tab->hdr.nsteps = steps;
+      }
+    }
   }
   __syncthreads();
 }
@@ -496,7 +703,7 @@ __device__ __forceinline__ void store_row(const DecodeParams& p, int b, int unit
     if (write_lse && g == 0) p.part_lse[(int64_t)slot * p.rows_per_unit + local_row] = lse2;
     return;
   }
-  const int qi = r / p.n_heads, qh = r % p.n_heads;
+  const int qi = fdiv(r, p.div_nh), qh = r - qi * p.n_heads;
   const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)qh * p.o_s2 + c0;
   if constexpr (C::F32) {
     float* dst = (float*)p.out + ooff;
@@ -525,37 +732,39 @@ struct Seg {
   int t_hi;    // one past the last key token (capped by the unit's visible keys)
   int ntiles;  // tiles of TT tokens
   int slot;    // partial slot, or -1 when this workgroup holds the whole unit
+  int poff;    // staged block-table position of the segment's first page
 };
 
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ SegHdr read_hdr(const SegLds* tab) {
+  SegHdr h;
+  h.u0 = uni(tab->hdr.u0);
+  h.u1 = uni(tab->hdr.u1);
+  h.tlo0 = uni(tab->hdr.tlo0);
+  h.thi1 = uni(tab->hdr.thi1);
+  h.nsteps = uni(tab->hdr.nsteps);
+  return h;
+}
+
+// Unit u's segment from the workgroup's plan (u past the last unit in range:
+// an empty segment with u = num_units). The table reads go out together.
 template <class C>
-__device__ __forceinline__ Seg make_seg(const DecodeParams& p, const PlanLds* pl, int u, int w0,
-                                        int w1, int chunk) {
+__device__ __forceinline__ Seg seg_of(const DecodeParams& p, const SegLds* tab, const SegHdr& h,
+                                      int u) {
+  const bool valid = u <= h.u1 && u < p.num_units;
+  const int i = p.split ? (u < 256 ? u : 255) : 0;
+  const int n = uni(tab->kv[i]), s = uni(tab->sl[i]), po = uni(tab->poff[i]);
+  const int pw = uni((int)(tab->part[i >> 6] >> (i & 63)));
   Seg sg;
-  sg.u = u;
-  sg.b = u / p.row_tiles;
-  if (u >= p.num_units) {
-    sg.s = sg.t_lo = sg.t_hi = sg.ntiles = 0;
-    sg.slot = -1;
-    return sg;
-  }
-  const int kvlen = p.split ? pl->kv[u] : unit_kvlen(p, u);
-  sg.s = p.split ? pl->sl[u] : seq_len(p, sg.b);
-  if (!p.split) {
-    sg.t_lo = 0;
-    sg.t_hi = kvlen;
-    sg.slot = -1;
-  } else {
-    // work blocks [i_lo, i_hi) of the unit lie in this workgroup's positions [w0, w1)
-    const int first = (u > 0 ? pl->scan[u - 1] : 0) + p.alpha, end = pl->scan[u];
-    const int i_lo = (w0 > first ? w0 : first) - first;
-    const int i_hi = (w1 < end ? w1 : end) - first;
-    sg.t_lo = i_lo * p.wb;
-    sg.t_hi = i_hi * p.wb < kvlen ? i_hi * p.wb : kvlen;
-    if (sg.t_hi < sg.t_lo) sg.t_hi = sg.t_lo;
-    // split when the unit's work blocks reach more than one workgroup
-    sg.slot = (first / chunk != (end - 1) / chunk) ? (int)blockIdx.x + u : -1;
-  }
+  sg.u = valid ? u : p.num_units;
+  sg.b = valid ? fdiv(u, p.div_rt) : 0;
+  sg.s = valid ? s : 0;
+  sg.t_lo = valid && u == h.u0 ? h.tlo0 : 0;
+  sg.t_hi = !valid ? 0 : (u == h.u1 ? h.thi1 : n);
+  sg.slot = valid && (pw & 1) ? (int)blockIdx.x + u : -1;
   sg.ntiles = sg.t_hi > sg.t_lo ? ceil_div(sg.t_hi - sg.t_lo, C::TT) : 0;
+  sg.poff = valid ? po : 0;
   return sg;
 }
 
@@ -564,60 +773,16 @@ __device__ __forceinline__ int seg_pages(const DecodeParams& p, const Seg& sg) {
   return sg.ntiles > 0 ? page_of(p, sg.t_hi - 1) - page_of(p, sg.t_lo) + 1 : 0;
 }
 
-
-
-// Whether unit u has work blocks among positions [w0, w1).
-__device__ __forceinline__ bool unit_in_range(const DecodeParams& p, const int* sh, int u, int w0,
-                                              int w1) {
-  const int first = (u > 0 ? sh[u - 1] : 0) + p.alpha, end = sh[u];
-  return (w0 > first ? w0 : first) < (w1 < end ? w1 : end);
-}
-
-// Next unit with work in [w0, w1) after u, or num_units.
-__device__ __forceinline__ int next_unit(const DecodeParams& p, const int* sh, int u, int w0,
-                                         int w1) {
+// The next unit in the workgroup's range after u, or num_units.
+__device__ __forceinline__ int next_live(const DecodeParams& p, const SegLds* tab, int u) {
   if (!p.split) return p.num_units;
-  for (++u; u < p.num_units; ++u) {
-    if ((u > 0 ? sh[u - 1] : 0) >= w1) return p.num_units;
-    if (unit_in_range(p, sh, u, w0, w1)) return u;
+  for (int i = u + 1; i < 256; i = (i | 63) + 1) {
+    const uint64_t w = tab->live[i >> 6] >> (i & 63);
+    const uint32_t lo = (uint32_t)uni((int)(uint32_t)w), hi = (uint32_t)uni((int)(uint32_t)(w >> 32));
+    const uint64_t ws = ((uint64_t)hi << 32) | lo;
+    if (ws) return i + __builtin_ctzll(ws);
   }
   return p.num_units;
-}
-
-// Stage the block-table entries of the workgroup's segments, in stream order,
-// in LDS (the first kBlkCache of them; the loader reads any beyond that from
-// global memory). Entries are clamped to [0, num_blocks) so every tile read
-// stays inside the cache.
-template <class C>
-__device__ void stage_block_table(const DecodeParams& p, const PlanLds* pl, int u0, int w0, int w1,
-                                  int chunk, int* sh_blk) {
-  constexpr int PER = (kBlkCache + C::NT - 1) / C::NT;
-  int64_t idx[PER];
-  bool need[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) need[k] = false;
-  int off = 0;
-  for (int u = u0; u < p.num_units && off < kBlkCache; u = next_unit(p, pl->scan, u, w0, w1)) {
-    const Seg sg = make_seg<C>(p, pl, u, w0, w1, chunk);
-    const int n = seg_pages(p, sg), pf = page_of(p, sg.t_lo);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = (int)threadIdx.x + C::NT * k;
-      if (i < kBlkCache && i >= off && i < off + n) {
-        idx[k] = (int64_t)sg.b * p.bt_s0 + pf + (i - off);
-        need[k] = true;
-      }
-    }
-    off += n;
-  }
-  int v[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) v[k] = need[k] ? p.block_table[idx[k]] : 0;
-#pragma unroll
-  for (int k = 0; k < PER; ++k)
-    if (need[k])
-      sh_blk[threadIdx.x + C::NT * k] = v[k] < 0 ? 0 : (v[k] >= p.num_blocks ? (int)p.num_blocks - 1 : v[k]);
-  __syncthreads();
 }
 
 // ------------------------------------------------------ the tile stream
@@ -631,10 +796,8 @@ __device__ void stage_block_table(const DecodeParams& p, const PlanLds* pl, int 
 // never stall on a full memory queue; without them the compute waves send the
 // next tile's reads in three groups between their own phases.
 template <class C>
-__device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl, int* sh_blk, int u0,
-                              int w0, int w1, int chunk, MLA_LDS char* ring,
-                              MLA_LDS f32x4_t* xchg) {
-  const int* sh = pl->scan;
+__device__ __forceinline__ void process_range(const DecodeParams& p, const SegLds* tab, int* sh_blk,
+                                              MLA_LDS char* ring, MLA_LDS f32x4_t* xchg) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const bool loader = C::NP == 0 || wave >= C::NW;
@@ -649,12 +812,8 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
   const char* kvbase = (const char*)p.kv;
   const int64_t pitch_g = p.kv_s1 * C::ES;
 
-  // total tiles of the range
-  int nsteps = 0;
-  for (int u = u0; u < p.num_units; u = next_unit(p, sh, u, w0, w1)) {
-    const int nt = make_seg<C>(p, pl, u, w0, w1, chunk).ntiles;
-    nsteps += nt + (C::QT && nt > 0 && u != u0 ? 1 : 0);
-  }
+  const SegHdr h = read_hdr(tab);
+  const int nsteps = h.nsteps;
 
   // ---- loader walker: this wave's share of each tile's reads. A full tile
   // inside one page is read as page base + per-lane offsets computed once
@@ -670,13 +829,13 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
     lrow[n] = r;
     loff[n] = (uint32_t)(r * pitch_g) + (uint32_t)((cpos ^ lds_swz(r & 15)) << 4);
   }
-  Seg ls = make_seg<C>(p, pl, u0, w0, w1, chunk);
+  const Seg seg0 = seg_of<C>(p, tab, h, h.u0);
+  Seg ls = seg0;
   int lk = 0;         // tile within ls
   bool lq = true;     // ls's query tile sent (the first segment has none)
-  int ls_off = 0;     // staged block-table position of ls's first page
   // cache block of page pg of segment ls (staged entry, or a global read past the stage)
   auto block_of = [&](int pg) -> int {
-    const int ti = ls_off + pg - page_of(p, ls.t_lo);
+    const int ti = ls.poff + pg - page_of(p, ls.t_lo);
     int blk;
     if (ti < kBlkCache) {
       blk = sh_blk[ti];
@@ -700,8 +859,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
   auto prep_next = [&](int step) -> NextTile {
     // segments in split mode have tiles; an empty unit (no split) is never reached
     while (lk >= ls.ntiles && (lq || !C::QT) && ls.u < p.num_units) {
-      ls_off += seg_pages(p, ls);
-      ls = make_seg<C>(p, pl, next_unit(p, sh, ls.u, w0, w1), w0, w1, chunk);
+      ls = seg_of<C>(p, tab, h, next_live(p, tab, ls.u));
       lk = 0;
       lq = false;
     }
@@ -712,7 +870,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
       lq = true;
       t.query = true;
       t.qb = ls.b;
-      t.qrow0 = (ls.u % p.row_tiles) * p.rows_per_unit;
+      t.qrow0 = (ls.u - ls.b * p.row_tiles) * p.rows_per_unit;
       return t;
     }
     const int j0 = ls.t_lo + lk * C::TT;
@@ -750,7 +908,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
         const int i = idx / C::CH, cpos = idx % C::CH;
         int r = t.qrow0 + i;
         r = r < rows_seq ? r : rows_seq - 1;  // rows past the end are zeroed by the compute waves
-        const int qi = p.q_len == 1 ? 0 : r / p.n_heads, qh = p.q_len == 1 ? r : r % p.n_heads;
+        const int qi = p.q_len == 1 ? 0 : fdiv(r, p.div_nh), qh = r - qi * p.n_heads;
         const char* src = (const char*)p.q +
                           ((int64_t)t.qb * p.q_s0 + (int64_t)qi * p.q_s1 + (int64_t)qh * p.q_s2) * C::ES +
                           ((cpos ^ lds_swz(i & 15)) << 4);
@@ -806,16 +964,16 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
   QV qreg[C::RT][C::KW];
   bool qvalid[C::RT];
   WaveState<C> st;
-  Seg cs = make_seg<C>(p, pl, u0, w0, w1, chunk);
+  Seg cs = seg0;
   int ck = 0;
   // state of a new segment: this lane's row limits, empty softmax state
   auto begin_state = [&]() {
-    const int unit_row0 = (cs.u % p.row_tiles) * p.rows_per_unit;
+    const int unit_row0 = (cs.u - cs.b * p.row_tiles) * p.rows_per_unit;
 #pragma unroll
     for (int rt = 0; rt < C::RT; ++rt) {
       const int r = unit_row0 + wrow0 + 16 * rt + li;
       qvalid[rt] = r < rows_seq;
-      const int lim = qvalid[rt] ? row_limit(p, cs.s, r / p.n_heads) : 0;
+      const int lim = qvalid[rt] ? row_limit(p, cs.s, fdiv(r, p.div_nh)) : 0;
       st.lim[rt] = lim < cs.t_hi ? lim : cs.t_hi;
       st.m[rt] = kNegInf;
       st.l[rt] = 0.f;
@@ -827,11 +985,11 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
   // loaded asynchronously from global memory (no query tiles); rows past the
   // end load row 0 and are zeroed by settle_q
   auto load_q = [&]() {
-    const int unit_row0 = (cs.u % p.row_tiles) * p.rows_per_unit;
+    const int unit_row0 = (cs.u - cs.b * p.row_tiles) * p.rows_per_unit;
 #pragma unroll
     for (int rt = 0; rt < C::RT; ++rt) {
       const int r = unit_row0 + wrow0 + 16 * rt + li;
-      const int qi = qvalid[rt] ? r / p.n_heads : 0, qh = qvalid[rt] ? r % p.n_heads : 0;
+      const int qi = qvalid[rt] ? fdiv(r, p.div_nh) : 0, qh = qvalid[rt] ? r - qi * p.n_heads : 0;
       const int64_t qoff = (int64_t)cs.b * p.q_s0 + (int64_t)qi * p.q_s1 + (int64_t)qh * p.q_s2;
       const char* qp = (const char*)p.q + qoff * C::ES + 16 * g;
 #pragma unroll
@@ -868,7 +1026,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
       }
   };
   auto end_seg = [&]() {
-    const int unit_row0 = (cs.u % p.row_tiles) * p.rows_per_unit;
+    const int unit_row0 = (cs.u - cs.b * p.row_tiles) * p.rows_per_unit;
 #pragma unroll
     for (int rt = 0; rt < C::RT; ++rt) {
       const float lt = wave_sum16(st.l[rt]);
@@ -881,9 +1039,8 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
 
   if (compute) {
     begin_state();
-    load_q();  // out before the block-table staging waits
+    load_q();  // ahead of the first tiles' reads
   }
-  stage_block_table<C>(p, pl, u0, w0, w1, chunk, sh_blk);
   if (loader) {
 #pragma unroll
     for (int k = 0; k < C::NSLOT - 1; ++k)
@@ -932,7 +1089,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
                       [](int) {});
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
-        cs = make_seg<C>(p, pl, next_unit(p, sh, cs.u, w0, w1), w0, w1, chunk);
+        cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
         ck = 0;
         begin_state();
         q_tile = true;
@@ -958,7 +1115,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, PlanLds* pl
                       p.scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); });
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
-        cs = make_seg<C>(p, pl, next_unit(p, sh, cs.u, w0, w1), w0, w1, chunk);
+        cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
         ck = 0;
         begin_state();
         load_q();
@@ -974,32 +1131,15 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(C::NT, C::NT),
                                amdgpu_waves_per_eu(C::NT / 256, C::NT / 256)))
 decode_partial(DecodeParams p) {
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
-  __shared__ PlanLds plan;
+  __shared__ SegLds tab;
   __shared__ int sh_blk[kBlkCache];
   MLA_LDS char* ring = (MLA_LDS char*)smem_raw;
   MLA_LDS f32x4_t* xchg = (MLA_LDS f32x4_t*)(smem_raw + C::RING_BYTES);
-  // this workgroup's stream: units from u0, plan positions [w0, w1)
-  int u0, w0 = 0, w1 = 0x7fffffff, chunk = 1;
-  if (!p.split) {
-    u0 = p.num_units - 1 - (int)blockIdx.x;  // one unit per workgroup, heaviest row tiles first
-  } else {
-    plan_units(p, plan.scan, &plan);
-    const int total = plan.scan[p.num_units - 1];
-    chunk = total > 0 ? ceil_div(total, p.grid) : 1;
-    w0 = (int)blockIdx.x * chunk;
-    w1 = w0 + chunk < total ? w0 + chunk : total;
-    if (w0 >= w1) return;
-    // first unit whose positions end past w0, or the next one if only its entry cost is in range
-    int lo = 0, hi = p.num_units - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (plan.scan[mid] > w0) hi = mid; else lo = mid + 1;
-    }
-    if (!unit_in_range(p, plan.scan, lo, w0, w1)) lo = next_unit(p, plan.scan, lo, w0, w1);
-    if (lo >= p.num_units) return;
-    u0 = lo;
-  }
-  process_range<C>(p, &plan, sh_blk, u0, w0, w1, chunk, ring, xchg);
+  plan_workgroup<C>(p, &tab, sh_blk);
+  // a workgroup whose chunk holds no keys (split mode) has nothing to write;
+  // without split an empty unit still writes its zero rows
+  if (p.split && tab.hdr.u0 > tab.hdr.u1) return;
+  process_range<C>(p, &tab, sh_blk, ring, xchg);
 }
 
 // ------------------------------------------------------------------- merge
@@ -1011,7 +1151,7 @@ decode_partial(DecodeParams p) {
 template <bool F32>
 __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   __shared__ int sh_scan[256];
-  plan_units(p, sh_scan, nullptr);
+  plan_units(p, sh_scan);
   const int groups = (p.rows_per_unit + 3) / 4;
   const int u = blockIdx.x / groups;
   const int lane = threadIdx.x & 63;
@@ -1021,8 +1161,8 @@ __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   const int total = sh_scan[p.num_units - 1];
   const int chunk = total > 0 ? ceil_div(total, p.grid) : 1;
   const int end = sh_scan[u], start = u > 0 ? sh_scan[u - 1] : 0;
-  const int b = u / p.row_tiles;
-  const int r = (u % p.row_tiles) * p.rows_per_unit + row;
+  const int b = fdiv(u, p.div_rt);
+  const int r = (u - b * p.row_tiles) * p.rows_per_unit + row;
   if (r >= p.q_len * p.n_heads) return;
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float lse2 = kNegInf;
@@ -1091,7 +1231,7 @@ __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
     acc1 *= inv;
     lse2 = Lt > 0.f ? M + fast_log2(Lt) : kNegInf;
   }
-  const int qi = r / p.n_heads, qh = r % p.n_heads;
+  const int qi = fdiv(r, p.div_nh), qh = r - qi * p.n_heads;
   const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)qh * p.o_s2 + c0;
   if constexpr (F32) {
     float* dst = (float*)p.out + ooff;
@@ -1124,6 +1264,8 @@ enum Variant { kCols64 = 0, kCols0, kMixed64, kMixed0, kRows64, kRows0, kColsF64
 
 template <class C>
 hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStream_t s) {
+  // the partial kernel plans in tiles; the merge reads the work block size
+  if (plan.wb != C::TT || p.wb != C::TT) return hipErrorInvalidValue;
   const size_t smem = C::SMEM_BYTES;
   static bool attr_set = false;  // the attribute is per function, set once per process
   if (!attr_set) {

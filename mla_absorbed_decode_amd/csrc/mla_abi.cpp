@@ -259,6 +259,8 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
     if (((int64_t)1 << sh) == p.page) p.page_shift = sh;
   p.rows_per_unit = plan.rows_per_unit;
   p.row_tiles = plan.row_tiles;
+  p.div_rt = mla::make_fastdiv((uint32_t)plan.row_tiles);
+  p.div_nh = mla::make_fastdiv((uint32_t)N);
   p.num_units = plan.num_units;
   p.split = plan.split;
   p.grid = plan.grid;

@@ -40,6 +40,25 @@ struct BmmParams {
 hipError_t launch_bmm(const BmmParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ decode
+// Division of 32-bit unsigned integers by a fixed d >= 1 as a multiply-high,
+// an add and two shifts (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994, the round-up method): with
+// l = ceil(log2 d) and mul = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0) where t = mulhi(n, mul),
+// exact for every n < 2^32.
+struct FastDiv {
+  uint32_t mul, sh1, sh2;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while (l < 32 && ((uint64_t)1 << l) < d) ++l;
+  FastDiv f;
+  f.mul = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+  f.sh1 = l < 1 ? l : 1;
+  f.sh2 = l > 1 ? l - 1 : 0;
+  return f;
+}
+
 struct DecodeParams {
   const void* q; int64_t q_s0, q_s1, q_s2;          // q [B, Sq, N, E]
   const void* kv; int64_t kv_s0, kv_s1;              // cache [NB, PG, E]
@@ -58,6 +77,8 @@ struct DecodeParams {
   float* part_lse;        // [slots][rows_per_unit] (log2 domain)
   int rows_per_unit;      // rows of (query, head) per unit
   int row_tiles;          // units per sequence
+  FastDiv div_rt;         // divides by row_tiles
+  FastDiv div_nh;         // divides by n_heads
   int num_units;
   int split;              // 1: split-KV over `grid` workgroups + merge
   int grid;
