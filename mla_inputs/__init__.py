@@ -266,3 +266,15 @@ def nope_prefill(seed=0, dtype=BF16, t=2048):
     w_uk_t, w_uv = mla_weights(seed, d, dtype)
     return dict(dims=d, dtype=dtype, t=t, q_nope=q_nope, c_kv=c_kv, w_uk_t=w_uk_t, w_uv=w_uv,
                 scale=(d.d_nope + d.d_rope) ** -0.5, page=64)
+
+
+ROPE_BASE = 8_000_000.0  # the rotary base of the interleaved-rope gate
+
+
+def rope_case(seed=0, n_pos=7, n_vec=5, d_rope=64, dtype=F32, pos_step=13, pos_offset=0):
+    """Interleaved-rope inputs: x [n_pos, n_vec, d_rope] uniform in [-1, 1) and
+    positions pos_offset + pos_step * p (the gate's shape: 7 positions 13 apart,
+    5 vectors each)."""
+    x = uniform(seed, 60, (n_pos, n_vec, d_rope), -1.0, 1.0, dtype)
+    positions = (pos_offset + pos_step * np.arange(n_pos)).astype(np.int32)
+    return x, positions

@@ -81,6 +81,8 @@ def _load():
         lib.mla_oracle_attend_split.restype = None
         lib.mla_oracle_cache_write.argtypes = [i64] * 4 + [u8p, i64, u8p, i64, ip64, u8p] + [i64] * 6
         lib.mla_oracle_cache_write.restype = c_int
+        lib.mla_oracle_rope_interleaved.argtypes = [i64, i64, i64, dp, ip32, dbl]
+        lib.mla_oracle_rope_interleaved.restype = None
         _lib = lib
     return _lib
 
@@ -297,3 +299,23 @@ def cache_write(buf, kv_c, k_pe, slots, offset, num_blocks, page, s0, s1):
     if rc != 0:
         raise ValueError("cache write would fall outside the buffer")
     return out
+
+
+def rope_interleaved(x, positions, base):
+    """Interleaved rotary embedding ([P2] gate 3): x [T, V, d] (or [T, d]) rotated
+    pair by pair, (2i, 2i+1) by positions[t] * base^(-2i/d). Returns a new
+    float64 array of x's shape; d == 0 returns x unchanged."""
+    x = _f64(x)
+    shape = x.shape
+    T = shape[0]
+    d = shape[-1]
+    if d % 2:
+        raise ValueError("rope width must be even")
+    y = np.array(x.reshape(T, -1, d) if d else x, dtype=np.float64, copy=True, order="C")
+    if d == 0 or T == 0:
+        return y.reshape(shape)
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    if pos.shape != (T,):
+        raise ValueError("one position per token")
+    _load().mla_oracle_rope_interleaved(T, y.shape[1], d, _dp(y), _i32p(pos), float(base))
+    return y.reshape(shape)

@@ -31,6 +31,9 @@
  *     it sees keys 0..pos, otherwise all t_kv keys.
  *   - a query with no visible key returns o = 0 and lse = -inf.
  *   - lse is the natural log of the sum of exp over the SCALED scores.
+ *   - interleaved rope ([P2] gate 3) rotates the pairs (2i, 2i+1) of a vector
+ *     by theta_i = position * base^(-2i/d), the standard rotary frequencies;
+ *     the page names the rotation but does not print its body.
  *
  * All floating arrays are double, dense, row-major unless a stride is passed;
  * strides are in elements. Nothing here is blocked, fused or reordered beyond
@@ -411,4 +414,32 @@ int mla_oracle_cache_write(int64_t T, int64_t L, int64_t R, int64_t esize, const
     }
   }
   return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Interleaved rotary position embedding ([P2] "tests/mla_gpu_forward.rs",
+ * gate 3, gpu_mla_rope_interleaved_matches_cpu: d_rope 8 and 64, base 8e6,
+ * positions 13 * p, and d_rope == 0 is a no-op).
+ *
+ * Every vector x[t, v, 0:d] of token t is rotated in place, pair by pair: for
+ * i < d / 2, with theta = positions[t] * base^(-2i / d),
+ *   x[2i]   <- x[2i] cos(theta) - x[2i+1] sin(theta)
+ *   x[2i+1] <- x[2i] sin(theta) + x[2i+1] cos(theta)
+ *   x      [T, V, d] double, dense
+ *   pos    [T] int32
+ * ------------------------------------------------------------------------- */
+void mla_oracle_rope_interleaved(int64_t T, int64_t V, int64_t d, double* x, const int32_t* pos,
+                                 double base) {
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t v = 0; v < V; ++v) {
+      double* row = x + (t * V + v) * d;
+      for (int64_t i = 0; i < d / 2; ++i) {
+        const double theta = (double)pos[t] * pow(base, -2.0 * (double)i / (double)d);
+        const double c = cos(theta), s = sin(theta);
+        const double a = row[2 * i], b = row[2 * i + 1];
+        row[2 * i] = a * c - b * s;
+        row[2 * i + 1] = a * s + b * c;
+      }
+    }
+  }
 }

@@ -361,3 +361,75 @@ def test_cache_write_skips_bad_slots_and_copies_bits():
     assert out[0] == 0x7FC01234 and out[1] == np.float32(-0.0).view(np.int32)
     assert out[2] == k_pe[0, 0]
     assert np.all(out[3:] == 99)  # slot -5 and slot 4 (= NB*page) are skipped
+
+
+# ------------------------------------------------------------ interleaved rope
+
+
+def _rope_complex(x, positions, base):
+    """The rotation as complex multiplication (numpy complex exp): pair
+    (2i, 2i+1) is the number x[2i] + j x[2i+1], turned by exp(j theta_i)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    freq = np.power(float(base), -np.arange(0, d, 2, dtype=np.float64) / d)
+    angle = np.asarray(positions, dtype=np.float64).reshape(-1, *([1] * (x.ndim - 1))) * freq
+    z = z * np.exp(1j * angle)
+    out = np.empty_like(x)
+    out[..., 0::2] = z.real
+    out[..., 1::2] = z.imag
+    return out
+
+
+@pytest.mark.parametrize("d_rope", [2, 8, 64])
+def test_rope_matches_complex_rotation(d_rope):
+    x, pos = mi.rope_case(1, d_rope=d_rope)
+    got = oracle.rope_interleaved(x, pos, mi.ROPE_BASE)
+    want = _rope_complex(x, pos, mi.ROPE_BASE)
+    assert np.max(np.abs(got - want)) < 1e-12
+    # large positions (long contexts) and another base
+    x, pos = mi.rope_case(2, d_rope=d_rope, pos_step=9973, pos_offset=100_000)
+    got = oracle.rope_interleaved(x, pos, 10_000.0)
+    assert np.max(np.abs(got - _rope_complex(x, pos, 10_000.0))) < 1e-9
+
+
+def test_rope_first_pair_turns_by_the_position():
+    # i = 0 has frequency base^0 = 1: (1, 0) goes to (cos p, sin p), counter-clockwise
+    pos = np.array([0, 1, 13, 78], dtype=np.int32)
+    x = np.zeros((4, 1, 8))
+    x[:, 0, 0] = 1.0
+    got = oracle.rope_interleaved(x, pos, mi.ROPE_BASE)
+    for t, p in enumerate(pos):
+        assert got[t, 0, 0] == pytest.approx(math.cos(p), abs=1e-15)
+        assert got[t, 0, 1] == pytest.approx(math.sin(p), abs=1e-15)
+        assert np.all(got[t, 0, 2:] == 0.0)
+    # the last pair of d = 8 turns by p * base^(-6/8)
+    x = np.zeros((1, 1, 8))
+    x[0, 0, 6] = 1.0
+    got = oracle.rope_interleaved(x, np.array([78], np.int32), mi.ROPE_BASE)
+    th = 78 * mi.ROPE_BASE ** (-0.75)
+    assert got[0, 0, 6] == pytest.approx(math.cos(th), abs=1e-15)
+    assert got[0, 0, 7] == pytest.approx(math.sin(th), abs=1e-15)
+
+
+def test_rope_invariants():
+    x, pos = mi.rope_case(3, d_rope=64)
+    x = x.astype(np.float64)
+    y = oracle.rope_interleaved(x, pos, mi.ROPE_BASE)
+    # position 0 is the identity, exactly
+    assert np.array_equal(oracle.rope_interleaved(x, np.zeros_like(pos), mi.ROPE_BASE), x)
+    # each pair keeps its length
+    n0 = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    n1 = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    assert np.max(np.abs(n0 - n1)) < 1e-13
+    # turning back by -p recovers x
+    back = oracle.rope_interleaved(y, -pos, mi.ROPE_BASE)
+    assert np.max(np.abs(back - x)) < 1e-13
+    # [T, d] is the V = 1 case
+    assert np.array_equal(oracle.rope_interleaved(x[:, 0, :], pos, mi.ROPE_BASE), y[:, 0, :])
+
+
+def test_rope_width_zero_is_a_no_op():
+    x = np.zeros((2, 3, 0))
+    got = oracle.rope_interleaved(x, np.array([0, 5], np.int32), mi.ROPE_BASE)
+    assert got.shape == x.shape
