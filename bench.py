@@ -275,6 +275,57 @@ def v3_secondary(dev, steps: int, warmup: int):
     }
 
 
+def rope_secondary(step: Step, dev, steps: int, warmup: int):
+    """Interleaved rope at the V2-Lite decode step's shapes: the q fold and the
+    cache write with and without the fused rotation (positions seqlen_b - 1),
+    and the in-place rotation of a prefill-sized q_pe [32768, 16, 64] bf16
+    (five copies, 335 MB, so the stream is not cache-resident)."""
+    pos = (step.seqlens - 1).to(torch.int32)
+    c0 = step.caches[0]
+    calls = {
+        "fold_us": lambda i: mla.mla_absorb_q(step.q_nope, step.w_uk_t, step.q_pe, step.q[:, 0]),
+        "fold_rope_us": lambda i: mla.mla_absorb_q_rope(step.q_nope, step.w_uk_t, step.q_pe, pos,
+                                                        mi.ROPE_BASE, step.q[:, 0]),
+        "cache_write_us": lambda i: mla.mla_concat_and_cache(step.kv_new, step.pe_new, step.slots,
+                                                             c0),
+        "cache_write_rope_us": lambda i: mla.mla_concat_and_cache_rope(
+            step.kv_new, step.pe_new, step.slots, pos, mi.ROPE_BASE, c0),
+    }
+    res = {"workload": "V2-Lite decode step shapes (64 tokens x 16 heads, d_rope 64, base 8e6); "
+                       "in-place rope of [32768, 16, 64] bf16"}
+    reps = 20  # calls per graph, so one replay's launch cost is spread over them
+
+    def repeated(fn):
+        def run(i):
+            for _ in range(reps):
+                fn(i)
+        return run
+
+    for name, fn in calls.items():
+        for i in range(2):
+            fn(i)
+        graphs = capture(repeated(fn), 1)
+        if warmup:
+            replay(graphs, 0, warmup)
+        res[name] = round(replay(graphs, 0, steps) / (steps * reps) * 1e3, 2)
+    T, V, D = 32768, 16, 64
+    xs = [torch.randn(T, V, D, device=dev).to(torch.bfloat16) for _ in range(5)]
+    pos_l = torch.arange(T, dtype=torch.int32, device=dev)
+    fn = lambda i: mla.mla_rope_interleaved(xs[i % len(xs)], pos_l, mi.ROPE_BASE)
+    for i in range(len(xs)):
+        fn(i)
+    graphs = capture(fn, len(xs))
+    if warmup:
+        replay(graphs, 0, warmup)
+    ms = replay(graphs, 0, steps) / steps
+    nbytes = 2 * T * V * D * 2  # read and write each element once
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res["inplace_us"] = round(ms * 1e3, 2)
+    res["inplace_gbs"] = round(gbs, 1)
+    res["inplace_hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +333,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-v3", action="store_true", help="skip the 128-head secondary line")
+    ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from the host instead of replaying graphs "
                          "(for counter collection)")
@@ -355,6 +407,8 @@ def main():
     }
     if not args.no_v3:
         line["v3_decode"] = v3_secondary(dev, max(10, args.steps // 2), args.warmup)
+    if not args.no_rope:
+        line["rope"] = rope_secondary(step, dev, max(10, args.steps // 2), args.warmup)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, step)
     print(json.dumps(line), flush=True)

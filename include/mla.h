@@ -3,7 +3,7 @@
  * weight-absorbed form, for decode and chunked prefill, on AMD Instinct
  * MI355X (gfx950).
  *
- * The four compute calls follow the statement of the method on these pages:
+ * The compute calls follow the statement of the method on these pages:
  *   [P1] vllm.cpp "tests/vt/test_ops_mla_absorb.cpp" -- the batched matmul
  *        (q-side W_UK fold and W_UV un-projection) and the nope/rope concat;
  *   [P2] memra-engine 0.124.1 "tests/mla_gpu_forward.rs" -- absorb q,
@@ -124,6 +124,46 @@ int mla_absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_t
 int mla_concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
                          const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
                          mla_stream stream);
+
+/*
+ * Interleaved rotary position embedding (memra-engine 0.124.1
+ * "tests/mla_gpu_forward.rs", gate 3, gpu_mla_rope_interleaved_matches_cpu:
+ * d_rope 8 and 64, base 8e6, positions 13 * p; d_rope 0 is a no-op). With
+ * d = the rope width, pair (2i, 2i+1) of token t's vector turns by
+ * theta = positions[t] * base^(-2i/d):
+ *   (x[2i], x[2i+1]) -> (x[2i] cos theta - x[2i+1] sin theta,
+ *                        x[2i] sin theta + x[2i+1] cos theta)
+ * The angle and the rotation are computed in double and rounded once to the
+ * value dtype.
+ *
+ * mla_rope_interleaved -- rotate x in place.
+ *   x          [T, V, d] bf16 or f32, any strides (inner 1); d even
+ *   positions  [T] MLA_I32, contiguous (any values, negative included)
+ *   base       > 0, finite
+ * d == 0, T == 0 or V == 0: nothing is launched and x is untouched.
+ */
+int mla_rope_interleaved(const mla_tensor* x, const mla_tensor* positions, double base,
+                         mla_stream stream);
+
+/*
+ * mla_absorb_q_rope -- mla_absorb_q with the rotary part rotated as it is
+ * appended: q_out[t, h, L:L+R] = rope(q_pe[t, h, :], positions[t]) (the
+ * rotation fused into the fold's epilogue). R must be even; positions and
+ * base as for mla_rope_interleaved; positions may not be NULL.
+ */
+int mla_absorb_q_rope(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_tensor* q_pe,
+                      const mla_tensor* positions, double base, const mla_tensor* q_out,
+                      mla_stream stream);
+
+/*
+ * mla_concat_and_cache_rope -- mla_concat_and_cache with each token's k_pe
+ * rotated by positions[t] as it is written: kv_cache[blk, off, L:L+R] =
+ * rope(k_pe[t, :], positions[t]); the kv_c part stays a bit copy. R must be
+ * even; positions [T] MLA_I32 contiguous, not NULL; base as above.
+ */
+int mla_concat_and_cache_rope(const mla_tensor* kv_c, const mla_tensor* k_pe,
+                              const mla_tensor* slot_mapping, const mla_tensor* positions,
+                              double base, const mla_tensor* kv_cache, mla_stream stream);
 
 /*
  * mla_decode_workspace_size -- bytes of device workspace mla_decode_attend

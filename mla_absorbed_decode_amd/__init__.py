@@ -7,13 +7,20 @@ Every step of the computation runs in the HIP kernels of ``libmla.so``; there
 is no fallback of any kind, so a missing or unbuilt library raises at the first
 call.
 
-The four compute calls mirror include/mla.h:
+The compute calls mirror include/mla.h:
 
 * ``mla_absorb_q(q_nope, w_uk_t, q_pe, q_out)``
 * ``mla_concat_and_cache(kv_c, k_pe, slot_mapping, kv_cache)``
 * ``mla_decode_attend(q, kv_cache, block_table, seqlens, max_seqlen,
   softmax_scale, causal, out, lse=None, workspace=None)``
 * ``mla_v_up(o_lat, w_uv, out)``
+
+and the interleaved rotary embedding, alone or fused into the fold and the
+cache write:
+
+* ``mla_rope_interleaved(x, positions, base)``
+* ``mla_absorb_q_rope(q_nope, w_uk_t, q_pe, positions, base, q_out)``
+* ``mla_concat_and_cache_rope(kv_c, k_pe, slot_mapping, positions, base, kv_cache)``
 """
 from __future__ import annotations
 
@@ -30,6 +37,9 @@ __all__ = [
     "mla_decode_workspace_size",
     "mla_decode_attend",
     "mla_v_up",
+    "mla_rope_interleaved",
+    "mla_absorb_q_rope",
+    "mla_concat_and_cache_rope",
     "mla_status_str",
     "lib_path",
     "load",
@@ -85,8 +95,13 @@ def load() -> ctypes.CDLL:
                                                   ctypes.POINTER(sz)]
         lib.mla_decode_attend.argtypes = [P, P, P, P, i64, f32, i32, P, P, vp, sz, vp]
         lib.mla_v_up.argtypes = [P, P, P, vp]
+        dbl = ctypes.c_double
+        lib.mla_rope_interleaved.argtypes = [P, P, dbl, vp]
+        lib.mla_absorb_q_rope.argtypes = [P, P, P, P, dbl, P, vp]
+        lib.mla_concat_and_cache_rope.argtypes = [P, P, P, P, dbl, P, vp]
         for fn in ("mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
-                   "mla_decode_attend", "mla_v_up"):
+                   "mla_decode_attend", "mla_v_up", "mla_rope_interleaved", "mla_absorb_q_rope",
+                   "mla_concat_and_cache_rope"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_status_str.argtypes = [ctypes.c_int]
         lib.mla_status_str.restype = ctypes.c_char_p
@@ -158,6 +173,36 @@ def mla_concat_and_cache(kv_c, k_pe, slot_mapping, kv_cache):
     _check(lib.mla_concat_and_cache(_ref(desc(kv_c)), _ref(desc(k_pe)), _ref(desc(slot_mapping)),
                                     _ref(desc(kv_cache)), _stream(kv_cache)),
            "mla_concat_and_cache")
+    return kv_cache
+
+
+def mla_rope_interleaved(x, positions, base):
+    """Rotate x [T, V, d] in place: pair (2i, 2i+1) of token t by positions[t] * base^(-2i/d)."""
+    _device_check(x, positions)
+    lib = load()
+    _check(lib.mla_rope_interleaved(_ref(desc(x)), _ref(desc(positions)), float(base),
+                                    _stream(x)), "mla_rope_interleaved")
+    return x
+
+
+def mla_absorb_q_rope(q_nope, w_uk_t, q_pe, positions, base, q_out):
+    """mla_absorb_q with q_out[t,h,L:] = q_pe[t,h|0,:] rotated by positions[t]."""
+    _device_check(q_nope, w_uk_t, q_pe, positions, q_out)
+    lib = load()
+    _check(lib.mla_absorb_q_rope(_ref(desc(q_nope)), _ref(desc(w_uk_t)), _ref(desc(q_pe)),
+                                 _ref(desc(positions)), float(base), _ref(desc(q_out)),
+                                 _stream(q_out)), "mla_absorb_q_rope")
+    return q_out
+
+
+def mla_concat_and_cache_rope(kv_c, k_pe, slot_mapping, positions, base, kv_cache):
+    """mla_concat_and_cache with k_pe[t] rotated by positions[t] as it is written."""
+    _device_check(kv_c, k_pe, slot_mapping, positions, kv_cache)
+    lib = load()
+    _check(lib.mla_concat_and_cache_rope(_ref(desc(kv_c)), _ref(desc(k_pe)),
+                                         _ref(desc(slot_mapping)), _ref(desc(positions)),
+                                         float(base), _ref(desc(kv_cache)), _stream(kv_cache)),
+           "mla_concat_and_cache_rope")
     return kv_cache
 
 

@@ -38,6 +38,21 @@ __device__ __forceinline__ void copy_rope(const BmmParams& p, int t0, int h) {
   const int nwg = (int)gridDim.x, tid = (int)(blockIdx.x * blockDim.x + threadIdx.x);
   const int stride = nwg * (int)blockDim.x;
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte piece
+  if (p.rope.pos) {
+    // rotated by the token's position: one pair per thread, the angle in double
+    constexpr bool F32 = sizeof(T) == 4;
+    const int half = (int)p.R / 2;
+    for (int e = tid; e < nt * half; e += stride) {
+      const int t = t0 + e / half, i = e % half;
+      const T* src = (const T*)p.pe + (int64_t)t * p.pe_st + (int64_t)h * p.pe_sh;
+      T* dst = (T*)p.out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + p.N;
+      double a = load_value<F32>(src, 2 * i), b = load_value<F32>(src, 2 * i + 1);
+      rope_rotate(a, b, p.rope.pos[t], i, (int)p.R, p.rope.log2_base);
+      store_value<F32>(dst, 2 * i, a);
+      store_value<F32>(dst, 2 * i + 1, b);
+    }
+    return;
+  }
   const bool vec = p.R % V == 0 && ((uintptr_t)p.pe % 16 == 0) && ((uintptr_t)p.out % 16 == 0) &&
                    (p.pe_st % V == 0) && (p.pe_sh % V == 0) && (p.o_st % V == 0) &&
                    (p.o_sh % V == 0) && ((p.N) % V == 0);

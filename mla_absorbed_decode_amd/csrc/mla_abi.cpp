@@ -7,6 +7,7 @@
 // require of their op).
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -56,6 +57,18 @@ bool rows_aligned16(const mla_tensor* t) {
   return true;
 }
 
+// rotary positions [T] int32 contiguous, base finite and > 0
+int check_rope(const mla_tensor* positions, int64_t T, double base, mla::RopeSpec* spec) {
+  int rc;
+  if ((rc = check_desc(positions, 1))) return rc;
+  if (positions->dtype != MLA_I32) return MLA_ERR_DTYPE;
+  if (positions->shape[0] != T) return MLA_ERR_SHAPE;
+  if (!(base > 0.0) || !isfinite(base)) return MLA_ERR_UNSUPPORTED;
+  spec->pos = (const int32_t*)positions->data;
+  spec->log2_base = log2(base);
+  return MLA_OK;
+}
+
 hipError_t g_last_hip = hipSuccess;
 
 int launched(hipError_t e) {
@@ -84,8 +97,9 @@ const char* mla_status_str(int status) {
   return "unknown mla status";
 }
 
-int mla_absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_tensor* q_pe,
-                 const mla_tensor* q_out, mla_stream stream) {
+static int absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_tensor* q_pe,
+                    const mla_tensor* positions, double base, const mla_tensor* q_out,
+                    mla_stream stream) {
   int rc;
   if ((rc = check_desc(q_nope, 3)) || (rc = check_desc(w_uk_t, 3)) || (rc = check_desc(q_out, 3)))
     return rc;
@@ -104,8 +118,16 @@ int mla_absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_t
   }
   if (q_out->shape[0] != T || q_out->shape[1] != N || q_out->shape[2] != L + R) return MLA_ERR_SHAPE;
   if (P == 0 || L == 0) return MLA_ERR_SHAPE;
+  mla::RopeSpec rope;
+  memset(&rope, 0, sizeof(rope));
+  if (positions) {
+    if (R % 2) return MLA_ERR_SHAPE;
+    if ((rc = check_rope(positions, T, base, &rope))) return rc;
+    if (R == 0) rope.pos = nullptr;  // no rope part: nothing to rotate
+  }
   mla::BmmParams p;
   memset(&p, 0, sizeof(p));
+  p.rope = rope;
   p.a = q_nope->data; p.a_st = q_nope->stride[0]; p.a_sh = q_nope->stride[1];
   p.w = w_uk_t->data; p.w_sh = w_uk_t->stride[0]; p.w_sk = w_uk_t->stride[1];
   p.out = q_out->data; p.o_st = q_out->stride[0]; p.o_sh = q_out->stride[1];
@@ -115,6 +137,18 @@ int mla_absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_t
   p.T = T; p.H = N; p.K = P; p.N = L; p.R = R;
   p.is_f32 = dt == MLA_F32;
   return launched(mla::launch_bmm(p, (hipStream_t)stream));
+}
+
+int mla_absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_tensor* q_pe,
+                 const mla_tensor* q_out, mla_stream stream) {
+  return absorb_q(q_nope, w_uk_t, q_pe, nullptr, 0.0, q_out, stream);
+}
+
+int mla_absorb_q_rope(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_tensor* q_pe,
+                      const mla_tensor* positions, double base, const mla_tensor* q_out,
+                      mla_stream stream) {
+  if (!positions) return MLA_ERR_NULL;
+  return absorb_q(q_nope, w_uk_t, q_pe, positions, base, q_out, stream);
 }
 
 int mla_v_up(const mla_tensor* o_lat, const mla_tensor* w_uv, const mla_tensor* out,
@@ -139,9 +173,9 @@ int mla_v_up(const mla_tensor* o_lat, const mla_tensor* w_uv, const mla_tensor* 
   return launched(mla::launch_bmm(p, (hipStream_t)stream));
 }
 
-int mla_concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
-                         const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
-                         mla_stream stream) {
+static int concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
+                            const mla_tensor* slot_mapping, const mla_tensor* positions,
+                            double base, const mla_tensor* kv_cache, mla_stream stream) {
   int rc;
   if ((rc = check_desc(kv_c, 2)) || (rc = check_desc(slot_mapping, 1)) ||
       (rc = check_desc(kv_cache, 3)))
@@ -159,6 +193,11 @@ int mla_concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
   const int es = esize_of(dt);
   mla::CacheWriteParams p;
   memset(&p, 0, sizeof(p));
+  if (positions) {
+    if (R % 2) return MLA_ERR_SHAPE;
+    if ((rc = check_rope(positions, T, base, &p.rope))) return rc;
+    if (R == 0) p.rope.pos = nullptr;
+  }
   p.kv_c = kv_c->data; p.kv_c_s0 = kv_c->stride[0];
   p.k_pe = k_pe ? k_pe->data : nullptr; p.k_pe_s0 = k_pe ? k_pe->stride[0] : 0;
   p.slots = slot_mapping->data; p.slot_is_i64 = slot_mapping->dtype == MLA_I64;
@@ -169,6 +208,40 @@ int mla_concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
             (!k_pe || rows_aligned16(k_pe)) && rows_aligned16(kv_cache);
   if (T == 0 || p.num_blocks == 0 || p.page == 0) return MLA_OK;
   return launched(mla::launch_cache_write(p, (hipStream_t)stream));
+}
+
+int mla_concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
+                         const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
+                         mla_stream stream) {
+  return concat_and_cache(kv_c, k_pe, slot_mapping, nullptr, 0.0, kv_cache, stream);
+}
+
+int mla_concat_and_cache_rope(const mla_tensor* kv_c, const mla_tensor* k_pe,
+                              const mla_tensor* slot_mapping, const mla_tensor* positions,
+                              double base, const mla_tensor* kv_cache, mla_stream stream) {
+  if (!positions) return MLA_ERR_NULL;
+  return concat_and_cache(kv_c, k_pe, slot_mapping, positions, base, kv_cache, stream);
+}
+
+int mla_rope_interleaved(const mla_tensor* x, const mla_tensor* positions, double base,
+                         mla_stream stream) {
+  int rc;
+  if ((rc = check_desc(x, 3))) return rc;
+  if (!is_value_dtype(x->dtype)) return MLA_ERR_DTYPE;
+  const int64_t T = x->shape[0], V = x->shape[1], d = x->shape[2];
+  if (d % 2) return MLA_ERR_SHAPE;
+  if (d > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  mla::RopeParams p;
+  memset(&p, 0, sizeof(p));
+  if (!positions) return MLA_ERR_NULL;
+  if ((rc = check_rope(positions, T, base, &p.rope))) return rc;
+  p.x = x->data; p.s0 = x->stride[0]; p.s1 = x->stride[1];
+  p.T = T; p.V = V; p.d = (int)d;
+  p.is_f32 = x->dtype == MLA_F32;
+  p.pair_aligned = (uintptr_t)x->data % (2 * esize_of(x->dtype)) == 0 && p.s0 % 2 == 0 &&
+                   p.s1 % 2 == 0;
+  if (T == 0 || V == 0 || d == 0) return MLA_OK;  // nothing to rotate: nothing is launched
+  return launched(mla::launch_rope(p, (hipStream_t)stream));
 }
 
 int mla_decode_workspace_size(int64_t batch, int64_t q_len, int64_t n_heads, int64_t kv_rank,

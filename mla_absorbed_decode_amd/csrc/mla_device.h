@@ -176,4 +176,39 @@ __device__ __forceinline__ float wave_sum16(float v) {
   return a + b;
 }
 
+// Element e of a value row (bf16 bits or f32) as a double, and back (RNE).
+template <bool F32>
+__device__ __forceinline__ double load_value(const void* row, int64_t e) {
+  if constexpr (F32) return (double)((const float*)row)[e];
+  else return (double)bf16_to_f32(((const uint16_t*)row)[e]);
+}
+template <bool F32>
+__device__ __forceinline__ void store_value(void* row, int64_t e, double v) {
+  if constexpr (F32) ((float*)row)[e] = (float)v;
+  else ((uint16_t*)row)[e] = f32_to_bf16((float)v);
+}
+
+// Interleaved rotary embedding of one pair (a, b) = (x[2i], x[2i+1]) of a
+// d-wide vector at position pos (memra-engine 0.124.1 "tests/mla_gpu_forward.rs",
+// gate 3): theta = pos * base^(-2i/d), (a, b) -> (a cos - b sin, a sin + b cos).
+// The frequency, the angle and its reduction to [-pi, pi] are computed in
+// double and the rotation too, so the single rounding to the output type is
+// the only error that matters even for positions in the millions.
+__device__ __forceinline__ void rope_angle(double& sn, double& cs, int pos, int i, int d,
+                                           double log2_base) {
+  const double freq = exp2(-(2.0 * i / d) * log2_base);
+  const double theta = (double)pos * freq;
+  constexpr double kTwoPi = 6.283185307179586476925;
+  const double r = theta - kTwoPi * rint(theta * (1.0 / kTwoPi));
+  sincos(r, &sn, &cs);
+}
+__device__ __forceinline__ void rope_rotate(double& a, double& b, int pos, int i, int d,
+                                            double log2_base) {
+  double sn, cs;
+  rope_angle(sn, cs, pos, i, d, log2_base);
+  const double x = a * cs - b * sn, y = a * sn + b * cs;
+  a = x;
+  b = y;
+}
+
 }  // namespace mla

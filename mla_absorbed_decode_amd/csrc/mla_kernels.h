@@ -13,6 +13,25 @@ constexpr int kKvRank = 512;     // latent width L the attention kernels impleme
 constexpr int kSplitUnits = 256; // fewer (sequence, row-tile) units than this => split KV
 constexpr int kMaxUnitsSplit = 1024;
 
+// ------------------------------------------------------------ rotary embedding
+// Interleaved rotation of the rope part: pair (2i, 2i+1) of token t's vector
+// turns by pos[t] * base^(-2i/d). pos == NULL: no rotation (a bit copy).
+struct RopeSpec {
+  const int32_t* pos;  // [T] positions, or NULL
+  double log2_base;    // log2(base)
+};
+
+// In-place rotation of x [T, V, d] (strides s0, s1, 1).
+struct RopeParams {
+  void* x; int64_t s0, s1;
+  int64_t T, V;
+  int d;
+  int is_f32;
+  int pair_aligned;  // every pair starts on a 2-element boundary: one access per pair
+  RopeSpec rope;
+};
+hipError_t launch_rope(const RopeParams& p, hipStream_t s);
+
 // ------------------------------------------------------------ cache write
 struct CacheWriteParams {
   const void* kv_c;  int64_t kv_c_s0;    // [T, L] row stride (elements)
@@ -23,12 +42,13 @@ struct CacheWriteParams {
   int64_t T, L, R;
   int esize;         // 2 (bf16) or 4 (f32)
   int vec16;         // 1 when every row start is 16-byte aligned and L, R are multiples of 16/esize
+  RopeSpec rope;     // rotate k_pe by its token's position before writing
 };
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
 
 // ------------------------------------------------------------- batched matmul
-// out[t, h, n] = sum_k a[t, h, k] * w[h, k, n]  (+ optional bit copy of the
-// rope rows into out[t, h, Nout : Nout + R]).
+// out[t, h, n] = sum_k a[t, h, k] * w[h, k, n]  (+ optional copy of the rope
+// rows into out[t, h, Nout : Nout + R], rotated when rope.pos is set).
 struct BmmParams {
   const void* a; int64_t a_st, a_sh;        // a[t, h, k]: t stride, h stride (k stride 1)
   const void* w; int64_t w_sh, w_sk;        // w[h, k, n]: h stride, k stride (n stride 1)
@@ -36,6 +56,7 @@ struct BmmParams {
   const void* pe; int64_t pe_st, pe_sh;     // rope rows [t, h or broadcast, R] (pe_sh 0 = broadcast)
   int64_t T, H, K, N, R;
   int is_f32;
+  RopeSpec rope;  // rotate the rope rows by their token's position while copying
 };
 hipError_t launch_bmm(const BmmParams& p, hipStream_t s);
 

@@ -48,7 +48,8 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     names = mla.header_symbols()
     assert set(names) == {"mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
-                          "mla_decode_attend", "mla_v_up", "mla_status_str"}
+                          "mla_decode_attend", "mla_v_up", "mla_status_str",
+                          "mla_rope_interleaved", "mla_absorb_q_rope", "mla_concat_and_cache_rope"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -119,6 +120,49 @@ def test_concat_and_cache_validation(lib):
     assert f(None, pe, sl, cache) == NULL
     assert f(kv, pe, sl, T([32, 64, 576], strides=[110592, 576, 2])) == STRIDE
     assert f(T([0, 512]), T([0, 64]), T([0], I64), cache) == OK
+
+
+# ------------------------------------------------------------- rotary embedding
+
+
+def test_rope_validation(lib):
+    f = lambda x, pos, base: lib.mla_rope_interleaved(R(x), R(pos), ctypes.c_double(base), None)
+    x, pos = T([7, 5, 64], F32), T([7], I32)
+    assert f(x, pos, 0.0) == UNSUP                     # base must be > 0 and finite
+    assert f(x, pos, float("inf")) == UNSUP
+    assert f(x, pos, float("nan")) == UNSUP
+    assert f(T([7, 5, 63], F32), pos, 8e6) == SHAPE    # odd width
+    assert f(x, T([6], I32), 8e6) == SHAPE             # one position per token
+    assert f(x, T([7], I64), 8e6) == DTYPE             # positions are int32
+    assert f(T([7, 5, 64], I32), pos, 8e6) == DTYPE
+    assert f(x, None, 8e6) == NULL
+    assert f(T([7, 64], F32), pos, 8e6) == SHAPE       # rank 3
+    assert f(T([7, 5, 64], F32, strides=[640, 128, 2]), pos, 8e6) == STRIDE
+    # width 0 (NoPE), no tokens or no vectors: nothing is launched
+    assert f(T([7, 5, 0], F32), pos, 8e6) == OK
+    assert f(T([0, 5, 64], F32), T([0], I32), 8e6) == OK
+    assert f(T([7, 0, 64], F32), pos, 8e6) == OK
+
+
+def test_fused_rope_validation(lib):
+    dbl = ctypes.c_double
+    q = lambda qn, w, pe, pos, out, base=8e6: lib.mla_absorb_q_rope(R(qn), R(w), R(pe), R(pos),
+                                                                     dbl(base), R(out), None)
+    qn, w, pe, out = T([4, 16, 128]), T([16, 128, 512]), T([4, 16, 64]), T([4, 16, 576])
+    assert q(qn, w, pe, None, out) == NULL
+    assert q(qn, w, pe, T([5], I32), out) == SHAPE
+    assert q(qn, w, pe, T([4], I64), out) == DTYPE
+    assert q(qn, w, pe, T([4], I32), out, base=-1.0) == UNSUP
+    assert q(qn, w, T([4, 16, 63]), T([4], I32), T([4, 16, 575])) == SHAPE  # odd rope width
+    assert q(T([0, 16, 128]), w, T([0, 16, 64]), T([0], I32), T([0, 16, 576])) == OK
+    c = lambda kv, pe, sl, pos, cache, base=8e6: lib.mla_concat_and_cache_rope(
+        R(kv), R(pe), R(sl), R(pos), dbl(base), R(cache), None)
+    kv, pe, sl, cache = T([200, 512]), T([200, 64]), T([200], I64), T([32, 64, 576])
+    assert c(kv, pe, sl, None, cache) == NULL
+    assert c(kv, pe, sl, T([199], I32), cache) == SHAPE
+    assert c(kv, pe, sl, T([200], I64), cache) == DTYPE
+    assert c(kv, pe, sl, T([200], I32), cache, base=float("inf")) == UNSUP
+    assert c(T([0, 512]), T([0, 64]), T([0], I64), T([0], I32), cache) == OK
 
 
 # ------------------------------------------------------------------ decode
