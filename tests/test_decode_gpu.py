@@ -140,6 +140,17 @@ def test_prefill_many_units_no_split():
     check(c, "NoPE prefill 300 x 64 heads")
 
 
+def test_long_sequence_past_the_staged_block_table():
+    # 256 sequences (one unit each, no split): the long one has 1250 pages of 16
+    # tokens, more than the 1024 block-table entries a workgroup stages, so its
+    # last pages come through the loader's direct block-table reads
+    rng = mi.stream(19, 0)
+    seqlens = rng.integers(1, 41, size=256).astype(np.int32)
+    seqlens[77] = 20_000
+    c = mi.decode_case(19, V2, "bf16", seqlens, page=16)
+    check(c, "256 sequences, one of 1250 pages")
+
+
 # -------------------------------------------------------------------- fp32
 
 
