@@ -86,20 +86,22 @@ def test_strided_view_only_touches_the_view():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_odd_strides_take_the_element_path(dtype):
-    # rows 129 elements apart and starting at element 1: pairs are not aligned
+@pytest.mark.parametrize("width,start", [(129, 1), (66, 2)])
+def test_unaligned_rows(dtype, width, start):
+    # rows `width` elements apart, starting at element `start`: 129/1 leaves pairs
+    # unaligned (element path), 66/2 leaves rows off 16 bytes but pairs aligned
     x, pos = mi.rope_case(3, n_pos=6, n_vec=4, d_rope=64, dtype=dtype)
     td = torch.bfloat16 if dtype == "bf16" else torch.float32
-    big = torch.full((6, 4, 129), float("nan"), dtype=td, device=dev())
-    view = big[:, :, 1:65]
+    big = torch.full((6, 4, width), float("nan"), dtype=td, device=dev())
+    view = big[:, :, start:start + 64]
     view.copy_(t_dev(x, dtype))
-    say(f"[rope] odd strides {dtype}")
+    say(f"[rope] rows {width} apart from {start}, {dtype}")
     mla.mla_rope_interleaved(view, torch.from_numpy(pos).to(dev()), mi.ROPE_BASE)
     torch.cuda.synchronize()
     want = oracle.rope_interleaved(x, pos, mi.ROPE_BASE)
-    assert_ulp(to_np(view), want, dtype, 1.0, f"odd strides {dtype}", pos.max())
+    assert_ulp(to_np(view), want, dtype, 1.0, f"rows {width}/{start} {dtype}", pos.max())
     b = big.float().cpu()
-    assert torch.isnan(b[:, :, 0]).all() and torch.isnan(b[:, :, 65:]).all()
+    assert torch.isnan(b[:, :, :start]).all() and torch.isnan(b[:, :, start + 64:]).all()
 
 
 def test_width_zero_is_a_no_op():
