@@ -13,15 +13,18 @@ workload (16 heads, kv_rank 512 + rope 64, batch 64, seqlens uniform on
 
 Inputs are resident in HBM before timing. The latent cache is held in enough
 copies (rotated per step) that the step's working set exceeds twice the
-256 MB last-level cache, so the cache read is an HBM read. Each step is
-captured once per cache copy as a HIP graph (as a serving decode loop runs
-it) and the graphs are replayed in turn: W warm-up steps, then K timed steps
-between device synchronisations; one JSON line is printed.
+256 MB last-level cache, so the cache read is an HBM read. The steps over the
+cache copies, one after another, are captured in one HIP graph, the way a
+serving decode loop captures every layer of a token's step in one graph
+(each copy stands for one layer's cache); single-step graphs cover a
+remainder. W warm-up steps, then K timed steps between device
+synchronisations; one JSON line is printed.
 
 value = latent-KV bytes the step must read (sum of seqlens x 576 x 2 B) per
 second of step time. The roofline object covers the attention call (its
-partial and merge kernels): graphs holding only that call are replayed K times
-right after the steps and timed with HIP events on the stream they run on.
+partial and merge kernels): a graph holding only that call, once per cache
+copy, is replayed for K calls right after the steps and timed with HIP events
+on the stream it runs on.
 """
 from __future__ import annotations
 
@@ -158,6 +161,23 @@ def copy_calibration(dev):
     torch.cuda.synchronize()
 
 
+def replay_steps(whole, singles, count: int):
+    """Replay `count` steps: whole graphs of len(singles) steps each, then
+    single-step graphs for the remainder, between two events; returns ms."""
+    n = len(singles)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(count // n):
+        whole.replay()
+    for i in range(count % n):
+        singles[i].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
 def time_steps(step: Step, steps: int, warmup: int):
     """(ms for `steps` whole steps, host seconds for them, ms per attention call)."""
     n = len(step.caches)
@@ -166,12 +186,14 @@ def time_steps(step: Step, steps: int, warmup: int):
     torch.cuda.synchronize()
     step_graphs = capture(step.run, n)
     attn_graphs = capture(step.attend, n)
+    all_steps = capture(lambda _: [step.run(k) for k in range(n)], 1)[0]
+    all_attn = capture(lambda _: [step.attend(k) for k in range(n)], 1)[0]
     if warmup:
-        replay(step_graphs, 0, warmup)
+        replay_steps(all_steps, step_graphs, warmup)
     wall0 = time.perf_counter()
-    total_ms = replay(step_graphs, warmup, steps)
+    total_ms = replay_steps(all_steps, step_graphs, steps)
     wall = time.perf_counter() - wall0
-    attn_ms = replay(attn_graphs, warmup, steps) / steps
+    attn_ms = replay_steps(all_attn, attn_graphs, steps) / steps
     return total_ms, wall, attn_ms
 
 
@@ -260,9 +282,10 @@ def v3_secondary(dev, steps: int, warmup: int):
         run(i)
     torch.cuda.synchronize()
     graphs = capture(run, len(views))
+    whole = capture(lambda _: [run(k) for k in range(len(views))], 1)[0]
     if warmup:
-        replay(graphs, 0, warmup)
-    ms = replay(graphs, warmup, steps) / steps
+        replay_steps(whole, graphs, warmup)
+    ms = replay_steps(whole, graphs, steps) / steps
     byts, flops = attention_bytes(c), attention_flops(c)
     return {
         "workload": "V3 decode bf16: 128 heads, entry 576 / v 512, batch 4 x 4096, 64-token "
