@@ -259,8 +259,9 @@ def cpu_baseline(case: mi.DecodeCase, step: Step, budget_s: float = 10.0):
     }
 
 
-def v3_secondary(dev, steps: int, warmup: int):
-    """128-head V3 decode (B=4 x 4096, block-major view): attention call only."""
+def v3_secondary(dev, steps: int, warmup: int, eager: bool = False):
+    """128-head V3 decode (B=4 x 4096, block-major view): attention call only
+    (eager: every call launched from the host, for counter collection)."""
     c = mi.v3_decode(seed=0, neighbour_fill=0.0)
     d = c.dims
     bf = torch.bfloat16
@@ -281,11 +282,27 @@ def v3_secondary(dev, steps: int, warmup: int):
     for i in range(len(views)):
         run(i)
     torch.cuda.synchronize()
+    if eager:
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for i in range(warmup):
+            run(i)
+        t0.record()
+        for i in range(steps):
+            run(i)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        return _v3_line(c, ms)
     graphs = capture(run, len(views))
     whole = capture(lambda _: [run(k) for k in range(len(views))], 1)[0]
     if warmup:
         replay_steps(whole, graphs, warmup)
     ms = replay_steps(whole, graphs, steps) / steps
+    return _v3_line(c, ms)
+
+
+def _v3_line(c, ms):
     byts, flops = attention_bytes(c), attention_flops(c)
     return {
         "workload": "V3 decode bf16: 128 heads, entry 576 / v 512, batch 4 x 4096, 64-token "
@@ -429,7 +446,8 @@ def main():
         "roofline": roof,
     }
     if not args.no_v3:
-        line["v3_decode"] = v3_secondary(dev, max(10, args.steps // 2), args.warmup)
+        line["v3_decode"] = v3_secondary(dev, max(10, args.steps // 2), args.warmup,
+                                         eager=args.eager)
     if not args.no_rope:
         line["rope"] = rope_secondary(step, dev, max(10, args.steps // 2), args.warmup)
     if not args.no_cpu:
