@@ -50,12 +50,18 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 LLC_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRC = os.path.join(ROOT, "mla_absorbed_decode_amd", "csrc", "decode.hip")
+# the sources the attention kernels are compiled from
+DECODE_SRC = [os.path.join(ROOT, "mla_absorbed_decode_amd", "csrc", f)
+              for f in ("decode.hip", "mla_device.h", "mla_kernels.h")]
 
 
-def src_sha(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_sha(paths) -> str:
+    """sha256 prefix of the concatenated source files."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 class Step:
