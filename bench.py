@@ -6,8 +6,9 @@ A step is one pass of the whole hot path over one batch of the V2-Lite decode
 workload (16 heads, kv_rank 512 + rope 64, batch 64, seqlens uniform on
 [512, 4096], 64-token pages, random block table, bf16, values N(0, 0.1^2)):
 
-  1. mla_absorb_q          q_nope [64,16,128] x W_UK_T [16,128,512] -> q[..., :512], q_pe -> q[..., 512:]
-  2. mla_concat_and_cache  each sequence's newest [c_kv | k_pe] row into its page
+  1+2. mla_absorb_q_and_cache, one launch:
+       q fold   q_nope [64,16,128] x W_UK_T [16,128,512] -> q[..., :512], q_pe -> q[..., 512:]
+       cache    each sequence's newest [c_kv | k_pe] row into its page
   3. mla_decode_attend     split-KV attention over the paged latent cache + log-sum-exp merge
   4. mla_v_up              o_lat [64,16,512] x W_UV [16,512,128]
 
@@ -105,8 +106,9 @@ class Step:
 
     def run(self, i: int):
         c = self.caches[i % len(self.caches)]
-        mla.mla_absorb_q(self.q_nope, self.w_uk_t, self.q_pe, self.q[:, 0])
-        mla.mla_concat_and_cache(self.kv_new, self.pe_new, self.slots, c)
+        # q fold and latent write of the new tokens in one launch
+        mla.mla_absorb_q_and_cache(self.q_nope, self.w_uk_t, self.q_pe, self.q[:, 0],
+                                   self.kv_new, self.pe_new, self.slots, c)
         self.attend(i)
         mla.mla_v_up(self.o_lat[:, 0], self.w_uv, self.out)
 
@@ -336,6 +338,12 @@ def rope_secondary(step: Step, dev, steps: int, warmup: int):
                                                              c0),
         "cache_write_rope_us": lambda i: mla.mla_concat_and_cache_rope(
             step.kv_new, step.pe_new, step.slots, pos, mi.ROPE_BASE, c0),
+        "fold_and_cache_us": lambda i: mla.mla_absorb_q_and_cache(
+            step.q_nope, step.w_uk_t, step.q_pe, step.q[:, 0], step.kv_new, step.pe_new,
+            step.slots, c0),
+        "fold_and_cache_rope_us": lambda i: mla.mla_absorb_q_and_cache(
+            step.q_nope, step.w_uk_t, step.q_pe, step.q[:, 0], step.kv_new, step.pe_new,
+            step.slots, c0, pos, mi.ROPE_BASE),
     }
     res = {"workload": "V2-Lite decode step shapes (64 tokens x 16 heads, d_rope 64, base 8e6); "
                        "in-place rope of [32768, 16, 64] bf16"}

@@ -166,6 +166,24 @@ int mla_concat_and_cache_rope(const mla_tensor* kv_c, const mla_tensor* k_pe,
                               double base, const mla_tensor* kv_cache, mla_stream stream);
 
 /*
+ * mla_absorb_q_and_cache -- a decode step's two input calls in one launch:
+ * mla_absorb_q (q_nope, w_uk_t, q_pe -> q_out) and mla_concat_and_cache
+ * (kv_c, k_pe -> kv_cache at slot_mapping) for the same T new tokens, each
+ * query token bringing its own latent row ([P2] gate 2: every decode step
+ * appends the new token's [c_kv | k_pe] row and decodes its query). With
+ * positions (not NULL) q_pe and k_pe are both rotated by their token's
+ * position as in mla_absorb_q_rope and mla_concat_and_cache_rope; with NULL
+ * both are copied. Every argument is validated as for those calls, and
+ * kv_c must have T rows; on any error nothing is launched. The results equal
+ * the two calls made one after the other, bit for bit.
+ */
+int mla_absorb_q_and_cache(const mla_tensor* q_nope, const mla_tensor* w_uk_t,
+                           const mla_tensor* q_pe, const mla_tensor* q_out,
+                           const mla_tensor* kv_c, const mla_tensor* k_pe,
+                           const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
+                           const mla_tensor* positions, double base, mla_stream stream);
+
+/*
  * mla_decode_workspace_size -- bytes of device workspace mla_decode_attend
  * needs for a call of these sizes (an upper bound that depends only on the
  * arguments, never on the device or on seqlens' contents).

@@ -21,6 +21,11 @@ cache write:
 * ``mla_rope_interleaved(x, positions, base)``
 * ``mla_absorb_q_rope(q_nope, w_uk_t, q_pe, positions, base, q_out)``
 * ``mla_concat_and_cache_rope(kv_c, k_pe, slot_mapping, positions, base, kv_cache)``
+
+and the decode step's fold and cache write as one launch:
+
+* ``mla_absorb_q_and_cache(q_nope, w_uk_t, q_pe, q_out, kv_c, k_pe, slot_mapping,
+  kv_cache, positions=None, base=0.0)``
 """
 from __future__ import annotations
 
@@ -40,6 +45,7 @@ __all__ = [
     "mla_rope_interleaved",
     "mla_absorb_q_rope",
     "mla_concat_and_cache_rope",
+    "mla_absorb_q_and_cache",
     "mla_status_str",
     "lib_path",
     "load",
@@ -99,9 +105,10 @@ def load() -> ctypes.CDLL:
         lib.mla_rope_interleaved.argtypes = [P, P, dbl, vp]
         lib.mla_absorb_q_rope.argtypes = [P, P, P, P, dbl, P, vp]
         lib.mla_concat_and_cache_rope.argtypes = [P, P, P, P, dbl, P, vp]
+        lib.mla_absorb_q_and_cache.argtypes = [P, P, P, P, P, P, P, P, P, dbl, vp]
         for fn in ("mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
                    "mla_decode_attend", "mla_v_up", "mla_rope_interleaved", "mla_absorb_q_rope",
-                   "mla_concat_and_cache_rope"):
+                   "mla_concat_and_cache_rope", "mla_absorb_q_and_cache"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_status_str.argtypes = [ctypes.c_int]
         lib.mla_status_str.restype = ctypes.c_char_p
@@ -204,6 +211,20 @@ def mla_concat_and_cache_rope(kv_c, k_pe, slot_mapping, positions, base, kv_cach
                                          float(base), _ref(desc(kv_cache)), _stream(kv_cache)),
            "mla_concat_and_cache_rope")
     return kv_cache
+
+
+def mla_absorb_q_and_cache(q_nope, w_uk_t, q_pe, q_out, kv_c, k_pe, slot_mapping, kv_cache,
+                           positions=None, base=0.0):
+    """mla_absorb_q and mla_concat_and_cache for the same tokens in one launch
+    (with positions: both rope parts rotated)."""
+    _device_check(q_nope, w_uk_t, q_pe, q_out, kv_c, k_pe, slot_mapping, kv_cache, positions)
+    lib = load()
+    _check(lib.mla_absorb_q_and_cache(_ref(desc(q_nope)), _ref(desc(w_uk_t)), _ref(desc(q_pe)),
+                                      _ref(desc(q_out)), _ref(desc(kv_c)), _ref(desc(k_pe)),
+                                      _ref(desc(slot_mapping)), _ref(desc(kv_cache)),
+                                      _ref(desc(positions)), float(base), _stream(q_out)),
+           "mla_absorb_q_and_cache")
+    return q_out
 
 
 def mla_decode_workspace_size(batch, q_len, n_heads, kv_rank, max_seqlen, page, dtype) -> int:

@@ -19,6 +19,7 @@
 // v_mfma_f32_16x16x4_f32 on a 64 x 64 tiling (one element per lane, no
 // transpose needed). Sizes the MFMA tiling does not cover (K not a multiple of
 // 32, N not a multiple of 16) take a plain one-thread-per-output kernel.
+#include "cache_write.h"
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -101,8 +102,19 @@ __device__ __forceinline__ int slab_off(int r, int c) {
   else return (r ^ (((r >> 3) & 1) << 2)) * (CW * 16) + (c << 4);
 }
 
+// With a fused cache write the grid has one more head slot: its workgroups
+// perform the write (grid-stride over its items) and nothing else.
+__device__ __forceinline__ bool cache_write_slot(const BmmParams& p) {
+  if (!p.with_cw || (int64_t)blockIdx.z < p.H) return false;
+  const int64_t per = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+  cache_write_range(p.cw, ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x,
+                    per);
+  return true;
+}
+
 template <int TN>
 __global__ void __launch_bounds__(256) bmm_bf16_mfma(BmmParams p) {
+  if (cache_write_slot(p)) return;
   extern __shared__ __attribute__((aligned(1024))) char slab_raw[];
   constexpr int CW = TN / 8;     // 16-byte chunks per weight row
   constexpr int NT = TN / 16;    // 16-column MFMA tiles
@@ -177,6 +189,7 @@ __global__ void __launch_bounds__(256) bmm_bf16_mfma(BmmParams p) {
 }
 
 __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
+  if (cache_write_slot(p)) return;
   __shared__ __attribute__((aligned(16))) float wt[2][kKB * kTN];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
   const int n0 = blockIdx.x * kTN, t0 = blockIdx.y * kTM, h = blockIdx.z;
@@ -282,8 +295,9 @@ hipError_t launch_bmm(const BmmParams& p, hipStream_t s) {
       ((uintptr_t)p.a % 16 == 0) && ((uintptr_t)p.w % 16 == 0) && (p.a_st * es % 16 == 0) &&
       (p.a_sh * es % 16 == 0) && (p.w_sh * es % 16 == 0) && (p.w_sk * es % 16 == 0);
   const bool mfma_ok = aligned && p.K % kKB == 0 && p.N % 16 == 0 && p.N >= 16;
+  const unsigned hz = (unsigned)p.H + (p.with_cw ? 1u : 0u);  // head slots (+ the cache write)
   if (mfma_ok && p.is_f32) {
-    dim3 grid((unsigned)((p.N + kTN - 1) / kTN), (unsigned)((p.T + kTM - 1) / kTM), (unsigned)p.H);
+    dim3 grid((unsigned)((p.N + kTN - 1) / kTN), (unsigned)((p.T + kTM - 1) / kTM), hz);
     hipLaunchKernelGGL(bmm_f32_mfma, grid, dim3(256), 0, s, p);
   } else if (mfma_ok) {
     // 64-wide tiles when they give the chip at least 128 workgroups
@@ -292,7 +306,7 @@ hipError_t launch_bmm(const BmmParams& p, hipStream_t s) {
     const int tn = wide ? 64 : 16;
     const int64_t kc = p.K < kSlabK ? p.K : kSlabK;
     const size_t smem = (size_t)kc * tn * 2;
-    dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)tiles_t, (unsigned)p.H);
+    dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)tiles_t, hz);
     if (wide) {
       static bool attr = false;
       if (!attr) {
@@ -311,6 +325,11 @@ hipError_t launch_bmm(const BmmParams& p, hipStream_t s) {
     const int64_t blocks = (total + 255) / 256 + (p.T * p.H * p.R + 255) / 256;
     if (p.is_f32) hipLaunchKernelGGL(bmm_plain<true>, dim3((unsigned)blocks), dim3(256), 0, s, p);
     else hipLaunchKernelGGL(bmm_plain<false>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    if (p.with_cw) {  // the plain path has no head slots: the write is a launch of its own
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_cache_write(p.cw, s);
+    }
   }
   return hipGetLastError();
 }

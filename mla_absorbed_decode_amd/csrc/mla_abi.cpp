@@ -97,9 +97,10 @@ const char* mla_status_str(int status) {
   return "unknown mla status";
 }
 
-static int absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_tensor* q_pe,
-                    const mla_tensor* positions, double base, const mla_tensor* q_out,
-                    mla_stream stream) {
+// Validate a q fold and fill its launch parameters (nothing is launched).
+static int build_absorb(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_tensor* q_pe,
+                        const mla_tensor* positions, double base, const mla_tensor* q_out,
+                        mla::BmmParams* out) {
   int rc;
   if ((rc = check_desc(q_nope, 3)) || (rc = check_desc(w_uk_t, 3)) || (rc = check_desc(q_out, 3)))
     return rc;
@@ -136,6 +137,16 @@ static int absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const ml
   }
   p.T = T; p.H = N; p.K = P; p.N = L; p.R = R;
   p.is_f32 = dt == MLA_F32;
+  *out = p;
+  return MLA_OK;
+}
+
+static int absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_tensor* q_pe,
+                    const mla_tensor* positions, double base, const mla_tensor* q_out,
+                    mla_stream stream) {
+  mla::BmmParams p;
+  const int rc = build_absorb(q_nope, w_uk_t, q_pe, positions, base, q_out, &p);
+  if (rc) return rc;
   return launched(mla::launch_bmm(p, (hipStream_t)stream));
 }
 
@@ -173,9 +184,10 @@ int mla_v_up(const mla_tensor* o_lat, const mla_tensor* w_uv, const mla_tensor* 
   return launched(mla::launch_bmm(p, (hipStream_t)stream));
 }
 
-static int concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
-                            const mla_tensor* slot_mapping, const mla_tensor* positions,
-                            double base, const mla_tensor* kv_cache, mla_stream stream) {
+// Validate a cache write and fill its launch parameters (nothing is launched).
+static int build_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
+                       const mla_tensor* slot_mapping, const mla_tensor* positions, double base,
+                       const mla_tensor* kv_cache, mla::CacheWriteParams* out) {
   int rc;
   if ((rc = check_desc(kv_c, 2)) || (rc = check_desc(slot_mapping, 1)) ||
       (rc = check_desc(kv_cache, 3)))
@@ -206,7 +218,17 @@ static int concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
   p.T = T; p.L = L; p.R = R; p.esize = es;
   p.vec16 = (L * es) % 16 == 0 && (R * es) % 16 == 0 && rows_aligned16(kv_c) &&
             (!k_pe || rows_aligned16(k_pe)) && rows_aligned16(kv_cache);
-  if (T == 0 || p.num_blocks == 0 || p.page == 0) return MLA_OK;
+  *out = p;
+  return MLA_OK;
+}
+
+static int concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
+                            const mla_tensor* slot_mapping, const mla_tensor* positions,
+                            double base, const mla_tensor* kv_cache, mla_stream stream) {
+  mla::CacheWriteParams p;
+  const int rc = build_cache(kv_c, k_pe, slot_mapping, positions, base, kv_cache, &p);
+  if (rc) return rc;
+  if (p.T == 0 || p.num_blocks == 0 || p.page == 0) return MLA_OK;
   return launched(mla::launch_cache_write(p, (hipStream_t)stream));
 }
 
@@ -221,6 +243,23 @@ int mla_concat_and_cache_rope(const mla_tensor* kv_c, const mla_tensor* k_pe,
                               double base, const mla_tensor* kv_cache, mla_stream stream) {
   if (!positions) return MLA_ERR_NULL;
   return concat_and_cache(kv_c, k_pe, slot_mapping, positions, base, kv_cache, stream);
+}
+
+int mla_absorb_q_and_cache(const mla_tensor* q_nope, const mla_tensor* w_uk_t,
+                           const mla_tensor* q_pe, const mla_tensor* q_out,
+                           const mla_tensor* kv_c, const mla_tensor* k_pe,
+                           const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
+                           const mla_tensor* positions, double base, mla_stream stream) {
+  mla::BmmParams p;
+  mla::CacheWriteParams cw;
+  int rc;
+  if ((rc = build_absorb(q_nope, w_uk_t, q_pe, positions, base, q_out, &p))) return rc;
+  if ((rc = build_cache(kv_c, k_pe, slot_mapping, positions, base, kv_cache, &cw))) return rc;
+  if (cw.T != p.T) return MLA_ERR_SHAPE;  // one new latent row per query token
+  if (p.T == 0) return MLA_OK;
+  p.with_cw = cw.num_blocks > 0 && cw.page > 0;
+  p.cw = cw;
+  return launched(mla::launch_bmm(p, (hipStream_t)stream));
 }
 
 int mla_rope_interleaved(const mla_tensor* x, const mla_tensor* positions, double base,

@@ -57,6 +57,8 @@ struct BmmParams {
   int64_t T, H, K, N, R;
   int is_f32;
   RopeSpec rope;  // rotate the rope rows by their token's position while copying
+  int with_cw;    // also perform the cache write cw, in extra workgroups (head slot H)
+  CacheWriteParams cw;
 };
 hipError_t launch_bmm(const BmmParams& p, hipStream_t s);
 

@@ -49,7 +49,8 @@ def test_library_exports_every_declared_symbol(lib):
     names = mla.header_symbols()
     assert set(names) == {"mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
                           "mla_decode_attend", "mla_v_up", "mla_status_str",
-                          "mla_rope_interleaved", "mla_absorb_q_rope", "mla_concat_and_cache_rope"}
+                          "mla_rope_interleaved", "mla_absorb_q_rope", "mla_concat_and_cache_rope",
+                          "mla_absorb_q_and_cache"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -163,6 +164,22 @@ def test_fused_rope_validation(lib):
     assert c(kv, pe, sl, T([200], I64), cache) == DTYPE
     assert c(kv, pe, sl, T([200], I32), cache, base=float("inf")) == UNSUP
     assert c(T([0, 512]), T([0, 64]), T([0], I64), T([0], I32), cache) == OK
+
+
+def test_fused_fold_and_cache_validation(lib):
+    dbl = ctypes.c_double
+    f = lambda qn, w, pe, out, kv, kpe, sl, cache, pos=None, base=0.0: lib.mla_absorb_q_and_cache(
+        R(qn), R(w), R(pe), R(out), R(kv), R(kpe), R(sl), R(cache), R(pos), dbl(base), None)
+    qn, w, pe, out = T([64, 16, 128]), T([16, 128, 512]), T([64, 16, 64]), T([64, 16, 576])
+    kv, kpe, sl, cache = T([64, 512]), T([64, 64]), T([64], I64), T([32, 64, 576])
+    assert f(qn, w, pe, out, T([63, 512]), T([63, 64]), T([63], I64), cache) == SHAPE  # one row per token
+    assert f(qn, w, pe, out, kv, kpe, sl, T([32, 64, 512])) == SHAPE   # fold ok, cache entry wrong
+    assert f(qn, T([16, 100, 512]), pe, out, kv, kpe, sl, cache) == SHAPE
+    assert f(qn, w, pe, out, kv, kpe, T([64], F32), cache) == DTYPE
+    assert f(qn, w, pe, out, kv, kpe, sl, cache, T([64], I32), -1.0) == UNSUP
+    assert f(qn, w, pe, out, None, kpe, sl, cache) == NULL
+    assert f(T([0, 16, 128]), w, T([0, 16, 64]), T([0, 16, 576]), T([0, 512]), T([0, 64]),
+             T([0], I64), cache) == OK
 
 
 # ------------------------------------------------------------------ decode
