@@ -9,8 +9,8 @@ workload (16 heads, kv_rank 512 + rope 64, batch 64, seqlens uniform on
   1+2. mla_absorb_q_and_cache, one launch:
        q fold   q_nope [64,16,128] x W_UK_T [16,128,512] -> q[..., :512], q_pe -> q[..., 512:]
        cache    each sequence's newest [c_kv | k_pe] row into its page
-  3. mla_decode_attend     split-KV attention over the paged latent cache + log-sum-exp merge
-  4. mla_v_up              o_lat [64,16,512] x W_UV [16,512,128]
+  3+4. mla_decode_attend_v_up: split-KV attention over the paged latent cache, then
+       the log-sum-exp merge and o_lat [64,16,512] x W_UV [16,512,128] in one kernel
 
 Inputs are resident in HBM before timing. The latent cache is held in enough
 copies (rotated per step) that the step's working set exceeds twice the
@@ -109,8 +109,11 @@ class Step:
         # q fold and latent write of the new tokens in one launch
         mla.mla_absorb_q_and_cache(self.q_nope, self.w_uk_t, self.q_pe, self.q[:, 0],
                                    self.kv_new, self.pe_new, self.slots, c)
-        self.attend(i)
-        mla.mla_v_up(self.o_lat[:, 0], self.w_uv, self.out)
+        # attention, then the split merge fused with the W_UV un-projection
+        mla.mla_decode_attend_v_up(self.q, c, self.bt, self.seqlens, self.max_seqlen,
+                                   self.case.scale, True, self.w_uv, self.o_lat,
+                                   self.out.view(self.case.batch, 1, self.case.dims.n_head, -1),
+                                   self.lse, workspace=self.ws)
 
 
 def capture(fn, n: int):

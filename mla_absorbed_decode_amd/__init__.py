@@ -46,6 +46,7 @@ __all__ = [
     "mla_absorb_q_rope",
     "mla_concat_and_cache_rope",
     "mla_absorb_q_and_cache",
+    "mla_decode_attend_v_up",
     "mla_status_str",
     "lib_path",
     "load",
@@ -106,9 +107,11 @@ def load() -> ctypes.CDLL:
         lib.mla_absorb_q_rope.argtypes = [P, P, P, P, dbl, P, vp]
         lib.mla_concat_and_cache_rope.argtypes = [P, P, P, P, dbl, P, vp]
         lib.mla_absorb_q_and_cache.argtypes = [P, P, P, P, P, P, P, P, P, dbl, vp]
+        lib.mla_decode_attend_v_up.argtypes = [P, P, P, P, i64, f32, i32, P, P, P, P, vp, sz, vp]
         for fn in ("mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
                    "mla_decode_attend", "mla_v_up", "mla_rope_interleaved", "mla_absorb_q_rope",
-                   "mla_concat_and_cache_rope", "mla_absorb_q_and_cache"):
+                   "mla_concat_and_cache_rope", "mla_absorb_q_and_cache",
+                   "mla_decode_attend_v_up"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_status_str.argtypes = [ctypes.c_int]
         lib.mla_status_str.restype = ctypes.c_char_p
@@ -251,6 +254,25 @@ def mla_decode_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_sca
                                  int(bool(causal)), _ref(desc(out)), _ref(desc(lse)),
                                  workspace.data_ptr(), workspace.numel(), _stream(out)),
            "mla_decode_attend")
+    return out
+
+
+def mla_decode_attend_v_up(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal,
+                           w_uv, o_lat, out, lse=None, workspace=None):
+    """mla_decode_attend into o_lat (and lse), then out[b,i,h,:] = o_lat[b,i,h,:] @ w_uv[h];
+    the split merge and the un-projection run as one kernel where they can."""
+    _device_check(q, kv_cache, block_table, seqlens, w_uv, o_lat, out, lse, workspace)
+    lib = load()
+    if workspace is None:
+        nbytes = mla_decode_workspace_size(q.shape[0], q.shape[1], q.shape[2], o_lat.shape[3],
+                                           max_seqlen, kv_cache.shape[1], q.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.mla_decode_attend_v_up(_ref(desc(q)), _ref(desc(kv_cache)),
+                                      _ref(desc(block_table)), _ref(desc(seqlens)), int(max_seqlen),
+                                      float(softmax_scale), int(bool(causal)), _ref(desc(w_uv)),
+                                      _ref(desc(o_lat)), _ref(desc(out)), _ref(desc(lse)),
+                                      workspace.data_ptr(), workspace.numel(), _stream(out)),
+           "mla_decode_attend_v_up")
     return out
 
 

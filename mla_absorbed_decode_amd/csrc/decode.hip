@@ -1148,27 +1148,22 @@ decode_partial(DecodeParams p) {
 // and its first 8 partial rows are read together, so the merge costs one
 // memory round trip after the plan; the weights reach every lane by shuffle.
 // Splits are combined in split order (deterministic).
-template <bool F32>
-__global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
-  __shared__ int sh_scan[256];
-  plan_units(p, sh_scan);
-  const int groups = (p.rows_per_unit + 3) / 4;
-  const int u = blockIdx.x / groups;
-  const int lane = threadIdx.x & 63;
-  const int row = (blockIdx.x % groups) * 4 + (threadIdx.x >> 6);
-  const int c0 = lane * 8;
-  if (u >= p.num_units || row >= p.rows_per_unit) return;
+// One row of the merge: row `row` (0 .. rows_per_unit) of unit u, this lane's
+// 8 columns c0 .. c0 + 7. Returns false when the unit was not split (its only
+// workgroup wrote the row itself); else the merged row (acc0, acc1) and its
+// log2-domain lse (-inf for a unit with no keys, whose row is zero).
+__device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_scan, int u, int row,
+                                          f32x4_t& acc0, f32x4_t& acc1, float& lse2) {
+  const int lane = threadIdx.x & 63, c0 = lane * 8;
   const int total = sh_scan[p.num_units - 1];
   const int chunk = total > 0 ? ceil_div(total, p.grid) : 1;
   const int end = sh_scan[u], start = u > 0 ? sh_scan[u - 1] : 0;
-  const int b = fdiv(u, p.div_rt);
-  const int r = (u - b * p.row_tiles) * p.rows_per_unit + row;
-  if (r >= p.q_len * p.n_heads) return;
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  float lse2 = kNegInf;
+  acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  lse2 = kNegInf;
   if (end > start) {
     const int first = (start + p.alpha) / chunk, last = (end - 1) / chunk;
-    if (first == last) return;  // written directly by its only workgroup
+    if (first == last) return false;  // written directly by its only workgroup
     const int n = last - first + 1;
     const int64_t srow = p.rows_per_unit;
     const float* lp = p.part_lse + (int64_t)(first + u) * srow + row;
@@ -1231,6 +1226,25 @@ __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
     acc1 *= inv;
     lse2 = Lt > 0.f ? M + fast_log2(Lt) : kNegInf;
   }
+  return true;
+}
+
+template <bool F32>
+__global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
+  __shared__ int sh_scan[256];
+  plan_units(p, sh_scan);
+  const int groups = (p.rows_per_unit + 3) / 4;
+  const int u = blockIdx.x / groups;
+  const int lane = threadIdx.x & 63;
+  const int row = (blockIdx.x % groups) * 4 + (threadIdx.x >> 6);
+  const int c0 = lane * 8;
+  if (u >= p.num_units || row >= p.rows_per_unit) return;
+  const int b = fdiv(u, p.div_rt);
+  const int r = (u - b * p.row_tiles) * p.rows_per_unit + row;
+  if (r >= p.q_len * p.n_heads) return;
+  f32x4_t acc0, acc1;
+  float lse2;
+  if (!merge_row(p, sh_scan, u, row, acc0, acc1, lse2)) return;
   const int qi = fdiv(r, p.div_nh), qh = r - qi * p.n_heads;
   const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)qh * p.o_s2 + c0;
   if constexpr (F32) {
@@ -1245,6 +1259,102 @@ __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   if (c0 == 0 && p.lse)
     p.lse[(int64_t)b * p.l_s0 + (int64_t)qi * p.l_s1 + (int64_t)qh * p.l_s2] =
         lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+}
+
+// ------------------------------------------ merge + W_UV un-projection, fused
+// For one head h and 16 query tokens: merge each token's row of head h from
+// its split partials (one wave per token; unsplit rows are read back from
+// o_lat), keep the 16 merged rows in LDS as bf16 (the values written to
+// o_lat), then out[token, h, :] = o_lat row . W_UV[h] with 16x16x32 MFMAs,
+// W_UV[h] staged in LDS by one burst of global->LDS loads issued before the
+// merge. The products run in the same k order as mla_v_up's kernel, so out
+// is bit-identical to the two calls made one after the other.
+constexpr int kVupTok = 16;                       // query tokens per workgroup
+constexpr int kVupMaxV = 128;                     // W_UV columns one workgroup stages
+constexpr int kVupAPitch = kKvRank * 2 + 32;      // bf16 o_lat row in LDS (padded: the 16
+                                                  // rows of an A read fall in distinct banks)
+// W_UV slab in LDS: 16-byte chunk c of row r at chunk position c ^ vswz(r), so
+// the 16 rows one transposed B read touches (4 per lane group, 8 apart between
+// groups) fall in distinct 32-byte bank segments.
+__device__ __forceinline__ int vswz(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 3) << 1)); }
+
+__global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupParams v) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  __shared__ int sh_scan[256];
+  MLA_LDS char* wslab = (MLA_LDS char*)smem_raw;           // [kKvRank][V] bf16, dense
+  MLA_LDS char* atile = wslab + kKvRank * v.V * 2;          // [16][kVupAPitch]
+  const int h = blockIdx.y, tok0 = blockIdx.x * kVupTok;
+  const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T = p.batch * p.q_len;
+  // W_UV[h] -> LDS: chunk q (16 bytes) of the dense [L][V] slab, 64 per load
+  {
+    const char* W = (const char*)v.w + (int64_t)h * v.w_sh * 2;
+    const int cpr = v.V / 8;  // 16-byte chunks per row
+    const int ninst = kKvRank * cpr / 64;
+    for (int inst = wave; inst < ninst; inst += 16) {
+      const int q = inst * 64 + lane, r = q / cpr, cp = q % cpr;
+      const int c = cp ^ (vswz(r) & (cpr - 1));  // the source chunk stored at position cp
+      load_lds_16(W + (int64_t)r * v.w_sk * 2 + c * 16, wslab + inst * 1024);
+    }
+  }
+  plan_units(p, sh_scan);
+  // merge: wave w takes token tok0 + w
+  const int t = tok0 + wave;
+  const int c0 = lane * 8;
+  u32x4_t packed = {0u, 0u, 0u, 0u};
+  if (t < T) {
+    const int b = t / p.q_len, qi = t - b * p.q_len;
+    const int r = qi * p.n_heads + h;
+    const int rt = r / p.rows_per_unit, row = r - rt * p.rows_per_unit;
+    const int u = b * p.row_tiles + rt;
+    f32x4_t acc0, acc1;
+    float lse2;
+    const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)h * p.o_s2 + c0;
+    uint16_t* orow = (uint16_t*)p.out + ooff;
+    if (merge_row(p, sh_scan, u, row, acc0, acc1, lse2)) {
+      packed = u32x4_t{pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
+                       pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
+      *(u32x4_t*)orow = packed;
+      if (c0 == 0 && p.lse)
+        p.lse[(int64_t)b * p.l_s0 + (int64_t)qi * p.l_s1 + (int64_t)h * p.l_s2] =
+            lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+    } else {
+      packed = *(const u32x4_t*)orow;  // the unit's only workgroup wrote it
+    }
+  }
+  *(MLA_LDS u32x4_t*)(atile + wave * kVupAPitch + c0 * 2) = packed;
+  wait_vmcnt<0>();  // this wave's part of the W_UV slab has landed
+  __syncthreads();
+  // out tile: waves 0 .. V/16 - 1 take 16 columns each, all 16 tokens
+  if (wave < v.V / 16) {
+    const int n0 = wave * 16;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int row_bytes = v.V * 2, cmask = v.V / 8 - 1;
+#pragma unroll 4
+    for (int ks = 0; ks < kKvRank / 32; ++ks) {
+      const i16x8_t av = *(const MLA_LDS i16x8_t*)(atile + li * kVupAPitch + (ks * 32 + 8 * g) * 2);
+      // rows k0 .. k0 + 3 and k0 + 4 .. k0 + 7, columns n0 + 4 (li % 4) .. + 3
+      const int k0 = ks * 32 + 8 * g + (li >> 2), col = n0 + 4 * (li & 3);
+      const int cw = col >> 3, within = (col & 7) * 2;
+      const i16x4_t b0 =
+          lds_read_tr16(wslab + k0 * row_bytes + ((cw ^ (vswz(k0) & cmask)) << 4) + within);
+      const i16x4_t b1 = lds_read_tr16(wslab + (k0 + 4) * row_bytes +
+                                       ((cw ^ (vswz(k0 + 4) & cmask)) << 4) + within);
+      const i16x8_t bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      acc = mfma_16x16x32(av, bv, acc);
+    }
+    // lane holds out[token tok0 + 4g + j][column n0 + li]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tt = tok0 + 4 * g + j;
+      if (tt < T) {
+        const int b = tt / p.q_len, qi = tt - b * p.q_len;
+        ((uint16_t*)v.out)[(int64_t)b * v.o_s0 + (int64_t)qi * v.o_s1 + (int64_t)h * v.o_s2 +
+                           n0 + li] = f32_to_bf16(acc[j]);
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------- variants
@@ -1263,7 +1373,7 @@ constexpr int kColsEntryCost = 3;  // work blocks (measured: 3-4 best on V2-Lite
 enum Variant { kCols64 = 0, kCols0, kMixed64, kMixed0, kRows64, kRows0, kColsF64, kColsF0 };
 
 template <class C>
-hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStream_t s) {
+hipError_t launch_partial(const DecodePlan& plan, const DecodeParams& p, hipStream_t s) {
   // the partial kernel plans in tiles; the merge reads the work block size
   if (plan.wb != C::TT || p.wb != C::TT) return hipErrorInvalidValue;
   const size_t smem = C::SMEM_BYTES;
@@ -1275,7 +1385,12 @@ hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStre
     attr_set = true;
   }
   hipLaunchKernelGGL(decode_partial<C>, dim3(plan.grid), dim3(C::NT), smem, s, p);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <class C>
+hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStream_t s) {
+  hipError_t e = launch_partial<C>(plan, p, s);
   if (e != hipSuccess || !plan.split) return e;
   const int groups = (plan.rows_per_unit + 3) / 4;
   hipLaunchKernelGGL(decode_merge<C::F32>, dim3(plan.num_units * groups), dim3(256), 0, s, p);
@@ -1283,6 +1398,42 @@ hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStre
 }
 
 }  // namespace
+
+bool can_merge_vup(const DecodePlan& plan, int is_f32, const VupParams& v) {
+  // V a power of two from 16 to 128: the slab swizzle stays inside a row
+  return plan.split && !is_f32 && v.V >= 16 && v.V <= kVupMaxV && (v.V & (v.V - 1)) == 0 &&
+         (uintptr_t)v.w % 16 == 0 && (v.w_sh * 2) % 16 == 0 && (v.w_sk * 2) % 16 == 0;
+}
+
+hipError_t launch_decode_vup(const DecodePlan& plan, DecodeParams p, const VupParams& v,
+                             hipStream_t s) {
+  if (!can_merge_vup(plan, 0, v)) return hipErrorInvalidValue;
+  // the partial kernel exactly as launch_decode runs it, then the fused merge
+  hipError_t e = hipSuccess;
+  switch (plan.variant) {
+    case kCols64: e = launch_partial<Cols64>(plan, p, s); break;
+    case kCols0: e = launch_partial<Cols0>(plan, p, s); break;
+    case kMixed64: e = launch_partial<Mixed64>(plan, p, s); break;
+    case kMixed0: e = launch_partial<Mixed0>(plan, p, s); break;
+    case kRows64: e = launch_partial<Rows64>(plan, p, s); break;
+    case kRows0: e = launch_partial<Rows0>(plan, p, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const size_t smem = (size_t)kKvRank * v.V * 2 + (size_t)kVupTok * kVupAPitch;
+  static bool attr_set = false;
+  if (!attr_set) {
+    e = hipFuncSetAttribute((const void*)decode_merge_vup,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)((size_t)kKvRank * kVupMaxV * 2 + (size_t)kVupTok * kVupAPitch));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t T = (int64_t)p.batch * p.q_len;
+  dim3 grid((unsigned)((T + kVupTok - 1) / kVupTok), (unsigned)p.n_heads);
+  hipLaunchKernelGGL(decode_merge_vup, grid, dim3(1024), smem, s, p, v);
+  return hipGetLastError();
+}
 
 int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int64_t max_seqlen,
                 int is_f32, DecodePlan* plan) {

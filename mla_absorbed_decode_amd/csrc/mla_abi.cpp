@@ -298,12 +298,16 @@ int mla_decode_workspace_size(int64_t batch, int64_t q_len, int64_t n_heads, int
   return MLA_OK;
 }
 
-int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
-                      const mla_tensor* block_table, const mla_tensor* seqlens,
-                      int64_t max_seqlen, float softmax_scale, int32_t causal,
-                      const mla_tensor* out, const mla_tensor* lse, void* workspace,
-                      size_t workspace_bytes, mla_stream stream) {
+// Validate an attention call and fill its plan and launch parameters (nothing
+// is launched). *empty is set when the call has nothing to do.
+static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
+                        const mla_tensor* block_table, const mla_tensor* seqlens,
+                        int64_t max_seqlen, float softmax_scale, int32_t causal,
+                        const mla_tensor* out, const mla_tensor* lse, void* workspace,
+                        size_t workspace_bytes, mla::DecodePlan* plan_out,
+                        mla::DecodeParams* params_out, int* empty) {
   int rc;
+  *empty = 0;
   if ((rc = check_desc(q, 4)) || (rc = check_desc(kv_cache, 3)) ||
       (rc = check_desc(block_table, 2)) || (rc = check_desc(seqlens, 1)) ||
       (rc = check_desc(out, 4)))
@@ -329,7 +333,10 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   if (max_seqlen > INT32_MAX || B > INT32_MAX || Sq * N > INT32_MAX || PG > INT32_MAX ||
       MB > INT32_MAX)
     return MLA_ERR_UNSUPPORTED;
-  if (B == 0 || Sq == 0 || N == 0) return MLA_OK;
+  if (B == 0 || Sq == 0 || N == 0) {
+    *empty = 1;
+    return MLA_OK;
+  }
   mla::DecodePlan plan;
   if (mla::plan_decode(B, Sq, N, R, max_seqlen, dt == MLA_F32, &plan)) return MLA_ERR_UNSUPPORTED;
   if (plan.workspace_bytes > 0) {
@@ -376,7 +383,72 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   p.num_units = plan.num_units;
   p.split = plan.split;
   p.grid = plan.grid;
-  return launched(mla::launch_decode(plan, p, R, dt == MLA_F32, (hipStream_t)stream));
+  *plan_out = plan;
+  *params_out = p;
+  return MLA_OK;
+}
+
+int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
+                      const mla_tensor* block_table, const mla_tensor* seqlens,
+                      int64_t max_seqlen, float softmax_scale, int32_t causal,
+                      const mla_tensor* out, const mla_tensor* lse, void* workspace,
+                      size_t workspace_bytes, mla_stream stream) {
+  mla::DecodePlan plan;
+  mla::DecodeParams p;
+  int empty;
+  const int rc = build_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal,
+                              out, lse, workspace, workspace_bytes, &plan, &p, &empty);
+  if (rc || empty) return rc;
+  const int64_t R = q->shape[3] - out->shape[3];
+  return launched(mla::launch_decode(plan, p, R, q->dtype == MLA_F32, (hipStream_t)stream));
+}
+
+int mla_decode_attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,
+                           const mla_tensor* block_table, const mla_tensor* seqlens,
+                           int64_t max_seqlen, float softmax_scale, int32_t causal,
+                           const mla_tensor* w_uv, const mla_tensor* o_lat, const mla_tensor* out,
+                           const mla_tensor* lse, void* workspace, size_t workspace_bytes,
+                           mla_stream stream) {
+  mla::DecodePlan plan;
+  mla::DecodeParams p;
+  int empty, rc;
+  if ((rc = build_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal,
+                         o_lat, lse, workspace, workspace_bytes, &plan, &p, &empty)))
+    return rc;
+  // the un-projection's arguments: o_lat [B, Sq, N, L] seen as [B*Sq, N, L] tokens
+  if ((rc = check_desc(w_uv, 3)) || (rc = check_desc(out, 4))) return rc;
+  const int32_t dt = q->dtype;
+  if (w_uv->dtype != dt || out->dtype != dt) return MLA_ERR_DTYPE;
+  const int64_t B = q->shape[0], Sq = q->shape[1], N = q->shape[2], L = o_lat->shape[3];
+  if (w_uv->shape[0] != N || w_uv->shape[1] != L) return MLA_ERR_SHAPE;
+  const int64_t V = w_uv->shape[2];
+  if (out->shape[0] != B || out->shape[1] != Sq || out->shape[2] != N || out->shape[3] != V)
+    return MLA_ERR_SHAPE;
+  if (V == 0) return MLA_ERR_SHAPE;
+  if (empty) return MLA_OK;
+  const int64_t R = q->shape[3] - L;
+  mla::VupParams v;
+  memset(&v, 0, sizeof(v));
+  v.w = w_uv->data; v.w_sh = w_uv->stride[0]; v.w_sk = w_uv->stride[1];
+  v.out = out->data; v.o_s0 = out->stride[0]; v.o_s1 = out->stride[1]; v.o_s2 = out->stride[2];
+  v.V = (int)V;
+  if (mla::can_merge_vup(plan, dt == MLA_F32, v))
+    return launched(mla::launch_decode_vup(plan, p, v, (hipStream_t)stream));
+  // otherwise the attention call, then the un-projection over the B*Sq tokens,
+  // which needs one token stride in o_lat and out
+  if (Sq > 1 && (o_lat->stride[0] != Sq * o_lat->stride[1] || out->stride[0] != Sq * out->stride[1]))
+    return MLA_ERR_UNSUPPORTED;
+  rc = launched(mla::launch_decode(plan, p, R, dt == MLA_F32, (hipStream_t)stream));
+  if (rc) return rc;
+  mla::BmmParams b;
+  memset(&b, 0, sizeof(b));
+  b.a = o_lat->data; b.a_st = o_lat->stride[1]; b.a_sh = o_lat->stride[2];
+  if (Sq == 1) b.a_st = o_lat->stride[0];
+  b.w = w_uv->data; b.w_sh = w_uv->stride[0]; b.w_sk = w_uv->stride[1];
+  b.out = out->data; b.o_st = Sq == 1 ? out->stride[0] : out->stride[1]; b.o_sh = out->stride[2];
+  b.T = B * Sq; b.H = N; b.K = L; b.N = V; b.R = 0;
+  b.is_f32 = dt == MLA_F32;
+  return launched(mla::launch_bmm(b, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -109,6 +109,14 @@ struct DecodeParams {
   int alpha;              // plan cost of entering a unit, in work blocks
 };
 
+// The W_UV un-projection fused into the split merge: out[b, i, h, 0:V] =
+// o_lat[b, i, h, :] . W_UV[h] (o_lat is DecodeParams::out).
+struct VupParams {
+  const void* w; int64_t w_sh, w_sk;   // W_UV [N, L, V], V contiguous
+  void* out; int64_t o_s0, o_s1, o_s2;  // out [B, Sq, N, V], V contiguous
+  int V;
+};
+
 // Launch plan chosen on the host from sizes alone (never from seqlens).
 struct DecodePlan {
   int variant;        // kernel variant id
@@ -125,5 +133,11 @@ int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int
                 int is_f32, DecodePlan* plan);
 hipError_t launch_decode(const DecodePlan& plan, DecodeParams p, int64_t rope, int is_f32,
                          hipStream_t s);
+// The same with the merge and the W_UV un-projection in one kernel; only for a
+// split plan (see can_merge_vup). The caller launches the plain un-projection
+// otherwise.
+bool can_merge_vup(const DecodePlan& plan, int is_f32, const VupParams& v);
+hipError_t launch_decode_vup(const DecodePlan& plan, DecodeParams p, const VupParams& v,
+                             hipStream_t s);
 
 }  // namespace mla

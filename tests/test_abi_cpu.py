@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) == {"mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
                           "mla_decode_attend", "mla_v_up", "mla_status_str",
                           "mla_rope_interleaved", "mla_absorb_q_rope", "mla_concat_and_cache_rope",
-                          "mla_absorb_q_and_cache"}
+                          "mla_absorb_q_and_cache", "mla_decode_attend_v_up"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -238,6 +238,30 @@ def test_decode_validation(lib):
     assert decode(lib, None, kv, bt, sl, out) == NULL
     # empty batch: nothing to do
     assert decode(lib, T([0, 1, N, 576]), kv, T([0, 4], I32), T([0], I32), T([0, 1, N, 512])) == OK
+
+
+def test_decode_v_up_validation(lib):
+    B, N = 2, 16
+    q, kv, bt, sl = T([B, 1, N, 576]), T([8, 64, 576]), T([B, 4], I32), T([B], I32)
+    o_lat, lse, w, out = T([B, 1, N, 512]), T([B, 1, N], F32), T([N, 512, 128]), T([B, 1, N, 128])
+    rc, need = ws_size(lib, B, 1, N, 512, 128, 64)
+    f = lambda w_, o_, out_, ws=FAKE, ws_bytes=need, q_=q: lib.mla_decode_attend_v_up(
+        R(q_), R(kv), R(bt), R(sl), 128, ctypes.c_float(0.04), 1, R(w_), R(o_), R(out_), R(lse),
+        ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), None)
+    assert f(w, o_lat, out, ws=0) == WS                       # the attention's own checks first
+    assert f(T([N, 256, 128]), o_lat, out) == SHAPE           # w_uv rows must be L
+    assert f(T([8, 512, 128]), o_lat, out) == SHAPE           # one w_uv per head
+    assert f(w, o_lat, T([B, 1, N, 64])) == SHAPE             # out width is V
+    assert f(T([N, 512, 128], F32), o_lat, out) == DTYPE
+    assert f(w, o_lat, None) == NULL
+    assert f(w, None, out) == NULL                            # o_lat is required
+    # two queries per sequence, o_lat without one token stride, fused kernel not
+    # available (f32): refused before launching
+    q2, o2 = T([B, 2, N, 576], F32), T([B, 2, N, 512], F32, strides=[4 * N * 512, N * 512, 512, 1])
+    assert lib.mla_decode_attend_v_up(R(q2), R(T([8, 64, 576], F32)), R(bt), R(sl), 128,
+                                      ctypes.c_float(0.04), 1, R(T([N, 512, 128], F32)), R(o2),
+                                      R(T([B, 2, N, 128], F32)), None, ctypes.c_void_p(FAKE),
+                                      ctypes.c_size_t(1 << 30), None) == UNSUP
 
 
 # ----------------------------------------------------------- python layer

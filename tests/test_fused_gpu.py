@@ -75,3 +75,60 @@ def test_fused_with_an_empty_pool_only_folds():
     mla.mla_absorb_q_and_cache(q_nope, w, q_pe, q_b, kv, kpe, slots, cache)
     torch.cuda.synchronize()
     assert torch.equal(bits(q_a), bits(q_b))
+
+
+# ------------------------------------------- attention + W_UV un-projection
+
+
+def run_attend_v_up(c, w_uv_np, fused):
+    from helpers import DeviceCache, to_dev
+    d = c.dims
+    td = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    q = to_dev(c.q, c.dtype)
+    cache = DeviceCache(c, False)
+    bt = torch.from_numpy(c.block_table).to(dev())
+    sl = torch.from_numpy(c.seqlens).to(dev())
+    w_uv = to_dev(w_uv_np, c.dtype)
+    o_lat = torch.full((c.batch, c.q_len, d.n_head, d.kv_rank), float("nan"), dtype=td, device=dev())
+    lse = torch.full((c.batch, c.q_len, d.n_head), float("nan"), dtype=torch.float32, device=dev())
+    V = w_uv_np.shape[2]
+    out = torch.full((c.batch, c.q_len, d.n_head, V), float("nan"), dtype=td, device=dev())
+    if fused:
+        mla.mla_decode_attend_v_up(q, cache.view, bt, sl, c.max_seqlen, c.scale, c.causal, w_uv,
+                                   o_lat, out, lse)
+    else:
+        mla.mla_decode_attend(q, cache.view, bt, sl, c.max_seqlen, c.scale, c.causal, o_lat, lse)
+        mla.mla_v_up(o_lat.view(c.batch * c.q_len, d.n_head, d.kv_rank), w_uv,
+                     out.view(c.batch * c.q_len, d.n_head, V))
+    torch.cuda.synchronize()
+    return o_lat, lse, out
+
+
+CASES = [
+    ("V2-Lite full batch", lambda: mi.v2lite_decode(seed=0), 128),
+    ("16 heads ragged with empty sequences",
+     lambda: mi.decode_case(41, mi.V2_LITE, "bf16", [0, 1, 77, 300, 2000, 0, 64]), 128),
+    ("16 heads x 2 queries", lambda: mi.decode_case(42, mi.V2_LITE, "bf16", [3, 700, 1500], q_len=2), 128),
+    ("128 heads (two units per sequence)", lambda: mi.decode_case(43, mi.V3, "bf16", [1024, 4096, 1]), 128),
+    ("V = 64", lambda: mi.decode_case(44, mi.V2_LITE, "bf16", [500, 900]), 64),
+    ("V = 16", lambda: mi.decode_case(49, mi.V2_LITE, "bf16", [33, 1300]), 16),
+    ("V = 48 (two kernels)", lambda: mi.decode_case(50, mi.V2_LITE, "bf16", [33, 1300]), 48),
+    ("V = 256 (two kernels)", lambda: mi.decode_case(45, mi.V2_LITE, "bf16", [500, 900]), 256),
+    ("no split: 256 sequences", lambda: mi.decode_case(46, mi.V2_LITE, "bf16",
+                                                       list(range(1, 257))), 128),
+    ("fp32 (two kernels)", lambda: mi.decode_case(47, mi.V2_LITE, "f32", [200, 64, 5], q_len=1,
+                                                  dist="uniform", std=1.0), 128),
+]
+
+
+@pytest.mark.parametrize("what,make,V", CASES, ids=[c[0] for c in CASES])
+def test_attend_v_up_equals_two_calls(what, make, V):
+    c = make()
+    w_uv = mi.uniform(48, 5, (c.dims.n_head, c.dims.kv_rank, V), -0.05, 0.05, c.dtype)
+    say(f"[fused] attend + v_up: {what}")
+    o_a, l_a, out_a = run_attend_v_up(c, w_uv, fused=False)
+    o_b, l_b, out_b = run_attend_v_up(c, w_uv, fused=True)
+    assert torch.equal(bits(o_a), bits(o_b))
+    assert torch.equal(l_a.view(torch.int32), l_b.view(torch.int32))
+    assert torch.equal(bits(out_a), bits(out_b))
+    assert not torch.isnan(out_b.float()).any()
