@@ -83,6 +83,15 @@ def _load():
         lib.mla_oracle_cache_write.restype = c_int
         lib.mla_oracle_rope_interleaved.argtypes = [i64, i64, i64, dp, ip32, dbl]
         lib.mla_oracle_rope_interleaved.restype = None
+        fp = ctypes.POINTER(ctypes.c_float)
+        lib.mla_oracle_e4m3_decode_array.argtypes = [i64, u8p, dp]
+        lib.mla_oracle_e4m3_decode_array.restype = None
+        lib.mla_oracle_e4m3_encode_array.argtypes = [i64, fp, u8p]
+        lib.mla_oracle_e4m3_encode_array.restype = None
+        lib.mla_oracle_cache_write_fp8.argtypes = (
+            [i64] * 3 + [fp, fp, ip64, ctypes.c_float, u8p] + [i64] * 6
+        )
+        lib.mla_oracle_cache_write_fp8.restype = c_int
         _lib = lib
     return _lib
 
@@ -319,3 +328,67 @@ def rope_interleaved(x, positions, base):
         raise ValueError("one position per token")
     _load().mla_oracle_rope_interleaved(T, y.shape[1], d, _dp(y), _i32p(pos), float(base))
     return y.reshape(shape)
+
+
+# ------------------------------------------------------------------ fp8 cache
+# [P3] dense fp8 decode tests: a float8_e4m3fn latent cache, descale_q and
+# descale_k; concat_and_cache_mla with a cache dtype and a scale. The format,
+# and the readings of what the pages leave open, are stated in mla_oracle.c.
+
+
+def _u8p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def _fp(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def e4m3_decode(codes):
+    """Values (float64) of OCP e4m3fn codes (any integer array of bytes)."""
+    c = np.ascontiguousarray(np.asarray(codes).astype(np.uint8))
+    out = np.zeros(c.shape, dtype=np.float64)
+    _load().mla_oracle_e4m3_decode_array(c.size, _u8p(c), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    return out
+
+
+def e4m3_encode(values):
+    """Nearest e4m3fn codes (uint8) of float32 values: ties to the even
+    mantissa, magnitudes past 448 saturate, NaN stays NaN."""
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float32))
+    out = np.zeros(v.shape, dtype=np.uint8)
+    _load().mla_oracle_e4m3_encode_array(v.size, _fp(v), _u8p(out))
+    return out
+
+
+def cache_write_fp8(buf, kv_c, k_pe, slots, scale, offset, num_blocks, page, s0, s1):
+    """Expected image of an fp8 latent-cache write: ``buf`` is the whole byte
+    allocation (uint8, copied, not modified); kv_c [T,L] and k_pe [T,R] (or None)
+    as float32 values; the row of token t lands at slot slots[t] of the view
+    (offset, s0, s1 in bytes) as e4m3(x / scale) per element."""
+    out = np.array(buf, dtype=np.uint8, copy=True)
+    flat = out.reshape(-1)
+    kv = np.ascontiguousarray(np.asarray(kv_c, dtype=np.float32))
+    T, L = kv.shape
+    if k_pe is None or np.asarray(k_pe).size == 0:
+        R = 0
+        kp = np.zeros((1,), dtype=np.float32)
+    else:
+        kp = np.ascontiguousarray(np.asarray(k_pe, dtype=np.float32))
+        R = kp.shape[1]
+    sl = np.ascontiguousarray(np.asarray(slots, dtype=np.int64))
+    rc = _load().mla_oracle_cache_write_fp8(
+        T, L, R, _fp(kv if T else np.zeros((1,), np.float32)), _fp(kp), _i64p(sl), float(scale),
+        _u8p(flat), flat.size, offset, num_blocks, page, s0, s1,
+    )
+    if rc != 0:
+        raise ValueError("cache write would fall outside the buffer")
+    return out
+
+
+def attend_paged_fp8(q, pool_codes, block_table, seqlens, scale, causal, L, descale_q, descale_k):
+    """Dense decode over an fp8 cache: the query is q * descale_q and the cache
+    rows are e4m3 values times descale_k; then attend_paged."""
+    q = _f64(q) * float(descale_q)
+    pool = e4m3_decode(pool_codes) * float(descale_k)
+    return attend_paged(q, pool, block_table, seqlens, scale, causal, L)

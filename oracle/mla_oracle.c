@@ -443,3 +443,83 @@ void mla_oracle_rope_interleaved(int64_t T, int64_t V, int64_t d, double* x, con
     }
   }
 }
+
+/* ---------------------------------------------------------------------------
+ * fp8 latent cache ([P3] test_flashmla_dense_fp8_decode_unified_slot_view and
+ * test_flashinfer_mla_dense_fp8_decode_unified_slot_view: the cache holds
+ * torch.float8_e4m3fn values; the dense fp8 decode takes descale_q and
+ * descale_k; concat_and_cache_mla takes a cache dtype and a scale).
+ *
+ * The element format is OCP FP8 E4M3 ("fn": finite, no infinities): one sign
+ * bit, four exponent bits with bias 7, three mantissa bits. Exponent field 0
+ * holds the subnormals m * 2^-9; the all-ones pattern S.1111.111 is NaN; the
+ * largest finite magnitude is 1.75 * 2^8 = 448.
+ *
+ * Readings of what the pages leave open:
+ *   - the write stores e4m3(x / scale) for every element x of [kv_c | k_pe],
+ *     the quotient taken in float (the precision the kernel decides the code
+ *     in), rounded to the nearest e4m3 value with ties to the even mantissa;
+ *     magnitudes above 448 (infinities included) saturate to +-448, NaN stays
+ *     NaN, and the sign of a zero result is kept.
+ *   - dense fp8 decode: the query's values are q * descale_q, the key and value
+ *     rows e4m3 values times descale_k; everything else is the bf16 decode.
+ * ------------------------------------------------------------------------- */
+double mla_oracle_e4m3_decode(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double mag;
+  if (e == 15 && m == 7) return sign ? -NAN : NAN;
+  if (e == 0) mag = ldexp((double)m, -9);
+  else mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+void mla_oracle_e4m3_decode_array(int64_t n, const uint8_t* codes, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = mla_oracle_e4m3_decode(codes[i]);
+}
+
+/* Nearest e4m3 code to v by exhaustive search over the 127 non-negative finite
+ * codes (ties: the even code, i.e. the even mantissa). */
+uint8_t mla_oracle_e4m3_encode(float v) {
+  if (isnan(v)) return signbit(v) ? 0xff : 0x7f;
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  double a = fabs((double)v);
+  if (a > 448.0) a = 448.0;
+  int best = 0;
+  double best_err = a;
+  for (int c = 1; c <= 0x7e; ++c) {
+    const double err = fabs(mla_oracle_e4m3_decode((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+void mla_oracle_e4m3_encode_array(int64_t n, const float* v, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = mla_oracle_e4m3_encode(v[i]);
+}
+
+/* fp8 latent-cache write: token t's row [kv_c[t] | k_pe[t]] (float values, the
+ * inputs' values converted exactly) goes to slot slots[t] of a byte cache view
+ * (offset, block stride s0, row stride s1, in bytes), each element stored as
+ * e4m3(x / scale). Slots outside [0, num_blocks * page) are skipped. Returns 0,
+ * or -1 if a written byte would fall outside buf. */
+int mla_oracle_cache_write_fp8(int64_t T, int64_t L, int64_t R, const float* kv_c,
+                               const float* k_pe, const int64_t* slots, float scale, uint8_t* buf,
+                               int64_t buf_bytes, int64_t offset, int64_t num_blocks, int64_t page,
+                               int64_t s0, int64_t s1) {
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_blocks * page) continue;
+    const int64_t blk = slot / page, off = slot % page;
+    for (int64_t d = 0; d < L + R; ++d) {
+      const int64_t dst = offset + blk * s0 + off * s1 + d;
+      if (dst < 0 || dst >= buf_bytes) return -1;
+      const float x = d < L ? kv_c[t * L + d] : k_pe[t * R + (d - L)];
+      const float q = x / scale;
+      buf[dst] = mla_oracle_e4m3_encode(q);
+    }
+  }
+  return 0;
+}

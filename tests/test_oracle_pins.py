@@ -433,3 +433,120 @@ def test_rope_width_zero_is_a_no_op():
     x = np.zeros((2, 3, 0))
     got = oracle.rope_interleaved(x, np.array([0, 5], np.int32), mi.ROPE_BASE)
     assert got.shape == x.shape
+
+
+# ------------------------------------------------------------------ fp8 e4m3
+# [P3] dense fp8 decode tests keep the cache as torch.float8_e4m3fn: torch's
+# own conversion of that dtype is the library route the oracle's format code
+# is pinned to, plus closed forms of the OCP E4M3 encoding.
+
+
+def _torch_e4m3_values(codes):
+    t = torch.from_numpy(np.asarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.double().numpy()
+
+
+def _torch_e4m3_codes(values):
+    return torch.from_numpy(np.asarray(values, dtype=np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    codes = np.arange(256)
+    got = oracle.e4m3_decode(codes)
+    want = _torch_e4m3_values(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert np.array_equal(got[fin], want[fin])
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    assert np.isnan(got).sum() == 2  # S.1111.111 only
+
+
+def test_e4m3_decode_closed_forms():
+    d = lambda c: float(oracle.e4m3_decode([c])[0])  # noqa: E731
+    assert d(0x00) == 0.0 and math.copysign(1.0, d(0x80)) == -1.0
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9  # subnormals m * 2^-9
+    assert d(0x08) == 2.0 ** -6  # smallest normal: exponent 1 - 7
+    assert d(0x38) == 1.0 and d(0x3C) == 1.5 and d(0xB8) == -1.0
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert math.isnan(d(0x7F)) and math.isnan(d(0xFF))
+    vals = oracle.e4m3_decode(np.arange(0x7F))
+    assert np.all(np.diff(vals) > 0)  # codes order like their values
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(5)
+    pos = oracle.e4m3_decode(np.arange(0x7F))
+    mids = (pos[:-1] + pos[1:]) / 2  # exact ties between neighbours
+    parts = [
+        rng.standard_normal(20000) * 0.1,
+        rng.standard_normal(20000) * 60.0,
+        rng.uniform(-2.0 ** -6, 2.0 ** -6, 20000),  # subnormal range
+        mids, -mids,
+        np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+        np.nextafter(mids.astype(np.float32), np.float32(-np.inf)),
+        pos, -pos,
+    ]
+    v = np.concatenate([np.asarray(x, dtype=np.float32) for x in parts])
+    v = v[np.abs(v) <= 448.0]
+    assert np.array_equal(oracle.e4m3_encode(v), _torch_e4m3_codes(v))
+
+
+def test_e4m3_encode_ties_saturation_nan_and_sign():
+    e = lambda x: int(oracle.e4m3_encode([x])[0])  # noqa: E731
+    assert e(2.0 ** -10) == 0x00  # halfway between 0 and 2^-9: the even code 0
+    assert e(3 * 2.0 ** -10) == 0x02  # halfway between codes 1 and 2: code 2
+    assert e(1.0625) == 0x38  # halfway between 1 and 1.125: mantissa 0
+    assert e(1.1875) == 0x3A  # halfway between 1.125 and 1.25: mantissa 2
+    assert e(449.0) == 0x7E and e(1e9) == 0x7E and e(float("inf")) == 0x7E
+    assert e(-1e9) == 0xFE and e(float("-inf")) == 0xFE
+    assert e(float("nan")) in (0x7F, 0xFF)
+    assert e(-0.0) == 0x80 and e(-1e-12) == 0x80 and e(1e-12) == 0x00
+    fin = np.array([c for c in range(256) if c & 0x7F != 0x7F])
+    assert np.array_equal(oracle.e4m3_encode(oracle.e4m3_decode(fin)), fin)
+
+
+def test_fp8_cache_write_places_quantised_rows():
+    # a layer view of a block-major byte allocation, skipped slots, and codes
+    # that must equal torch's e4m3 conversion of x / scale taken in float32
+    rng = np.random.default_rng(6)
+    T, L, R, NB, PG, layers, layer = 40, 16, 8, 6, 8, 3, 1
+    E = L + R
+    kv_c = (rng.standard_normal((T, L)) * 3).astype(np.float32)
+    k_pe = (rng.standard_normal((T, R)) * 3).astype(np.float32)
+    slots = rng.permutation(NB * PG)[:T].astype(np.int64)
+    slots[3] = -1
+    slots[7] = NB * PG
+    scale = np.float32(0.37)
+    buf = rng.integers(0, 256, size=(NB, layers, PG, E)).astype(np.uint8)
+    got = oracle.cache_write_fp8(buf, kv_c, k_pe, slots, scale, layer * PG * E, NB, PG,
+                                 layers * PG * E, E)
+    want = buf.copy()
+    rows = np.concatenate([kv_c, k_pe], axis=1)
+    codes = _torch_e4m3_codes(rows / scale)  # float32 division, as in the oracle
+    for t in range(T):
+        if 0 <= slots[t] < NB * PG:
+            want[slots[t] // PG, layer, slots[t] % PG] = codes[t]
+    assert np.array_equal(got, want)
+
+
+def test_fp8_attend_reduces_to_the_bf16_decode():
+    # descales 1: attention over the decoded cache (torch's decode); descales
+    # a, b: scores see q * a and keys * b, values scale by b, which equals
+    # b * attention with query q * a * b over the unscaled keys
+    rng = np.random.default_rng(7)
+    B, Sq, N, L, R, NB, PG = 2, 2, 4, 16, 8, 8, 16
+    E = L + R
+    q = rng.standard_normal((B, Sq, N, E))
+    codes = _torch_e4m3_codes(rng.standard_normal((NB, PG, E)) * 0.5)
+    bt = np.stack([rng.permutation(NB)[:4] for _ in range(B)]).astype(np.int32)
+    sl = np.array([37, 50], dtype=np.int32)
+    vals = _torch_e4m3_values(codes)
+    o1, l1 = oracle.attend_paged_fp8(q, codes, bt, sl, 0.3, True, L, 1.0, 1.0)
+    o0, l0 = oracle.attend_paged(q, vals, bt, sl, 0.3, True, L)
+    assert np.array_equal(o1, o0) and np.array_equal(l1, l0)
+    a, b = 0.75, 2.5
+    o2, l2 = oracle.attend_paged_fp8(q, codes, bt, sl, 0.3, True, L, a, b)
+    o3, l3 = oracle.attend_paged(q * a * b, vals, bt, sl, 0.3, True, L)
+    np.testing.assert_allclose(o2, b * o3, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l2, l3, rtol=1e-12, atol=1e-12)
