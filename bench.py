@@ -1,6 +1,6 @@
 """Benchmark of one absorbed-MLA decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-v3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-v3] [--no-fp8]
 
 A step is one pass of the whole hot path over one batch of the V2-Lite decode
 workload (16 heads, kv_rank 512 + rope 64, batch 64, seqlens uniform on
@@ -326,6 +326,81 @@ def _v3_line(c, ms):
     }
 
 
+def fp8_secondary(step: Step, dev, steps: int, warmup: int, eager: bool = False):
+    """The V2-Lite decode over an fp8 (e4m3) latent cache: the same sequences,
+    pages and block table, the cache values converted to e4m3, descales 1.
+    Times the attention call (mla_decode_attend_fp8) and a whole fp8 step: q
+    fold, fp8 write of the new rows (mla_concat_and_cache_fp8), attention,
+    W_UV un-projection. Cache copies as for the bf16 step."""
+    c = step.case
+    d = c.dims
+    codes = torch.from_numpy(mi.fp8_codes(c.pool)).to(dev).view(torch.float8_e4m3fn)
+    touched = int(c.seqlens.astype(np.int64).sum()) * d.entry
+    copies = max(2, math.ceil(2 * LLC_BYTES / touched) + 1)
+    caches = [codes] + [codes.clone() for _ in range(copies - 1)]
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    B, N = c.batch, d.n_head
+    q = torch.from_numpy(np.ascontiguousarray(c.q)).to(torch.bfloat16).to(dev)
+    o_lat = torch.empty(B, 1, N, d.kv_rank, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, 1, N, dtype=torch.float32, device=dev)
+    nbytes = mla.mla_decode_workspace_size(B, 1, N, d.kv_rank, c.max_seqlen, c.page,
+                                           torch.float8_e4m3fn)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+    def attend(i):
+        mla.mla_decode_attend_fp8(q, caches[i % copies], step.bt, step.seqlens, c.max_seqlen,
+                                  c.scale, True, one, one, o_lat, lse, workspace=ws)
+
+    def run(i):
+        cache = caches[i % copies]
+        mla.mla_absorb_q(step.q_nope, step.w_uk_t, step.q_pe, step.q[:, 0])
+        mla.mla_concat_and_cache_fp8(step.kv_new, step.pe_new, step.slots, cache, one)
+        mla.mla_decode_attend_fp8(step.q, cache, step.bt, step.seqlens, c.max_seqlen, c.scale,
+                                  True, one, one, step.o_lat, step.lse, workspace=ws)
+        mla.mla_v_up(step.o_lat[:, 0], step.w_uv, step.out)
+
+    for i in range(copies):
+        run(i)
+        attend(i)
+    torch.cuda.synchronize()
+    if eager:
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        res_ms = []
+        for fn in (attend, run):
+            for i in range(warmup):
+                fn(i)
+            t0.record()
+            for i in range(steps):
+                fn(i)
+            t1.record()
+            torch.cuda.synchronize()
+            res_ms.append(t0.elapsed_time(t1) / steps)
+        attn_ms, step_ms = res_ms
+    else:
+        def timed(fn):
+            graphs = capture(fn, copies)
+            whole = capture(lambda _: [fn(k) for k in range(copies)], 1)[0]
+            if warmup:
+                replay_steps(whole, graphs, warmup)
+            return replay_steps(whole, graphs, steps) / steps
+        attn_ms, step_ms = timed(attend), timed(run)
+    rows = B * N
+    a_bytes = touched + rows * (d.entry * 2 + d.kv_rank * 2 + 4)
+    gbs = a_bytes / (attn_ms * 1e-3) / 1e9
+    return {
+        "workload": "V2-Lite decode with an fp8 e4m3 latent cache (576 B rows): batch 64, "
+                    "seqlens U[512,4096], 64-token pages, descales 1",
+        "attention_us": round(attn_ms * 1e3, 2),
+        "attention_gbs": round(gbs, 1),
+        "attention_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "attention_algorithmic_bytes": a_bytes,
+        "step_us": round(step_ms * 1e3, 2),
+        "step_kv_gbs": round(touched / (step_ms * 1e-3) / 1e9, 1),
+        "kv_bytes": touched,
+        "cache_copies": copies,
+    }
+
+
 def rope_secondary(step: Step, dev, steps: int, warmup: int):
     """Interleaved rope at the V2-Lite decode step's shapes: the q fold and the
     cache write with and without the fused rotation (positions seqlen_b - 1),
@@ -391,6 +466,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-v3", action="store_true", help="skip the 128-head secondary line")
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding line")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from the host instead of replaying graphs "
                          "(for counter collection)")
@@ -465,6 +541,9 @@ def main():
     if not args.no_v3:
         line["v3_decode"] = v3_secondary(dev, max(10, args.steps // 2), args.warmup,
                                          eager=args.eager)
+    if not args.no_fp8:
+        line["fp8_cache"] = fp8_secondary(step, dev, max(10, args.steps // 2), args.warmup,
+                                          eager=args.eager)
     if not args.no_rope:
         line["rope"] = rope_secondary(step, dev, max(10, args.steps // 2), args.warmup)
     if not args.no_cpu:

@@ -52,7 +52,8 @@ enum {
   MLA_BF16 = 1,
   MLA_F32 = 2,
   MLA_I32 = 3,
-  MLA_I64 = 4
+  MLA_I64 = 4,
+  MLA_FP8_E4M3 = 5 /* OCP FP8 E4M3 ("e4m3fn") bytes: the fp8 latent cache */
 };
 
 /* status codes */
@@ -71,7 +72,7 @@ enum {
 
 typedef struct mla_tensor {
   void* data;                     /* device address of element [0,...,0] */
-  int32_t dtype;                  /* MLA_BF16 / MLA_F32 / MLA_I32 / MLA_I64 */
+  int32_t dtype;                  /* MLA_BF16 / MLA_F32 / MLA_I32 / MLA_I64 / MLA_FP8_E4M3 */
   int32_t rank;                   /* 1..MLA_MAX_RANK */
   int64_t shape[MLA_MAX_RANK];    /* sizes; entries >= rank are ignored */
   int64_t stride[MLA_MAX_RANK];   /* element strides; stride[rank-1] must be 1 */
@@ -124,6 +125,27 @@ int mla_absorb_q(const mla_tensor* q_nope, const mla_tensor* w_uk_t, const mla_t
 int mla_concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
                          const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
                          mla_stream stream);
+
+/*
+ * mla_concat_and_cache_fp8 -- the latent-cache write into an fp8 cache ([P3]
+ * concat_and_cache_mla with its cache dtype and scale arguments; the dense
+ * fp8 decode tests hold the cache as torch.float8_e4m3fn). As
+ * mla_concat_and_cache, except that every element x of [kv_c | k_pe] is
+ * stored as the OCP E4M3 code of x / *scale: the quotient in float, rounded
+ * to the nearest e4m3 value with ties to the even mantissa; magnitudes above
+ * 448 (infinities included) saturate to +-448, NaN becomes the NaN code with
+ * x's sign, a zero result keeps its sign.
+ *
+ *   kv_c, k_pe     as mla_concat_and_cache (bf16 or f32)
+ *   slot_mapping   as mla_concat_and_cache
+ *   kv_cache       [NB, PG, L + R] MLA_FP8_E4M3, strides any (in bytes, since
+ *                  an element is one byte)
+ *   scale          device pointer to one float, read by the kernel when it
+ *                  runs (so a captured graph follows later values); not NULL
+ */
+int mla_concat_and_cache_fp8(const mla_tensor* kv_c, const mla_tensor* k_pe,
+                             const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
+                             const float* scale, mla_stream stream);
 
 /*
  * Interleaved rotary position embedding (memra-engine 0.124.1
@@ -189,7 +211,8 @@ int mla_absorb_q_and_cache(const mla_tensor* q_nope, const mla_tensor* w_uk_t,
  * arguments, never on the device or on seqlens' contents).
  *
  *   batch B, q_len Sq (query tokens per sequence), n_heads N, kv_rank L,
- *   max_seqlen (>= every seqlens[b]), page PG, dtype of q.
+ *   max_seqlen (>= every seqlens[b]), page PG, dtype of q -- or
+ *   MLA_FP8_E4M3 for mla_decode_attend_fp8 (an fp8 cache plans differently).
  * Writes *bytes; returns MLA_OK or a validation error.
  */
 int mla_decode_workspace_size(int64_t batch, int64_t q_len, int64_t n_heads, int64_t kv_rank,
@@ -259,6 +282,35 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
  * out must keep one token stride: stride[0] == Sq * stride[1], else
  * MLA_ERR_UNSUPPORTED before anything is launched).
  */
+/*
+ * mla_decode_attend_fp8 -- mla_decode_attend over an fp8 latent cache ([P3]
+ * test_flashmla_dense_fp8_decode_unified_slot_view: flash_mla_with_kvcache_fp8
+ * with a bf16 query, a float8_e4m3fn paged cache, descale_q and descale_k).
+ * The query's values are q * descale_q and every cache value is its e4m3
+ * value times descale_k (keys and values alike); then exactly the
+ * mla_decode_attend definition:
+ *   s_j      = softmax_scale * descale_q * descale_k * sum_e q[e] * k8_j[e]
+ *   out[...] = descale_k * sum_j softmax(s)_j * k8_j[0:L]
+ *   q          [B, Sq, N, L + R] MLA_BF16, as mla_decode_attend
+ *   kv_cache   [NB, PG, L + R]  MLA_FP8_E4M3; stride[0] any (block-major views
+ *              allowed); pointer and strides multiples of 8 bytes
+ *   descale_q, descale_k   device pointers to one float each, read by the
+ *              kernel when it runs; not NULL
+ *   out        [B, Sq, N, L] MLA_BF16; lse, block_table, seqlens, workspace as
+ *              mla_decode_attend, with the workspace sized by
+ *              mla_decode_workspace_size(..., MLA_FP8_E4M3, ...)
+ * Supported: L == 512, R == 0 or 64, PG a multiple of 16. Every e4m3 value is
+ * exact in bf16: the widened rows enter the same bf16 MFMA arithmetic as a
+ * bf16 cache, and the same determinism holds (bit-identical outputs for a
+ * block-major view and a contiguous copy).
+ */
+int mla_decode_attend_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
+                          const mla_tensor* block_table, const mla_tensor* seqlens,
+                          int64_t max_seqlen, float softmax_scale, int32_t causal,
+                          const float* descale_q, const float* descale_k, const mla_tensor* out,
+                          const mla_tensor* lse, void* workspace, size_t workspace_bytes,
+                          mla_stream stream);
+
 int mla_decode_attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,
                            const mla_tensor* block_table, const mla_tensor* seqlens,
                            int64_t max_seqlen, float softmax_scale, int32_t causal,

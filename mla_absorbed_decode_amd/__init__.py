@@ -57,9 +57,10 @@ lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 _HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                        "mla.h")
 
-MLA_BF16, MLA_F32, MLA_I32, MLA_I64 = 1, 2, 3, 4
+MLA_BF16, MLA_F32, MLA_I32, MLA_I64, MLA_FP8_E4M3 = 1, 2, 3, 4, 5
+# an fp8 cache is torch.float8_e4m3fn (as the pages hold it) or its uint8 bytes
 _DTYPES = {torch.bfloat16: MLA_BF16, torch.float32: MLA_F32, torch.int32: MLA_I32,
-           torch.int64: MLA_I64}
+           torch.int64: MLA_I64, torch.float8_e4m3fn: MLA_FP8_E4M3, torch.uint8: MLA_FP8_E4M3}
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_DTYPE", -3: "MLA_ERR_SHAPE",
           -4: "MLA_ERR_STRIDE", -5: "MLA_ERR_UNSUPPORTED", -6: "MLA_ERR_WORKSPACE",
           -7: "MLA_ERR_HIP"}
@@ -108,7 +109,9 @@ def load() -> ctypes.CDLL:
         lib.mla_concat_and_cache_rope.argtypes = [P, P, P, P, dbl, P, vp]
         lib.mla_absorb_q_and_cache.argtypes = [P, P, P, P, P, P, P, P, P, dbl, vp]
         lib.mla_decode_attend_v_up.argtypes = [P, P, P, P, i64, f32, i32, P, P, P, P, vp, sz, vp]
-        for fn in ("mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
+        lib.mla_concat_and_cache_fp8.argtypes = [P, P, P, P, vp, vp]
+        lib.mla_decode_attend_fp8.argtypes = [P, P, P, P, i64, f32, i32, vp, vp, P, P, vp, sz, vp]
+        for fn in ("mla_concat_and_cache_fp8", "mla_decode_attend_fp8","mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
                    "mla_decode_attend", "mla_v_up", "mla_rope_interleaved", "mla_absorb_q_rope",
                    "mla_concat_and_cache_rope", "mla_absorb_q_and_cache",
                    "mla_decode_attend_v_up"):
@@ -230,6 +233,25 @@ def mla_absorb_q_and_cache(q_nope, w_uk_t, q_pe, q_out, kv_c, k_pe, slot_mapping
     return q_out
 
 
+def mla_concat_and_cache_fp8(kv_c, k_pe, slot_mapping, kv_cache, scale):
+    """kv_cache[slot // PG, slot % PG, :] = e4m3([kv_c[t] | k_pe[t]] / scale) for valid
+    slots; kv_cache is float8_e4m3fn (or uint8), scale a one-element float32 device
+    tensor read when the kernel runs."""
+    _device_check(kv_c, k_pe, slot_mapping, kv_cache, scale)
+    _scalar_check(scale, "scale")
+    lib = load()
+    _check(lib.mla_concat_and_cache_fp8(_ref(desc(kv_c)), _ref(desc(k_pe)),
+                                        _ref(desc(slot_mapping)), _ref(desc(kv_cache)),
+                                        scale.data_ptr(), _stream(kv_cache)),
+           "mla_concat_and_cache_fp8")
+    return kv_cache
+
+
+def _scalar_check(t, what):
+    if t is None or t.dtype != torch.float32 or t.numel() < 1:
+        raise ValueError(f"{what} must be a float32 device tensor holding one value")
+
+
 def mla_decode_workspace_size(batch, q_len, n_heads, kv_rank, max_seqlen, page, dtype) -> int:
     out = ctypes.c_size_t(0)
     _check(load().mla_decode_workspace_size(int(batch), int(q_len), int(n_heads), int(kv_rank),
@@ -254,6 +276,28 @@ def mla_decode_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_sca
                                  int(bool(causal)), _ref(desc(out)), _ref(desc(lse)),
                                  workspace.data_ptr(), workspace.numel(), _stream(out)),
            "mla_decode_attend")
+    return out
+
+
+def mla_decode_attend_fp8(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal,
+                          descale_q, descale_k, out, lse=None, workspace=None):
+    """mla_decode_attend over an fp8 (float8_e4m3fn / uint8) cache: the scores take
+    q * descale_q and keys * descale_k, the output values * descale_k (descales: one-
+    element float32 device tensors read when the kernel runs)."""
+    _device_check(q, kv_cache, block_table, seqlens, descale_q, descale_k, out, lse, workspace)
+    _scalar_check(descale_q, "descale_q")
+    _scalar_check(descale_k, "descale_k")
+    lib = load()
+    if workspace is None:
+        nbytes = mla_decode_workspace_size(q.shape[0], q.shape[1], q.shape[2], out.shape[3],
+                                           max_seqlen, kv_cache.shape[1], torch.float8_e4m3fn)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.mla_decode_attend_fp8(_ref(desc(q)), _ref(desc(kv_cache)), _ref(desc(block_table)),
+                                     _ref(desc(seqlens)), int(max_seqlen), float(softmax_scale),
+                                     int(bool(causal)), descale_q.data_ptr(), descale_k.data_ptr(),
+                                     _ref(desc(out)), _ref(desc(lse)), workspace.data_ptr(),
+                                     workspace.numel(), _stream(out)),
+           "mla_decode_attend_fp8")
     return out
 
 

@@ -349,13 +349,21 @@ __device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk) 
 // R: rope width; WR x WC compute waves split the unit's rows and the 512
 // output columns; RT row tiles of 16 per wave; TT-token tiles, NSLOT deep;
 // F32 values; XS: the waves sharing rows split the score contraction; NP:
-// dedicated loader waves (0: the compute waves load).
-template <int R_, int WR_, int WC_, int RT_, int TT_, int NSLOT_, bool F32_, bool XS_, int NP_>
+// dedicated loader waves (0: the compute waves load); KV8: an fp8 (e4m3) cache
+// whose loader waves widen each row to bf16 on its way into LDS, so the LDS
+// tile and the compute are the bf16 ones. KV8 reads every stream item (key
+// tile or query tile) global->LDS into one of three staging slots, three
+// items ahead; at its step each loader lane widens (or, for query rows,
+// copies) the bytes it read itself into the NSLOT-deep bf16 ring.
+template <int R_, int WR_, int WC_, int RT_, int TT_, int NSLOT_, bool F32_, bool XS_, int NP_,
+          bool KV8_ = false>
 struct Cfg {
   static constexpr int R = R_, WR = WR_, WC = WC_, RT = RT_, TT = TT_, NSLOT = NSLOT_;
   static constexpr bool F32 = F32_, XS = XS_ && WC_ > 1;
   static constexpr int NP = NP_;
-  static constexpr int ES = F32 ? 4 : 2;           // element bytes
+  static constexpr bool KV8 = KV8_;
+  static constexpr int ES = F32 ? 4 : 2;           // element bytes (queries, LDS tile)
+  static constexpr int GES = KV8 ? 1 : ES;         // cache element bytes
   static constexpr int E = kKvRank + R;            // latent row width
   static constexpr int PITCH = E * ES;             // bytes per staged row
   static constexpr int CH = PITCH / 16;            // 16-byte chunks per row
@@ -377,12 +385,18 @@ struct Cfg {
   static constexpr int KW = XS ? (KSTEPS + WC - 1) / WC : KSTEPS;
   static constexpr int XCHG_BYTES = XS ? NW * SUB * RT * 64 * 16 : 0;
   static constexpr int RING_BYTES = NSLOT * TILE_BYTES;
-  static constexpr int SMEM_BYTES = RING_BYTES + XCHG_BYTES;
+  // KV8 staging: a key tile as e4m3 bytes (TT rows of E) or a query tile as
+  // bf16 (RTILE rows of 2E), P8 / QI 1 KB reads, L8 of them per loader wave
+  static constexpr int P8 = KV8 ? TT * E / 1024 : 0;
+  static constexpr int STAGE_SLOT = KV8 ? (TT * E > RTILE * E * 2 ? TT * E : RTILE * E * 2) : 0;
+  static constexpr int STAGE_BYTES = KV8 ? 3 * STAGE_SLOT : 0;
+  static constexpr int SMEM_BYTES = RING_BYTES + XCHG_BYTES + STAGE_BYTES;
   // With loader waves the query rows of every segment but the first travel
   // through the ring as a tile of their own ahead of its key tiles (QI 1 KB
   // reads); the first segment's are read straight into registers.
   static constexpr bool QT = NP > 0;
   static constexpr int QI = RTILE * CH / 64;
+  static constexpr int L8 = KV8 ? ((P8 > QI ? P8 : QI) + NP - 1) / (NP > 0 ? NP : 1) : 0;
   // operand-read batches (rows not shared): K reads per batch kept at about 6
   static constexpr int KB = F32 ? (KSTEPS % 6 == 0 ? 6 : 4) : (SUB == 1 ? (KSTEPS % 6 == 0 ? 6 : 4)
                                                 : (KSTEPS % 3 == 0 ? 3 : 4));
@@ -405,6 +419,9 @@ struct Cfg {
   static_assert(NSLOT >= 2 && NSLOT <= 4, "ring depth");
   static_assert(KSTEPS % KB == 0 && DW % PB == 0, "batching");
   static_assert(SMEM_BYTES + kStaticLds <= 160 * 1024, "LDS budget");
+  static_assert(!KV8 || (!F32 && NP > 0 && TT * E % 1024 == 0 && L8 * NP >= P8 && L8 * NP >= QI &&
+                         P8 <= 64 && QI <= 64),
+                "fp8: bf16 compute, loader waves, whole 1 KB staging reads");
 };
 
 // Everything a wave carries through one segment.
@@ -810,7 +827,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
   const int wrow0 = wr * C::ROWS_W;
   const int rows_seq = p.q_len * p.n_heads;
   const char* kvbase = (const char*)p.kv;
-  const int64_t pitch_g = p.kv_s1 * C::ES;
+  const int64_t pitch_g = p.kv_s1 * C::GES;
 
   const SegHdr h = read_hdr(tab);
   const int nsteps = h.nsteps;
@@ -879,7 +896,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     // each 16-token half of the tile lies in one page (page is a multiple of 16)
     const int pg0 = page_of(p, j0);
     const int blk0 = block_of(pg0);
-    t.base0 = kvbase + (int64_t)blk0 * p.kv_s0 * C::ES + (int64_t)(j0 - pg0 * p.page) * pitch_g;
+    t.base0 = kvbase + (int64_t)blk0 * p.kv_s0 * C::GES + (int64_t)(j0 - pg0 * p.page) * pitch_g;
     t.fast = fast_ok;  // the whole tile lies in one page
     t.base1 = t.base0 + 16 * pitch_g;
     if constexpr (C::TT == 32) {
@@ -887,7 +904,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
       if (!t.fast && j1 < ls.t_hi && page_of(p, j1) != pg0) {
         const int pg1 = page_of(p, j1);
         const int blk1 = block_of(pg1);
-        t.base1 = kvbase + (int64_t)blk1 * p.kv_s0 * C::ES + (int64_t)(j1 - pg1 * p.page) * pitch_g;
+        t.base1 = kvbase + (int64_t)blk1 * p.kv_s0 * C::GES + (int64_t)(j1 - pg1 * p.page) * pitch_g;
       }
     }
     return t;
@@ -949,6 +966,98 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
       }
     }
   };
+  // ---- fp8 cache (KV8): stream item k is read into staging slot k % 3 at
+  // step k - 3 and landed in ring slot k % NSLOT at step k, by the lanes that
+  // read it (so each wave's own vmcnt wait covers the bytes it lands).
+  MLA_LDS char* stage = ring + C::RING_BYTES + C::XCHG_BYTES;
+  auto kv8_issue = [&](const NextTile& t, int k) {
+    MLA_LDS char* stg = stage + (k % 3) * C::STAGE_SLOT;
+    if (t.query) {
+      // query rows in the bf16 query-tile layout (as issue_part); reads past
+      // QI repeat one, so every loader wave sends L8 reads per item
+#pragma unroll
+      for (int n = 0; n < C::L8; ++n) {
+        const int qinst = (lwave + n * C::LW) % C::QI;
+        const int idx = qinst * 64 + lane;
+        const int i = idx / C::CH, cpos = idx % C::CH;
+        int r = t.qrow0 + i;
+        r = r < rows_seq ? r : rows_seq - 1;  // rows past the end are zeroed by the compute waves
+        const int qi = p.q_len == 1 ? 0 : fdiv(r, p.div_nh), qh = r - qi * p.n_heads;
+        const char* src = (const char*)p.q +
+                          ((int64_t)t.qb * p.q_s0 + (int64_t)qi * p.q_s1 + (int64_t)qh * p.q_s2) * C::ES +
+                          ((cpos ^ lds_swz(i & 15)) << 4);
+        load_lds_16(src, stg + qinst * 1024);
+      }
+      return;
+    }
+    // key tile as e4m3 bytes: 16-byte piece c of tile row r at r * E + 16 c;
+    // rows past the tile's end repeat its last valid row
+    constexpr int PR = C::E / 16;
+#pragma unroll
+    for (int n = 0; n < C::L8; ++n) {
+      const int d = (lwave + n * C::LW) % (C::P8 > 0 ? C::P8 : 1);
+      const int idx = d * 64 + lane;
+      const int r = idx / PR, c = idx % PR;
+      const int rr = r < t.nvalid ? r : t.nvalid - 1;
+      const char* src =
+          (C::TT == 32 && rr >= 16) ? t.base1 + (rr - 16) * pitch_g : t.base0 + rr * pitch_g;
+      load_lds_16<C::STREAM>(src + c * 16, stg + d * 1024);
+    }
+  };
+  auto kv8_land = [&](int k, bool query) {
+    const MLA_LDS char* stg = stage + (k % 3) * C::STAGE_SLOT + lane * 16;
+    MLA_LDS char* dst = ring + (k % C::NSLOT) * C::TILE_BYTES;
+    if (query) {
+#pragma unroll
+      for (int n = 0; n < C::L8; ++n) {
+        const int qinst = (lwave + n * C::LW) % C::QI;
+        *(MLA_LDS u32x4_t*)(dst + qinst * 1024 + lane * 16) =
+            *(const MLA_LDS u32x4_t*)(stg + qinst * 1024);
+      }
+      return;
+    }
+    // piece c of row r holds bf16 chunks 2c and 2c + 1 of the row; all the
+    // lane's staged pieces are read before any ring write
+    constexpr int PR = C::E / 16;
+    u32x4_t v8[C::L8 > 0 ? C::L8 : 1];
+#pragma unroll
+    for (int n = 0; n < C::L8; ++n) {
+      const int d = (lwave + n * C::LW) % (C::P8 > 0 ? C::P8 : 1);
+      v8[n] = *(const MLA_LDS u32x4_t*)(stg + d * 1024);
+    }
+#pragma unroll
+    for (int n = 0; n < C::L8; ++n) {
+      const int d = (lwave + n * C::LW) % (C::P8 > 0 ? C::P8 : 1);
+      const int idx = d * 64 + lane;
+      const int r = idx / PR, c = idx % PR;
+      const u32x4_t v = v8[n];
+      const int sw = lds_swz(r & 15);
+      MLA_LDS char* row = dst + r * C::PITCH;
+      *(MLA_LDS u32x4_t*)(row + (((2 * c) ^ sw) << 4)) = fp8x8_to_bf16x8(u32x2_t{v[0], v[1]});
+      *(MLA_LDS u32x4_t*)(row + (((2 * c + 1) ^ sw) << 4)) = fp8x8_to_bf16x8(u32x2_t{v[2], v[3]});
+    }
+  };
+  auto kv8_loader = [&]() {
+    uint32_t qmask = 0;  // bit k % 3: staging slot k % 3 holds query rows
+    auto issue = [&](int k) {
+      const NextTile t = prep_next(k);
+      kv8_issue(t, k);
+      const uint32_t bit = 1u << (k % 3);
+      qmask = t.query ? (qmask | bit) : (qmask & ~bit);
+    };
+    for (int k = 0; k < 3 && k < nsteps; ++k) issue(k);
+    for (int k = 0; k < nsteps; ++k) {
+      // item k's reads are older than those of the (at most two) items after it
+      const int ahead = nsteps - 1 - k;
+      if (ahead <= 0) wait_vmcnt<0>();
+      else if (ahead == 1) wait_vmcnt<C::L8>();
+      else wait_vmcnt<2 * C::L8>();
+      kv8_land(k, (qmask >> (k % 3)) & 1u);
+      __syncthreads();
+      if (k + 3 < nsteps) issue(k + 3);
+    }
+  };
+
   // wait until this loader wave's reads of tile k have landed
   auto wait_tile = [&](int k) {
     int ahead = nsteps - 1 - k;
@@ -959,6 +1068,12 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
   };
 
   // ---- compute walker state
+  // fp8: the scores take q * descale_q and keys * descale_k, the values * descale_k
+  float scale_log2 = p.scale_log2, vscale = 1.f;
+  if constexpr (C::KV8) {
+    scale_log2 = p.scale_log2 * (*p.descale_q * *p.descale_k);
+    vscale = *p.descale_k;
+  }
   using QV = typename std::conditional<C::F32, f32x4_t, i16x8_t>::type;
   // this wave's k-steps of the query rows: kg = wc + WC*kk (all of them when WC == 1)
   QV qreg[C::RT][C::KW];
@@ -1030,7 +1145,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
 #pragma unroll
     for (int rt = 0; rt < C::RT; ++rt) {
       const float lt = wave_sum16(st.l[rt]);
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float inv = lt > 0.f ? vscale / lt : 0.f;
       const float lse2 = lt > 0.f ? st.m[rt] + fast_log2(lt) : kNegInf;
       store_row<C>(p, cs.b, unit_row0, wrow0 + 16 * rt + li, cs.slot, st.o[rt], inv, lse2, dc0,
                    wc == 0);
@@ -1041,7 +1156,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     begin_state();
     load_q();  // ahead of the first tiles' reads
   }
-  if (loader) {
+  if (loader && !C::KV8) {
 #pragma unroll
     for (int k = 0; k < C::NSLOT - 1; ++k)
       if (k < nsteps) {
@@ -1065,7 +1180,9 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
   }
   if constexpr (C::NP > 0) {
     // ---- separate roles: each runs its own loop (one barrier per stream item)
-    if (loader) {
+    if (loader && C::KV8) {
+      kv8_loader();
+    } else if (loader) {
       for (int k = 0; k < nsteps; ++k) {
         wait_tile(k);
         __syncthreads();
@@ -1085,7 +1202,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
         q_tile = false;
         continue;
       }
-      tile_compute<C>(slot, xchg, cs.t_lo + ck * C::TT, qreg, st, p.scale_log2, wr, wc, dc0,
+      tile_compute<C>(slot, xchg, cs.t_lo + ck * C::TT, qreg, st, scale_log2, wr, wc, dc0,
                       [](int) {});
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
@@ -1112,7 +1229,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
       __syncthreads();
       const NextTile nt = k + C::NSLOT - 1 < nsteps ? prep_next(k + C::NSLOT - 1) : NextTile{};
       tile_compute<C>(ring + (k % C::NSLOT) * C::TILE_BYTES, xchg, cs.t_lo + ck * C::TT, qreg, st,
-                      p.scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); });
+                      scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); });
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
         cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
@@ -1367,10 +1484,13 @@ using Rows64  = Cfg<64, 4, 1, 1, 32, 4, false, false, 0>;  // many rows: rows sp
 using Rows0   = Cfg<0,  4, 1, 1, 32, 4, false, false, 0>;
 using ColsF64 = Cfg<64, 1, 4, 1, 16, 4, true,  true,  0>;  // f32
 using ColsF0  = Cfg<0,  1, 4, 1, 16, 4, true,  true,  0>;
+using Cols64F8 = Cfg<64, 1, 4, 1, 32, 2, false, false, 4, true>;  // fp8 cache, any row count
+using Cols0F8  = Cfg<0,  1, 4, 1, 32, 2, false, false, 4, true>;
 
 constexpr int kColsEntryCost = 3;  // work blocks (measured: 3-4 best on V2-Lite)
 
-enum Variant { kCols64 = 0, kCols0, kMixed64, kMixed0, kRows64, kRows0, kColsF64, kColsF0 };
+enum Variant { kCols64 = 0, kCols0, kMixed64, kMixed0, kRows64, kRows0, kColsF64, kColsF0,
+               kCols64F8, kCols0F8 };
 
 template <class C>
 hipError_t launch_partial(const DecodePlan& plan, const DecodeParams& p, hipStream_t s) {
@@ -1436,10 +1556,14 @@ hipError_t launch_decode_vup(const DecodePlan& plan, DecodeParams p, const VupPa
 }
 
 int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int64_t max_seqlen,
-                int is_f32, DecodePlan* plan) {
+                int is_f32, DecodePlan* plan, int kv8) {
   const int64_t rows = q_len * n_heads;
   int variant, rtile;
-  if (is_f32) {
+  if (kv8) {
+    if (is_f32) return -1;
+    variant = rope ? kCols64F8 : kCols0F8;
+    rtile = Cols64F8::RTILE;
+  } else if (is_f32) {
     variant = rope ? kColsF64 : kColsF0;
     rtile = ColsF64::RTILE;
   } else if (rows <= 16) {
@@ -1462,7 +1586,8 @@ int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int
   // plan granularity: the variant's tile
   plan->wb = is_f32 ? ColsF64::TT : Cols64::TT;
   // entering a unit costs the few-head layout a query tile and a partial tile
-  plan->alpha = (variant == kCols64 || variant == kCols0) ? kColsEntryCost : 0;
+  plan->alpha = (variant == kCols64 || variant == kCols0 || variant == kCols64F8 ||
+                  variant == kCols0F8) ? kColsEntryCost : 0;
   const int64_t wb_bound = batch * row_tiles * ((max_seqlen + plan->wb - 1) / plan->wb);
   if (units < kSplitUnits && wb_bound > units) {
     plan->split = 1;
@@ -1494,6 +1619,8 @@ hipError_t launch_decode(const DecodePlan& plan, DecodeParams p, int64_t rope, i
     case kRows0: return launch_variant<Rows0>(plan, p, s);
     case kColsF64: return launch_variant<ColsF64>(plan, p, s);
     case kColsF0: return launch_variant<ColsF0>(plan, p, s);
+    case kCols64F8: return launch_variant<Cols64F8>(plan, p, s);
+    case kCols0F8: return launch_variant<Cols0F8>(plan, p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -22,6 +22,7 @@ int esize_of(int32_t dt) {
     case MLA_F32: return 4;
     case MLA_I32: return 4;
     case MLA_I64: return 8;
+    case MLA_FP8_E4M3: return 1;
   }
   return 0;
 }
@@ -48,14 +49,15 @@ int check_desc(const mla_tensor* t, int rank) {
   return MLA_OK;
 }
 
-// every row start (all leading strides and the pointer) 16-byte aligned
-bool rows_aligned16(const mla_tensor* t) {
+// every row start (all leading strides and the pointer) n-byte aligned
+bool rows_aligned(const mla_tensor* t, int64_t n) {
   const int64_t es = esize_of(t->dtype);
-  if ((uintptr_t)t->data % 16) return false;
+  if ((uintptr_t)t->data % n) return false;
   for (int i = 0; i + 1 < t->rank; ++i)
-    if ((t->stride[i] * es) % 16) return false;
+    if ((t->stride[i] * es) % n) return false;
   return true;
 }
+bool rows_aligned16(const mla_tensor* t) { return rows_aligned(t, 16); }
 
 // rotary positions [T] int32 contiguous, base finite and > 0
 int check_rope(const mla_tensor* positions, int64_t T, double base, mla::RopeSpec* spec) {
@@ -187,14 +189,16 @@ int mla_v_up(const mla_tensor* o_lat, const mla_tensor* w_uv, const mla_tensor* 
 // Validate a cache write and fill its launch parameters (nothing is launched).
 static int build_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
                        const mla_tensor* slot_mapping, const mla_tensor* positions, double base,
-                       const mla_tensor* kv_cache, mla::CacheWriteParams* out) {
+                       const mla_tensor* kv_cache, mla::CacheWriteParams* out,
+                       const float* fp8_scale = nullptr) {
   int rc;
   if ((rc = check_desc(kv_c, 2)) || (rc = check_desc(slot_mapping, 1)) ||
       (rc = check_desc(kv_cache, 3)))
     return rc;
   if (k_pe && (rc = check_desc(k_pe, 2))) return rc;
   const int32_t dt = kv_c->dtype;
-  if (!is_value_dtype(dt) || kv_cache->dtype != dt || (k_pe && k_pe->dtype != dt))
+  if (!is_value_dtype(dt) || kv_cache->dtype != (fp8_scale ? MLA_FP8_E4M3 : dt) ||
+      (k_pe && k_pe->dtype != dt))
     return MLA_ERR_DTYPE;
   if (slot_mapping->dtype != MLA_I64 && slot_mapping->dtype != MLA_I32) return MLA_ERR_DTYPE;
   const int64_t T = kv_c->shape[0], L = kv_c->shape[1];
@@ -218,6 +222,12 @@ static int build_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
   p.T = T; p.L = L; p.R = R; p.esize = es;
   p.vec16 = (L * es) % 16 == 0 && (R * es) % 16 == 0 && rows_aligned16(kv_c) &&
             (!k_pe || rows_aligned16(k_pe)) && rows_aligned16(kv_cache);
+  if (fp8_scale) {
+    // 8-element items: 16-byte aligned input rows, 8-byte aligned cache rows
+    p.fp8_scale = fp8_scale;
+    p.vec16 = L % 8 == 0 && R % 8 == 0 && rows_aligned16(kv_c) && (!k_pe || rows_aligned16(k_pe)) &&
+              rows_aligned(kv_cache, 8);
+  }
   *out = p;
   return MLA_OK;
 }
@@ -236,6 +246,17 @@ int mla_concat_and_cache(const mla_tensor* kv_c, const mla_tensor* k_pe,
                          const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
                          mla_stream stream) {
   return concat_and_cache(kv_c, k_pe, slot_mapping, nullptr, 0.0, kv_cache, stream);
+}
+
+int mla_concat_and_cache_fp8(const mla_tensor* kv_c, const mla_tensor* k_pe,
+                             const mla_tensor* slot_mapping, const mla_tensor* kv_cache,
+                             const float* scale, mla_stream stream) {
+  if (!scale) return MLA_ERR_NULL;
+  mla::CacheWriteParams p;
+  const int rc = build_cache(kv_c, k_pe, slot_mapping, nullptr, 0.0, kv_cache, &p, scale);
+  if (rc) return rc;
+  if (p.T == 0 || p.num_blocks == 0 || p.page == 0) return MLA_OK;
+  return launched(mla::launch_cache_write(p, (hipStream_t)stream));
 }
 
 int mla_concat_and_cache_rope(const mla_tensor* kv_c, const mla_tensor* k_pe,
@@ -287,12 +308,13 @@ int mla_decode_workspace_size(int64_t batch, int64_t q_len, int64_t n_heads, int
                               int64_t max_seqlen, int64_t page, int32_t dtype, size_t* bytes) {
   if (!bytes) return MLA_ERR_NULL;
   if (batch < 0 || q_len < 0 || n_heads < 0 || max_seqlen < 0 || page <= 0) return MLA_ERR_SHAPE;
-  if (!is_value_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (!is_value_dtype(dtype) && dtype != MLA_FP8_E4M3) return MLA_ERR_DTYPE;
   if (kv_rank != mla::kKvRank || page % 16) return MLA_ERR_UNSUPPORTED;
   *bytes = 0;
   if (batch == 0 || q_len == 0 || n_heads == 0) return MLA_OK;
   mla::DecodePlan plan;
-  if (mla::plan_decode(batch, q_len, n_heads, 64, max_seqlen, dtype == MLA_F32, &plan))
+  if (mla::plan_decode(batch, q_len, n_heads, 64, max_seqlen, dtype == MLA_F32, &plan,
+                       dtype == MLA_FP8_E4M3))
     return MLA_ERR_UNSUPPORTED;
   *bytes = plan.workspace_bytes;
   return MLA_OK;
@@ -305,7 +327,8 @@ static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
                         int64_t max_seqlen, float softmax_scale, int32_t causal,
                         const mla_tensor* out, const mla_tensor* lse, void* workspace,
                         size_t workspace_bytes, mla::DecodePlan* plan_out,
-                        mla::DecodeParams* params_out, int* empty) {
+                        mla::DecodeParams* params_out, int* empty,
+                        const float* descale_q = nullptr, const float* descale_k = nullptr) {
   int rc;
   *empty = 0;
   if ((rc = check_desc(q, 4)) || (rc = check_desc(kv_cache, 3)) ||
@@ -314,7 +337,10 @@ static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
     return rc;
   if (lse && (rc = check_desc(lse, 3))) return rc;
   const int32_t dt = q->dtype;
-  if (!is_value_dtype(dt) || kv_cache->dtype != dt || out->dtype != dt) return MLA_ERR_DTYPE;
+  const bool kv8 = descale_q != nullptr;  // fp8 cache, bf16 queries and output
+  if (!is_value_dtype(dt) || out->dtype != dt) return MLA_ERR_DTYPE;
+  if (kv8 ? (kv_cache->dtype != MLA_FP8_E4M3 || dt != MLA_BF16) : kv_cache->dtype != dt)
+    return MLA_ERR_DTYPE;
   if (block_table->dtype != MLA_I32 || seqlens->dtype != MLA_I32) return MLA_ERR_DTYPE;
   if (lse && lse->dtype != MLA_F32) return MLA_ERR_DTYPE;
   const int64_t B = q->shape[0], Sq = q->shape[1], N = q->shape[2], E = q->shape[3];
@@ -328,7 +354,7 @@ static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   const int64_t PG = kv_cache->shape[1], NB = kv_cache->shape[0], MB = block_table->shape[1];
   if (L != mla::kKvRank || (R != 0 && R != 64)) return MLA_ERR_UNSUPPORTED;
   if (PG <= 0 || PG % 16) return MLA_ERR_UNSUPPORTED;
-  if (!rows_aligned16(q) || !rows_aligned16(kv_cache) || !rows_aligned16(out))
+  if (!rows_aligned16(q) || !rows_aligned(kv_cache, kv8 ? 8 : 16) || !rows_aligned16(out))
     return MLA_ERR_UNSUPPORTED;
   if (max_seqlen > INT32_MAX || B > INT32_MAX || Sq * N > INT32_MAX || PG > INT32_MAX ||
       MB > INT32_MAX)
@@ -338,7 +364,8 @@ static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
     return MLA_OK;
   }
   mla::DecodePlan plan;
-  if (mla::plan_decode(B, Sq, N, R, max_seqlen, dt == MLA_F32, &plan)) return MLA_ERR_UNSUPPORTED;
+  if (mla::plan_decode(B, Sq, N, R, max_seqlen, dt == MLA_F32, &plan, kv8))
+    return MLA_ERR_UNSUPPORTED;
   if (plan.workspace_bytes > 0) {
     if (!workspace) return MLA_ERR_WORKSPACE;
     if (workspace_bytes < plan.workspace_bytes) return MLA_ERR_WORKSPACE;
@@ -383,6 +410,8 @@ static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   p.num_units = plan.num_units;
   p.split = plan.split;
   p.grid = plan.grid;
+  p.descale_q = descale_q;
+  p.descale_k = descale_k;
   *plan_out = plan;
   *params_out = p;
   return MLA_OK;
@@ -401,6 +430,24 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   if (rc || empty) return rc;
   const int64_t R = q->shape[3] - out->shape[3];
   return launched(mla::launch_decode(plan, p, R, q->dtype == MLA_F32, (hipStream_t)stream));
+}
+
+int mla_decode_attend_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
+                          const mla_tensor* block_table, const mla_tensor* seqlens,
+                          int64_t max_seqlen, float softmax_scale, int32_t causal,
+                          const float* descale_q, const float* descale_k, const mla_tensor* out,
+                          const mla_tensor* lse, void* workspace, size_t workspace_bytes,
+                          mla_stream stream) {
+  if (!descale_q || !descale_k) return MLA_ERR_NULL;
+  mla::DecodePlan plan;
+  mla::DecodeParams p;
+  int empty;
+  const int rc = build_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal,
+                              out, lse, workspace, workspace_bytes, &plan, &p, &empty, descale_q,
+                              descale_k);
+  if (rc || empty) return rc;
+  const int64_t R = q->shape[3] - out->shape[3];
+  return launched(mla::launch_decode(plan, p, R, 0, (hipStream_t)stream));
 }
 
 int mla_decode_attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,

@@ -32,6 +32,41 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
 }
 
+// ----------------------------------------------------------------- fp8
+// OCP FP8 E4M3 ("e4m3fn": bias 7, subnormals m * 2^-9, S.1111.111 NaN, no
+// infinities, largest magnitude 448), the format of gfx950's fp8 conversions.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Eight e4m3 values (bytes 0..7 of v) as eight bf16 values: every e4m3 value
+// is exact in bf16, so the widening is exact (NaN stays NaN).
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t v) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[0], false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[0], true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[1], false);
+  const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[1], true);
+  return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
+                 pack_bf16x2(d[0], d[1])};
+}
+
+// Four floats to e4m3 codes (byte i of the result from x[i]): nearest value,
+// ties to the even mantissa (the hardware conversion), magnitudes above 448
+// saturate (the conversion alone would give NaN), NaN gives S.1111.111 with
+// the input's sign.
+__device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, float x3) {
+  auto sat = [](float v) { return __builtin_isnan(v) ? 0.f : fminf(fmaxf(v, -448.f), 448.f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(x0), sat(x1), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(x2), sat(x3), w, true);
+  uint32_t r = (uint32_t)w;
+  const float xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (__builtin_isnan(xs[i])) {
+      const uint32_t code = (__builtin_bit_cast(uint32_t, xs[i]) >> 31) ? 0xffu : 0x7fu;
+      r = (r & ~(0xffu << (8 * i))) | (code << (8 * i));
+    }
+  return r;
+}
+
 // ---------------------------------------------------------------- MFMA
 // 16x16x32 bf16 -> f32. Lane l holds A[l%16][8*(l/16)+i], B[8*(l/16)+i][l%16]
 // (i = 0..7) and receives D[4*(l/16)+j][l%16] (j = 0..3).

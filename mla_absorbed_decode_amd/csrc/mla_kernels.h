@@ -43,6 +43,10 @@ struct CacheWriteParams {
   int esize;         // 2 (bf16) or 4 (f32)
   int vec16;         // 1 when every row start is 16-byte aligned and L, R are multiples of 16/esize
   RopeSpec rope;     // rotate k_pe by its token's position before writing
+  // fp8 cache (OCP e4m3fn bytes; strides in bytes): each element is stored as
+  // e4m3(x / *fp8_scale); NULL for a bf16 / f32 cache. With it, vec16 means
+  // 8-element items (16-byte aligned input rows, 8-byte aligned cache rows).
+  const float* fp8_scale;
 };
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
 
@@ -107,6 +111,11 @@ struct DecodeParams {
   int grid;
   int wb;                 // plan granularity: tokens per work block (the tile size)
   int alpha;              // plan cost of entering a unit, in work blocks
+  // fp8 cache (OCP e4m3fn bytes, kv strides in bytes): the scores take
+  // q * descale_q and keys * descale_k, the output values * descale_k. NULL
+  // for a bf16 / f32 cache.
+  const float* descale_q;
+  const float* descale_k;
 };
 
 // The W_UV un-projection fused into the split merge: out[b, i, h, 0:V] =
@@ -129,8 +138,9 @@ struct DecodePlan {
   int alpha;
   size_t workspace_bytes;
 };
+// kv8: an fp8 cache (bf16 queries); its layout takes units of 16 rows.
 int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int64_t max_seqlen,
-                int is_f32, DecodePlan* plan);
+                int is_f32, DecodePlan* plan, int kv8 = 0);
 hipError_t launch_decode(const DecodePlan& plan, DecodeParams p, int64_t rope, int is_f32,
                          hipStream_t s);
 // The same with the merge and the W_UV un-projection in one kernel; only for a

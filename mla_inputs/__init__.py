@@ -44,6 +44,16 @@ import torch
 BF16 = "bf16"
 F32 = "f32"
 TORCH_DTYPE = {BF16: torch.bfloat16, F32: torch.float32}
+# fp8 latent cache: OCP e4m3fn codes held as uint8 (the pages' torch.float8_e4m3fn)
+FP8 = "fp8"
+FP8_NAN = 0x7F
+
+
+def fp8_codes(x) -> np.ndarray:
+    """float32 values -> e4m3fn codes through torch's float8_e4m3fn conversion
+    (how the pages build their fp8 caches)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 def stream(seed: int, k: int) -> np.random.Generator:
@@ -111,6 +121,9 @@ class DecodeCase:
     layer: int = 0
     neighbour_fill: float = float("nan")
     extras: dict = field(default_factory=dict)
+    kv_dtype: str = ""  # FP8: pool holds e4m3fn codes (uint8); else the value dtype
+    descale_q: float = 1.0
+    descale_k: float = 1.0
 
     @property
     def num_blocks(self) -> int:
@@ -124,6 +137,10 @@ class DecodeCase:
         """The block-major allocation [NB, n_layers, page, entry] with the
         pool in layer ``layer``."""
         NB, PG, E = self.pool.shape
+        if self.kv_dtype == FP8:
+            u = np.full((NB, self.n_layers, PG, E), FP8_NAN, dtype=np.uint8)
+            u[:, self.layer] = self.pool
+            return u
         u = np.full((NB, self.n_layers, PG, E), self.neighbour_fill, dtype=np.float32)
         u[:, self.layer] = self.pool
         return u
@@ -168,15 +185,24 @@ def fill_pool(seed, k, num_blocks, page, entry, std, dtype, seqlens, block_table
 def decode_case(seed, dims: Dims, dtype, seqlens, q_len=1, page=64, num_blocks=None,
                 std=0.1, scale=None, causal=True, n_layers=1, layer=0,
                 neighbour_fill=float("nan"), permute=True, tail_fill=float("nan"),
-                max_blocks=None, dist="normal") -> DecodeCase:
-    """A generic paged decode / chunked-prefill case."""
+                max_blocks=None, dist="normal", kv_dtype="", descale_q=1.0,
+                descale_k=1.0) -> DecodeCase:
+    """A generic paged decode / chunked-prefill case. With kv_dtype FP8 the
+    pool holds e4m3fn codes of the drawn values (rows no sequence uses hold
+    the NaN code) and the case carries the decode's two descales."""
     seqlens = np.asarray(seqlens, dtype=np.int32)
     need = sum(int(math.ceil(int(s) / page)) for s in seqlens)
     if num_blocks is None:
         num_blocks = max(need, 1)
     bt = paged_layout(seed, 1, seqlens, page, num_blocks, max_blocks=max_blocks, permute=permute)
-    pool = fill_pool(seed, 2, num_blocks, page, dims.entry, std, dtype, seqlens, bt,
-                     tail_fill=tail_fill, dist=dist)
+    if kv_dtype == FP8:
+        vals = fill_pool(seed, 2, num_blocks, page, dims.entry, std, F32, seqlens, bt,
+                         tail_fill=float("nan"), dist=dist)
+        pool = fp8_codes(vals)
+        pool[np.isnan(vals)] = FP8_NAN
+    else:
+        pool = fill_pool(seed, 2, num_blocks, page, dims.entry, std, dtype, seqlens, bt,
+                         tail_fill=tail_fill, dist=dist)
     qshape = (len(seqlens), q_len, dims.n_head, dims.entry)
     q = normal(seed, 3, qshape, std, dtype) if dist == "normal" else uniform(
         seed, 3, qshape, -std, std, dtype)
@@ -185,7 +211,8 @@ def decode_case(seed, dims: Dims, dtype, seqlens, q_len=1, page=64, num_blocks=N
     return DecodeCase(dims=dims, dtype=dtype, batch=len(seqlens), q_len=q_len, page=page,
                       seqlens=seqlens, block_table=bt, pool=pool, q=q, scale=float(scale),
                       causal=causal, n_layers=n_layers, layer=layer,
-                      neighbour_fill=neighbour_fill)
+                      neighbour_fill=neighbour_fill, kv_dtype=kv_dtype,
+                      descale_q=float(descale_q), descale_k=float(descale_k))
 
 
 def mla_weights(seed, dims: Dims, dtype, dist="uniform", std=None):

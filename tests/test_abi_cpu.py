@@ -16,7 +16,7 @@ import mla_absorbed_decode_amd as mla
 from mla_absorbed_decode_amd import MlaTensor
 
 OK, NULL, DTYPE, SHAPE, STRIDE, UNSUP, WS = 0, -1, -2, -3, -4, -5, -6
-BF16, F32, I32, I64 = 1, 2, 3, 4
+BF16, F32, I32, I64, FP8 = 1, 2, 3, 4, 5
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced on error paths
 
 
@@ -50,7 +50,8 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) == {"mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
                           "mla_decode_attend", "mla_v_up", "mla_status_str",
                           "mla_rope_interleaved", "mla_absorb_q_rope", "mla_concat_and_cache_rope",
-                          "mla_absorb_q_and_cache", "mla_decode_attend_v_up"}
+                          "mla_absorb_q_and_cache", "mla_decode_attend_v_up",
+                          "mla_concat_and_cache_fp8", "mla_decode_attend_fp8"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -262,6 +263,50 @@ def test_decode_v_up_validation(lib):
                                       ctypes.c_float(0.04), 1, R(T([N, 512, 128], F32)), R(o2),
                                       R(T([B, 2, N, 128], F32)), None, ctypes.c_void_p(FAKE),
                                       ctypes.c_size_t(1 << 30), None) == UNSUP
+
+
+# ------------------------------------------------------------------- fp8
+
+
+def test_fp8_cache_write_validation(lib):
+    T_, L, R_ = 5, 512, 64
+    kv, kpe, sl = T([T_, L]), T([T_, R_]), T([T_], I64)
+    cache = T([8, 64, L + R_], FP8)
+    f = lambda kv_=kv, kpe_=kpe, c=cache, scale=FAKE: lib.mla_concat_and_cache_fp8(
+        R(kv_), R(kpe_), R(sl), R(c), ctypes.c_void_p(scale), None)
+    assert f(scale=0) == NULL                      # the scale pointer is required
+    assert f(c=T([8, 64, L + R_])) == DTYPE        # the cache must be fp8
+    assert f(kv_=T([T_, L], FP8)) == DTYPE         # the rows are bf16 or f32
+    assert f(kpe_=T([T_, R_], F32)) == DTYPE       # one dtype for both row parts
+    assert f(c=T([8, 64, 512], FP8)) == SHAPE      # entry = L + R
+    # the copy-of-bits write takes no fp8 cache
+    assert lib.mla_concat_and_cache(R(kv), R(kpe), R(sl), R(cache), None) == DTYPE
+    # nothing to write: no launch
+    assert lib.mla_concat_and_cache_fp8(R(T([0, L])), R(T([0, R_])), R(T([0], I64)), R(cache),
+                                        ctypes.c_void_p(FAKE), None) == OK
+
+
+def test_fp8_decode_validation(lib):
+    B, N = 2, 16
+    q, kv, bt, sl = T([B, 1, N, 576]), T([8, 64, 576], FP8), T([B, 4], I32), T([B], I32)
+    out, lse = T([B, 1, N, 512]), T([B, 1, N], F32)
+    rc, need = ws_size(lib, B, 1, N, 512, 128, 64)
+    assert rc == OK
+    need8 = ctypes.c_size_t(0)
+    assert lib.mla_decode_workspace_size(B, 1, N, 512, 128, 64, FP8, ctypes.byref(need8)) == OK
+    f = lambda q_=q, kv_=kv, out_=out, dq=FAKE, dk=FAKE, ws=FAKE: lib.mla_decode_attend_fp8(
+        R(q_), R(kv_), R(bt), R(sl), 128, ctypes.c_float(0.04), 1, ctypes.c_void_p(dq),
+        ctypes.c_void_p(dk), R(out_), R(lse), ctypes.c_void_p(ws), ctypes.c_size_t(need8.value),
+        None)
+    assert f(dq=0) == NULL and f(dk=0) == NULL
+    assert f(kv_=T([8, 64, 576])) == DTYPE                      # the cache must be fp8
+    assert f(q_=T([B, 1, N, 576], F32), out_=T([B, 1, N, 512], F32)) == DTYPE  # bf16 queries
+    assert f(kv_=T([8, 64, 576], FP8, strides=[64 * 580, 580, 1])) == UNSUP  # 8-byte rows
+    assert f(kv_=T([8, 64, 512], FP8)) == SHAPE
+    assert f(ws=0) == WS
+    # the bf16 entry point takes no fp8 cache
+    assert decode(lib, q, kv, bt, sl, out) == DTYPE
+    assert f(kv_=T([8, 64, 584], FP8), q_=T([B, 1, N, 584])) == UNSUP  # R = 72: not 0 or 64
 
 
 # ----------------------------------------------------------- python layer
