@@ -92,6 +92,10 @@ def _load():
             [i64] * 3 + [fp, fp, ip64, ctypes.c_float, u8p] + [i64] * 6
         )
         lib.mla_oracle_cache_write_fp8.restype = c_int
+        lib.mla_oracle_decompress_kv.argtypes = [i64] * 6 + [dp] * 6
+        lib.mla_oracle_decompress_kv.restype = None
+        lib.mla_oracle_mha.argtypes = [i64] * 5 + [dp] * 3 + [ip64, dbl, c_int, dp, dp]
+        lib.mla_oracle_mha.restype = None
         _lib = lib
     return _lib
 
@@ -392,3 +396,58 @@ def attend_paged_fp8(q, pool_codes, block_table, seqlens, scale, causal, L, desc
     q = _f64(q) * float(descale_q)
     pool = e4m3_decode(pool_codes) * float(descale_k)
     return attend_paged(q, pool, block_table, seqlens, scale, causal, L)
+
+
+# ------------------------------------------------------- naive prefill
+# [P2] naive oracle (K and V decompressed per head, then plain attention);
+# [P1] ConcatMlaNopeRope broadcast case (one k_pe row shared by every head).
+
+
+def decompress_kv(c_kv, k_pe, w_uk_t, w_uv):
+    """Per-head keys [T,N,P+R] = [c_kv . W_UK_T[h]^T | k_pe] and values
+    [T,N,V] = c_kv . W_UV[h]. k_pe [T,R] or None (R = 0)."""
+    c_kv, w_uk_t, w_uv = map(_f64, (c_kv, w_uk_t, w_uv))
+    T, L = c_kv.shape
+    N, P, _ = w_uk_t.shape
+    V = w_uv.shape[2]
+    R = 0 if k_pe is None else np.asarray(k_pe).shape[1]
+    kp = _f64(k_pe) if R and T else np.zeros((1,))
+    cp = c_kv if T else np.zeros((1, L))
+    k = np.zeros((max(T, 1), N, P + R))
+    v = np.zeros((max(T, 1), N, V))
+    _load().mla_oracle_decompress_kv(T, N, P, R, V, L, _dp(cp), _dp(kp), _dp(w_uk_t), _dp(w_uv),
+                                     _dp(k), _dp(v))
+    return k[:T], v[:T]
+
+
+def mha(q, k, v, pos, scale, causal):
+    """Multi-head softmax attention of one sequence: q [nq,N,DK], k [T,N,DK],
+    v [T,N,DV], pos [nq] absolute query positions. Returns (out [nq,N,DV],
+    lse [nq,N] natural log)."""
+    q, k, v = map(_f64, (q, k, v))
+    nq, N, DK = q.shape
+    T = k.shape[0]
+    DV = v.shape[2]
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64))
+    kp = k if T else np.zeros((1, N, DK))
+    vp = v if T else np.zeros((1, N, DV))
+    out = np.zeros((nq, N, DV))
+    lse = np.zeros((nq, N))
+    _load().mla_oracle_mha(nq, T, N, DK, DV, _dp(q), _dp(kp), _dp(vp), _i64p(pos), float(scale),
+                           int(bool(causal)), _dp(out), _dp(lse))
+    return out, lse
+
+
+def mha_varlen(q, k, v, cu_q, cu_k, scale, causal):
+    """mha over packed sequences: sequence b owns query rows cu_q[b]:cu_q[b+1]
+    and key rows cu_k[b]:cu_k[b+1]; its queries are the suffix of its keys."""
+    q, k, v = map(_f64, (q, k, v))
+    out = np.zeros(q.shape[:2] + (v.shape[2],))
+    lse = np.zeros(q.shape[:2])
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0:
+            continue
+        pos = np.arange(q1 - q0) + (k1 - k0) - (q1 - q0)
+        out[q0:q1], lse[q0:q1] = mha(q[q0:q1], k[k0:k1], v[k0:k1], pos, scale, causal)
+    return out, lse

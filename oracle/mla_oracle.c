@@ -523,3 +523,83 @@ int mla_oracle_cache_write_fp8(int64_t T, int64_t L, int64_t R, const float* kv_
   }
   return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Naive (decompressed) prefill, first step: per-head keys and values rebuilt
+ * from the latent rows ([P2] the naive oracle `mla_attend_naive`, which
+ * decompresses K and V per head; [P1] ConcatMlaNopeRope, the broadcast case
+ * "broadcasts the single k_pe head across every head": the key of head h is
+ * [k_nope of head h | the token's one k_pe row]).
+ *   k[j, h, 0:P]   = sum_l W_UK_T[h, p, l] * c_kv[j, l]
+ *   k[j, h, P:P+R] = k_pe[j, 0:R]            (the same row for every head)
+ *   v[j, h, :]     = sum_l c_kv[j, l] * W_UV[h, l, :]
+ *   c_kv [t_kv, L]  k_pe [t_kv, R]  w_uk_t [n_head, P, L]  w_uv [n_head, L, V]
+ *   k_out [t_kv, n_head, P + R]     v_out [t_kv, n_head, V]
+ * ------------------------------------------------------------------------- */
+void mla_oracle_decompress_kv(int64_t t_kv, int64_t n_head, int64_t P, int64_t R, int64_t V,
+                              int64_t L, const double* c_kv, const double* k_pe,
+                              const double* w_uk_t, const double* w_uv, double* k_out,
+                              double* v_out) {
+  const int64_t DK = P + R;
+  int64_t jh;
+#pragma omp parallel for schedule(static)
+  for (jh = 0; jh < t_kv * n_head; ++jh) {
+    const int64_t j = jh / n_head, h = jh % n_head;
+    for (int64_t p = 0; p < P; ++p) {
+      double acc = 0.0;
+      for (int64_t l = 0; l < L; ++l) acc += w_uk_t[(h * P + p) * L + l] * c_kv[j * L + l];
+      k_out[jh * DK + p] = acc;
+    }
+    for (int64_t e = 0; e < R; ++e) k_out[jh * DK + P + e] = k_pe[j * R + e];
+    for (int64_t d = 0; d < V; ++d) {
+      double acc = 0.0;
+      for (int64_t l = 0; l < L; ++l) acc += c_kv[j * L + l] * w_uv[(h * L + l) * V + d];
+      v_out[jh * V + d] = acc;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------------
+ * Naive (decompressed) prefill, second step: standard multi-head softmax
+ * attention of one sequence over its own per-head keys and values ([P2] the
+ * naive oracle's attention after decompression; causal queries are a suffix
+ * of the keys as in gate 1's chunked shape).
+ *   s_j        = scale * sum_e q[i, h, e] * k[j, h, e]     over visible j
+ *   out[i,h,:] = sum_j softmax(s)_j * v[j, h, :]
+ *   lse[i,h]   = natural log of sum_j exp(s_j)  (-inf, and out = 0, with no key)
+ *   q [nq, n_head, DK]   k [t_kv, n_head, DK]   v [t_kv, n_head, DV]
+ *   pos [nq] absolute query positions   out [nq, n_head, DV]   lse [nq, n_head]
+ * ------------------------------------------------------------------------- */
+void mla_oracle_mha(int64_t nq, int64_t t_kv, int64_t n_head, int64_t DK, int64_t DV,
+                    const double* q, const double* k, const double* v, const int64_t* pos,
+                    double scale, int causal, double* out, double* lse) {
+  int64_t r;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (r = 0; r < nq * n_head; ++r) {
+    const int64_t i = r / n_head, h = r % n_head;
+    const int64_t nvis = visible_keys(pos[i], t_kv, causal);
+    double* o = out + r * DV;
+    for (int64_t d = 0; d < DV; ++d) o[d] = 0.0;
+    if (nvis <= 0) {
+      lse[r] = -INFINITY;
+      continue;
+    }
+    double* s = (double*)malloc((size_t)nvis * sizeof(double));
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < nvis; ++j) {
+      double acc = 0.0;
+      for (int64_t e = 0; e < DK; ++e) acc += q[r * DK + e] * k[(j * n_head + h) * DK + e];
+      s[j] = scale * acc;
+      if (s[j] > mx) mx = s[j];
+    }
+    double sum = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) sum += exp(s[j] - mx);
+    const double l = mx + log(sum);
+    for (int64_t j = 0; j < nvis; ++j) {
+      const double pj = exp(s[j] - l);
+      for (int64_t d = 0; d < DV; ++d) o[d] += pj * v[(j * n_head + h) * DV + d];
+    }
+    lse[r] = l;
+    free(s);
+  }
+}

@@ -550,3 +550,140 @@ def test_fp8_attend_reduces_to_the_bf16_decode():
     o3, l3 = oracle.attend_paged(q * a * b, vals, bt, sl, 0.3, True, L)
     np.testing.assert_allclose(o2, b * o3, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(l2, l3, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------- naive (decompressed) prefill
+def _rand(rng, *shape):
+    return rng.uniform(-1.0, 1.0, size=shape)
+
+
+def test_decompress_kv_against_einsum_and_broadcast_rope():
+    """k = [c_kv . W_UK_T[h]^T | k_pe], v = c_kv . W_UV[h], by numpy einsum in
+    float64; every head carries the token's one k_pe row ([P1] broadcast
+    concat case)."""
+    rng = np.random.default_rng(11)
+    T, N, P, R, V, L = 7, 3, 5, 4, 6, 9
+    c_kv, k_pe = _rand(rng, T, L), _rand(rng, T, R)
+    w_uk_t, w_uv = _rand(rng, N, P, L), _rand(rng, N, L, V)
+    k, v = oracle.decompress_kv(c_kv, k_pe, w_uk_t, w_uv)
+    np.testing.assert_allclose(k[:, :, :P], np.einsum("tl,hpl->thp", c_kv, w_uk_t), rtol=1e-13,
+                               atol=1e-14)
+    np.testing.assert_allclose(v, np.einsum("tl,hlv->thv", c_kv, w_uv), rtol=1e-13, atol=1e-14)
+    for h in range(N):
+        assert np.array_equal(k[:, h, P:], k_pe)
+
+
+def test_decompress_kv_selection_weights_closed_form():
+    """W_UK_T[h, p, l] = [l == p + h] picks latent column p + h; W_UV[h, l, d]
+    = [l == 2d + h] picks column 2d + h. A transposed weight or a swapped
+    head index picks other columns."""
+    rng = np.random.default_rng(12)
+    T, N, P, V, L = 5, 3, 4, 3, 8
+    c_kv = _rand(rng, T, L)
+    w_uk_t = np.zeros((N, P, L))
+    w_uv = np.zeros((N, L, V))
+    for h in range(N):
+        for p in range(P):
+            w_uk_t[h, p, p + h] = 1.0
+        for d in range(V):
+            w_uv[h, 2 * d + h, d] = 1.0
+    k, v = oracle.decompress_kv(c_kv, None, w_uk_t, w_uv)
+    assert k.shape == (T, N, P)
+    for h in range(N):
+        assert np.array_equal(k[:, h, :], c_kv[:, h:h + P])
+        assert np.array_equal(v[:, h, :], c_kv[:, h:h + 2 * V:2])
+
+
+def _sdpa_heads(q, k, v, pos, scale, causal):
+    """Per-head attention through torch's float64 scaled_dot_product_attention
+    with an explicit suffix-aligned causal mask."""
+    qt = torch.from_numpy(q).permute(1, 0, 2).contiguous()
+    kt = torch.from_numpy(k).permute(1, 0, 2).contiguous()
+    vt = torch.from_numpy(v).permute(1, 0, 2).contiguous()
+    j = torch.arange(k.shape[0]).unsqueeze(0)
+    mask = (j <= torch.as_tensor(pos).unsqueeze(1)) if causal else torch.ones(len(pos), k.shape[0],
+                                                                              dtype=torch.bool)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    return out.permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("nq,T,N,DK,DV,causal", [
+    (6, 6, 3, 12, 5, True), (3, 11, 2, 8, 7, True), (4, 9, 4, 16, 16, False), (1, 13, 2, 6, 3, True),
+])
+def test_mha_vs_sdpa_float64(nq, T, N, DK, DV, causal):
+    rng = np.random.default_rng(nq * 100 + T)
+    q, k, v = _rand(rng, nq, N, DK), _rand(rng, T, N, DK), _rand(rng, T, N, DV)
+    pos = np.arange(nq) + T - nq
+    out, lse = oracle.mha(q, k, v, pos, 0.37, causal)
+    np.testing.assert_allclose(out, _sdpa_heads(q, k, v, pos, 0.37, causal), rtol=1e-11, atol=1e-12)
+    # lse against its definition, row by row with a visible-key count
+    i, h = nq - 1, N - 1
+    nvis = pos[i] + 1 if causal else T
+    s = 0.37 * (k[:nvis, h, :] @ q[i, h, :])
+    assert math.isclose(lse[i, h], math.log(np.exp(s).sum()), rel_tol=1e-12)
+
+
+def test_mha_closed_forms():
+    rng = np.random.default_rng(13)
+    N, DK, DV, T = 2, 8, 4, 6
+    q, k, v = _rand(rng, T, N, DK), _rand(rng, T, N, DK), _rand(rng, T, N, DV)
+    pos = np.arange(T)
+    # query 0 sees only key 0: out = v[0], lse = its scaled score
+    out, lse = oracle.mha(q, k, v, pos, 0.5, True)
+    np.testing.assert_allclose(out[0], v[0], rtol=1e-14)
+    np.testing.assert_allclose(lse[0], 0.5 * np.einsum("hd,hd->h", q[0], k[0]), rtol=1e-13)
+    # values all one: softmax rows sum to one
+    out1, _ = oracle.mha(q, k, np.ones_like(v), pos, 0.5, True)
+    np.testing.assert_allclose(out1, 1.0, rtol=1e-13)
+    # q = 0: uniform weights, out = mean of the visible values, lse = ln n
+    out0, lse0 = oracle.mha(np.zeros_like(q), k, v, pos, 0.5, True)
+    for i in range(T):
+        np.testing.assert_allclose(out0[i], v[:i + 1].mean(axis=0), rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(lse0[i], math.log(i + 1), rtol=1e-13, atol=1e-15)
+    # a query with no visible key (more queries than keys): 0 and -inf
+    outn, lsen = oracle.mha(q[:3], k[:1], v[:1], np.array([-2, -1, 0]), 0.5, True)
+    assert np.all(outn[:2] == 0.0) and np.all(np.isneginf(lsen[:2]))
+    np.testing.assert_allclose(outn[2], v[0], rtol=1e-14)
+
+
+@pytest.mark.parametrize("N,P,R,V,L,nq,T,causal", [
+    (4, 24, 8, 32, 64, 6, 6, True), (3, 12, 4, 20, 48, 3, 11, True), (4, 32, 0, 32, 64, 5, 9, True),
+    (2, 16, 8, 16, 32, 4, 7, False),
+])
+def test_decompressed_prefill_equals_absorbed(N, P, R, V, L, nq, T, causal):
+    """The naive route (decompress, then multi-head attention) and the absorbed
+    route (fold q, attend over latent rows, un-project) compute one result
+    ([P2] gate 1 checks the kernels against both oracle forms); the absorbed
+    route never forms per-head keys or values."""
+    rng = np.random.default_rng(N * 1000 + T)
+    q_nope, c_kv = _rand(rng, nq, N, P), _rand(rng, T, L)
+    q_pe, k_pe = (_rand(rng, nq, N, R), _rand(rng, T, R)) if R else (None, None)
+    w_uk_t, w_uv = _rand(rng, N, P, L) / math.sqrt(L), _rand(rng, N, L, V) / math.sqrt(L)
+    pos = np.arange(nq) + T - nq
+    scale = 1.0 / math.sqrt(P + R)
+    k, v = oracle.decompress_kv(c_kv, k_pe, w_uk_t, w_uv)
+    q = np.concatenate([q_nope, q_pe], axis=2) if R else q_nope
+    out, lse = oracle.mha(q, k, v, pos, scale, causal)
+    want, _, _, want_lse = oracle.absorbed(q_nope, q_pe, c_kv, k_pe, w_uk_t, w_uv, pos, scale,
+                                           causal)
+    np.testing.assert_allclose(out, want, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(lse, want_lse, rtol=1e-12, atol=1e-13)
+
+
+def test_mha_varlen_equals_per_sequence_calls():
+    rng = np.random.default_rng(14)
+    N, DK, DV = 2, 8, 4
+    lens_q, lens_k = [3, 0, 5, 2], [7, 4, 5, 1]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lens_q)]), np.concatenate([[0], np.cumsum(lens_k)])
+    q, k, v = _rand(rng, cu_q[-1], N, DK), _rand(rng, cu_k[-1], N, DK), _rand(rng, cu_k[-1], N, DV)
+    out, lse = oracle.mha_varlen(q, k, v, cu_q, cu_k, 0.3, True)
+    for b in range(4):
+        if lens_q[b] == 0:
+            continue
+        qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        pos = np.arange(lens_q[b]) + lens_k[b] - lens_q[b]
+        np.testing.assert_allclose(out[qs], _sdpa_heads(q[qs], k[ks], v[ks], pos, 0.3, True)
+                                   if min(pos) >= 0 else oracle.mha(q[qs], k[ks], v[ks], pos, 0.3,
+                                                                    True)[0], rtol=1e-11, atol=1e-12)
+    # sequence 3 has 2 queries on 1 key: its first query sees nothing
+    assert np.all(out[cu_q[3]] == 0.0) and np.isneginf(lse[cu_q[3]]).all()
