@@ -333,6 +333,70 @@ int mla_decode_attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,
 int mla_v_up(const mla_tensor* o_lat, const mla_tensor* w_uv, const mla_tensor* out,
              mla_stream stream);
 
+/*
+ * Naive (decompressed) prefill -- for long prompts, per-head keys and values
+ * are rebuilt from the latent rows and attended with standard multi-head
+ * attention, which costs 2 (d_nope + d_rope + d_v) flops per (query, key,
+ * head) against 2 (2 kv_rank + d_rope) for the absorbed form.
+ *
+ * mla_decompress_kv -- the keys and values of every head (memra-engine 0.124.1
+ * "tests/mla_gpu_forward.rs", the naive oracle mla_attend_naive, which
+ * decompresses K and V per head; vllm.cpp "tests/vt/test_ops_mla_absorb.cpp",
+ * "ConcatMlaNopeRope broadcasts the single k_pe head across every head": the
+ * key of head h is [its k_nope | the token's one k_pe row]).
+ *
+ *   k_out[s, h, 0:P]   = sum_l kv_c[s, l] * w_uk_t[h, p, l]
+ *   k_out[s, h, P:P+R] = k_pe[s, :]            (bit copy, the same for every head)
+ *   v_out[s, h, :]     = sum_l kv_c[s, l] * w_uv[h, l, :]
+ *
+ *   kv_c   [S, L]       bf16 or f32, any strides (inner 1)
+ *   k_pe   [S, R]       same dtype, or NULL (R = 0, NoPE)
+ *   w_uk_t [N, P, L]    same dtype (the W_UK_T of mla_absorb_q)
+ *   w_uv   [N, L, V]    same dtype (the W_UV of mla_v_up)
+ *   k_out  [S, N, P+R]  same dtype, any strides (inner 1)
+ *   v_out  [S, N, V]    same dtype, any strides (inner 1)
+ * Products accumulate in f32 and round once (RNE) to the output dtype. S may
+ * be 0. Two launches on `stream` (keys, then values); errors as everywhere:
+ * nothing is launched when a check fails.
+ */
+int mla_decompress_kv(const mla_tensor* kv_c, const mla_tensor* k_pe, const mla_tensor* w_uk_t,
+                      const mla_tensor* w_uv, const mla_tensor* k_out, const mla_tensor* v_out,
+                      mla_stream stream);
+
+/*
+ * mla_prefill_attend -- causal (or full) multi-head attention of packed
+ * sequences over their own per-head keys and values (memra-engine 0.124.1
+ * gate 1, gpu_mla_prefill_parity_vs_cpu_oracle: the naive oracle's attention
+ * after decompression; queries are the suffix of their sequence's keys, as in
+ * the gate's chunked shape).
+ *
+ * Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and key
+ * rows cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1. With lq queries and lk keys,
+ * its query i sits at position lk - lq + i and, when causal, sees keys
+ * 0 .. lk - lq + i; otherwise all lk keys.
+ *   s_j          = softmax_scale * sum_e q[t, h, e] * k[j, h, e]
+ *   out[t, h, :] = sum_j softmax(s)_j * v[j, h, :]
+ *   lse[t, h]    = natural log of sum_j exp(s_j)
+ * A query with no visible key gets out = 0 and lse = -inf.
+ *
+ *   q      [T, N, DK]  MLA_BF16, any strides (inner 1), rows 16-byte aligned
+ *   k      [S, N, DK]  MLA_BF16, as q
+ *   v      [S, N, DV]  MLA_BF16, as q
+ *   cu_seqlens_q, cu_seqlens_k  [B + 1] MLA_I32 on the device, non-decreasing,
+ *          within [0, T] and [0, S] (values outside are clamped to them)
+ *   max_seqlen_q  host bound on every lq; query rows past it are not written
+ *   out    [T, N, DV]  MLA_BF16, rows 8-byte aligned; rows no sequence owns
+ *          are not written
+ *   lse    [T, N]      MLA_F32, or NULL
+ * Supported (DK, DV): (192, 128) (d_nope 128 + d_rope 64, V2-Lite/V3 heads),
+ * (256, 256) (NoPE, d_nope 256), (128, 128), (64, 64); bf16 with f32
+ * accumulation; otherwise MLA_ERR_UNSUPPORTED.
+ */
+int mla_prefill_attend(const mla_tensor* q, const mla_tensor* k, const mla_tensor* v,
+                       const mla_tensor* cu_seqlens_q, const mla_tensor* cu_seqlens_k,
+                       int64_t max_seqlen_q, float softmax_scale, int32_t causal,
+                       const mla_tensor* out, const mla_tensor* lse, mla_stream stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* mla_status_str(int status);
 

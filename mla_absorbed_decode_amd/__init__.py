@@ -111,10 +111,13 @@ def load() -> ctypes.CDLL:
         lib.mla_decode_attend_v_up.argtypes = [P, P, P, P, i64, f32, i32, P, P, P, P, vp, sz, vp]
         lib.mla_concat_and_cache_fp8.argtypes = [P, P, P, P, vp, vp]
         lib.mla_decode_attend_fp8.argtypes = [P, P, P, P, i64, f32, i32, vp, vp, P, P, vp, sz, vp]
-        for fn in ("mla_concat_and_cache_fp8", "mla_decode_attend_fp8","mla_absorb_q", "mla_concat_and_cache", "mla_decode_workspace_size",
+        lib.mla_decompress_kv.argtypes = [P, P, P, P, P, P, vp]
+        lib.mla_prefill_attend.argtypes = [P, P, P, P, P, i64, f32, i32, P, P, vp]
+        for fn in ("mla_concat_and_cache_fp8", "mla_decode_attend_fp8", "mla_absorb_q",
+                   "mla_concat_and_cache", "mla_decode_workspace_size",
                    "mla_decode_attend", "mla_v_up", "mla_rope_interleaved", "mla_absorb_q_rope",
                    "mla_concat_and_cache_rope", "mla_absorb_q_and_cache",
-                   "mla_decode_attend_v_up"):
+                   "mla_decode_attend_v_up", "mla_decompress_kv", "mla_prefill_attend"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_status_str.argtypes = [ctypes.c_int]
         lib.mla_status_str.restype = ctypes.c_char_p
@@ -326,4 +329,29 @@ def mla_v_up(o_lat, w_uv, out):
     lib = load()
     _check(lib.mla_v_up(_ref(desc(o_lat)), _ref(desc(w_uv)), _ref(desc(out)), _stream(out)),
            "mla_v_up")
+    return out
+
+
+def mla_decompress_kv(kv_c, k_pe, w_uk_t, w_uv, k_out, v_out):
+    """k_out[s,h,:P] = kv_c[s] @ w_uk_t[h]^T, k_out[s,h,P:] = k_pe[s] (every head),
+    v_out[s,h,:] = kv_c[s] @ w_uv[h]."""
+    _device_check(kv_c, k_pe, w_uk_t, w_uv, k_out, v_out)
+    lib = load()
+    _check(lib.mla_decompress_kv(_ref(desc(kv_c)), _ref(desc(k_pe)), _ref(desc(w_uk_t)),
+                                 _ref(desc(w_uv)), _ref(desc(k_out)), _ref(desc(v_out)),
+                                 _stream(k_out)), "mla_decompress_kv")
+    return k_out, v_out
+
+
+def mla_prefill_attend(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, softmax_scale, causal,
+                       out, lse=None):
+    """Multi-head attention of packed sequences over per-head k [S,N,DK], v [S,N,DV];
+    queries of sequence b are the suffix of its keys. Writes out [T,N,DV] and lse [T,N]."""
+    _device_check(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse)
+    lib = load()
+    _check(lib.mla_prefill_attend(_ref(desc(q)), _ref(desc(k)), _ref(desc(v)),
+                                  _ref(desc(cu_seqlens_q)), _ref(desc(cu_seqlens_k)),
+                                  int(max_seqlen_q), float(softmax_scale), int(bool(causal)),
+                                  _ref(desc(out)), _ref(desc(lse)), _stream(out)),
+           "mla_prefill_attend")
     return out

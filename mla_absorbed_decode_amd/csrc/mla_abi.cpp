@@ -498,4 +498,91 @@ int mla_decode_attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,
   return launched(mla::launch_bmm(b, (hipStream_t)stream));
 }
 
+int mla_decompress_kv(const mla_tensor* kv_c, const mla_tensor* k_pe, const mla_tensor* w_uk_t,
+                      const mla_tensor* w_uv, const mla_tensor* k_out, const mla_tensor* v_out,
+                      mla_stream stream) {
+  int rc;
+  if ((rc = check_desc(kv_c, 2)) || (rc = check_desc(w_uk_t, 3)) || (rc = check_desc(w_uv, 3)) ||
+      (rc = check_desc(k_out, 3)) || (rc = check_desc(v_out, 3)))
+    return rc;
+  if (k_pe && (rc = check_desc(k_pe, 2))) return rc;
+  const int32_t dt = kv_c->dtype;
+  if (!is_value_dtype(dt) || w_uk_t->dtype != dt || w_uv->dtype != dt || k_out->dtype != dt ||
+      v_out->dtype != dt || (k_pe && k_pe->dtype != dt))
+    return MLA_ERR_DTYPE;
+  const int64_t S = kv_c->shape[0], L = kv_c->shape[1];
+  const int64_t N = w_uk_t->shape[0], P = w_uk_t->shape[1];
+  if (w_uk_t->shape[2] != L || w_uv->shape[0] != N || w_uv->shape[1] != L) return MLA_ERR_SHAPE;
+  const int64_t V = w_uv->shape[2];
+  const int64_t R = k_pe ? k_pe->shape[1] : 0;
+  if (k_pe && k_pe->shape[0] != S) return MLA_ERR_SHAPE;
+  if (k_out->shape[0] != S || k_out->shape[1] != N || k_out->shape[2] != P + R) return MLA_ERR_SHAPE;
+  if (v_out->shape[0] != S || v_out->shape[1] != N || v_out->shape[2] != V) return MLA_ERR_SHAPE;
+  if (L == 0 || P == 0 || V == 0) return MLA_ERR_SHAPE;
+  mla::BmmNtParams kp;
+  memset(&kp, 0, sizeof(kp));
+  kp.a = kv_c->data; kp.a_st = kv_c->stride[0]; kp.a_sh = 0;  // one latent row for every head
+  kp.w = w_uk_t->data; kp.w_sh = w_uk_t->stride[0]; kp.w_sn = w_uk_t->stride[1];
+  kp.out = k_out->data; kp.o_st = k_out->stride[0]; kp.o_sh = k_out->stride[1];
+  if (k_pe) { kp.pe = k_pe->data; kp.pe_st = k_pe->stride[0]; }
+  kp.T = S; kp.H = N; kp.K = L; kp.N = P; kp.R = R;
+  kp.is_f32 = dt == MLA_F32;
+  mla::BmmParams vp;
+  memset(&vp, 0, sizeof(vp));
+  vp.a = kv_c->data; vp.a_st = kv_c->stride[0]; vp.a_sh = 0;
+  vp.w = w_uv->data; vp.w_sh = w_uv->stride[0]; vp.w_sk = w_uv->stride[1];
+  vp.out = v_out->data; vp.o_st = v_out->stride[0]; vp.o_sh = v_out->stride[1];
+  vp.T = S; vp.H = N; vp.K = L; vp.N = V; vp.R = 0;
+  vp.is_f32 = dt == MLA_F32;
+  if ((rc = launched(mla::launch_bmm_nt(kp, (hipStream_t)stream)))) return rc;
+  return launched(mla::launch_bmm(vp, (hipStream_t)stream));
+}
+
+int mla_prefill_attend(const mla_tensor* q, const mla_tensor* k, const mla_tensor* v,
+                       const mla_tensor* cu_seqlens_q, const mla_tensor* cu_seqlens_k,
+                       int64_t max_seqlen_q, float softmax_scale, int32_t causal,
+                       const mla_tensor* out, const mla_tensor* lse, mla_stream stream) {
+  int rc;
+  if ((rc = check_desc(q, 3)) || (rc = check_desc(k, 3)) || (rc = check_desc(v, 3)) ||
+      (rc = check_desc(cu_seqlens_q, 1)) || (rc = check_desc(cu_seqlens_k, 1)) ||
+      (rc = check_desc(out, 3)))
+    return rc;
+  if (lse && (rc = check_desc(lse, 2))) return rc;
+  const int32_t dt = q->dtype;
+  if (!is_value_dtype(dt) || k->dtype != dt || v->dtype != dt || out->dtype != dt)
+    return MLA_ERR_DTYPE;
+  if (cu_seqlens_q->dtype != MLA_I32 || cu_seqlens_k->dtype != MLA_I32) return MLA_ERR_DTYPE;
+  if (lse && lse->dtype != MLA_F32) return MLA_ERR_DTYPE;
+  const int64_t T = q->shape[0], N = q->shape[1], DK = q->shape[2];
+  const int64_t S = k->shape[0], DV = v->shape[2];
+  if (k->shape[1] != N || k->shape[2] != DK) return MLA_ERR_SHAPE;
+  if (v->shape[0] != S || v->shape[1] != N) return MLA_ERR_SHAPE;
+  if (out->shape[0] != T || out->shape[1] != N || out->shape[2] != DV) return MLA_ERR_SHAPE;
+  if (lse && (lse->shape[0] != T || lse->shape[1] != N)) return MLA_ERR_SHAPE;
+  const int64_t B = cu_seqlens_q->shape[0] - 1;
+  if (B < 0 || cu_seqlens_k->shape[0] != B + 1) return MLA_ERR_SHAPE;
+  if (max_seqlen_q < 0) return MLA_ERR_SHAPE;
+  if (dt != MLA_BF16 || !mla::mha_supported((int)DK, (int)DV)) return MLA_ERR_UNSUPPORTED;
+  if (!rows_aligned16(q) || !rows_aligned16(k) || !rows_aligned16(v) || !rows_aligned(out, 8))
+    return MLA_ERR_UNSUPPORTED;
+  if (T > INT32_MAX || S > INT32_MAX || max_seqlen_q > INT32_MAX || N > 65535 || B > 65535)
+    return MLA_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0 || max_seqlen_q == 0 || T == 0) return MLA_OK;
+  mla::MhaParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q->data; p.q_s0 = q->stride[0]; p.q_s1 = q->stride[1];
+  p.k = k->data; p.k_s0 = k->stride[0]; p.k_s1 = k->stride[1];
+  p.v = v->data; p.v_s0 = v->stride[0]; p.v_s1 = v->stride[1];
+  p.out = out->data; p.o_s0 = out->stride[0]; p.o_s1 = out->stride[1];
+  if (lse) { p.lse = (float*)lse->data; p.l_s0 = lse->stride[0]; p.l_s1 = lse->stride[1]; }
+  p.cu_q = (const int32_t*)cu_seqlens_q->data;
+  p.cu_k = (const int32_t*)cu_seqlens_k->data;
+  p.T = T; p.S = S;
+  p.n_heads = (int)N; p.batch = (int)B; p.max_q = (int)max_seqlen_q;
+  p.dk = (int)DK; p.dv = (int)DV;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return launched(mla::launch_mha(p, (hipStream_t)stream));
+}
+
 }  // extern "C"

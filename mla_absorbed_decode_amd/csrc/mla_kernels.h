@@ -66,6 +66,40 @@ struct BmmParams {
 };
 hipError_t launch_bmm(const BmmParams& p, hipStream_t s);
 
+// ------------------------------------------------- naive (decompressed) prefill
+// Key decompression, a batched product with both operands contiguous along k:
+//   out[t, h, n]       = sum_k a[t, h, k] * w[h, n, k]
+//   out[t, h, N + r]   = pe[t, r]   (one rope row per token, copied to every head)
+struct BmmNtParams {
+  const void* a;  int64_t a_st, a_sh;   // a[t, h, k] (h stride 0: one latent row per token)
+  const void* w;  int64_t w_sh, w_sn;   // w[h, n, k]
+  void* out;      int64_t o_st, o_sh;   // out[t, h, 0 : N + R]
+  const void* pe; int64_t pe_st;        // pe[t, r] (NULL when R == 0)
+  int64_t T, H, K, N, R;
+  int is_f32;
+};
+hipError_t launch_bmm_nt(const BmmNtParams& p, hipStream_t s);
+
+// Multi-head attention over per-head keys and values of packed sequences:
+// sequence b owns query rows cu_q[b] .. cu_q[b+1] and key rows cu_k[b] ..
+// cu_k[b+1]; its queries are the suffix of its keys (causal: query i of a
+// sequence with lq queries and lk keys sees keys 0 .. lk - lq + i).
+struct MhaParams {
+  const void* q; int64_t q_s0, q_s1;    // [T, N, DK] bf16
+  const void* k; int64_t k_s0, k_s1;    // [S, N, DK] bf16
+  const void* v; int64_t v_s0, v_s1;    // [S, N, DV] bf16
+  void* out;     int64_t o_s0, o_s1;    // [T, N, DV] bf16
+  float* lse;    int64_t l_s0, l_s1;    // [T, N] natural log, or NULL
+  const int32_t* cu_q; const int32_t* cu_k;  // [B + 1] each
+  int64_t T, S;                         // rows of q and of k / v (bounds for cu_q, cu_k)
+  int n_heads, batch, max_q;
+  int dk, dv;
+  int causal;
+  float scale_log2;                     // softmax scale * log2(e)
+};
+hipError_t launch_mha(const MhaParams& p, hipStream_t s);
+bool mha_supported(int dk, int dv);
+
 // ------------------------------------------------------------------ decode
 // Division of 32-bit unsigned integers by a fixed d >= 1 as a multiply-high,
 // an add and two shifts (Granlund and Montgomery, "Division by invariant

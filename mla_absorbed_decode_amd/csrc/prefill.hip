@@ -1,0 +1,365 @@
+// prefill.hip -- the naive (decompressed) prefill route on gfx950: per-head
+// keys and values rebuilt from the latent rows, then standard multi-head
+// attention over them (memra-engine 0.124.1 "tests/mla_gpu_forward.rs": the
+// naive oracle `mla_attend_naive`, which decompresses K and V per head;
+// vllm.cpp "tests/vt/test_ops_mla_absorb.cpp": ConcatMlaNopeRope, the case
+// that broadcasts the single k_pe head across every head). For long prompts
+// this costs 2 (d_nope + d_rope + d_v) flops per (query, key, head) against
+// 2 (2 kv_rank + d_rope) for the absorbed form.
+//
+// Key decompression (bmm_nt_bf16): out[t, h, n] = sum_k a[t, h, k] w[h, n, k]
+// with the token's rope row copied behind every head's n columns. Both
+// operands are contiguous along k, which is exactly the per-lane layout of
+// v_mfma_f32_16x16x32_bf16's A and B operands (8 consecutive k per lane), so
+// each lane loads its 16-byte pieces straight from global memory. A 64 x 64
+// output tile per workgroup; each wave owns 32 x 32 of it (2 x 2 MFMA tiles,
+// two A and two B loads per four MFMAs).
+//
+// Attention (mha_fwd<DK, DV>): one workgroup per (64 query rows, head,
+// sequence), 16 rows per wave. 32-key tiles of K and V are loaded into
+// registers one tile ahead and stored to a two-slot LDS ring (one barrier per
+// tile). Scores are computed transposed, S^T = K Q^T, with the wave's query
+// rows held in registers as the B operand: S^T's accumulator layout (lane l:
+// keys 4(l/16) + j and 16 + 4(l/16) + j of query l % 16) is then the B-operand
+// layout of P^T in O^T += V^T P^T, so P never leaves registers, and V^T comes
+// from LDS through ds_read_b64_tr_b16. Online softmax in the exp2 domain; the
+// running max is shared by a query's four lanes (two cross-lane exchanges per
+// tile), each lane keeps its own partial sum until the end.
+#include "mla_device.h"
+#include "mla_kernels.h"
+
+namespace mla {
+namespace {
+
+// ------------------------------------------------------------ key decompression
+constexpr int kNtM = 64, kNtN = 64, kNtK = 32;
+
+// out[t, h, N + r] = pe[t, r] for the tile's tokens, in the workgroups of the
+// first column tile.
+template <class T>
+__device__ __forceinline__ void copy_rope_broadcast(const BmmNtParams& p, int t0, int h) {
+  if (p.R == 0 || blockIdx.x != 0) return;
+  const int nt = (int)(p.T - t0 < kNtM ? p.T - t0 : kNtM);
+  const int R = (int)p.R;
+  for (int e = threadIdx.x; e < nt * R; e += blockDim.x) {
+    const int t = t0 + e / R, r = e % R;
+    ((T*)p.out)[(int64_t)t * p.o_st + (int64_t)h * p.o_sh + p.N + r] =
+        ((const T*)p.pe)[(int64_t)t * p.pe_st + r];
+  }
+}
+
+__global__ void __launch_bounds__(256) bmm_nt_bf16(BmmNtParams p) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+  const int wr = w >> 1, wc = w & 1;
+  const int n0 = blockIdx.x * kNtN, t0 = blockIdx.y * kNtM, h = blockIdx.z;
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+  bool aok[2], bok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + 32 * wr + 16 * i + li;
+    aok[i] = t < p.T;
+    arow[i] = (const uint16_t*)p.a + (int64_t)(aok[i] ? t : 0) * p.a_st + (int64_t)h * p.a_sh + 8 * g;
+    const int n = n0 + 32 * wc + 16 * i + li;
+    bok[i] = n < p.N;
+    brow[i] = (const uint16_t*)p.w + (int64_t)h * p.w_sh + (int64_t)(bok[i] ? n : 0) * p.w_sn + 8 * g;
+  }
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const i16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 4
+  for (int k0 = 0; k0 < p.K; k0 += kNtK) {
+    i16x8_t av[2], bv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      av[i] = aok[i] ? *(const i16x8_t*)(arow[i] + k0) : zero;
+      bv[i] = bok[i] ? *(const i16x8_t*)(brow[i] + k0) : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_16x16x32(av[i], bv[j], acc[i][j]);
+  }
+  // lane holds out[t0 + 32 wr + 16 i + 4 g + jj][n0 + 32 wc + 16 j + li]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + 32 * wc + 16 * j + li;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int t = t0 + 32 * wr + 16 * i + 4 * g + jj;
+        if (t < p.T)
+          ((uint16_t*)p.out)[(int64_t)t * p.o_st + (int64_t)h * p.o_sh + n] = f32_to_bf16(acc[i][j][jj]);
+      }
+    }
+  copy_rope_broadcast<uint16_t>(p, t0, h);
+}
+
+// Any size or alignment, bf16 or f32: one thread per output element, f32
+// accumulation in k order.
+template <bool F32>
+__global__ void __launch_bounds__(256) bmm_nt_plain(BmmNtParams p) {
+  const int64_t W = p.N + p.R;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= p.T * p.H * W) return;
+  const int64_t t = idx / (p.H * W), rem = idx % (p.H * W), h = rem / W, n = rem % W;
+  float v;
+  if (n < p.N) {
+    float acc = 0.f;
+    for (int64_t k = 0; k < p.K; ++k) {
+      const int64_t ai = t * p.a_st + h * p.a_sh + k, wi = h * p.w_sh + n * p.w_sn + k;
+      const float a = F32 ? ((const float*)p.a)[ai] : bf16_to_f32(((const uint16_t*)p.a)[ai]);
+      const float b = F32 ? ((const float*)p.w)[wi] : bf16_to_f32(((const uint16_t*)p.w)[wi]);
+      acc = __builtin_fmaf(a, b, acc);
+    }
+    v = acc;
+    const int64_t oi = t * p.o_st + h * p.o_sh + n;
+    if (F32) ((float*)p.out)[oi] = v;
+    else ((uint16_t*)p.out)[oi] = f32_to_bf16(v);
+  } else {  // the rope row, copied bit for bit
+    const int64_t oi = t * p.o_st + h * p.o_sh + n, pi = t * p.pe_st + (n - p.N);
+    if (F32) ((uint32_t*)p.out)[oi] = ((const uint32_t*)p.pe)[pi];
+    else ((uint16_t*)p.out)[oi] = ((const uint16_t*)p.pe)[pi];
+  }
+}
+
+// -------------------------------------------------------------------- attention
+constexpr int kQT = 64;  // query rows per workgroup (16 per wave)
+constexpr int kKT = 32;  // keys per tile
+
+// LDS rows are padded so that the K-operand reads (16 consecutive rows, one
+// 16-byte piece each per 16 lanes) and the transposed V reads (4 consecutive
+// rows x 32 bytes per 16 lanes) fall in distinct banks.
+template <int DK, int DV>
+struct MhaShape {
+  static constexpr int KP = DK * 2 + 16;  // K row pitch, bytes
+  static constexpr int VP = DV * 2 + 32;  // V row pitch, bytes
+  static constexpr int KBYTES = kKT * KP, VBYTES = kKT * VP;
+  static constexpr int SLOT = KBYTES + VBYTES;
+  static constexpr int LDS = 2 * SLOT;
+  static constexpr int KCH = DK / 8, VCH = DV / 8;  // 16-byte pieces per row
+  static constexpr int NKL = kKT * KCH / 256, NVL = kKT * VCH / 256;  // pieces per thread
+  static_assert(DK % 32 == 0 && DV % 16 == 0, "MFMA tiling");
+  static_assert((kKT * KCH) % 256 == 0 && (kKT * VCH) % 256 == 0, "whole pieces per thread");
+};
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) mha_fwd(MhaParams p) {
+  using Sh = MhaShape<DK, DV>;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest causal tiles first
+  // the sequence's rows, clamped to the buffers
+  int q0 = p.cu_q[b], q1 = p.cu_q[b + 1], k0 = p.cu_k[b], k1 = p.cu_k[b + 1];
+  q1 = q1 < 0 ? 0 : (q1 > p.T ? (int)p.T : q1);
+  q0 = q0 < 0 ? 0 : (q0 > q1 ? q1 : q0);
+  k1 = k1 < 0 ? 0 : (k1 > p.S ? (int)p.S : k1);
+  k0 = k0 < 0 ? 0 : (k0 > k1 ? k1 : k0);
+  const int lq = q1 - q0, lk = k1 - k0;
+  const int qbase = qt * kQT;
+  if (qbase >= lq) return;
+  // keys this workgroup needs: up to the last visible key of its last row
+  int kend = lk;
+  if (p.causal) {
+    const int last = (qbase + kQT < lq ? qbase + kQT : lq) - 1;
+    kend = lk - lq + last + 1;
+    kend = kend < 0 ? 0 : (kend > lk ? lk : kend);
+  }
+  const int ntiles = (kend + kKT - 1) / kKT;
+
+  const int qi = qbase + 16 * w + li;  // this lane's query row (index in the sequence)
+  const bool qok = qi < lq;
+  const int pos = lk - lq + qi;
+  const int vis_end = p.causal ? (pos + 1 < lk ? pos + 1 : lk) : lk;  // keys [0, vis_end) visible
+
+  // the wave's query rows as the B operand: lane holds q[row li][32 kk + 8 g .. + 7]
+  constexpr int KK = DK / 32;
+  i16x8_t qreg[KK];
+  {
+    const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)(q0 + (qok ? qi : 0)) * p.q_s0 +
+                           (int64_t)h * p.q_s1 + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qreg[kk] = qok ? *(const i16x8_t*)(qrow + 32 * kk) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  const uint16_t* kbase = (const uint16_t*)p.k + (int64_t)k0 * p.k_s0 + (int64_t)h * p.k_s1;
+  const uint16_t* vbase = (const uint16_t*)p.v + (int64_t)k0 * p.v_s0 + (int64_t)h * p.v_s1;
+  u32x4_t kr[Sh::NKL], vr[Sh::NVL];
+  // global -> registers: piece i of the tile starting at key j0 (rows past the
+  // sequence repeat its last key; their scores are masked)
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < Sh::NKL; ++i) {
+      const int idx = tid + 256 * i, r = idx / Sh::KCH, c = idx % Sh::KCH;
+      const int j = j0 + r < lk ? j0 + r : lk - 1;
+      kr[i] = *(const u32x4_t*)(kbase + (int64_t)j * p.k_s0 + 8 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < Sh::NVL; ++i) {
+      const int idx = tid + 256 * i, r = idx / Sh::VCH, c = idx % Sh::VCH;
+      const int j = j0 + r < lk ? j0 + r : lk - 1;
+      vr[i] = *(const u32x4_t*)(vbase + (int64_t)j * p.v_s0 + 8 * c);
+    }
+  };
+  auto store_tile = [&](int slot) {
+    MLA_LDS char* kb = smem + slot * Sh::SLOT;
+    MLA_LDS char* vb = kb + Sh::KBYTES;
+#pragma unroll
+    for (int i = 0; i < Sh::NKL; ++i) {
+      const int idx = tid + 256 * i, r = idx / Sh::KCH, c = idx % Sh::KCH;
+      *(MLA_LDS u32x4_t*)(kb + r * Sh::KP + 16 * c) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Sh::NVL; ++i) {
+      const int idx = tid + 256 * i, r = idx / Sh::VCH, c = idx % Sh::VCH;
+      *(MLA_LDS u32x4_t*)(vb + r * Sh::VP + 16 * c) = vr[i];
+    }
+  };
+
+  constexpr int DB = DV / 16;
+  f32x4_t o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_inff(), l = 0.f;
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile((t + 1) * kKT);
+    const MLA_LDS char* kb = smem + (t & 1) * Sh::SLOT;
+    const MLA_LDS char* vb = kb + Sh::KBYTES;
+    const int j0 = t * kKT;
+    // S^T[key 16 kb + 4 g + jj][query li]
+    f32x4_t s[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      s[kb2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const MLA_LDS char* krow = kb + (16 * kb2 + li) * Sh::KP + 16 * g;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s[kb2] = mfma_16x16x32(*(const MLA_LDS i16x8_t*)(krow + 64 * kk), qreg[kk], s[kb2]);
+    }
+    float x[2][4];
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int key = j0 + 16 * kb2 + 4 * g + jj;
+        x[kb2][jj] = key < vis_end ? s[kb2][jj] * p.scale_log2 : -__builtin_inff();
+        tmax = fmaxf(tmax, x[kb2][jj]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(m, tmax);
+    const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
+    const float alpha = exp2f(m - muse);
+    m = mnew;
+    float psum = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const float p0 = exp2f(x[kb2][0] - muse), p1 = exp2f(x[kb2][1] - muse);
+      const float p2 = exp2f(x[kb2][2] - muse), p3 = exp2f(x[kb2][3] - muse);
+      psum += (p0 + p1) + (p2 + p3);
+      pk[2 * kb2] = pack_bf16x2(p0, p1);
+      pk[2 * kb2 + 1] = pack_bf16x2(p2, p3);
+    }
+    l = l * alpha + psum;
+    // P^T slots 8 g + i: keys 4 g + i (i < 4) and 16 + 4 g + (i - 4)
+    const i16x8_t pb = __builtin_bit_cast(i16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+    // V^T rows d = 16 db + li from two transposed reads (keys 4 g .. 4 g + 3, then 16 + ...)
+    const int vr0 = 4 * g + (li >> 2);
+    const MLA_LDS char* vrow0 = vb + vr0 * Sh::VP + 8 * (li & 3);
+    const MLA_LDS char* vrow1 = vrow0 + 16 * Sh::VP;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4_t a0 = lds_read_tr16(vrow0 + 32 * db);
+      const i16x4_t a1 = lds_read_tr16(vrow1 + 32 * db);
+      const i16x8_t av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      o[db] = mfma_16x16x32(av, pb, o[db] * alpha);
+    }
+    if (more) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // a query's four lanes hold partial sums over their keys
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!qok) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* orow = (uint16_t*)p.out + (int64_t)(q0 + qi) * p.o_s0 + (int64_t)h * p.o_s1 + 4 * g;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const u32x2_t v = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
+                       pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
+    *(u32x2_t*)(orow + 16 * db) = v;
+  }
+  if (p.lse && g == 0)
+    p.lse[(int64_t)(q0 + qi) * p.l_s0 + (int64_t)h * p.l_s1] =
+        l > 0.f ? (m + __log2f(l)) * 0.69314718055994530942f : -__builtin_inff();
+}
+
+template <int DK, int DV>
+hipError_t launch_mha_t(const MhaParams& p, hipStream_t s) {
+  using Sh = MhaShape<DK, DV>;
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute((const void*)mha_fwd<DK, DV>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  dim3 grid((unsigned)((p.max_q + kQT - 1) / kQT), (unsigned)p.n_heads, (unsigned)p.batch);
+  hipLaunchKernelGGL((mha_fwd<DK, DV>), grid, dim3(256), Sh::LDS, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bmm_nt(const BmmNtParams& p, hipStream_t s) {
+  if (p.T == 0 || p.H == 0) return hipSuccess;
+  const int64_t es = p.is_f32 ? 4 : 2;
+  const bool aligned = ((uintptr_t)p.a % 16 == 0) && ((uintptr_t)p.w % 16 == 0) &&
+                       (p.a_st * es % 16 == 0) && (p.a_sh * es % 16 == 0) &&
+                       (p.w_sh * es % 16 == 0) && (p.w_sn * es % 16 == 0);
+  if (!p.is_f32 && aligned && p.K % kNtK == 0 && p.K > 0 && p.N > 0) {
+    dim3 grid((unsigned)((p.N + kNtN - 1) / kNtN), (unsigned)((p.T + kNtM - 1) / kNtM), (unsigned)p.H);
+    hipLaunchKernelGGL(bmm_nt_bf16, grid, dim3(256), 0, s, p);
+  } else {
+    const int64_t total = p.T * p.H * (p.N + p.R);
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (p.is_f32) hipLaunchKernelGGL(bmm_nt_plain<true>, dim3(blocks), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(bmm_nt_plain<false>, dim3(blocks), dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+bool mha_supported(int dk, int dv) {
+  return (dk == 192 && dv == 128) || (dk == 256 && dv == 256) || (dk == 128 && dv == 128) ||
+         (dk == 64 && dv == 64);
+}
+
+hipError_t launch_mha(const MhaParams& p, hipStream_t s) {
+  if (p.batch == 0 || p.max_q == 0 || p.n_heads == 0) return hipSuccess;
+  if (p.dk == 192 && p.dv == 128) return launch_mha_t<192, 128>(p, s);
+  if (p.dk == 256 && p.dv == 256) return launch_mha_t<256, 256>(p, s);
+  if (p.dk == 128 && p.dv == 128) return launch_mha_t<128, 128>(p, s);
+  if (p.dk == 64 && p.dv == 64) return launch_mha_t<64, 64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla

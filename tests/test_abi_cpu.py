@@ -51,7 +51,8 @@ def test_library_exports_every_declared_symbol(lib):
                           "mla_decode_attend", "mla_v_up", "mla_status_str",
                           "mla_rope_interleaved", "mla_absorb_q_rope", "mla_concat_and_cache_rope",
                           "mla_absorb_q_and_cache", "mla_decode_attend_v_up",
-                          "mla_concat_and_cache_fp8", "mla_decode_attend_fp8"}
+                          "mla_concat_and_cache_fp8", "mla_decode_attend_fp8",
+                          "mla_decompress_kv", "mla_prefill_attend"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -327,3 +328,53 @@ def test_binding_descriptor_matches_view():
     assert d.rank == 3 and list(d.shape[:3]) == [32, 64, 576]
     assert list(d.stride[:3]) == [110592, 576, 1]
     assert d.data == big.data_ptr() + 64 * 576 * 2  # storage offset folded into the pointer
+
+
+# ------------------------------------------------------------ naive prefill
+
+
+def test_decompress_kv_validation(lib):
+    f = lambda c, pe, wk, wv, k, v: lib.mla_decompress_kv(R(c), R(pe), R(wk), R(wv), R(k), R(v),
+                                                          None)
+    S, N, P, Rr, V, L = 8, 16, 128, 64, 128, 512
+    c, pe = T([S, L]), T([S, Rr])
+    wk, wv = T([N, P, L]), T([N, L, V])
+    k, v = T([S, N, P + Rr]), T([S, N, V])
+    assert f(c, pe, wk, wv, T([S, N, P]), v) == SHAPE            # no room for the rope row
+    assert f(T([0, L]), None, wk, wv, T([0, N, P]), T([0, N, V])) == OK  # NoPE, no rows
+    assert f(c, pe, T([N, P, 256]), wv, k, v) == SHAPE           # latent width mismatch
+    assert f(c, pe, wk, T([N, L, 64]), k, v) == SHAPE            # v width mismatch
+    assert f(c, T([S + 1, Rr]), wk, wv, k, v) == SHAPE
+    assert f(c, pe, wk, T([N, L, V], F32), k, v) == DTYPE
+    assert f(c, pe, wk, wv, k, T([S, N, V], strides=[N * V * 2, V * 2, 2])) == STRIDE
+    assert f(None, pe, wk, wv, k, v) == NULL
+    assert f(T([0, L]), T([0, Rr]), wk, wv, T([0, N, P + Rr]), T([0, N, V])) == OK
+
+
+def test_prefill_attend_validation(lib):
+    def f(q, k, v, cq, ck, out, lse=None, max_q=64, scale=0.1, causal=1):
+        return lib.mla_prefill_attend(R(q), R(k), R(v), R(cq), R(ck), max_q, scale, causal, R(out),
+                                      R(lse), None)
+    Tq, S, N = 64, 96, 16
+    q, k, v = T([Tq, N, 192]), T([S, N, 192]), T([S, N, 128])
+    cq, ck = T([3], I32), T([3], I32)
+    out, lse = T([Tq, N, 128]), T([Tq, N], F32)
+    assert f(q, k, v, cq, T([4], I32), out, lse) == SHAPE        # batch mismatch
+    assert f(q, T([S, N, 128]), v, cq, ck, out) == SHAPE          # key width != query width
+    assert f(q, k, T([S + 1, N, 128]), cq, ck, out) == SHAPE
+    assert f(q, k, v, cq, ck, T([Tq, N, 64])) == SHAPE
+    assert f(q, k, v, cq, ck, out, T([Tq, 8], F32)) == SHAPE
+    assert f(q, k, v, cq, ck, out, max_q=-1) == SHAPE
+    assert f(q, k, v, T([3], I64), ck, out) == DTYPE
+    assert f(q, k, v, cq, ck, out, T([Tq, N], BF16)) == DTYPE
+    assert f(q, k, T([S, N, 128], F32), cq, ck, out) == DTYPE
+    # f32 and unsupported widths are refused, as are misaligned rows
+    assert f(T([Tq, N, 192], F32), T([S, N, 192], F32), T([S, N, 128], F32), cq, ck,
+             T([Tq, N, 128], F32)) == UNSUP
+    assert f(T([Tq, N, 96]), T([S, N, 96]), v, cq, ck, out) == UNSUP
+    assert f(T([Tq, N, 192], data=FAKE + 2), k, v, cq, ck, out) == UNSUP
+    assert f(q, k, v, cq, ck, T([Tq, N, 128], data=FAKE + 4)) == UNSUP
+    assert f(None, k, v, cq, ck, out) == NULL
+    # nothing to do
+    assert f(q, k, v, T([1], I32), T([1], I32), out) == OK        # no sequence
+    assert f(q, k, v, cq, ck, out, max_q=0) == OK
