@@ -401,6 +401,75 @@ def fp8_secondary(step: Step, dev, steps: int, warmup: int, eager: bool = False)
     }
 
 
+def prefill_secondary(dev, steps: int, warmup: int):
+    """The NoPE prefill workload (64 heads x d_nope 256, rank 512, v 256, one
+    causal sequence of 2048 tokens, bf16) by both routes: absorbed (fold q
+    through W_UK_T, attend over the latent rows, un-project through W_UV) and
+    naive (decompress per-head K and V, multi-head attention). Each call is
+    timed on its own (events around `steps` eager launches: the calls run for
+    tens to hundreds of microseconds, so launch gaps do not matter)."""
+    c = mi.nope_prefill(0, mi.BF16)
+    d, t, scale = c["dims"], c["t"], c["scale"]
+    N, P, V, L = d.n_head, d.d_nope, d.d_v, d.kv_rank
+    bf = torch.bfloat16
+    to = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(bf).to(dev)
+    q_nope, c_kv, w_uk_t, w_uv = to(c["q_nope"]), to(c["c_kv"]), to(c["w_uk_t"]), to(c["w_uv"])
+    page = c["page"]
+    nb = t // page
+    cache = c_kv.view(nb, page, L)
+    bt = torch.arange(nb, dtype=torch.int32, device=dev).view(1, nb)
+    sl = torch.tensor([t], dtype=torch.int32, device=dev)
+    q = torch.empty(1, t, N, L, dtype=bf, device=dev)
+    o_lat = torch.empty(1, t, N, L, dtype=bf, device=dev)
+    out = torch.empty(t, N, V, dtype=bf, device=dev)
+    ws = torch.empty(max(1, mla.mla_decode_workspace_size(1, t, N, L, t, page, bf)),
+                     dtype=torch.uint8, device=dev)
+    k_out = torch.empty(t, N, P, dtype=bf, device=dev)
+    v_out = torch.empty(t, N, V, dtype=bf, device=dev)
+    out2 = torch.empty(t, N, V, dtype=bf, device=dev)
+    cu = torch.tensor([0, t], dtype=torch.int32, device=dev)
+    calls = {
+        "fold_us": lambda: mla.mla_absorb_q(q_nope, w_uk_t, None, q[0]),
+        "absorbed_attend_us": lambda: mla.mla_decode_attend(q, cache, bt, sl, t, scale, True,
+                                                            o_lat, None, workspace=ws),
+        "v_up_us": lambda: mla.mla_v_up(o_lat[0], w_uv, out),
+        "decompress_kv_us": lambda: mla.mla_decompress_kv(c_kv, None, w_uk_t, w_uv, k_out, v_out),
+        "naive_attend_us": lambda: mla.mla_prefill_attend(q_nope, k_out, v_out, cu, cu, t, scale,
+                                                          True, out2),
+    }
+    res = {"workload": "NoPE prefill bf16: 64 heads, d_nope 256, d_rope 0, d_v 256, kv_rank 512, "
+                       "one causal sequence of 2048 tokens, U[-1,1] activations, "
+                       "U[+-1/sqrt(512)] weights"}
+    for name, fn in calls.items():
+        for _ in range(max(1, warmup)):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        res[name] = round(t0.elapsed_time(t1) / steps * 1e3, 2)
+    pairs = N * t * (t + 1) // 2
+    fold = 2 * t * N * P * L
+    tf = lambda flop, us: flop / (us * 1e-6) / 1e12
+    abs_att, nai_att = pairs * 2 * (L + L), pairs * 2 * (P + V)
+    res["absorbed_attend_tflops"] = round(tf(abs_att, res["absorbed_attend_us"]), 1)
+    res["absorbed_attend_mfma_frac"] = round(res["absorbed_attend_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    res["naive_attend_tflops"] = round(tf(nai_att, res["naive_attend_us"]), 1)
+    res["naive_attend_mfma_frac"] = round(res["naive_attend_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    res["decompress_kv_tflops"] = round(tf(2 * fold, res["decompress_kv_us"]), 1)
+    res["absorbed_route_us"] = round(res["fold_us"] + res["absorbed_attend_us"] + res["v_up_us"], 2)
+    res["naive_route_us"] = round(res["decompress_kv_us"] + res["naive_attend_us"], 2)
+    res["algorithmic_gflop"] = {"absorbed_attend": round(abs_att / 1e9, 1),
+                                "naive_attend": round(nai_att / 1e9, 1),
+                                "fold": round(fold / 1e9, 1), "v_up": round(fold / 1e9, 1),
+                                "decompress_kv": round(2 * fold / 1e9, 1)}
+    return res
+
+
 def rope_secondary(step: Step, dev, steps: int, warmup: int):
     """Interleaved rope at the V2-Lite decode step's shapes: the q fold and the
     cache write with and without the fused rotation (positions seqlen_b - 1),
@@ -467,6 +536,8 @@ def main():
     ap.add_argument("--no-v3", action="store_true", help="skip the 128-head secondary line")
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding line")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache line")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the NoPE prefill line (absorbed and naive routes)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from the host instead of replaying graphs "
                          "(for counter collection)")
@@ -546,6 +617,8 @@ def main():
                                           eager=args.eager)
     if not args.no_rope:
         line["rope"] = rope_secondary(step, dev, max(10, args.steps // 2), args.warmup)
+    if not args.no_prefill:
+        line["nope_prefill"] = prefill_secondary(dev, max(5, args.steps // 10), min(args.warmup, 3))
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, step)
     print(json.dumps(line), flush=True)

@@ -15,7 +15,7 @@
 // output tile per workgroup; each wave owns 32 x 32 of it (2 x 2 MFMA tiles,
 // two A and two B loads per four MFMAs).
 //
-// Attention (mha_fwd<DK, DV>): one workgroup per (64 query rows, head,
+// Attention (mha_fwd<DK, DV>): one workgroup per (128 query rows, head,
 // sequence), 16 rows per wave. 32-key tiles of K and V are loaded into
 // registers one tile ahead and stored to a two-slot LDS ring (one barrier per
 // tile). Scores are computed transposed, S^T = K Q^T, with the wave's query
@@ -129,8 +129,10 @@ __global__ void __launch_bounds__(256) bmm_nt_plain(BmmNtParams p) {
 }
 
 // -------------------------------------------------------------------- attention
-constexpr int kQT = 64;  // query rows per workgroup (16 per wave)
-constexpr int kKT = 32;  // keys per tile
+constexpr int kNW = 8;         // waves per workgroup
+constexpr int kQT = 16 * kNW;  // query rows per workgroup (16 per wave)
+constexpr int kKT = 32;        // keys per tile
+constexpr int kThreads = 64 * kNW;
 
 // LDS rows are padded so that the K-operand reads (16 consecutive rows, one
 // 16-byte piece each per 16 lanes) and the transposed V reads (4 consecutive
@@ -143,20 +145,34 @@ struct MhaShape {
   static constexpr int SLOT = KBYTES + VBYTES;
   static constexpr int LDS = 2 * SLOT;
   static constexpr int KCH = DK / 8, VCH = DV / 8;  // 16-byte pieces per row
-  static constexpr int NKL = kKT * KCH / 256, NVL = kKT * VCH / 256;  // pieces per thread
+  static constexpr int KPC = kKT * KCH, VPC = kKT * VCH;  // pieces per tile
+  static constexpr int NKL = (KPC + kThreads - 1) / kThreads;  // pieces per thread (at most)
+  static constexpr int NVL = (VPC + kThreads - 1) / kThreads;
   static_assert(DK % 32 == 0 && DV % 16 == 0, "MFMA tiling");
-  static_assert((kKT * KCH) % 256 == 0 && (kKT * VCH) % 256 == 0, "whole pieces per thread");
 };
 
 template <int DK, int DV>
-__global__ void __launch_bounds__(256) mha_fwd(MhaParams p) {
+__global__ void __launch_bounds__(kThreads) mha_fwd(MhaParams p) {
   using Sh = MhaShape<DK, DV>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest causal tiles first
+  const int b = blockIdx.z;
+  // (query tile, head) of this workgroup. Consecutive workgroups go to the 8
+  // XCDs in turn, each with its own L2: with a head count divisible by 8, XCD x
+  // runs only heads x, x + 8, ..., two heads' keys and values at a time, and
+  // within a head the longest causal tiles first.
+  const int ntq = (int)gridDim.x;
+  int h, qt;
+  if (p.n_heads % 8 == 0) {
+    const int i = (int)blockIdx.x + ntq * (int)blockIdx.y, j = i >> 3;
+    h = (j / ntq) * 8 + (i & 7);
+    qt = ntq - 1 - j % ntq;
+  } else {
+    h = (int)blockIdx.y;
+    qt = ntq - 1 - (int)blockIdx.x;
+  }
   // the sequence's rows, clamped to the buffers
   int q0 = p.cu_q[b], q1 = p.cu_q[b + 1], k0 = p.cu_k[b], k1 = p.cu_k[b + 1];
   q1 = q1 < 0 ? 0 : (q1 > p.T ? (int)p.T : q1);
@@ -179,6 +195,13 @@ __global__ void __launch_bounds__(256) mha_fwd(MhaParams p) {
   const bool qok = qi < lq;
   const int pos = lk - lq + qi;
   const int vis_end = p.causal ? (pos + 1 < lk ? pos + 1 : lk) : lk;  // keys [0, vis_end) visible
+  // keys past the wave's last visible key need no arithmetic (wave-uniform)
+  int wave_end = 0;
+  if (qbase + 16 * w < lq) {
+    const int wlast = (qbase + 16 * w + 15 < lq ? qbase + 16 * w + 15 : lq - 1);
+    wave_end = p.causal ? lk - lq + wlast + 1 : lk;
+    wave_end = wave_end < 0 ? 0 : (wave_end > lk ? lk : wave_end);
+  }
 
   // the wave's query rows as the B operand: lane holds q[row li][32 kk + 8 g .. + 7]
   constexpr int KK = DK / 32;
@@ -199,15 +222,15 @@ __global__ void __launch_bounds__(256) mha_fwd(MhaParams p) {
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < Sh::NKL; ++i) {
-      const int idx = tid + 256 * i, r = idx / Sh::KCH, c = idx % Sh::KCH;
+      const int idx = tid + kThreads * i, r = idx / Sh::KCH, c = idx % Sh::KCH;
       const int j = j0 + r < lk ? j0 + r : lk - 1;
-      kr[i] = *(const u32x4_t*)(kbase + (int64_t)j * p.k_s0 + 8 * c);
+      if (idx < Sh::KPC) kr[i] = *(const u32x4_t*)(kbase + (int64_t)j * p.k_s0 + 8 * c);
     }
 #pragma unroll
     for (int i = 0; i < Sh::NVL; ++i) {
-      const int idx = tid + 256 * i, r = idx / Sh::VCH, c = idx % Sh::VCH;
+      const int idx = tid + kThreads * i, r = idx / Sh::VCH, c = idx % Sh::VCH;
       const int j = j0 + r < lk ? j0 + r : lk - 1;
-      vr[i] = *(const u32x4_t*)(vbase + (int64_t)j * p.v_s0 + 8 * c);
+      if (idx < Sh::VPC) vr[i] = *(const u32x4_t*)(vbase + (int64_t)j * p.v_s0 + 8 * c);
     }
   };
   auto store_tile = [&](int slot) {
@@ -215,13 +238,13 @@ __global__ void __launch_bounds__(256) mha_fwd(MhaParams p) {
     MLA_LDS char* vb = kb + Sh::KBYTES;
 #pragma unroll
     for (int i = 0; i < Sh::NKL; ++i) {
-      const int idx = tid + 256 * i, r = idx / Sh::KCH, c = idx % Sh::KCH;
-      *(MLA_LDS u32x4_t*)(kb + r * Sh::KP + 16 * c) = kr[i];
+      const int idx = tid + kThreads * i, r = idx / Sh::KCH, c = idx % Sh::KCH;
+      if (idx < Sh::KPC) *(MLA_LDS u32x4_t*)(kb + r * Sh::KP + 16 * c) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < Sh::NVL; ++i) {
-      const int idx = tid + 256 * i, r = idx / Sh::VCH, c = idx % Sh::VCH;
-      *(MLA_LDS u32x4_t*)(vb + r * Sh::VP + 16 * c) = vr[i];
+      const int idx = tid + kThreads * i, r = idx / Sh::VCH, c = idx % Sh::VCH;
+      if (idx < Sh::VPC) *(MLA_LDS u32x4_t*)(vb + r * Sh::VP + 16 * c) = vr[i];
     }
   };
 
@@ -242,6 +265,7 @@ __global__ void __launch_bounds__(256) mha_fwd(MhaParams p) {
     const MLA_LDS char* kb = smem + (t & 1) * Sh::SLOT;
     const MLA_LDS char* vb = kb + Sh::KBYTES;
     const int j0 = t * kKT;
+    if (j0 < wave_end) {
     // S^T[key 16 kb + 4 g + jj][query li]
     f32x4_t s[2];
 #pragma unroll
@@ -292,6 +316,7 @@ __global__ void __launch_bounds__(256) mha_fwd(MhaParams p) {
       const i16x8_t av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       o[db] = mfma_16x16x32(av, pb, o[db] * alpha);
     }
+    }
     if (more) store_tile((t + 1) & 1);
     __syncthreads();
   }
@@ -324,7 +349,7 @@ hipError_t launch_mha_t(const MhaParams& p, hipStream_t s) {
     attr = true;
   }
   dim3 grid((unsigned)((p.max_q + kQT - 1) / kQT), (unsigned)p.n_heads, (unsigned)p.batch);
-  hipLaunchKernelGGL((mha_fwd<DK, DV>), grid, dim3(256), Sh::LDS, s, p);
+  hipLaunchKernelGGL((mha_fwd<DK, DV>), grid, dim3(kThreads), Sh::LDS, s, p);
   return hipGetLastError();
 }
 
