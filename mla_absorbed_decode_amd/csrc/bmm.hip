@@ -20,6 +20,7 @@
 // transpose needed). Sizes the MFMA tiling does not cover (K not a multiple of
 // 32, N not a multiple of 16) take a plain one-thread-per-output kernel.
 #include "cache_write.h"
+#include "gemm_tile.h"
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -188,6 +189,25 @@ __global__ void __launch_bounds__(256) bmm_bf16_mfma(BmmParams p) {
   if (p.R > 0) copy_rope<uint16_t>(p, t0, h);
 }
 
+// Prefill-sized token counts (bf16): 128 x 128 output tiles of the shared
+// pipelined tile (gemm_tile.h); the rope rows are copied after the product,
+// as in bmm_bf16_mfma.
+__global__ void __launch_bounds__(256) bmm_bf16_big(BmmParams p) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[kGLds];
+  const int h = blockIdx.z;
+  GemmTileArgs g;
+  g.a = (const uint16_t*)p.a + (int64_t)h * p.a_sh; g.a_st = p.a_st;
+  g.w = (const uint16_t*)p.w + (int64_t)h * p.w_sh; g.w_s1 = p.w_sk;
+  g.out = (uint16_t*)p.out + (int64_t)h * p.o_sh; g.o_st = p.o_st;
+  g.T = (int)p.T; g.K = (int)p.K; g.N = (int)p.N;
+  g.t0 = blockIdx.y * kGT; g.n0 = blockIdx.x * kGT;
+  gemm_tile_128<false>(g, (MLA_LDS char*)lds_raw);
+  if (p.R > 0) {
+    copy_rope<uint16_t>(p, g.t0, h);
+    if (g.t0 + kTM < p.T) copy_rope<uint16_t>(p, g.t0 + kTM, h);
+  }
+}
+
 __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
   if (cache_write_slot(p)) return;
   __shared__ __attribute__((aligned(16))) float wt[2][kKB * kTN];
@@ -299,6 +319,9 @@ hipError_t launch_bmm(const BmmParams& p, hipStream_t s) {
   if (mfma_ok && p.is_f32) {
     dim3 grid((unsigned)((p.N + kTN - 1) / kTN), (unsigned)((p.T + kTM - 1) / kTM), hz);
     hipLaunchKernelGGL(bmm_f32_mfma, grid, dim3(256), 0, s, p);
+  } else if (mfma_ok && !p.with_cw && p.T >= kBigT && p.K <= INT32_MAX && p.T <= INT32_MAX) {
+    dim3 grid((unsigned)((p.N + kGT - 1) / kGT), (unsigned)((p.T + kGT - 1) / kGT), (unsigned)p.H);
+    hipLaunchKernelGGL(bmm_bf16_big, grid, dim3(256), 0, s, p);
   } else if (mfma_ok) {
     // 64-wide tiles when they give the chip at least 128 workgroups
     const int64_t tiles_t = (p.T + kTM - 1) / kTM;

@@ -65,6 +65,8 @@ struct BmmParams {
   CacheWriteParams cw;
 };
 hipError_t launch_bmm(const BmmParams& p, hipStream_t s);
+// token counts from which the bf16 products use 128 x 128 pipelined tiles
+constexpr int64_t kBigT = 256;
 
 // ------------------------------------------------- naive (decompressed) prefill
 // Key decompression, a batched product with both operands contiguous along k:

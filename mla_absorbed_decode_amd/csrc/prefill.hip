@@ -25,6 +25,7 @@
 // from LDS through ds_read_b64_tr_b16. Online softmax in the exp2 domain; the
 // running max is shared by a query's four lanes (two cross-lane exchanges per
 // tile), each lane keeps its own partial sum until the end.
+#include "gemm_tile.h"
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -37,9 +38,10 @@ constexpr int kNtM = 64, kNtN = 64, kNtK = 32;
 // out[t, h, N + r] = pe[t, r] for the tile's tokens, in the workgroups of the
 // first column tile.
 template <class T>
-__device__ __forceinline__ void copy_rope_broadcast(const BmmNtParams& p, int t0, int h) {
+__device__ __forceinline__ void copy_rope_broadcast(const BmmNtParams& p, int t0, int h,
+                                                    int rows = kNtM) {
   if (p.R == 0 || blockIdx.x != 0) return;
-  const int nt = (int)(p.T - t0 < kNtM ? p.T - t0 : kNtM);
+  const int nt = (int)(p.T - t0 < rows ? p.T - t0 : rows);
   const int R = (int)p.R;
   for (int e = threadIdx.x; e < nt * R; e += blockDim.x) {
     const int t = t0 + e / R, r = e % R;
@@ -98,6 +100,21 @@ __global__ void __launch_bounds__(256) bmm_nt_bf16(BmmNtParams p) {
       }
     }
   copy_rope_broadcast<uint16_t>(p, t0, h);
+}
+
+// Prefill-sized token counts: 128 x 128 output tiles of the shared pipelined
+// tile (gemm_tile.h), then the rope rows of the tile's 128 tokens.
+__global__ void __launch_bounds__(256) bmm_nt_big(BmmNtParams p) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[kGLds];
+  const int h = blockIdx.z;
+  GemmTileArgs g;
+  g.a = (const uint16_t*)p.a + (int64_t)h * p.a_sh; g.a_st = p.a_st;
+  g.w = (const uint16_t*)p.w + (int64_t)h * p.w_sh; g.w_s1 = p.w_sn;
+  g.out = (uint16_t*)p.out + (int64_t)h * p.o_sh; g.o_st = p.o_st;
+  g.T = (int)p.T; g.K = (int)p.K; g.N = (int)p.N;
+  g.t0 = blockIdx.y * kGT; g.n0 = blockIdx.x * kGT;
+  gemm_tile_128<true>(g, (MLA_LDS char*)lds_raw);
+  copy_rope_broadcast<uint16_t>(p, g.t0, h, kGT);
 }
 
 // Any size or alignment, bf16 or f32: one thread per output element, f32
@@ -361,7 +378,11 @@ hipError_t launch_bmm_nt(const BmmNtParams& p, hipStream_t s) {
   const bool aligned = ((uintptr_t)p.a % 16 == 0) && ((uintptr_t)p.w % 16 == 0) &&
                        (p.a_st * es % 16 == 0) && (p.a_sh * es % 16 == 0) &&
                        (p.w_sh * es % 16 == 0) && (p.w_sn * es % 16 == 0);
-  if (!p.is_f32 && aligned && p.K % kNtK == 0 && p.K > 0 && p.N > 0) {
+  if (!p.is_f32 && aligned && p.K % kNtK == 0 && p.K > 0 && p.N > 0 && p.T >= kBigT &&
+      p.T <= INT32_MAX && p.K <= INT32_MAX) {
+    dim3 grid((unsigned)((p.N + kGT - 1) / kGT), (unsigned)((p.T + kGT - 1) / kGT), (unsigned)p.H);
+    hipLaunchKernelGGL(bmm_nt_big, grid, dim3(256), 0, s, p);
+  } else if (!p.is_f32 && aligned && p.K % kNtK == 0 && p.K > 0 && p.N > 0) {
     dim3 grid((unsigned)((p.N + kNtN - 1) / kNtN), (unsigned)((p.T + kNtM - 1) / kNtM), (unsigned)p.H);
     hipLaunchKernelGGL(bmm_nt_bf16, grid, dim3(256), 0, s, p);
   } else {

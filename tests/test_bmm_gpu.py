@@ -128,3 +128,59 @@ def test_fp32_folds(T, K, N):
     ref = oracle.v_up(a.cpu().numpy(), w.cpu().numpy())
     got = out.cpu().numpy()
     assert np.abs(got - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
+# prefill-sized token counts take the 128 x 128 pipelined tiles
+@pytest.mark.parametrize("T,H,N", [(256, 4, 512), (300, 3, 512), (700, 2, 512)])
+def test_large_fold_with_rope_concat(T, H, N):
+    say(f"[bmm] large absorb_q T={T} H={H} N={N}")
+    qn_store = rand((H, T, 128), 56)
+    q_nope = qn_store.to(dev()).permute(1, 0, 2)   # the transposed nope operand
+    w = rand((H, 128, N), 67, scale=512 ** -0.5).to(dev())
+    q_pe = rand((T, H, 64), 78).to(dev())
+    q_out = torch.full((T, H, N + 64), float("nan"), dtype=torch.bfloat16, device=dev())
+    mla.mla_absorb_q(q_nope, w, q_pe, q_out)
+    torch.cuda.synchronize()
+    assert torch.equal(q_out[..., N:].view(torch.int16), q_pe.view(torch.int16))
+    ref = oracle.fold_q(q_nope.float().cpu().numpy(), w.float().cpu().numpy())
+    got = q_out[..., :N].float().cpu().numpy()
+    assert worst_rel(got, ref, 1e-2) < 1e-2
+    for _ in range(2):
+        again = torch.full_like(q_out, float("nan"))
+        mla.mla_absorb_q(q_nope, w, q_pe, again)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), q_out.view(torch.int16))
+
+
+def test_large_fold_with_rotated_rope():
+    T, H = 333, 2
+    say(f"[bmm] large absorb_q_rope T={T}")
+    q_nope = rand((T, H, 128), 57).to(dev())
+    w = rand((H, 128, 512), 68, scale=512 ** -0.5).to(dev())
+    q_pe = rand((T, H, 64), 79).to(dev())
+    pos = torch.arange(T, dtype=torch.int32, device=dev()) * 13
+    a = torch.full((T, H, 576), float("nan"), dtype=torch.bfloat16, device=dev())
+    mla.mla_absorb_q_rope(q_nope, w, q_pe, pos, 8e6, a)
+    # the same rotation applied in place, then a plain concat
+    q_rot = q_pe.clone()
+    mla.mla_rope_interleaved(q_rot, pos, 8e6)
+    b = torch.full_like(a, float("nan"))
+    mla.mla_absorb_q(q_nope, w, q_rot, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("T,H,K,N", [(333, 16, 512, 128), (260, 3, 512, 48), (512, 2, 256, 256)])
+def test_large_v_up_transposed_output(T, H, K, N):
+    say(f"[bmm] large v_up T={T} H={H} K={K} N={N}")
+    o_lat = rand((T, H, K), 91).to(dev())
+    w = rand((H, K, N), 92, scale=K ** -0.5).to(dev())
+    store = torch.full((H, T, N + 8), float("nan"), dtype=torch.bfloat16, device=dev())
+    out = store[:, :, :N].transpose(0, 1)           # [T, H, N] view of head-major rows
+    mla.mla_v_up(o_lat, w, out)
+    torch.cuda.synchronize()
+    ref = oracle.v_up(o_lat.float().cpu().numpy(), w.float().cpu().numpy())
+    got = out.float().cpu().numpy()
+    assert not np.isnan(got).any()
+    assert worst_rel(got, ref, 1e-2) < 1e-2
+    assert torch.isnan(store[:, :, N:]).all()

@@ -44,7 +44,8 @@ def _bits(t):
 
 # ------------------------------------------------------------ decompression
 @pytest.mark.parametrize("S,N,P,R,V", [(200, 16, 128, 64, 128), (77, 8, 256, 0, 256),
-                                       (33, 3, 32, 16, 48)])
+                                       (33, 3, 32, 16, 48), (600, 4, 32, 16, 48),
+                                       (300, 2, 256, 0, 256)])
 def test_decompress_kv_matches_oracle(S, N, P, R, V):
     mla = _mla()
     L = 512
@@ -116,7 +117,8 @@ def _run_mha(q, k, v, cu_q, cu_k, scale, causal, max_q=None):
     return out, lse
 
 
-@pytest.mark.parametrize("DK,DV,N", [(192, 128, 4), (256, 256, 3), (128, 128, 2), (64, 64, 2)])
+@pytest.mark.parametrize("DK,DV,N", [(192, 128, 4), (256, 256, 3), (128, 128, 2), (64, 64, 2),
+                                      (192, 128, 8)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_attend_varlen_matches_oracle(DK, DV, N, causal):
     # ragged sequences: one row, a partial tile, exactly one tile, several tiles
