@@ -16,7 +16,8 @@
 // two A and two B loads per four MFMAs).
 //
 // Attention (mha_fwd<DK, DV>): one workgroup per (128 query rows, head,
-// sequence), 16 rows per wave. 32-key tiles of K and V are loaded into
+// sequence): four waves of two 16-row query blocks (eight waves of one for
+// the widest heads). 32-key tiles of K and V are loaded into
 // registers one tile ahead and stored to a two-slot LDS ring (one barrier per
 // tile). Scores are computed transposed, S^T = K Q^T, with the wave's query
 // rows held in registers as the B operand: S^T's accumulator layout (lane l:
@@ -25,6 +26,8 @@
 // from LDS through ds_read_b64_tr_b16. Online softmax in the exp2 domain; the
 // running max is shared by a query's four lanes (two cross-lane exchanges per
 // tile), each lane keeps its own partial sum until the end.
+#include <type_traits>
+
 #include "gemm_tile.h"
 #include "mla_device.h"
 #include "mla_kernels.h"
@@ -146,16 +149,24 @@ __global__ void __launch_bounds__(256) bmm_nt_plain(BmmNtParams p) {
 }
 
 // -------------------------------------------------------------------- attention
-constexpr int kNW = 8;         // waves per workgroup
-constexpr int kQT = 16 * kNW;  // query rows per workgroup (16 per wave)
-constexpr int kKT = 32;        // keys per tile
-constexpr int kThreads = 64 * kNW;
+constexpr int kKT = 32;  // keys per tile
 
-// LDS rows are padded so that the K-operand reads (16 consecutive rows, one
-// 16-byte piece each per 16 lanes) and the transposed V reads (4 consecutive
-// rows x 32 bytes per 16 lanes) fall in distinct banks.
+// Launch shape per head width: NW waves of QB 16-row query blocks each. A
+// wave's query blocks share every K and V^T operand it reads from LDS, which
+// is what bounds this kernel: two blocks halve the LDS bytes per flop. The
+// widest heads keep one block per wave (two would not fit the registers).
 template <int DK, int DV>
 struct MhaShape {
+  // Two blocks per wave (4 waves) passed the parity tests but ran slower than
+  // one block per wave (8 waves) at 192/128 and 128/128 on MI355X: the kernel
+  // waits on its tile loads more than on LDS.
+  static constexpr int QB = 1;                             // query blocks per wave
+  static constexpr int NW = QB == 2 ? 4 : 8;               // waves per workgroup
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int QT = 16 * QB * NW;                  // query rows per workgroup
+  // LDS rows are padded so that the K-operand reads (16 consecutive rows, one
+  // 16-byte piece each per 16 lanes) and the transposed V reads (4
+  // consecutive rows x 32 bytes per 16 lanes) fall in distinct banks.
   static constexpr int KP = DK * 2 + 16;  // K row pitch, bytes
   static constexpr int VP = DV * 2 + 32;  // V row pitch, bytes
   static constexpr int KBYTES = kKT * KP, VBYTES = kKT * VP;
@@ -163,14 +174,21 @@ struct MhaShape {
   static constexpr int LDS = 2 * SLOT;
   static constexpr int KCH = DK / 8, VCH = DV / 8;  // 16-byte pieces per row
   static constexpr int KPC = kKT * KCH, VPC = kKT * VCH;  // pieces per tile
-  static constexpr int NKL = (KPC + kThreads - 1) / kThreads;  // pieces per thread (at most)
-  static constexpr int NVL = (VPC + kThreads - 1) / kThreads;
+  static constexpr int NKL = (KPC + THREADS - 1) / THREADS;  // pieces per thread (at most)
+  static constexpr int NVL = (VPC + THREADS - 1) / THREADS;
   static_assert(DK % 32 == 0 && DV % 16 == 0, "MFMA tiling");
 };
 
+// Rescale threshold of the online softmax (log2 domain): the running maximum
+// a row's probabilities are taken against moves only when a score exceeds it
+// by more than 2^8, so most tiles skip rescaling the output; probabilities
+// stay below 2^8, well inside bf16 and f32 range.
+constexpr float kRescale = 8.f;
+
 template <int DK, int DV>
-__global__ void __launch_bounds__(kThreads) mha_fwd(MhaParams p) {
+__global__ void __launch_bounds__((MhaShape<DK, DV>::THREADS), 2) mha_fwd(MhaParams p) {
   using Sh = MhaShape<DK, DV>;
+  constexpr int QB = Sh::QB, NW = Sh::NW, THREADS = Sh::THREADS, QT = Sh::QT;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -197,162 +215,212 @@ __global__ void __launch_bounds__(kThreads) mha_fwd(MhaParams p) {
   k1 = k1 < 0 ? 0 : (k1 > p.S ? (int)p.S : k1);
   k0 = k0 < 0 ? 0 : (k0 > k1 ? k1 : k0);
   const int lq = q1 - q0, lk = k1 - k0;
-  const int qbase = qt * kQT;
+  const int qbase = qt * QT;
   if (qbase >= lq) return;
   // keys this workgroup needs: up to the last visible key of its last row
   int kend = lk;
   if (p.causal) {
-    const int last = (qbase + kQT < lq ? qbase + kQT : lq) - 1;
+    const int last = (qbase + QT < lq ? qbase + QT : lq) - 1;
     kend = lk - lq + last + 1;
     kend = kend < 0 ? 0 : (kend > lk ? lk : kend);
   }
   const int ntiles = (kend + kKT - 1) / kKT;
 
-  const int qi = qbase + 16 * w + li;  // this lane's query row (index in the sequence)
-  const bool qok = qi < lq;
-  const int pos = lk - lq + qi;
-  const int vis_end = p.causal ? (pos + 1 < lk ? pos + 1 : lk) : lk;  // keys [0, vis_end) visible
+  // this lane's query row in block qb: wrow + 16 qb + li (index in the sequence)
+  const int wrow = qbase + 16 * QB * w;
+  int vis_end[QB];
+  bool qok[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = wrow + 16 * qb + li;
+    qok[qb] = qi < lq;
+    const int pos = lk - lq + qi;
+    vis_end[qb] = p.causal ? (pos + 1 < lk ? pos + 1 : lk) : lk;  // keys [0, vis_end) visible
+  }
   // keys past the wave's last visible key need no arithmetic (wave-uniform)
   int wave_end = 0;
-  if (qbase + 16 * w < lq) {
-    const int wlast = (qbase + 16 * w + 15 < lq ? qbase + 16 * w + 15 : lq - 1);
+  if (wrow < lq) {
+    const int wlast = wrow + 16 * QB - 1 < lq ? wrow + 16 * QB - 1 : lq - 1;
     wave_end = p.causal ? lk - lq + wlast + 1 : lk;
     wave_end = wave_end < 0 ? 0 : (wave_end > lk ? lk : wave_end);
   }
 
-  // the wave's query rows as the B operand: lane holds q[row li][32 kk + 8 g .. + 7]
+  // the wave's query rows as the B operand: lane holds q[row][32 kk + 8 g .. + 7]
   constexpr int KK = DK / 32;
-  i16x8_t qreg[KK];
-  {
-    const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)(q0 + (qok ? qi : 0)) * p.q_s0 +
+  i16x8_t qreg[QB][KK];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = wrow + 16 * qb + li;
+    const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)(q0 + (qok[qb] ? qi : 0)) * p.q_s0 +
                            (int64_t)h * p.q_s1 + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qreg[kk] = qok ? *(const i16x8_t*)(qrow + 32 * kk) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      qreg[qb][kk] = qok[qb] ? *(const i16x8_t*)(qrow + 32 * kk) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
   const uint16_t* kbase = (const uint16_t*)p.k + (int64_t)k0 * p.k_s0 + (int64_t)h * p.k_s1;
   const uint16_t* vbase = (const uint16_t*)p.v + (int64_t)k0 * p.v_s0 + (int64_t)h * p.v_s1;
-  u32x4_t kr[Sh::NKL], vr[Sh::NVL];
+  // two register sets: tile t + 2 is read from memory while tile t is in use
+  // and tile t + 1 waits in the other set for its slot of the LDS ring
+  u32x4_t kr2[2][Sh::NKL], vr2[2][Sh::NVL];
   // global -> registers: piece i of the tile starting at key j0 (rows past the
   // sequence repeat its last key; their scores are masked)
-  auto load_tile = [&](int j0) {
+  auto load_tile = [&](int j0, u32x4_t (&kr)[Sh::NKL], u32x4_t (&vr)[Sh::NVL]) {
 #pragma unroll
     for (int i = 0; i < Sh::NKL; ++i) {
-      const int idx = tid + kThreads * i, r = idx / Sh::KCH, c = idx % Sh::KCH;
+      const int idx = tid + THREADS * i, r = idx / Sh::KCH, c = idx % Sh::KCH;
       const int j = j0 + r < lk ? j0 + r : lk - 1;
       if (idx < Sh::KPC) kr[i] = *(const u32x4_t*)(kbase + (int64_t)j * p.k_s0 + 8 * c);
     }
 #pragma unroll
     for (int i = 0; i < Sh::NVL; ++i) {
-      const int idx = tid + kThreads * i, r = idx / Sh::VCH, c = idx % Sh::VCH;
+      const int idx = tid + THREADS * i, r = idx / Sh::VCH, c = idx % Sh::VCH;
       const int j = j0 + r < lk ? j0 + r : lk - 1;
       if (idx < Sh::VPC) vr[i] = *(const u32x4_t*)(vbase + (int64_t)j * p.v_s0 + 8 * c);
     }
   };
-  auto store_tile = [&](int slot) {
+  auto store_tile = [&](int slot, const u32x4_t (&kr)[Sh::NKL], const u32x4_t (&vr)[Sh::NVL]) {
     MLA_LDS char* kb = smem + slot * Sh::SLOT;
     MLA_LDS char* vb = kb + Sh::KBYTES;
 #pragma unroll
     for (int i = 0; i < Sh::NKL; ++i) {
-      const int idx = tid + kThreads * i, r = idx / Sh::KCH, c = idx % Sh::KCH;
+      const int idx = tid + THREADS * i, r = idx / Sh::KCH, c = idx % Sh::KCH;
       if (idx < Sh::KPC) *(MLA_LDS u32x4_t*)(kb + r * Sh::KP + 16 * c) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < Sh::NVL; ++i) {
-      const int idx = tid + kThreads * i, r = idx / Sh::VCH, c = idx % Sh::VCH;
+      const int idx = tid + THREADS * i, r = idx / Sh::VCH, c = idx % Sh::VCH;
       if (idx < Sh::VPC) *(MLA_LDS u32x4_t*)(vb + r * Sh::VP + 16 * c) = vr[i];
     }
   };
 
   constexpr int DB = DV / 16;
-  f32x4_t o[DB];
+  f32x4_t o[QB][DB];
+  float m[QB], l[QB];
 #pragma unroll
-  for (int d = 0; d < DB; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -__builtin_inff(), l = 0.f;
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d) o[qb][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[qb] = -__builtin_inff();
+    l[qb] = 0.f;
+  }
 
   if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_tile(0, kr2[0], vr2[0]);
+    store_tile(0, kr2[0], vr2[0]);
   }
+  if (ntiles > 1) load_tile(kKT, kr2[1], vr2[1]);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile((t + 1) * kKT);
-    const MLA_LDS char* kb = smem + (t & 1) * Sh::SLOT;
+  // one tile of the loop; SET is t % 2 (a constant, so the register sets stay registers)
+  auto tile_step = [&](int t, auto set_c) {
+    constexpr int SET = decltype(set_c)::value;
+    if (t + 2 < ntiles) load_tile((t + 2) * kKT, kr2[SET], vr2[SET]);
+    const MLA_LDS char* kb = smem + SET * Sh::SLOT;
     const MLA_LDS char* vb = kb + Sh::KBYTES;
     const int j0 = t * kKT;
     if (j0 < wave_end) {
-    // S^T[key 16 kb + 4 g + jj][query li]
-    f32x4_t s[2];
+      // S^T[key 16 kh + 4 g + jj][query li] of each query block, one K read for all
+      f32x4_t s[QB][2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      s[kb2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const MLA_LDS char* krow = kb + (16 * kb2 + li) * Sh::KP + 16 * g;
+      for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        s[kb2] = mfma_16x16x32(*(const MLA_LDS i16x8_t*)(krow + 64 * kk), qreg[kk], s[kb2]);
-    }
-    float x[2][4];
-    float tmax = -__builtin_inff();
+        for (int qb = 0; qb < QB; ++qb) s[qb][kh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const MLA_LDS char* krow = kb + (16 * kh + li) * Sh::KP + 16 * g;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kk = 0; kk < KK; ++kk) {
+          const i16x8_t ka = *(const MLA_LDS i16x8_t*)(krow + 64 * kk);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int key = j0 + 16 * kb2 + 4 * g + jj;
-        x[kb2][jj] = key < vis_end ? s[kb2][jj] * p.scale_log2 : -__builtin_inff();
-        tmax = fmaxf(tmax, x[kb2][jj]);
+          for (int qb = 0; qb < QB; ++qb) s[qb][kh] = mfma_16x16x32(ka, qreg[qb][kk], s[qb][kh]);
+        }
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
-    const float alpha = exp2f(m - muse);
-    m = mnew;
-    float psum = 0.f;
-    uint32_t pk[4];
+      i16x8_t pb[QB];
+      float alpha[QB];
+      bool rescale = false;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const float p0 = exp2f(x[kb2][0] - muse), p1 = exp2f(x[kb2][1] - muse);
-      const float p2 = exp2f(x[kb2][2] - muse), p3 = exp2f(x[kb2][3] - muse);
-      psum += (p0 + p1) + (p2 + p3);
-      pk[2 * kb2] = pack_bf16x2(p0, p1);
-      pk[2 * kb2 + 1] = pack_bf16x2(p2, p3);
+      for (int qb = 0; qb < QB; ++qb) {
+        float x[2][4];
+        float tmax = -__builtin_inff();
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int key = j0 + 16 * kh + 4 * g + jj;
+            x[kh][jj] = key < vis_end[qb] ? s[qb][kh][jj] * p.scale_log2 : -__builtin_inff();
+            tmax = fmaxf(tmax, x[kh][jj]);
+          }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        // move the reference maximum only when this tile exceeds it by more than 2^8
+        const bool move = tmax > m[qb] + kRescale;
+        const float mnew = move ? tmax : m[qb];
+        const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
+        alpha[qb] = move ? exp2f(m[qb] - muse) : 1.f;
+        rescale |= move;
+        m[qb] = mnew;
+        float psum = 0.f;
+        uint32_t pk[4];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const float p0 = exp2f(x[kh][0] - muse), p1 = exp2f(x[kh][1] - muse);
+          const float p2 = exp2f(x[kh][2] - muse), p3 = exp2f(x[kh][3] - muse);
+          psum += (p0 + p1) + (p2 + p3);
+          pk[2 * kh] = pack_bf16x2(p0, p1);
+          pk[2 * kh + 1] = pack_bf16x2(p2, p3);
+        }
+        l[qb] = l[qb] * alpha[qb] + psum;
+        // P^T slots 8 g + i: keys 4 g + i (i < 4) and 16 + 4 g + (i - 4)
+        pb[qb] = __builtin_bit_cast(i16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+      }
+      if (__builtin_amdgcn_ballot_w64(rescale)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[qb][db] *= alpha[qb];
+      }
+      // V^T rows d = 16 db + li from two transposed reads (keys 4 g .. 4 g + 3,
+      // then 16 + 4 g ..), shared by the query blocks
+      const int vr0 = 4 * g + (li >> 2);
+      const MLA_LDS char* vrow0 = vb + vr0 * Sh::VP + 8 * (li & 3);
+      const MLA_LDS char* vrow1 = vrow0 + 16 * Sh::VP;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x4_t a0 = lds_read_tr16(vrow0 + 32 * db);
+        const i16x4_t a1 = lds_read_tr16(vrow1 + 32 * db);
+        const i16x8_t av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma_16x16x32(av, pb[qb], o[qb][db]);
+      }
     }
-    l = l * alpha + psum;
-    // P^T slots 8 g + i: keys 4 g + i (i < 4) and 16 + 4 g + (i - 4)
-    const i16x8_t pb = __builtin_bit_cast(i16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-    // V^T rows d = 16 db + li from two transposed reads (keys 4 g .. 4 g + 3, then 16 + ...)
-    const int vr0 = 4 * g + (li >> 2);
-    const MLA_LDS char* vrow0 = vb + vr0 * Sh::VP + 8 * (li & 3);
-    const MLA_LDS char* vrow1 = vrow0 + 16 * Sh::VP;
+    if (t + 1 < ntiles) store_tile(SET ^ 1, kr2[SET ^ 1], vr2[SET ^ 1]);
+    __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    tile_step(t, std::integral_constant<int, 0>{});
+    tile_step(t + 1, std::integral_constant<int, 1>{});
+  }
+  if (t < ntiles) tile_step(t, std::integral_constant<int, 0>{});
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    // a query's four lanes hold partial sums over their keys
+    float lt = l[qb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (!qok[qb]) continue;
+    const int qi = wrow + 16 * qb + li;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* orow = (uint16_t*)p.out + (int64_t)(q0 + qi) * p.o_s0 + (int64_t)h * p.o_s1 + 4 * g;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const i16x4_t a0 = lds_read_tr16(vrow0 + 32 * db);
-      const i16x4_t a1 = lds_read_tr16(vrow1 + 32 * db);
-      const i16x8_t av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      o[db] = mfma_16x16x32(av, pb, o[db] * alpha);
+      const u32x2_t v = {pack_bf16x2(o[qb][db][0] * inv, o[qb][db][1] * inv),
+                         pack_bf16x2(o[qb][db][2] * inv, o[qb][db][3] * inv)};
+      *(u32x2_t*)(orow + 16 * db) = v;
     }
-    }
-    if (more) store_tile((t + 1) & 1);
-    __syncthreads();
+    if (p.lse && g == 0)
+      p.lse[(int64_t)(q0 + qi) * p.l_s0 + (int64_t)h * p.l_s1] =
+          lt > 0.f ? (m[qb] + __log2f(lt)) * 0.69314718055994530942f : -__builtin_inff();
   }
-
-  // a query's four lanes hold partial sums over their keys
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (!qok) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* orow = (uint16_t*)p.out + (int64_t)(q0 + qi) * p.o_s0 + (int64_t)h * p.o_s1 + 4 * g;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const u32x2_t v = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
-                       pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
-    *(u32x2_t*)(orow + 16 * db) = v;
-  }
-  if (p.lse && g == 0)
-    p.lse[(int64_t)(q0 + qi) * p.l_s0 + (int64_t)h * p.l_s1] =
-        l > 0.f ? (m + __log2f(l)) * 0.69314718055994530942f : -__builtin_inff();
 }
 
 template <int DK, int DV>
@@ -365,8 +433,8 @@ hipError_t launch_mha_t(const MhaParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  dim3 grid((unsigned)((p.max_q + kQT - 1) / kQT), (unsigned)p.n_heads, (unsigned)p.batch);
-  hipLaunchKernelGGL((mha_fwd<DK, DV>), grid, dim3(kThreads), Sh::LDS, s, p);
+  dim3 grid((unsigned)((p.max_q + Sh::QT - 1) / Sh::QT), (unsigned)p.n_heads, (unsigned)p.batch);
+  hipLaunchKernelGGL((mha_fwd<DK, DV>), grid, dim3(Sh::THREADS), Sh::LDS, s, p);
   return hipGetLastError();
 }
 
