@@ -305,3 +305,49 @@ def rope_case(seed=0, n_pos=7, n_vec=5, d_rope=64, dtype=F32, pos_step=13, pos_o
     x = uniform(seed, 60, (n_pos, n_vec, d_rope), -1.0, 1.0, dtype)
     positions = (pos_offset + pos_step * np.arange(n_pos)).astype(np.int32)
     return x, positions
+
+
+# --------------------------------------------------------------------------
+# Sparse fp8 decode (656-byte entries: 512 e4m3 codes, 4 f32 scales, 64 bf16
+# rope values), built the way the sparse-decode page builds its payload.
+DSMLA_ENTRY = 656
+
+
+def dsmla_payload(seed, num_blocks, page, std=0.1, scales="ones"):
+    """[num_blocks, page, 656] uint8 entries: e4m3 codes of N(0, std^2) latent
+    values, scales (all 1, or U[0.5, 2] per 128-code block), bf16 rope values
+    N(0, std^2)."""
+    nope = fp8_codes(stream(seed, 60).standard_normal((num_blocks, page, 512)) * std)
+    if scales == "ones":
+        sc = np.ones((num_blocks, page, 4), dtype=np.float32)
+    else:
+        sc = stream(seed, 61).uniform(0.5, 2.0, (num_blocks, page, 4)).astype(np.float32)
+    rope = round_to((stream(seed, 62).standard_normal((num_blocks, page, 64)) * std)
+                    .astype(np.float32), BF16)
+    rope_bits = torch.from_numpy(rope).to(torch.bfloat16).view(torch.int16).numpy()
+    payload = np.concatenate([nope.view(np.uint8), sc.view(np.uint8),
+                              rope_bits.view(np.uint8)], axis=-1)
+    assert payload.shape[-1] == DSMLA_ENTRY
+    return np.ascontiguousarray(payload)
+
+
+def dsmla_indices(seed, batch, q_len, topk, num_blocks, page, mode="disjoint", fill=0.75):
+    """[batch, q_len, topk] int32 slot lists. ``disjoint``: sequence b takes the
+    first topk slots of its own run of blocks, in order (the page's layout),
+    padded with -1. ``random``: a random subset of ``fill * topk`` distinct slots
+    in random order, the rest -1 at random positions."""
+    idx = np.full((batch, q_len, topk), -1, dtype=np.int32)
+    if mode == "disjoint":
+        per = num_blocks // batch
+        for b in range(batch):
+            slots = np.arange(b * per * page, (b + 1) * per * page, dtype=np.int32)[:topk]
+            idx[b, :, :slots.size] = slots
+        return idx
+    g = stream(seed, 63)
+    n = int(fill * topk)
+    for b in range(batch):
+        for i in range(q_len):
+            slots = g.permutation(num_blocks * page)[:n].astype(np.int32)
+            pos = g.permutation(topk)[:n]
+            idx[b, i, pos] = slots
+    return idx

@@ -96,6 +96,8 @@ def _load():
         lib.mla_oracle_decompress_kv.restype = None
         lib.mla_oracle_mha.argtypes = [i64] * 5 + [dp] * 3 + [ip64, dbl, c_int, dp, dp]
         lib.mla_oracle_mha.restype = None
+        lib.mla_oracle_dsmla_rows.argtypes = [i64, u8p, i64, dp]
+        lib.mla_oracle_dsmla_rows.restype = None
         _lib = lib
     return _lib
 
@@ -451,3 +453,44 @@ def mha_varlen(q, k, v, cu_q, cu_k, scale, causal):
         pos = np.arange(q1 - q0) + (k1 - k0) - (q1 - q0)
         out[q0:q1], lse[q0:q1] = mha(q[q0:q1], k[k0:k1], v[k0:k1], pos, scale, causal)
     return out, lse
+
+
+# ------------------------------------------------------ sparse fp8 decode
+# [P3] test_flashmla_fp8_sparse_decode_unified_slot_view: 656-byte entries
+# (512 e4m3 codes, 4 f32 scales, 64 bf16 rope values) reached through per-token
+# lists of top-k slot indices, -1 for none. Format and reading in mla_oracle.c.
+DSMLA_ENTRY = 656
+
+
+def dsmla_rows(entries):
+    """[..., 656] uint8 entries -> [..., 576] float64 latent rows [c_kv | k_pe]."""
+    e = np.ascontiguousarray(np.asarray(entries, dtype=np.uint8))
+    lead = e.shape[:-1]
+    flat = e.reshape(-1, DSMLA_ENTRY)
+    rows = np.zeros((max(flat.shape[0], 1), 576))
+    _load().mla_oracle_dsmla_rows(flat.shape[0], _u8p(flat if flat.size else np.zeros(
+        (1, DSMLA_ENTRY), np.uint8)), DSMLA_ENTRY, _dp(rows))
+    return rows[:flat.shape[0]].reshape(lead + (576,))
+
+
+def sparse_decode(q, pool_entries, indices, scale, L=512):
+    """Sparse absorbed decode: query token (b, i) of q [B,Sq,N,576] attends over
+    the latent rows at the slots indices[b,i,:] (slot = block * page + offset
+    into pool_entries [NB,PG,656]); slots < 0 or past the pool are no key; a
+    slot listed twice is two keys. Returns (o_lat [B,Sq,N,L], lse [B,Sq,N])."""
+    q = _f64(q)
+    B, Sq, N, E = q.shape
+    pool = dsmla_rows(pool_entries)
+    NB, PG = pool.shape[:2]
+    flat = pool.reshape(NB * PG, E)
+    idx = np.asarray(indices, dtype=np.int64)
+    o = np.zeros((B, Sq, N, L))
+    lse = np.full((B, Sq, N), -np.inf)
+    for b in range(B):
+        for i in range(Sq):
+            sl = idx[b, i]
+            sl = sl[(sl >= 0) & (sl < NB * PG)]
+            if sl.size == 0:
+                continue
+            o[b, i], lse[b, i], _ = attend_seq(q[b, i][None], flat[sl], [0], scale, False, L)
+    return o, lse

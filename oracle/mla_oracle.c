@@ -603,3 +603,35 @@ void mla_oracle_mha(int64_t nq, int64_t t_kv, int64_t n_head, int64_t DK, int64_
     free(s);
   }
 }
+
+/* ---------------------------------------------------------------------------
+ * Sparse fp8 decode entries ([P3] test_flashmla_fp8_sparse_decode_unified_slot_view,
+ * the DeepSeek V3.2 DSA path): a latent row is stored as one 656-byte entry,
+ *   bytes   0..511  512 e4m3fn codes of c_kv,
+ *   bytes 512..527  4 f32 scales (little-endian), scale j for codes 128j..128j+127,
+ *   bytes 528..655  64 bf16 values of k_pe (little-endian).
+ * Reading (the page builds the payload but does not print the kernel): the
+ * latent value of code i is e4m3(code_i) * scale[i / 128]; the rope part is
+ * the bf16 values as stored. The row [c_kv (512) | k_pe (64)] then enters the
+ * absorbed attention unchanged.
+ *   entries [n, 656] bytes (row i at entries + i * stride)   rows [n, 576]
+ * ------------------------------------------------------------------------- */
+void mla_oracle_dsmla_rows(int64_t n, const uint8_t* entries, int64_t stride, double* rows) {
+  for (int64_t i = 0; i < n; ++i) {
+    const uint8_t* e = entries + i * stride;
+    double* r = rows + i * 576;
+    for (int j = 0; j < 4; ++j) {
+      uint32_t bits = (uint32_t)e[512 + 4 * j] | ((uint32_t)e[513 + 4 * j] << 8) |
+                      ((uint32_t)e[514 + 4 * j] << 16) | ((uint32_t)e[515 + 4 * j] << 24);
+      float sc;
+      memcpy(&sc, &bits, 4);
+      for (int c = 0; c < 128; ++c) r[128 * j + c] = mla_oracle_e4m3_decode(e[128 * j + c]) * (double)sc;
+    }
+    for (int c = 0; c < 64; ++c) {
+      const uint32_t bits = ((uint32_t)e[528 + 2 * c] | ((uint32_t)e[529 + 2 * c] << 8)) << 16;
+      float v;
+      memcpy(&v, &bits, 4);
+      r[512 + c] = (double)v;
+    }
+  }
+}

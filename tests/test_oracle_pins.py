@@ -687,3 +687,66 @@ def test_mha_varlen_equals_per_sequence_calls():
                                                                     True)[0], rtol=1e-11, atol=1e-12)
     # sequence 3 has 2 queries on 1 key: its first query sees nothing
     assert np.all(out[cu_q[3]] == 0.0) and np.isneginf(lse[cu_q[3]]).all()
+
+
+# ------------------------------------------------------- sparse fp8 decode
+def test_dsmla_rows_against_torch_views():
+    """Entry decode against torch's own float8_e4m3fn and bfloat16 views of the
+    bytes and numpy's float32 view of the scales."""
+    e = mi.dsmla_payload(3, 2, 16, scales="random").reshape(-1, oracle.DSMLA_ENTRY)
+    rows = oracle.dsmla_rows(e)
+    codes = torch.from_numpy(e[:, :512].copy()).view(torch.float8_e4m3fn).double().numpy()
+    sc = np.frombuffer(e[:, 512:528].tobytes(), dtype=np.float32).reshape(-1, 4).astype(np.float64)
+    rope = torch.from_numpy(e[:, 528:].copy()).view(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(rows[:, :512], codes * np.repeat(sc, 128, axis=1))
+    np.testing.assert_array_equal(rows[:, 512:], rope)
+    # scale j governs codes 128j .. 128j + 127 only
+    e2 = e.copy()
+    e2[:, 516:520] = np.frombuffer(np.float32(3.0).tobytes(), np.uint8)
+    r2 = oracle.dsmla_rows(e2)
+    np.testing.assert_array_equal(r2[:, 128:256], codes[:, 128:256] * 3.0)
+    np.testing.assert_array_equal(r2[:, :128], rows[:, :128])
+
+
+def test_sparse_decode_with_every_slot_equals_dense_decode():
+    """Indices listing a sequence's slots in order give the dense paged decode
+    over the same decoded rows (the page's sparse call reads the cache the
+    dense call reads, through an index list instead of a block table)."""
+    B, N, NB, PG = 2, 4, 8, 16
+    pool = mi.dsmla_payload(4, NB, PG, scales="random")
+    q = mi.normal(4, 64, (B, 1, N, 576), 0.1, mi.BF16)
+    lens = [37, 64]
+    bt = np.array([[0, 1, 2, 3], [4, 5, 6, 7]], dtype=np.int32)
+    idx = np.full((B, 1, 80), -1, dtype=np.int32)
+    for b in range(B):
+        slots = (bt[b, np.arange(lens[b]) // PG] * PG + np.arange(lens[b]) % PG)
+        idx[b, 0, :lens[b]] = slots
+    o, lse = oracle.sparse_decode(q, pool, idx, 576 ** -0.5)
+    od, lsed = oracle.attend_paged(q, oracle.dsmla_rows(pool), bt, lens, 576 ** -0.5, True, 512)
+    np.testing.assert_allclose(o, od, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(lse, lsed, rtol=1e-13)
+
+
+def test_sparse_decode_index_list_invariants():
+    B, Sq, N, NB, PG, K = 2, 2, 3, 4, 16, 24
+    pool = mi.dsmla_payload(5, NB, PG)
+    q = mi.normal(5, 64, (B, Sq, N, 576), 0.1, mi.BF16)
+    idx = mi.dsmla_indices(5, B, Sq, K, NB, PG, mode="random")
+    o, lse = oracle.sparse_decode(q, pool, idx, 0.05)
+    # order of the list does not matter; -1 and out-of-pool entries are no key
+    perm = np.concatenate([idx[:, :, ::-1], np.full((B, Sq, 1), NB * PG + 5, np.int32)], 2)
+    o2, lse2 = oracle.sparse_decode(q, pool, perm, 0.05)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13)
+    # every slot twice: the same output, lse grows by ln 2
+    o3, lse3 = oracle.sparse_decode(q, pool, np.concatenate([idx, idx], 2), 0.05)
+    np.testing.assert_allclose(o3, o, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(lse3, lse + math.log(2.0), rtol=1e-12)
+    # no key at all: 0 and -inf
+    o4, lse4 = oracle.sparse_decode(q, pool, np.full((B, Sq, 4), -1, np.int32), 0.05)
+    assert np.all(o4 == 0.0) and np.all(np.isneginf(lse4))
+    # one key: that key's latent row exactly
+    one = np.full((B, Sq, 3), -1, np.int32)
+    one[:, :, 1] = 7
+    o5, _ = oracle.sparse_decode(q, pool, one, 0.05)
+    np.testing.assert_array_equal(o5[0, 0, 0], oracle.dsmla_rows(pool)[0, 7, :512])
