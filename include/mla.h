@@ -397,6 +397,38 @@ int mla_prefill_attend(const mla_tensor* q, const mla_tensor* k, const mla_tenso
                        int64_t max_seqlen_q, float softmax_scale, int32_t causal,
                        const mla_tensor* out, const mla_tensor* lse, mla_stream stream);
 
+/*
+ * mla_sparse_decode_fp8 -- sparse absorbed decode over an fp8 cache of
+ * 656-byte entries (vLLM "tests/kernels/attention/
+ * test_mla_cross_layer_kernel_equivalence.py",
+ * test_flashmla_fp8_sparse_decode_unified_slot_view: the DeepSeek V3.2 DSA
+ * decode with per-token top-k slot indices padded with -1). An entry holds
+ *   bytes   0..511  512 e4m3fn codes of c_kv,
+ *   bytes 512..527  4 f32 scales, scale j for codes 128 j .. 128 j + 127,
+ *   bytes 528..655  64 bf16 rope values;
+ * latent value i is e4m3(code_i) * scale[i / 128]. Query token (b, i) attends
+ * over the rows at the slots indices[b, i, :] (slot = block * PG + offset):
+ *   s_j      = softmax_scale * sum_e q[b, i, h, e] * row_j[e]   (e < 576)
+ *   out[...] = sum_j softmax(s)_j * row_j[0:512]
+ *   lse      = natural log of sum_j exp(s_j)
+ * Slots < 0 or >= NB * PG are no key; a slot listed twice is two keys; a
+ * token with no key gets out = 0 and lse = -inf. No causal rule applies: the
+ * list is the visibility.
+ *
+ *   q         [B, Sq, N, 576]  MLA_BF16, any strides (inner 1), rows 16-byte aligned
+ *   kv_cache  [NB, PG, 656]    MLA_FP8_E4M3 (bytes; strides in bytes), entries
+ *                              16-byte aligned; block-major views allowed
+ *   indices   [B, Sq, topk]    MLA_I32, any strides (inner 1), topk <= 4096
+ *   out       [B, Sq, N, 512]  MLA_BF16, rows 8-byte aligned
+ *   lse       [B, Sq, N]       MLA_F32, or NULL
+ * Each dequantized value is rounded once to bf16 before the bf16 MFMA
+ * products (f32 accumulation). Outputs for a block-major view equal those of a
+ * contiguous copy bit for bit.
+ */
+int mla_sparse_decode_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
+                          const mla_tensor* indices, float softmax_scale, const mla_tensor* out,
+                          const mla_tensor* lse, mla_stream stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* mla_status_str(int status);
 

@@ -113,11 +113,13 @@ def load() -> ctypes.CDLL:
         lib.mla_decode_attend_fp8.argtypes = [P, P, P, P, i64, f32, i32, vp, vp, P, P, vp, sz, vp]
         lib.mla_decompress_kv.argtypes = [P, P, P, P, P, P, vp]
         lib.mla_prefill_attend.argtypes = [P, P, P, P, P, i64, f32, i32, P, P, vp]
+        lib.mla_sparse_decode_fp8.argtypes = [P, P, P, f32, P, P, vp]
         for fn in ("mla_concat_and_cache_fp8", "mla_decode_attend_fp8", "mla_absorb_q",
                    "mla_concat_and_cache", "mla_decode_workspace_size",
                    "mla_decode_attend", "mla_v_up", "mla_rope_interleaved", "mla_absorb_q_rope",
                    "mla_concat_and_cache_rope", "mla_absorb_q_and_cache",
-                   "mla_decode_attend_v_up", "mla_decompress_kv", "mla_prefill_attend"):
+                   "mla_decode_attend_v_up", "mla_decompress_kv", "mla_prefill_attend",
+                   "mla_sparse_decode_fp8"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_status_str.argtypes = [ctypes.c_int]
         lib.mla_status_str.restype = ctypes.c_char_p
@@ -354,4 +356,16 @@ def mla_prefill_attend(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, softma
                                   int(max_seqlen_q), float(softmax_scale), int(bool(causal)),
                                   _ref(desc(out)), _ref(desc(lse)), _stream(out)),
            "mla_prefill_attend")
+    return out
+
+
+def mla_sparse_decode_fp8(q, kv_cache, indices, softmax_scale, out, lse=None):
+    """Sparse decode: token (b, i) of q [B,Sq,N,576] attends over the 656-byte
+    entries of kv_cache [NB,PG,656] (uint8) at the slots indices[b,i,:] (-1: none).
+    Writes out [B,Sq,N,512] and lse [B,Sq,N]."""
+    _device_check(q, kv_cache, indices, out, lse)
+    lib = load()
+    _check(lib.mla_sparse_decode_fp8(_ref(desc(q)), _ref(desc(kv_cache)), _ref(desc(indices)),
+                                     float(softmax_scale), _ref(desc(out)), _ref(desc(lse)),
+                                     _stream(out)), "mla_sparse_decode_fp8")
     return out

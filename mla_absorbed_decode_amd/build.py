@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmla.so")
 
-SOURCES = ["mla_abi.cpp", "cache_write.hip", "bmm.hip", "decode.hip", "rope.hip", "prefill.hip"]
+SOURCES = ["mla_abi.cpp", "cache_write.hip", "bmm.hip", "decode.hip", "rope.hip", "prefill.hip", "sparse.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -585,4 +585,44 @@ int mla_prefill_attend(const mla_tensor* q, const mla_tensor* k, const mla_tenso
   return launched(mla::launch_mha(p, (hipStream_t)stream));
 }
 
+int mla_sparse_decode_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
+                          const mla_tensor* indices, float softmax_scale, const mla_tensor* out,
+                          const mla_tensor* lse, mla_stream stream) {
+  int rc;
+  if ((rc = check_desc(q, 4)) || (rc = check_desc(kv_cache, 3)) || (rc = check_desc(indices, 3)) ||
+      (rc = check_desc(out, 4)))
+    return rc;
+  if (lse && (rc = check_desc(lse, 3))) return rc;
+  if (q->dtype != MLA_BF16 || out->dtype != MLA_BF16 || kv_cache->dtype != MLA_FP8_E4M3 ||
+      indices->dtype != MLA_I32 || (lse && lse->dtype != MLA_F32))
+    return MLA_ERR_DTYPE;
+  const int64_t B = q->shape[0], Sq = q->shape[1], N = q->shape[2], E = q->shape[3];
+  const int64_t NB = kv_cache->shape[0], PG = kv_cache->shape[1], K = indices->shape[2];
+  if (out->shape[0] != B || out->shape[1] != Sq || out->shape[2] != N) return MLA_ERR_SHAPE;
+  if (indices->shape[0] != B || indices->shape[1] != Sq) return MLA_ERR_SHAPE;
+  if (lse && (lse->shape[0] != B || lse->shape[1] != Sq || lse->shape[2] != N)) return MLA_ERR_SHAPE;
+  // the 656-byte entry of 512 e4m3 codes, 4 f32 scales and 64 bf16 rope values
+  if (E != 576 || out->shape[3] != 512 || kv_cache->shape[2] != 656) return MLA_ERR_UNSUPPORTED;
+  if (K > mla::kSparseMaxTopk || PG <= 0 || PG > INT32_MAX || B * Sq > INT32_MAX ||
+      N > 65535 * 64)
+    return MLA_ERR_UNSUPPORTED;
+  if (!rows_aligned16(q) || !rows_aligned16(kv_cache) || !rows_aligned(out, 8))
+    return MLA_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0 || N == 0) return MLA_OK;
+  mla::SparseParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q->data; p.q_s0 = q->stride[0]; p.q_s1 = q->stride[1]; p.q_s2 = q->stride[2];
+  p.kv = (const uint8_t*)kv_cache->data; p.kv_s0 = kv_cache->stride[0]; p.kv_s1 = kv_cache->stride[1];
+  p.num_slots = NB * PG; p.page = (int)PG;
+  p.idx = (const int32_t*)indices->data; p.i_s0 = indices->stride[0]; p.i_s1 = indices->stride[1];
+  p.topk = (int)K;
+  p.out = out->data; p.o_s0 = out->stride[0]; p.o_s1 = out->stride[1]; p.o_s2 = out->stride[2];
+  if (lse) {
+    p.lse = (float*)lse->data; p.l_s0 = lse->stride[0]; p.l_s1 = lse->stride[1]; p.l_s2 = lse->stride[2];
+  }
+  p.batch = (int)B; p.q_len = (int)Sq; p.n_heads = (int)N;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  return launched(mla::launch_sparse(p, (hipStream_t)stream));
+}
+
 }  // extern "C"

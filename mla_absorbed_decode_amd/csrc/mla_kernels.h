@@ -102,6 +102,24 @@ struct MhaParams {
 hipError_t launch_mha(const MhaParams& p, hipStream_t s);
 bool mha_supported(int dk, int dv);
 
+// ------------------------------------------------------ sparse fp8 decode
+// Query token (b, i) attends over the latent rows at the slots idx[b, i, :]
+// of a cache of 656-byte entries (512 e4m3 codes, 4 f32 scales, 64 bf16 rope
+// values); slots < 0 or >= num_slots are no key.
+constexpr int kSparseMaxTopk = 4096;  // slot list held in LDS
+struct SparseParams {
+  const void* q;     int64_t q_s0, q_s1, q_s2;   // [B, Sq, N, 576] bf16
+  const uint8_t* kv; int64_t kv_s0, kv_s1;       // [NB, PG, 656] bytes (strides in bytes)
+  int64_t num_slots; int page;                   // NB * PG, PG
+  const int32_t* idx; int64_t i_s0, i_s1;        // [B, Sq, topk]
+  int topk;
+  void* out;         int64_t o_s0, o_s1, o_s2;   // [B, Sq, N, 512] bf16
+  float* lse;        int64_t l_s0, l_s1, l_s2;   // [B, Sq, N] or NULL
+  int batch, q_len, n_heads;
+  float scale_log2;                              // softmax scale * log2(e)
+};
+hipError_t launch_sparse(const SparseParams& p, hipStream_t s);
+
 // ------------------------------------------------------------------ decode
 // Division of 32-bit unsigned integers by a fixed d >= 1 as a multiply-high,
 // an add and two shifts (Granlund and Montgomery, "Division by invariant

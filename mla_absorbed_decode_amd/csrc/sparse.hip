@@ -1,0 +1,237 @@
+// sparse.hip -- sparse absorbed decode over an fp8 latent cache of 656-byte
+// entries, each query token attending over its own list of slots (vLLM
+// "tests/kernels/attention/test_mla_cross_layer_kernel_equivalence.py",
+// test_flashmla_fp8_sparse_decode_unified_slot_view: the DeepSeek V3.2 DSA
+// decode reads 128 heads x 576 against top-k slot lists padded with -1).
+//
+// Entry layout (bytes): 0..511 e4m3fn codes of c_kv, 512..527 four f32
+// scales (scale j for codes 128 j .. 128 j + 127), 528..655 64 bf16 rope
+// values. Latent value i = e4m3(code_i) * scale[i / 128].
+//
+// One workgroup per (query token, 64 heads): four waves of 16 heads. The
+// token's slot list goes to LDS once (invalid slots as -1). Keys stream in
+// tiles of 32 entries: each thread reads its 16-byte pieces of the next tile
+// into registers while the current tile is in use; at the tile boundary the
+// e4m3 pieces are widened, multiplied by their block's scale and rounded to
+// bf16 (the rope pieces are copied), forming a [32, 576] bf16 tile in a
+// two-slot LDS ring. The arithmetic is the prefill attention's: S^T = K Q^T
+// with the heads' queries in registers, P^T straight from S^T's
+// accumulators, O^T += V^T P^T with V^T (the first 512 columns of the same
+// rows) read by ds_read_b64_tr_b16, online softmax in the exp2 domain.
+#include "mla_device.h"
+#include "mla_kernels.h"
+
+namespace mla {
+namespace {
+
+constexpr int kSE = 656;       // entry bytes
+constexpr int kSKT = 32;       // entries per tile
+constexpr int kSP = 1152 + 16; // LDS row pitch: 576 bf16 + 16 bytes of padding
+constexpr int kSSlot = kSKT * kSP;
+constexpr int kSPieces = 40;   // 16-byte pieces per entry read: 32 of codes, 8 of rope
+constexpr int kSTasks = (kSKT * kSPieces + 255) / 256;  // per thread, per tile
+constexpr float kSRescale = 8.f;
+
+// 8 e4m3 codes times a scale, as 8 bf16 values (round to nearest even)
+__device__ __forceinline__ u32x4_t fp8x8_scaled_bf16(uint32_t lo, uint32_t hi, float s) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+  const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  return u32x4_t{pack_bf16x2(a[0] * s, a[1] * s), pack_bf16x2(b[0] * s, b[1] * s),
+                 pack_bf16x2(c[0] * s, c[1] * s), pack_bf16x2(d[0] * s, d[1] * s)};
+}
+
+__global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  MLA_LDS char* ring = (MLA_LDS char*)smem_raw;
+  MLA_LDS int32_t* slots = (MLA_LDS int32_t*)(ring + 2 * kSSlot);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bi = blockIdx.x;  // query token b * Sq + i
+  const int b = bi / p.q_len, qi = bi - b * p.q_len;
+  const int h = (int)blockIdx.y * 64 + 16 * w + li;  // this lane's head
+  const bool hok = h < p.n_heads;
+
+  // the slot list, invalid entries as -1
+  const int32_t* idx = p.idx + (int64_t)b * p.i_s0 + (int64_t)qi * p.i_s1;
+  for (int j = tid; j < p.topk; j += 256) {
+    const int32_t s = idx[j];
+    slots[j] = (s >= 0 && (int64_t)s < p.num_slots) ? s : -1;
+  }
+
+  // the head's query row as the B operand: lane holds q[h][32 kk + 8 g .. + 7]
+  constexpr int KK = 576 / 32;
+  i16x8_t qreg[KK];
+  {
+    const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.q_s0 + (int64_t)qi * p.q_s1 +
+                           (int64_t)(hok ? h : 0) * p.q_s2 + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qreg[kk] = hok ? *(const i16x8_t*)(qrow + 32 * kk) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  __syncthreads();  // the slot list is in LDS
+
+  const int ntiles = (p.topk + kSKT - 1) / kSKT;
+  // task n of this thread: piece c of entry r of the tile
+  u32x4_t raw[kSTasks];
+  float rsc[kSTasks];
+  uint32_t nokey = 0;  // bit n: task n belongs to an entry that is no key
+  auto load_tile = [&](int t) {
+    nokey = 0;
+#pragma unroll
+    for (int n = 0; n < kSTasks; ++n) {
+      const int id = tid + 256 * n;
+      if (id >= kSKT * kSPieces) break;
+      const int r = id / kSPieces, c = id - r * kSPieces;
+      const int j = t * kSKT + r;
+      int s = j < p.topk ? slots[j] : -1;
+      if (s < 0) {  // no key: read a valid entry, store zeros in its place
+        s = 0;
+        nokey |= 1u << n;
+      }
+      const int blk = s / p.page, off = s - blk * p.page;
+      const uint8_t* e = p.kv + (int64_t)blk * p.kv_s0 + (int64_t)off * p.kv_s1;
+      raw[n] = *(const u32x4_t*)(e + (c < 32 ? 16 * c : 528 + 16 * (c - 32)));
+      rsc[n] = c < 32 ? *(const float*)(e + 512 + 4 * (c >> 3)) : 1.f;
+    }
+  };
+  auto store_tile = [&](int slot) {
+    MLA_LDS char* kb = ring + slot * kSSlot;
+#pragma unroll
+    for (int n = 0; n < kSTasks; ++n) {
+      const int id = tid + 256 * n;
+      if (id >= kSKT * kSPieces) break;
+      const int r = id / kSPieces, c = id - r * kSPieces;
+      MLA_LDS char* row = kb + r * kSP;
+      if (nokey & (1u << n)) {  // zeros, so that no bits of an unused entry reach P V
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        if (c < 32) {
+          *(MLA_LDS u32x4_t*)(row + 32 * c) = z;
+          *(MLA_LDS u32x4_t*)(row + 32 * c + 16) = z;
+        } else {
+          *(MLA_LDS u32x4_t*)(row + 1024 + 16 * (c - 32)) = z;
+        }
+      } else if (c < 32) {
+        *(MLA_LDS u32x4_t*)(row + 32 * c) = fp8x8_scaled_bf16(raw[n][0], raw[n][1], rsc[n]);
+        *(MLA_LDS u32x4_t*)(row + 32 * c + 16) = fp8x8_scaled_bf16(raw[n][2], raw[n][3], rsc[n]);
+      } else {
+        *(MLA_LDS u32x4_t*)(row + 1024 + 16 * (c - 32)) = raw[n];
+      }
+    }
+  };
+
+  constexpr int DB = 512 / 16;
+  f32x4_t o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_inff(), l = 0.f;
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(t + 1);
+    const MLA_LDS char* kb = ring + (t & 1) * kSSlot;
+    const int j0 = t * kSKT;
+    // S^T[key 16 kh + 4 g + jj][head li]
+    f32x4_t s[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      s[kh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const MLA_LDS char* krow = kb + (16 * kh + li) * kSP + 16 * g;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s[kh] = mfma_16x16x32(*(const MLA_LDS i16x8_t*)(krow + 64 * kk), qreg[kk], s[kh]);
+    }
+    float x[2][4];
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = j0 + 16 * kh + 4 * g + jj;
+        const bool ok = j < p.topk && slots[j < p.topk ? j : 0] >= 0;
+        x[kh][jj] = ok ? s[kh][jj] * p.scale_log2 : -__builtin_inff();
+        tmax = fmaxf(tmax, x[kh][jj]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // the reference maximum moves only when a tile exceeds it by more than 2^8
+    const bool move = tmax > m + kSRescale;
+    const float mnew = move ? tmax : m;
+    const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
+    const float alpha = move ? exp2f(m - muse) : 1.f;
+    m = mnew;
+    float psum = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const float p0 = exp2f(x[kh][0] - muse), p1 = exp2f(x[kh][1] - muse);
+      const float p2 = exp2f(x[kh][2] - muse), p3 = exp2f(x[kh][3] - muse);
+      psum += (p0 + p1) + (p2 + p3);
+      pk[2 * kh] = pack_bf16x2(p0, p1);
+      pk[2 * kh + 1] = pack_bf16x2(p2, p3);
+    }
+    l = l * alpha + psum;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    // P^T slots 8 g + i: keys 4 g + i (i < 4) and 16 + 4 g + (i - 4)
+    const i16x8_t pb = __builtin_bit_cast(i16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+    const MLA_LDS char* vrow0 = kb + (4 * g + (li >> 2)) * kSP + 8 * (li & 3);
+    const MLA_LDS char* vrow1 = vrow0 + 16 * kSP;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4_t a0 = lds_read_tr16(vrow0 + 32 * db);
+      const i16x4_t a1 = lds_read_tr16(vrow1 + 32 * db);
+      const i16x8_t av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      o[db] = mfma_16x16x32(av, pb, o[db]);
+    }
+    if (more) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // a head's four lanes hold partial sums over their keys
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!hok) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* orow = (uint16_t*)p.out + (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 +
+                   (int64_t)h * p.o_s2 + 4 * g;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const u32x2_t v = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
+                       pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
+    *(u32x2_t*)(orow + 16 * db) = v;
+  }
+  if (p.lse && g == 0)
+    p.lse[(int64_t)b * p.l_s0 + (int64_t)qi * p.l_s1 + (int64_t)h * p.l_s2] =
+        l > 0.f ? (m + __log2f(l)) * 0.69314718055994530942f : -__builtin_inff();
+}
+
+}  // namespace
+
+size_t sparse_lds_bytes(int topk) { return 2 * (size_t)kSSlot + 4 * (size_t)(topk > 0 ? topk : 1); }
+
+hipError_t launch_sparse(const SparseParams& p, hipStream_t s) {
+  if (p.batch == 0 || p.q_len == 0 || p.n_heads == 0) return hipSuccess;
+  const size_t lds = sparse_lds_bytes(p.topk);
+  static size_t attr = 0;
+  if (lds > attr) {
+    const hipError_t e = hipFuncSetAttribute((const void*)sparse_fp8_decode,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)(2 * kSSlot + 4 * kSparseMaxTopk));
+    if (e != hipSuccess) return e;
+    attr = 2 * kSSlot + 4 * kSparseMaxTopk;
+  }
+  dim3 grid((unsigned)((int64_t)p.batch * p.q_len), (unsigned)((p.n_heads + 63) / 64));
+  hipLaunchKernelGGL(sparse_fp8_decode, grid, dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
                           "mla_rope_interleaved", "mla_absorb_q_rope", "mla_concat_and_cache_rope",
                           "mla_absorb_q_and_cache", "mla_decode_attend_v_up",
                           "mla_concat_and_cache_fp8", "mla_decode_attend_fp8",
-                          "mla_decompress_kv", "mla_prefill_attend"}
+                          "mla_decompress_kv", "mla_prefill_attend", "mla_sparse_decode_fp8"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -378,3 +378,26 @@ def test_prefill_attend_validation(lib):
     # nothing to do
     assert f(q, k, v, T([1], I32), T([1], I32), out) == OK        # no sequence
     assert f(q, k, v, cq, ck, out, max_q=0) == OK
+
+
+# ------------------------------------------------------------ sparse fp8 decode
+
+
+def test_sparse_decode_validation(lib):
+    def f(q, kv, idx, out, lse=None):
+        return lib.mla_sparse_decode_fp8(R(q), R(kv), R(idx), 0.04, R(out), R(lse), None)
+    B, Sq, N = 2, 1, 128
+    q, kv, idx = T([B, Sq, N, 576]), T([32, 64, 656], FP8), T([B, Sq, 128], I32)
+    out, lse = T([B, Sq, N, 512]), T([B, Sq, N], F32)
+    assert f(q, kv, idx, out, T([B, Sq, 64], F32)) == SHAPE
+    assert f(q, kv, T([B, 2, 128], I32), out) == SHAPE
+    assert f(q, kv, idx, T([B, Sq, N - 1, 512])) == SHAPE
+    assert f(q, T([32, 64, 656], BF16), idx, out) == DTYPE
+    assert f(q, kv, T([B, Sq, 128], I64), out) == DTYPE
+    assert f(T([B, Sq, N, 576], F32), kv, idx, T([B, Sq, N, 512], F32)) == DTYPE
+    assert f(q, T([32, 64, 576], FP8), idx, out) == UNSUP               # not a 656-byte entry
+    assert f(T([B, Sq, N, 512]), kv, idx, out) == UNSUP                  # no rope part
+    assert f(q, kv, T([B, Sq, 8192], I32), out) == UNSUP                 # top-k past the LDS list
+    assert f(q, T([32, 64, 656], FP8, strides=[64 * 656 + 8, 656, 1]), idx, out) == UNSUP
+    assert f(None, kv, idx, out) == NULL
+    assert f(T([0, Sq, N, 576]), kv, T([0, Sq, 128], I32), T([0, Sq, N, 512])) == OK
