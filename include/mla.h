@@ -421,13 +421,28 @@ int mla_prefill_attend(const mla_tensor* q, const mla_tensor* k, const mla_tenso
  *   indices   [B, Sq, topk]    MLA_I32, any strides (inner 1), topk <= 4096
  *   out       [B, Sq, N, 512]  MLA_BF16, rows 8-byte aligned
  *   lse       [B, Sq, N]       MLA_F32, or NULL
+ *   workspace  device buffer of at least mla_sparse_workspace_size(B * Sq, N,
+ *              topk) bytes (NULL allowed when that is 0), else MLA_ERR_WORKSPACE
  * Each dequantized value is rounded once to bf16 before the bf16 MFMA
  * products (f32 accumulation). Outputs for a block-major view equal those of a
- * contiguous copy bit for bit.
+ * contiguous copy bit for bit, and reruns are bit-identical (the split plan
+ * depends only on the sizes; splits merge in order).
  */
 int mla_sparse_decode_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
                           const mla_tensor* indices, float softmax_scale, const mla_tensor* out,
-                          const mla_tensor* lse, mla_stream stream);
+                          const mla_tensor* lse, void* workspace, size_t workspace_bytes,
+                          mla_stream stream);
+
+/*
+ * mla_sparse_workspace_size -- bytes of device workspace mla_sparse_decode_fp8
+ * needs for `tokens` = B * Sq query tokens of n_heads heads and top-k lists
+ * (0 when the call runs unsplit; then workspace may be NULL). When the tokens
+ * and head groups alone would leave the chip idle, each slot list is split
+ * over several workgroups, whose f32 partials and lse the workspace holds
+ * until the merge. Caller-owned, 16-byte aligned, needs no initialisation,
+ * carries nothing between calls.
+ */
+int mla_sparse_workspace_size(int64_t tokens, int64_t n_heads, int64_t topk, size_t* bytes);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* mla_status_str(int status);

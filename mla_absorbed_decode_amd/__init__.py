@@ -113,13 +113,14 @@ def load() -> ctypes.CDLL:
         lib.mla_decode_attend_fp8.argtypes = [P, P, P, P, i64, f32, i32, vp, vp, P, P, vp, sz, vp]
         lib.mla_decompress_kv.argtypes = [P, P, P, P, P, P, vp]
         lib.mla_prefill_attend.argtypes = [P, P, P, P, P, i64, f32, i32, P, P, vp]
-        lib.mla_sparse_decode_fp8.argtypes = [P, P, P, f32, P, P, vp]
+        lib.mla_sparse_decode_fp8.argtypes = [P, P, P, f32, P, P, vp, sz, vp]
+        lib.mla_sparse_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
         for fn in ("mla_concat_and_cache_fp8", "mla_decode_attend_fp8", "mla_absorb_q",
                    "mla_concat_and_cache", "mla_decode_workspace_size",
                    "mla_decode_attend", "mla_v_up", "mla_rope_interleaved", "mla_absorb_q_rope",
                    "mla_concat_and_cache_rope", "mla_absorb_q_and_cache",
                    "mla_decode_attend_v_up", "mla_decompress_kv", "mla_prefill_attend",
-                   "mla_sparse_decode_fp8"):
+                   "mla_sparse_decode_fp8", "mla_sparse_workspace_size"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_status_str.argtypes = [ctypes.c_int]
         lib.mla_status_str.restype = ctypes.c_char_p
@@ -359,13 +360,25 @@ def mla_prefill_attend(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, softma
     return out
 
 
-def mla_sparse_decode_fp8(q, kv_cache, indices, softmax_scale, out, lse=None):
+def mla_sparse_workspace_size(tokens, n_heads, topk) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mla_sparse_workspace_size(int(tokens), int(n_heads), int(topk),
+                                            ctypes.byref(out)), "mla_sparse_workspace_size")
+    return int(out.value)
+
+
+def mla_sparse_decode_fp8(q, kv_cache, indices, softmax_scale, out, lse=None, workspace=None):
     """Sparse decode: token (b, i) of q [B,Sq,N,576] attends over the 656-byte
     entries of kv_cache [NB,PG,656] (uint8) at the slots indices[b,i,:] (-1: none).
-    Writes out [B,Sq,N,512] and lse [B,Sq,N]."""
-    _device_check(q, kv_cache, indices, out, lse)
+    Writes out [B,Sq,N,512] and lse [B,Sq,N]. ``workspace`` (uint8 device tensor
+    of at least mla_sparse_workspace_size() bytes) is allocated here when not given."""
+    _device_check(q, kv_cache, indices, out, lse, workspace)
     lib = load()
+    if workspace is None:
+        nbytes = mla_sparse_workspace_size(q.shape[0] * q.shape[1], q.shape[2], indices.shape[2])
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     _check(lib.mla_sparse_decode_fp8(_ref(desc(q)), _ref(desc(kv_cache)), _ref(desc(indices)),
                                      float(softmax_scale), _ref(desc(out)), _ref(desc(lse)),
-                                     _stream(out)), "mla_sparse_decode_fp8")
+                                     workspace.data_ptr(), workspace.numel(), _stream(out)),
+           "mla_sparse_decode_fp8")
     return out

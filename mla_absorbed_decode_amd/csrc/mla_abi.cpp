@@ -585,9 +585,19 @@ int mla_prefill_attend(const mla_tensor* q, const mla_tensor* k, const mla_tenso
   return launched(mla::launch_mha(p, (hipStream_t)stream));
 }
 
+int mla_sparse_workspace_size(int64_t tokens, int64_t n_heads, int64_t topk, size_t* bytes) {
+  if (!bytes) return MLA_ERR_NULL;
+  if (tokens < 0 || n_heads < 0 || topk < 0) return MLA_ERR_SHAPE;
+  if (topk > mla::kSparseMaxTopk) return MLA_ERR_UNSUPPORTED;
+  int split_len, nsplit;
+  *bytes = mla::plan_sparse(tokens, n_heads, topk, &split_len, &nsplit);
+  return MLA_OK;
+}
+
 int mla_sparse_decode_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
                           const mla_tensor* indices, float softmax_scale, const mla_tensor* out,
-                          const mla_tensor* lse, mla_stream stream) {
+                          const mla_tensor* lse, void* workspace, size_t workspace_bytes,
+                          mla_stream stream) {
   int rc;
   if ((rc = check_desc(q, 4)) || (rc = check_desc(kv_cache, 3)) || (rc = check_desc(indices, 3)) ||
       (rc = check_desc(out, 4)))
@@ -609,6 +619,10 @@ int mla_sparse_decode_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
   if (!rows_aligned16(q) || !rows_aligned16(kv_cache) || !rows_aligned(out, 8))
     return MLA_ERR_UNSUPPORTED;
   if (B == 0 || Sq == 0 || N == 0) return MLA_OK;
+  int split_len, nsplit;
+  const size_t need = mla::plan_sparse(B * Sq, N, K, &split_len, &nsplit);
+  if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 16))
+    return MLA_ERR_WORKSPACE;
   mla::SparseParams p;
   memset(&p, 0, sizeof(p));
   p.q = q->data; p.q_s0 = q->stride[0]; p.q_s1 = q->stride[1]; p.q_s2 = q->stride[2];
@@ -622,6 +636,11 @@ int mla_sparse_decode_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
   }
   p.batch = (int)B; p.q_len = (int)Sq; p.n_heads = (int)N;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.split_len = split_len; p.nsplit = nsplit;
+  if (nsplit > 1) {
+    p.part_o = (float*)workspace;
+    p.part_lse = (float*)((char*)workspace + (size_t)B * Sq * nsplit * N * 512 * sizeof(float));
+  }
   return launched(mla::launch_sparse(p, (hipStream_t)stream));
 }
 

@@ -117,7 +117,16 @@ struct SparseParams {
   float* lse;        int64_t l_s0, l_s1, l_s2;   // [B, Sq, N] or NULL
   int batch, q_len, n_heads;
   float scale_log2;                              // softmax scale * log2(e)
+  // split of each slot list over nsplit workgroups of split_len entries (a
+  // multiple of 32); with nsplit > 1 each writes its normalised partial
+  // output part_o [token][split][N][512] and part_lse [token][split][N]
+  // (natural log), and a merge kernel combines them
+  int split_len, nsplit;
+  float* part_o;
+  float* part_lse;
 };
+// split plan for a call; returns the workspace bytes it needs
+size_t plan_sparse(int64_t tokens, int64_t n_heads, int64_t topk, int* split_len, int* nsplit);
 hipError_t launch_sparse(const SparseParams& p, hipStream_t s);
 
 // ------------------------------------------------------------------ decode

@@ -8,8 +8,11 @@
 // scales (scale j for codes 128 j .. 128 j + 127), 528..655 64 bf16 rope
 // values. Latent value i = e4m3(code_i) * scale[i / 128].
 //
-// One workgroup per (query token, 64 heads): four waves of 16 heads. The
-// token's slot list goes to LDS once (invalid slots as -1). Keys stream in
+// One workgroup per (query token, 64 heads, part of the slot list): four
+// waves of 16 heads. When tokens x head groups alone would leave the chip
+// idle, each list is cut into splits of whole tiles; each split writes its
+// normalised partial and lse, and sparse_merge combines them in split order.
+// The workgroup's part of the slot list goes to LDS once (invalid slots as -1). Keys stream in
 // tiles of 32 entries: each thread reads its 16-byte pieces of the next tile
 // into registers while the current tile is in use; at the tile boundary the
 // e4m3 pieces are widened, multiplied by their block's scale and rounded to
@@ -52,10 +55,16 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
   const int b = bi / p.q_len, qi = bi - b * p.q_len;
   const int h = (int)blockIdx.y * 64 + 16 * w + li;  // this lane's head
   const bool hok = h < p.n_heads;
+  // a wave past the last head only helps load the tiles (wave-uniform)
+  const bool wave_heads = (int)blockIdx.y * 64 + 16 * w < p.n_heads;
 
-  // the slot list, invalid entries as -1
-  const int32_t* idx = p.idx + (int64_t)b * p.i_s0 + (int64_t)qi * p.i_s1;
-  for (int j = tid; j < p.topk; j += 256) {
+  // this workgroup's part of the slot list, invalid entries as -1
+  const int split = (int)blockIdx.z;
+  const int jbeg = split * p.split_len;
+  const int jend = p.topk - jbeg < p.split_len ? p.topk : jbeg + p.split_len;
+  const int nkeys = jend > jbeg ? jend - jbeg : 0;
+  const int32_t* idx = p.idx + (int64_t)b * p.i_s0 + (int64_t)qi * p.i_s1 + jbeg;
+  for (int j = tid; j < nkeys; j += 256) {
     const int32_t s = idx[j];
     slots[j] = (s >= 0 && (int64_t)s < p.num_slots) ? s : -1;
   }
@@ -72,7 +81,7 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
   }
   __syncthreads();  // the slot list is in LDS
 
-  const int ntiles = (p.topk + kSKT - 1) / kSKT;
+  const int ntiles = (nkeys + kSKT - 1) / kSKT;
   // task n of this thread: piece c of entry r of the tile
   u32x4_t raw[kSTasks];
   float rsc[kSTasks];
@@ -85,7 +94,7 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
       if (id >= kSKT * kSPieces) break;
       const int r = id / kSPieces, c = id - r * kSPieces;
       const int j = t * kSKT + r;
-      int s = j < p.topk ? slots[j] : -1;
+      int s = j < nkeys ? slots[j] : -1;
       if (s < 0) {  // no key: read a valid entry, store zeros in its place
         s = 0;
         nokey |= 1u << n;
@@ -137,6 +146,7 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
     if (more) load_tile(t + 1);
     const MLA_LDS char* kb = ring + (t & 1) * kSSlot;
     const int j0 = t * kSKT;
+    if (wave_heads) {
     // S^T[key 16 kh + 4 g + jj][head li]
     f32x4_t s[2];
 #pragma unroll
@@ -154,7 +164,7 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int j = j0 + 16 * kh + 4 * g + jj;
-        const bool ok = j < p.topk && slots[j < p.topk ? j : 0] >= 0;
+        const bool ok = j < nkeys && slots[j < nkeys ? j : 0] >= 0;
         x[kh][jj] = ok ? s[kh][jj] * p.scale_log2 : -__builtin_inff();
         tmax = fmaxf(tmax, x[kh][jj]);
       }
@@ -192,6 +202,7 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
       const i16x8_t av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       o[db] = mfma_16x16x32(av, pb, o[db]);
     }
+    }
     if (more) store_tile((t + 1) & 1);
     __syncthreads();
   }
@@ -201,6 +212,17 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
   l += __shfl_xor(l, 32);
   if (!hok) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (p.nsplit > 1) {  // normalised partial and its lse, merged by sparse_merge
+    const int64_t r = ((int64_t)bi * p.nsplit + split) * p.n_heads + h;
+    float* po = p.part_o + r * 512 + 4 * g;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *(f32x4_t*)(po + 16 * db) = f32x4_t{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
+                                          o[db][3] * inv};
+    if (g == 0)
+      p.part_lse[r] = l > 0.f ? (m + __log2f(l)) * 0.69314718055994530942f : -__builtin_inff();
+    return;
+  }
   uint16_t* orow = (uint16_t*)p.out + (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 +
                    (int64_t)h * p.o_s2 + 4 * g;
 #pragma unroll
@@ -214,13 +236,66 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
         l > 0.f ? (m + __log2f(l)) * 0.69314718055994530942f : -__builtin_inff();
 }
 
+// One wave per (token, head): lane l merges columns 8 l .. 8 l + 7 over the
+// splits in split order, out = sum_s exp(lse_s - lse) o_s with
+// lse = ln sum_s exp(lse_s); no key in any split gives 0 and -inf.
+__global__ void __launch_bounds__(256) sparse_merge(SparseParams p) {
+  const int lane = threadIdx.x & 63;
+  const int bi = blockIdx.x, h = (int)blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (h >= p.n_heads) return;
+  const int b = bi / p.q_len, qi = bi - b * p.q_len;
+  const int64_t r0 = (int64_t)bi * p.nsplit * p.n_heads + h;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < p.nsplit; ++s) mx = fmaxf(mx, p.part_lse[r0 + (int64_t)s * p.n_heads]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  if (mx != -__builtin_inff()) {
+    for (int s = 0; s < p.nsplit; ++s) {
+      const int64_t r = r0 + (int64_t)s * p.n_heads;
+      const float wgt = __expf(p.part_lse[r] - mx);
+      sum += wgt;
+      const f32x4_t a = *(const f32x4_t*)(p.part_o + r * 512 + 8 * lane);
+      const f32x4_t c = *(const f32x4_t*)(p.part_o + r * 512 + 8 * lane + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[k] += wgt * a[k];
+        acc[4 + k] += wgt * c[k];
+      }
+    }
+  }
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  uint16_t* orow = (uint16_t*)p.out + (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 +
+                   (int64_t)h * p.o_s2 + 8 * lane;
+  const u32x4_t v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                     pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  *(u32x2_t*)orow = u32x2_t{v[0], v[1]};
+  *(u32x2_t*)(orow + 4) = u32x2_t{v[2], v[3]};
+  if (p.lse && lane == 0)
+    p.lse[(int64_t)b * p.l_s0 + (int64_t)qi * p.l_s1 + (int64_t)h * p.l_s2] =
+        sum > 0.f ? mx + __logf(sum) : -__builtin_inff();
+}
+
 }  // namespace
+
+size_t plan_sparse(int64_t tokens, int64_t n_heads, int64_t topk, int* split_len, int* nsplit) {
+  // aim for at least 512 workgroups (two per CU), splits of whole 32-entry tiles
+  const int64_t tiles = (topk + kSKT - 1) / kSKT;
+  const int64_t base = tokens * ((n_heads + 63) / 64);
+  int64_t want = base > 0 ? (512 + base - 1) / base : 1;
+  if (want > tiles) want = tiles;
+  if (want < 1) want = 1;
+  const int64_t per = (tiles + want - 1) / want;  // tiles per split
+  *split_len = (int)(per * kSKT > 0 ? per * kSKT : kSKT);
+  *nsplit = (int)(tiles > 0 ? (tiles + per - 1) / per : 1);
+  if (*nsplit <= 1) return 0;
+  return (size_t)tokens * *nsplit * n_heads * (512 + 1) * sizeof(float);
+}
 
 size_t sparse_lds_bytes(int topk) { return 2 * (size_t)kSSlot + 4 * (size_t)(topk > 0 ? topk : 1); }
 
 hipError_t launch_sparse(const SparseParams& p, hipStream_t s) {
   if (p.batch == 0 || p.q_len == 0 || p.n_heads == 0) return hipSuccess;
-  const size_t lds = sparse_lds_bytes(p.topk);
+  const size_t lds = sparse_lds_bytes(p.split_len < p.topk ? p.split_len : p.topk);
   static size_t attr = 0;
   if (lds > attr) {
     const hipError_t e = hipFuncSetAttribute((const void*)sparse_fp8_decode,
@@ -229,8 +304,15 @@ hipError_t launch_sparse(const SparseParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = 2 * kSSlot + 4 * kSparseMaxTopk;
   }
-  dim3 grid((unsigned)((int64_t)p.batch * p.q_len), (unsigned)((p.n_heads + 63) / 64));
+  dim3 grid((unsigned)((int64_t)p.batch * p.q_len), (unsigned)((p.n_heads + 63) / 64),
+            (unsigned)p.nsplit);
   hipLaunchKernelGGL(sparse_fp8_decode, grid, dim3(256), lds, s, p);
+  if (p.nsplit > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 mg((unsigned)((int64_t)p.batch * p.q_len), (unsigned)((p.n_heads + 3) / 4));
+    hipLaunchKernelGGL(sparse_merge, mg, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

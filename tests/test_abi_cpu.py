@@ -52,7 +52,8 @@ def test_library_exports_every_declared_symbol(lib):
                           "mla_rope_interleaved", "mla_absorb_q_rope", "mla_concat_and_cache_rope",
                           "mla_absorb_q_and_cache", "mla_decode_attend_v_up",
                           "mla_concat_and_cache_fp8", "mla_decode_attend_fp8",
-                          "mla_decompress_kv", "mla_prefill_attend", "mla_sparse_decode_fp8"}
+                          "mla_decompress_kv", "mla_prefill_attend", "mla_sparse_decode_fp8",
+                          "mla_sparse_workspace_size"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -384,8 +385,9 @@ def test_prefill_attend_validation(lib):
 
 
 def test_sparse_decode_validation(lib):
-    def f(q, kv, idx, out, lse=None):
-        return lib.mla_sparse_decode_fp8(R(q), R(kv), R(idx), 0.04, R(out), R(lse), None)
+    def f(q, kv, idx, out, lse=None, ws=FAKE, ws_bytes=1 << 40):
+        return lib.mla_sparse_decode_fp8(R(q), R(kv), R(idx), 0.04, R(out), R(lse), ws, ws_bytes,
+                                         None)
     B, Sq, N = 2, 1, 128
     q, kv, idx = T([B, Sq, N, 576]), T([32, 64, 656], FP8), T([B, Sq, 128], I32)
     out, lse = T([B, Sq, N, 512]), T([B, Sq, N], F32)
@@ -401,3 +403,14 @@ def test_sparse_decode_validation(lib):
     assert f(q, T([32, 64, 656], FP8, strides=[64 * 656 + 8, 656, 1]), idx, out) == UNSUP
     assert f(None, kv, idx, out) == NULL
     assert f(T([0, Sq, N, 576]), kv, T([0, Sq, 128], I32), T([0, Sq, N, 512])) == OK
+    # a split call needs its workspace; a call small enough to run unsplit does not
+    need = ctypes.c_size_t(0)
+    assert lib.mla_sparse_workspace_size(B * Sq, N, 2048, ctypes.byref(need)) == OK
+    assert need.value > 0
+    big = T([B, Sq, 2048], I32)
+    assert f(q, kv, big, out, ws=None, ws_bytes=0) == WS
+    assert f(q, kv, big, out, ws=FAKE, ws_bytes=need.value - 1) == WS
+    assert f(q, kv, big, out, ws=FAKE + 4, ws_bytes=need.value) == WS
+    assert lib.mla_sparse_workspace_size(1, 128, 32, ctypes.byref(need)) == OK and need.value == 0
+    assert lib.mla_sparse_workspace_size(1, 128, 8192, ctypes.byref(need)) == UNSUP
+    assert lib.mla_sparse_workspace_size(-1, 128, 32, ctypes.byref(need)) == SHAPE

@@ -115,3 +115,36 @@ def test_zero_topk_gives_zero_and_minus_inf():
     empty = torch.empty((B, Sq, 0), dtype=torch.int32, device=dev())  # inner stride 1
     out, lse = _run(q, torch.from_numpy(payload).to(dev()), empty)
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_unsplit_many_tokens_and_workspace_reuse():
+    """Enough tokens to fill the chip unsplit (no workspace); then a split call
+    reusing one workspace twice gives the same bits."""
+    mla = _mla()
+    B, Sq, N, NB, PG, K = 256, 2, 128, 16, 64, 64
+    say(f"sparse fp8 decode: unsplit B={B} Sq={Sq} N={N} topk={K}")
+    assert mla.mla_sparse_workspace_size(B * Sq, N, K) == 0
+    payload = mi.dsmla_payload(4, NB, PG, scales="random")
+    q_np = mi.normal(4, 64, (B, Sq, N, 576), 0.1, mi.BF16)
+    idx = mi.dsmla_indices(4, B, Sq, K, NB, PG, mode="random", fill=0.9)
+    out, lse = _run(to_dev(q_np, "bf16"), torch.from_numpy(payload).to(dev()), idx)
+    want, want_lse = oracle.sparse_decode(q_np, payload, idx, SCALE)
+    assert_close(to_np(out), want, "bf16", "out")
+    assert_lse_close(to_np(lse), want_lse, "lse")
+    # a split call (few tokens, long lists) on a reused workspace
+    B2, K2 = 2, 1024
+    q2 = to_dev(mi.normal(5, 64, (B2, 1, N, 576), 0.1, mi.BF16), "bf16")
+    idx2 = torch.from_numpy(mi.dsmla_indices(5, B2, 1, K2, NB, PG, mode="random", fill=0.95)).to(dev())
+    need = mla.mla_sparse_workspace_size(B2, N, K2)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=dev())
+    cache = torch.from_numpy(payload).to(dev())
+    runs = []
+    for _ in range(2):
+        o = torch.full((B2, 1, N, 512), float("nan"), dtype=torch.bfloat16, device=dev())
+        mla.mla_sparse_decode_fp8(q2, cache, idx2, SCALE, o, None, workspace=ws)
+        runs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0].view(torch.int16), runs[1].view(torch.int16))
+    w2, _ = oracle.sparse_decode(to_np(q2), payload, idx2.cpu().numpy(), SCALE)
+    assert_close(to_np(runs[0]), w2, "bf16", "split out")
