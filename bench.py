@@ -470,6 +470,52 @@ def prefill_secondary(dev, steps: int, warmup: int):
     return res
 
 
+def sparse_secondary(dev, steps: int, warmup: int):
+    """Sparse fp8 decode over 656-byte entries: the sparse-decode page's shape
+    (batch 2 x 128 heads, top-128 over 32 blocks of 64 entries) and a longer
+    DSA-sized list (64 tokens x 128 heads, top-2048 random slots out of 2048
+    blocks of 64). Bytes count every listed entry once per token plus q and out;
+    flops are 2 (576 + 512) per (token, head, listed key)."""
+    res = {}
+    for name, (B, N, K, NB, mode) in {"page_case": (2, 128, 128, 32, "disjoint"),
+                                      "dsa_2048": (64, 128, 2048, 2048, "random")}.items():
+        PG = 64
+        cache = torch.from_numpy(mi.dsmla_payload(0, NB, PG)).to(dev)
+        q = torch.from_numpy(mi.normal(0, 64, (B, 1, N, 576), 0.1, mi.BF16)).to(torch.bfloat16).to(dev)
+        idx = torch.from_numpy(mi.dsmla_indices(0, B, 1, K, NB, PG, mode=mode, fill=1.0)).to(dev)
+        out = torch.empty(B, 1, N, 512, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(B, 1, N, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, mla.mla_sparse_workspace_size(B, N, K)), dtype=torch.uint8,
+                         device=dev)
+        run = lambda i: mla.mla_sparse_decode_fp8(q, cache, idx, 576 ** -0.5, out, lse,
+                                                  workspace=ws)
+        run(0)  # eager first: one-time kernel attributes are set outside capture
+        torch.cuda.synchronize()
+        whole = capture(lambda _: [run(k) for k in range(4)], 1)[0]
+        for _ in range(max(1, warmup)):
+            whole.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            whole.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / (4 * steps) * 1e3
+        byts = B * K * 656 + B * N * (576 + 512) * 2 + B * N * 4
+        flops = B * N * K * 2 * (576 + 512)
+        res[name] = {"batch": B, "heads": N, "topk": K, "us": round(us, 2),
+                     "gbs": round(byts / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                     "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+    res["workload"] = ("sparse fp8 decode, 656-byte entries (512 e4m3 + 4 f32 scales + 64 bf16 "
+                       "rope), 64-entry pages, N(0,0.1^2) values, scales 1; graphs of 4 calls "
+                       "on one pool (warm: the pools fit the last-level cache)")
+    return res
+
+
 def rope_secondary(step: Step, dev, steps: int, warmup: int):
     """Interleaved rope at the V2-Lite decode step's shapes: the q fold and the
     cache write with and without the fused rotation (positions seqlen_b - 1),
@@ -536,6 +582,7 @@ def main():
     ap.add_argument("--no-v3", action="store_true", help="skip the 128-head secondary line")
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding line")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache line")
+    ap.add_argument("--no-sparse", action="store_true", help="skip the sparse fp8 decode line")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the NoPE prefill line (absorbed and naive routes)")
     ap.add_argument("--eager", action="store_true",
@@ -617,6 +664,8 @@ def main():
                                           eager=args.eager)
     if not args.no_rope:
         line["rope"] = rope_secondary(step, dev, max(10, args.steps // 2), args.warmup)
+    if not args.no_sparse:
+        line["sparse_fp8"] = sparse_secondary(dev, max(5, args.steps // 5), min(args.warmup, 3))
     if not args.no_prefill:
         line["nope_prefill"] = prefill_secondary(dev, max(5, args.steps // 10), min(args.warmup, 3))
     if not args.no_cpu:
