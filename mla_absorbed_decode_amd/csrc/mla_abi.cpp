@@ -13,6 +13,7 @@
 
 #include "mla.h"
 #include "mla_kernels.h"
+#include "prefill_kernels.h"
 
 namespace {
 

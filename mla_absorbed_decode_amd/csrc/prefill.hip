@@ -31,6 +31,7 @@
 #include "gemm_tile.h"
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "prefill_kernels.h"
 
 namespace mla {
 namespace {

@@ -23,6 +23,7 @@
 // rows) read by ds_read_b64_tr_b16, online softmax in the exp2 domain.
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "prefill_kernels.h"
 
 namespace mla {
 namespace {
