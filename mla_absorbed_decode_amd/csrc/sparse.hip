@@ -13,14 +13,16 @@
 // idle, each list is cut into splits of whole tiles; each split writes its
 // normalised partial and lse, and sparse_merge combines them in split order.
 // The workgroup's part of the slot list goes to LDS once (invalid slots as -1). Keys stream in
-// tiles of 32 entries: each thread reads its 16-byte pieces of the next tile
-// into registers while the current tile is in use; at the tile boundary the
+// tiles of 32 entries: each thread reads its 16-byte pieces two tiles ahead
+// into one of two register sets while the current tile is in use; at the tile boundary the
 // e4m3 pieces are widened, multiplied by their block's scale and rounded to
 // bf16 (the rope pieces are copied), forming a [32, 576] bf16 tile in a
 // two-slot LDS ring. The arithmetic is the prefill attention's: S^T = K Q^T
 // with the heads' queries in registers, P^T straight from S^T's
 // accumulators, O^T += V^T P^T with V^T (the first 512 columns of the same
 // rows) read by ds_read_b64_tr_b16, online softmax in the exp2 domain.
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "prefill_kernels.h"
@@ -84,10 +86,12 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
 
   const int ntiles = (nkeys + kSKT - 1) / kSKT;
   // task n of this thread: piece c of entry r of the tile
-  u32x4_t raw[kSTasks];
-  float rsc[kSTasks];
-  uint32_t nokey = 0;  // bit n: task n belongs to an entry that is no key
-  auto load_tile = [&](int t) {
+  // two register sets: tile t + 2 is read from memory while tile t is in use
+  // and tile t + 1 waits in the other set for its slot of the LDS ring
+  u32x4_t raw2[2][kSTasks];
+  float rsc2[2][kSTasks];
+  uint32_t nokey2[2] = {0u, 0u};  // bit n: task n belongs to an entry that is no key
+  auto load_tile = [&](int t, u32x4_t (&raw)[kSTasks], float (&rsc)[kSTasks], uint32_t& nokey) {
     nokey = 0;
 #pragma unroll
     for (int n = 0; n < kSTasks; ++n) {
@@ -106,7 +110,8 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
       rsc[n] = c < 32 ? *(const float*)(e + 512 + 4 * (c >> 3)) : 1.f;
     }
   };
-  auto store_tile = [&](int slot) {
+  auto store_tile = [&](int slot, const u32x4_t (&raw)[kSTasks], const float (&rsc)[kSTasks],
+                        uint32_t nokey) {
     MLA_LDS char* kb = ring + slot * kSSlot;
 #pragma unroll
     for (int n = 0; n < kSTasks; ++n) {
@@ -138,14 +143,16 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
   float m = -__builtin_inff(), l = 0.f;
 
   if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_tile(0, raw2[0], rsc2[0], nokey2[0]);
+    store_tile(0, raw2[0], rsc2[0], nokey2[0]);
   }
+  if (ntiles > 1) load_tile(1, raw2[1], rsc2[1], nokey2[1]);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
-    const MLA_LDS char* kb = ring + (t & 1) * kSSlot;
+  // one tile of the loop; SET is t % 2 (a constant, so the register sets stay registers)
+  auto tile_step = [&](int t, auto set_c) {
+    constexpr int SET = decltype(set_c)::value;
+    if (t + 2 < ntiles) load_tile(t + 2, raw2[SET], rsc2[SET], nokey2[SET]);
+    const MLA_LDS char* kb = ring + SET * kSSlot;
     const int j0 = t * kSKT;
     if (wave_heads) {
     // S^T[key 16 kh + 4 g + jj][head li]
@@ -204,9 +211,15 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
       o[db] = mfma_16x16x32(av, pb, o[db]);
     }
     }
-    if (more) store_tile((t + 1) & 1);
+    if (t + 1 < ntiles) store_tile(SET ^ 1, raw2[SET ^ 1], rsc2[SET ^ 1], nokey2[SET ^ 1]);
     __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    tile_step(t, std::integral_constant<int, 0>{});
+    tile_step(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < ntiles) tile_step(t, std::integral_constant<int, 0>{});
 
   // a head's four lanes hold partial sums over their keys
   l += __shfl_xor(l, 16);
