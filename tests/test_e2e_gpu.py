@@ -210,3 +210,60 @@ def test_graph_replays_equal_eager():
         torch.cuda.synchronize()
         for got, want in zip((q, o_lat, lse, out), ref):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {i}"
+
+
+def test_prefill_and_sparse_graph_replays_equal_eager():
+    """The naive prefill (decompress, then attend; 300 tokens, so the pipelined
+    product tiles run) and a split sparse decode, captured in one graph: every
+    replay, with eager work and synchronisation between replays, reproduces
+    the eager outputs bit for bit."""
+    import mla_absorbed_decode_amd as mla
+
+    d = mi.V2_LITE
+    T = 300
+    q_nope, q_pe, c_kv, k_pe = mi.mla_activations(10, d, T, T, "bf16")
+    w_uk_t, w_uv = mi.mla_weights(10, d, "bf16")
+    qd = t_dev(np.concatenate([q_nope, q_pe], 2), "bf16")
+    ckv, kpe = t_dev(c_kv, "bf16"), t_dev(k_pe, "bf16")
+    wk, wv = t_dev(w_uk_t, "bf16"), t_dev(w_uv, "bf16")
+    k = torch.empty(T, d.n_head, d.d_nope + d.d_rope, dtype=torch.bfloat16, device=dev())
+    v = torch.empty(T, d.n_head, d.d_v, dtype=torch.bfloat16, device=dev())
+    out = torch.empty(T, d.n_head, d.d_v, dtype=torch.bfloat16, device=dev())
+    plse = torch.empty(T, d.n_head, dtype=torch.float32, device=dev())
+    cu = torch.tensor([0, 100, T], dtype=torch.int32, device=dev())
+    # sparse: 2 tokens x 128 heads, top-256 random lists (split over workgroups)
+    pool = torch.from_numpy(mi.dsmla_payload(10, 16, 64, scales="random")).to(dev())
+    sq = t_dev(mi.normal(10, 64, (2, 1, 128, 576), 0.1, "bf16"), "bf16")
+    idx = torch.from_numpy(mi.dsmla_indices(10, 2, 1, 256, 16, 64, mode="random")).to(dev())
+    sout = torch.empty(2, 1, 128, 512, dtype=torch.bfloat16, device=dev())
+    slse = torch.empty(2, 1, 128, dtype=torch.float32, device=dev())
+    need = mla.mla_sparse_workspace_size(2, 128, 256)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+
+    def step():
+        mla.mla_decompress_kv(ckv, kpe, wk, wv, k, v)
+        mla.mla_prefill_attend(qd, k, v, cu, cu, 200, (d.d_nope + d.d_rope) ** -0.5, True, out,
+                               plse)
+        mla.mla_sparse_decode_fp8(sq, pool, idx, 576 ** -0.5, sout, slse, workspace=ws)
+
+    say("[e2e] eager prefill + sparse step")
+    step()
+    torch.cuda.synchronize()
+    outs = (k, v, out, plse, sout, slse)
+    ref = tuple(x.clone() for x in outs)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    scratch = torch.zeros(1 << 20, device=dev())
+    for i in range(4):
+        for x in outs:
+            x.fill_(float("nan"))
+        scratch.add_(1.0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        say(f"[e2e] prefill + sparse graph replay {i}")
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {i}"
