@@ -168,6 +168,8 @@ struct SegLds {
 // LDS besides the tile ring and score exchange: the workgroup's plan and the
 // staged block table
 constexpr int kStaticLds = (int)sizeof(SegLds) + kBlkCache * 4;
+// the static LDS as allocated (the compiler reports 8 KB for these kernels)
+constexpr int kStaticLdsAlloc = (kStaticLds + 4095) / 4096 * 4096;
 
 // Block-table entries staged in LDS: entry e of the stage is read by lane
 // e % 64 of wave 0, from block-table index idx[e / 64] (0, always a valid
@@ -383,13 +385,20 @@ struct Cfg {
   // wc takes k-steps wc, wc + WC, wc + 2 WC, ... (at most KW of them) and the
   // partial scores are summed through LDS in wave order.
   static constexpr int KW = XS ? (KSTEPS + WC - 1) / WC : KSTEPS;
-  static constexpr int XCHG_BYTES = XS ? NW * SUB * RT * 64 * 16 : 0;
+  // partial score blocks, then (with loader waves) the compute waves' rendezvous counter
+  static constexpr int XPART_BYTES = XS ? NW * SUB * RT * 64 * 16 : 0;
+  static constexpr int XCHG_BYTES = XS ? XPART_BYTES + (NP > 0 ? 16 : 0) : 0;
   static constexpr int RING_BYTES = NSLOT * TILE_BYTES;
   // KV8 staging: a key tile as e4m3 bytes (TT rows of E) or a query tile as
   // bf16 (RTILE rows of 2E), P8 / QI 1 KB reads, L8 of them per loader wave
   static constexpr int P8 = KV8 ? TT * E / 1024 : 0;
   static constexpr int STAGE_SLOT = KV8 ? (TT * E > RTILE * E * 2 ? TT * E : RTILE * E * 2) : 0;
-  static constexpr int STAGE_BYTES = KV8 ? 3 * STAGE_SLOT : 0;
+  // staging depth: items read ahead of the one being landed (4 when the LDS
+  // holds them: more bytes in flight per CU against the memory latency)
+  static constexpr int NS8 =
+      KV8 ? (NSLOT * TILE_BYTES + XCHG_BYTES + 4 * STAGE_SLOT + kStaticLdsAlloc <= 160 * 1024 ? 4 : 3)
+          : 1;
+  static constexpr int STAGE_BYTES = KV8 ? NS8 * STAGE_SLOT : 0;
   static constexpr int SMEM_BYTES = RING_BYTES + XCHG_BYTES + STAGE_BYTES;
   // With loader waves the query rows of every segment but the first travel
   // through the ring as a tile of their own ahead of its key tiles (QI 1 KB
@@ -409,7 +418,7 @@ struct Cfg {
   static constexpr bool STREAM = !F32 && RTILE <= 32;
   static_assert(NW == 4, "four compute waves per workgroup");
   static_assert(NP == 0 || NP == 4, "no loader waves, or four");
-  static_assert(!XS || NP == 0, "the score exchange barrier assumes no loader waves");
+  static_assert(!XS || NP == 0 || WR == 1, "with loader waves the exchange spans all compute waves");
   static_assert(!QT || (RTILE <= TT && QI * 64 == RTILE * CH && QI <= LPT), "query tile fits a slot");
   static_assert(!XS || WC % 2 == 0, "k-step parity is the wave's when WC is even");
   static_assert(LPT * 64 == TT * CH, "tile chunk count");
@@ -418,7 +427,7 @@ struct Cfg {
   static_assert(!F32 || TT == 16, "the f32 path uses 16-token tiles");
   static_assert(NSLOT >= 2 && NSLOT <= 4, "ring depth");
   static_assert(KSTEPS % KB == 0 && DW % PB == 0, "batching");
-  static_assert(SMEM_BYTES + kStaticLds <= 160 * 1024, "LDS budget");
+  static_assert(SMEM_BYTES + kStaticLdsAlloc <= 160 * 1024, "LDS budget");
   static_assert(!KV8 || (!F32 && NP > 0 && TT * E % 1024 == 0 && L8 * NP >= P8 && L8 * NP >= QI &&
                          P8 <= 64 && QI <= 64),
                 "fp8: bf16 compute, loader waves, whole 1 KB staging reads");
@@ -438,7 +447,7 @@ template <class C, class QReg, class Hook>
 __device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, MLA_LDS f32x4_t* xchg,
                                              int j0, const QReg& qreg, WaveState<C>& st,
                                              float scale_log2, int wr, int wc, int dc0,
-                                             const Hook& hook) {
+                                             const Hook& hook, int& xs_seq) {
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   f32x4_t s[C::SUB][C::RT];
 
@@ -488,7 +497,25 @@ __device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, MLA_LDS f
     for (int a = 0; a < C::SUB; ++a)
 #pragma unroll
       for (int rt = 0; rt < C::RT; ++rt) mine[(a * C::RT + rt) * 64] = acc[0][a][rt] + acc[1][a][rt];
-    __syncthreads();
+    if constexpr (C::NP > 0) {
+      // The loader waves keep their own barrier schedule, so the compute waves
+      // meet on a counter: each adds 1 once its partials are stored, then waits
+      // until all NW have added for this tile. Every compute wave makes the same
+      // sequence of tile_compute calls between the same workgroup barriers, so
+      // the count is reached; the wait is bounded all the same.
+      MLA_LDS uint32_t* ctr = (MLA_LDS uint32_t*)((MLA_LDS char*)xchg + C::XPART_BYTES);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint32_t target = (uint32_t)C::NW * (uint32_t)(xs_seq + 1);
+      for (int it = 0; it < (1 << 22); ++it) {
+        if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      ++xs_seq;
+    } else {
+      __syncthreads();
+    }
     const MLA_LDS f32x4_t* grp = xchg + wr * C::WC * (C::SUB * C::RT * 64) + lane;
     f32x4_t part[C::WC][C::SUB][C::RT];
 #pragma unroll
@@ -966,12 +993,12 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
       }
     }
   };
-  // ---- fp8 cache (KV8): stream item k is read into staging slot k % 3 at
-  // step k - 3 and landed in ring slot k % NSLOT at step k, by the lanes that
+  // ---- fp8 cache (KV8): stream item k is read into staging slot k % NS8 at
+  // step k - NS8 and landed in ring slot k % NSLOT at step k, by the lanes that
   // read it (so each wave's own vmcnt wait covers the bytes it lands).
   MLA_LDS char* stage = ring + C::RING_BYTES + C::XCHG_BYTES;
   auto kv8_issue = [&](const NextTile& t, int k) {
-    MLA_LDS char* stg = stage + (k % 3) * C::STAGE_SLOT;
+    MLA_LDS char* stg = stage + (k % C::NS8) * C::STAGE_SLOT;
     if (t.query) {
       // query rows in the bf16 query-tile layout (as issue_part); reads past
       // QI repeat one, so every loader wave sends L8 reads per item
@@ -1005,7 +1032,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     }
   };
   auto kv8_land = [&](int k, bool query) {
-    const MLA_LDS char* stg = stage + (k % 3) * C::STAGE_SLOT + lane * 16;
+    const MLA_LDS char* stg = stage + (k % C::NS8) * C::STAGE_SLOT + lane * 16;
     MLA_LDS char* dst = ring + (k % C::NSLOT) * C::TILE_BYTES;
     if (query) {
 #pragma unroll
@@ -1038,23 +1065,25 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     }
   };
   auto kv8_loader = [&]() {
-    uint32_t qmask = 0;  // bit k % 3: staging slot k % 3 holds query rows
+    uint32_t qmask = 0;  // bit k % NS8: staging slot k % NS8 holds query rows
     auto issue = [&](int k) {
       const NextTile t = prep_next(k);
       kv8_issue(t, k);
-      const uint32_t bit = 1u << (k % 3);
+      const uint32_t bit = 1u << (k % C::NS8);
       qmask = t.query ? (qmask | bit) : (qmask & ~bit);
     };
-    for (int k = 0; k < 3 && k < nsteps; ++k) issue(k);
+    for (int k = 0; k < C::NS8 && k < nsteps; ++k) issue(k);
     for (int k = 0; k < nsteps; ++k) {
-      // item k's reads are older than those of the (at most two) items after it
+      // item k's reads are older than those of the (at most NS8 - 1) items after it
       const int ahead = nsteps - 1 - k;
       if (ahead <= 0) wait_vmcnt<0>();
       else if (ahead == 1) wait_vmcnt<C::L8>();
-      else wait_vmcnt<2 * C::L8>();
-      kv8_land(k, (qmask >> (k % 3)) & 1u);
+      else if (ahead == 2 || C::NS8 == 3) wait_vmcnt<2 * C::L8>();
+      else wait_vmcnt<(C::NS8 >= 4 ? 3 : 2) * C::L8>();
+      static_assert(C::NS8 * C::L8 < 64, "vmcnt range");
+      kv8_land(k, (qmask >> (k % C::NS8)) & 1u);
       __syncthreads();
-      if (k + 3 < nsteps) issue(k + 3);
+      if (k + C::NS8 < nsteps) issue(k + C::NS8);
     }
   };
 
@@ -1125,7 +1154,10 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
       const int sw = lds_swz(row & 15);
 #pragma unroll
       for (int kk = 0; kk < C::KW; ++kk) {
-        const int c = 4 * kk + g;  // 16-byte chunk of k-step kk
+        // with a split contraction the wave holds k-steps wc, wc + WC, ... (a
+        // step past the row end, never used, rereads the first)
+        const int kg = !C::XS ? kk : (wc + C::WC * kk < C::KSTEPS ? wc + C::WC * kk : wc);
+        const int c = 4 * kg + g;  // 16-byte chunk of k-step kg
         const MLA_LDS QV* qp = (const MLA_LDS QV*)(rb + (((c & ~7) | ((c & 7) ^ sw)) << 4));
         qreg[rt][kk] = qvalid[rt] ? *qp : QV{};
       }
@@ -1178,6 +1210,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     }
     settle_q();
   }
+  int xs_seq = 0;  // tile_compute calls so far (the split-contraction rendezvous count)
   if constexpr (C::NP > 0) {
     // ---- separate roles: each runs its own loop (one barrier per stream item)
     if (loader && C::KV8) {
@@ -1203,7 +1236,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
         continue;
       }
       tile_compute<C>(slot, xchg, cs.t_lo + ck * C::TT, qreg, st, scale_log2, wr, wc, dc0,
-                      [](int) {});
+                      [](int) {}, xs_seq);
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
         cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
@@ -1229,7 +1262,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
       __syncthreads();
       const NextTile nt = k + C::NSLOT - 1 < nsteps ? prep_next(k + C::NSLOT - 1) : NextTile{};
       tile_compute<C>(ring + (k % C::NSLOT) * C::TILE_BYTES, xchg, cs.t_lo + ck * C::TT, qreg, st,
-                      scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); });
+                      scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); }, xs_seq);
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
         cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
@@ -1252,6 +1285,9 @@ decode_partial(DecodeParams p) {
   __shared__ int sh_blk[kBlkCache];
   MLA_LDS char* ring = (MLA_LDS char*)smem_raw;
   MLA_LDS f32x4_t* xchg = (MLA_LDS f32x4_t*)(smem_raw + C::RING_BYTES);
+  if constexpr (C::XS && C::NP > 0) {  // rendezvous counter; the plan's barrier publishes it
+    if (threadIdx.x == 0) *(MLA_LDS uint32_t*)(smem_raw + C::RING_BYTES + C::XPART_BYTES) = 0u;
+  }
   plan_workgroup<C>(p, &tab, sh_blk);
   // a workgroup whose chunk holds no keys (split mode) has nothing to write;
   // without split an empty unit still writes its zero rows
@@ -1484,8 +1520,8 @@ using Rows64  = Cfg<64, 4, 1, 1, 32, 4, false, false, 0>;  // many rows: rows sp
 using Rows0   = Cfg<0,  4, 1, 1, 32, 4, false, false, 0>;
 using ColsF64 = Cfg<64, 1, 4, 1, 16, 4, true,  true,  0>;  // f32
 using ColsF0  = Cfg<0,  1, 4, 1, 16, 4, true,  true,  0>;
-using Cols64F8 = Cfg<64, 1, 4, 1, 32, 2, false, false, 4, true>;  // fp8 cache, any row count
-using Cols0F8  = Cfg<0,  1, 4, 1, 32, 2, false, false, 4, true>;
+using Cols64F8 = Cfg<64, 1, 4, 1, 32, 2, false, true,  4, true>;  // fp8 cache, any row count
+using Cols0F8  = Cfg<0,  1, 4, 1, 32, 2, false, true,  4, true>;
 
 constexpr int kColsEntryCost = 3;  // work blocks (measured: 3-4 best on V2-Lite)
 
