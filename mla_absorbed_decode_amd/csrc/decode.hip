@@ -164,6 +164,7 @@ struct SegLds {
   uint64_t live[4];
   uint64_t part[4];
   SegHdr hdr;
+  uint32_t xs_ctr;  // compute-wave rendezvous of the split score contraction (loader layouts)
 };
 // LDS besides the tile ring and score exchange: the workgroup's plan and the
 // staged block table
@@ -385,9 +386,7 @@ struct Cfg {
   // wc takes k-steps wc, wc + WC, wc + 2 WC, ... (at most KW of them) and the
   // partial scores are summed through LDS in wave order.
   static constexpr int KW = XS ? (KSTEPS + WC - 1) / WC : KSTEPS;
-  // partial score blocks, then (with loader waves) the compute waves' rendezvous counter
-  static constexpr int XPART_BYTES = XS ? NW * SUB * RT * 64 * 16 : 0;
-  static constexpr int XCHG_BYTES = XS ? XPART_BYTES + (NP > 0 ? 16 : 0) : 0;
+  static constexpr int XCHG_BYTES = XS ? NW * SUB * RT * 64 * 16 : 0;  // partial score blocks
   static constexpr int RING_BYTES = NSLOT * TILE_BYTES;
   // KV8 staging: a key tile as e4m3 bytes (TT rows of E) or a query tile as
   // bf16 (RTILE rows of 2E), P8 / QI 1 KB reads, L8 of them per loader wave
@@ -447,7 +446,8 @@ template <class C, class QReg, class Hook>
 __device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, MLA_LDS f32x4_t* xchg,
                                              int j0, const QReg& qreg, WaveState<C>& st,
                                              float scale_log2, int wr, int wc, int dc0,
-                                             const Hook& hook, int& xs_seq) {
+                                             const Hook& hook, MLA_LDS uint32_t* xs_ctr,
+                                             int& xs_seq) {
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   f32x4_t s[C::SUB][C::RT];
 
@@ -503,12 +503,13 @@ __device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, MLA_LDS f
       // until all NW have added for this tile. Every compute wave makes the same
       // sequence of tile_compute calls between the same workgroup barriers, so
       // the count is reached; the wait is bounded all the same.
-      MLA_LDS uint32_t* ctr = (MLA_LDS uint32_t*)((MLA_LDS char*)xchg + C::XPART_BYTES);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (lane == 0)
+        __hip_atomic_fetch_add(xs_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       const uint32_t target = (uint32_t)C::NW * (uint32_t)(xs_seq + 1);
       for (int it = 0; it < (1 << 22); ++it) {
-        if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        if (__hip_atomic_load(xs_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
+          break;
         __builtin_amdgcn_s_sleep(1);
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -1211,6 +1212,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     settle_q();
   }
   int xs_seq = 0;  // tile_compute calls so far (the split-contraction rendezvous count)
+  MLA_LDS uint32_t* xs_ctr = (MLA_LDS uint32_t*)const_cast<uint32_t*>(&tab->xs_ctr);
   if constexpr (C::NP > 0) {
     // ---- separate roles: each runs its own loop (one barrier per stream item)
     if (loader && C::KV8) {
@@ -1236,7 +1238,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
         continue;
       }
       tile_compute<C>(slot, xchg, cs.t_lo + ck * C::TT, qreg, st, scale_log2, wr, wc, dc0,
-                      [](int) {}, xs_seq);
+                      [](int) {}, xs_ctr, xs_seq);
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
         cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
@@ -1262,7 +1264,8 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
       __syncthreads();
       const NextTile nt = k + C::NSLOT - 1 < nsteps ? prep_next(k + C::NSLOT - 1) : NextTile{};
       tile_compute<C>(ring + (k % C::NSLOT) * C::TILE_BYTES, xchg, cs.t_lo + ck * C::TT, qreg, st,
-                      scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); }, xs_seq);
+                      scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); },
+                      xs_ctr, xs_seq);
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
         cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
@@ -1285,9 +1288,7 @@ decode_partial(DecodeParams p) {
   __shared__ int sh_blk[kBlkCache];
   MLA_LDS char* ring = (MLA_LDS char*)smem_raw;
   MLA_LDS f32x4_t* xchg = (MLA_LDS f32x4_t*)(smem_raw + C::RING_BYTES);
-  if constexpr (C::XS && C::NP > 0) {  // rendezvous counter; the plan's barrier publishes it
-    if (threadIdx.x == 0) *(MLA_LDS uint32_t*)(smem_raw + C::RING_BYTES + C::XPART_BYTES) = 0u;
-  }
+  if (threadIdx.x == 0) tab.xs_ctr = 0u;  // rendezvous counter; the plan's barrier publishes it
   plan_workgroup<C>(p, &tab, sh_blk);
   // a workgroup whose chunk holds no keys (split mode) has nothing to write;
   // without split an empty unit still writes its zero rows
@@ -1512,8 +1513,8 @@ __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupPara
 
 // ------------------------------------------------------------- variants
 //                      R   WR WC RT TT NSLOT F32    XS     NP
-using Cols64  = Cfg<64, 1, 4, 1, 32, 4, false, false, 4>;  // <= 16 rows: columns split over waves
-using Cols0   = Cfg<0,  1, 4, 1, 32, 4, false, false, 4>;
+using Cols64  = Cfg<64, 1, 4, 1, 32, 4, false, true,  4>;  // <= 16 rows: columns split over waves
+using Cols0   = Cfg<0,  1, 4, 1, 32, 4, false, true,  4>;
 using Mixed64 = Cfg<64, 2, 2, 1, 32, 4, false, true,  0>;  // <= 32 rows
 using Mixed0  = Cfg<0,  2, 2, 1, 32, 4, false, true,  0>;
 using Rows64  = Cfg<64, 4, 1, 1, 32, 4, false, false, 0>;  // many rows: rows split over waves
