@@ -24,6 +24,7 @@
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "prefill_kernels.h"
+#include "value_round.h"
 
 namespace mla {
 namespace {
@@ -51,8 +52,8 @@ __device__ __forceinline__ void copy_rope(const BmmParams& p, int t0, int h) {
       T* dst = (T*)p.out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + p.N;
       double a = load_value<F32>(src, 2 * i), b = load_value<F32>(src, 2 * i + 1);
       rope_rotate(a, b, p.rope.pos[t], i, (int)p.R, p.rope.log2_base);
-      store_value<F32>(dst, 2 * i, a);
-      store_value<F32>(dst, 2 * i + 1, b);
+      store_rounded<F32>(dst, 2 * i, a);
+      store_rounded<F32>(dst, 2 * i + 1, b);
     }
     return;
   }

@@ -21,6 +21,7 @@
 #include <type_traits>
 
 #include "mla_device.h"
+#include "value_round.h"
 #include "mla_kernels.h"
 
 namespace mla {
@@ -41,13 +42,13 @@ __device__ __forceinline__ void rope_pair(const CacheWriteParams& p, int64_t j) 
   if (p.esize == 4) {
     double a = load_value<true>(row, 2 * i), b = load_value<true>(row, 2 * i + 1);
     rope_rotate(a, b, p.rope.pos[t], i, (int)p.R, p.rope.log2_base);
-    store_value<true>(dst, 2 * i, a);
-    store_value<true>(dst, 2 * i + 1, b);
+    store_rounded<true>(dst, 2 * i, a);
+    store_rounded<true>(dst, 2 * i + 1, b);
   } else {
     double a = load_value<false>(row, 2 * i), b = load_value<false>(row, 2 * i + 1);
     rope_rotate(a, b, p.rope.pos[t], i, (int)p.R, p.rope.log2_base);
-    store_value<false>(dst, 2 * i, a);
-    store_value<false>(dst, 2 * i + 1, b);
+    store_rounded<false>(dst, 2 * i, a);
+    store_rounded<false>(dst, 2 * i + 1, b);
   }
 }
 

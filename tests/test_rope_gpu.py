@@ -234,3 +234,54 @@ def test_fused_cache_write_fp32_unaligned_rows():
         assert_ulp(got[s, 510:], k_rot[t], "f32", 1.0, f"token {t}", np.abs(pos).max())
         written[s] = True
     assert np.isnan(got[~written]).all()
+
+
+def _round_bf16(v):
+    """Round-to-nearest-even bf16 bits of float64 values, rounded once: to
+    float "to odd" first, then to bf16 to nearest even (the two-step form of
+    one correct rounding)."""
+    v = np.asarray(v, dtype=np.float64)
+    f = v.astype(np.float32)
+    bits = f.view(np.uint32).copy()
+    inexact = f.astype(np.float64) != v
+    fix = inexact & ((bits & 1) == 0)
+    up = np.abs(f.astype(np.float64)) < np.abs(v)
+    bits[fix & up] += 1
+    bits[fix & ~up] -= 1
+    rounded = (bits.astype(np.uint64) + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def test_bf16_rounds_once_on_every_path():
+    """A rotated value can sit within a float rounding of a bf16 midpoint
+    (token 86 of this input: 1.6e-8 from one); converting double -> float ->
+    bf16 would land on the midpoint and round it to even the wrong way. The
+    16-byte path (aligned rows) and the pair path (rows 4-byte aligned only)
+    give the same bits, and every element equals the correctly rounded bf16 of
+    the oracle's double result (elements within 1e-12 of a midpoint, where the
+    two doubles may legitimately differ, excepted)."""
+    T, H, D = 333, 2, 64
+    g = torch.Generator().manual_seed(0)
+    x = (torch.rand((T, H, D), generator=g) * 2 - 1).to(torch.bfloat16)
+    pos = np.arange(T, dtype=np.int32) * 13
+    say("[rope] single rounding, aligned and unaligned rows")
+    pd = torch.from_numpy(pos).to(dev())
+    a = x.to(dev()).clone()
+    mla.mla_rope_interleaved(a, pd, mi.ROPE_BASE)
+    buf = torch.zeros(T * H * D + 2, dtype=torch.bfloat16, device=dev())
+    b = buf[2:].view(T, H, D)
+    b.copy_(x.to(dev()))
+    mla.mla_rope_interleaved(b, pd, mi.ROPE_BASE)
+    torch.cuda.synchronize()
+    ab = a.view(torch.int16).cpu().numpy().view(np.uint16)
+    bb = b.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(ab, bb)
+    want = oracle.rope_interleaved(x.float().numpy(), pos, mi.ROPE_BASE)
+    ref = _round_bf16(want)
+    # distance of each double to the nearest bf16 midpoint, relative
+    lo = (ref.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    step = np.abs(lo) * 2.0 ** -8
+    near = np.minimum(np.abs(np.abs(want) - (np.abs(lo) - step / 2)),
+                      np.abs(np.abs(want) - (np.abs(lo) + step / 2))) < 1e-12 * np.maximum(np.abs(want), 1e-30)
+    assert np.array_equal(ab[~near], ref[~near])
+    assert ab[86, 1, 52] == ref[86, 1, 52]
