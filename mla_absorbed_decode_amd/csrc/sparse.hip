@@ -8,8 +8,9 @@
 // scales (scale j for codes 128 j .. 128 j + 127), 528..655 64 bf16 rope
 // values. Latent value i = e4m3(code_i) * scale[i / 128].
 //
-// One workgroup per (query token, 64 heads, part of the slot list): four
-// waves of 16 heads. When tokens x head groups alone would leave the chip
+// One workgroup per (query token, 64 heads, part of the slot list): eight
+// waves, each 16 heads x 256 of the 512 output columns (the two waves of a
+// head block both form its score block). When tokens x head groups alone would leave the chip
 // idle, each list is cut into splits of whole tiles; each split writes its
 // normalised partial and lse, and sparse_merge combines them in split order.
 // The workgroup's part of the slot list goes to LDS once (invalid slots as -1). Keys stream in
@@ -35,7 +36,9 @@ constexpr int kSKT = 32;       // entries per tile
 constexpr int kSP = 1152 + 16; // LDS row pitch: 576 bf16 + 16 bytes of padding
 constexpr int kSSlot = kSKT * kSP;
 constexpr int kSPieces = 40;   // 16-byte pieces per entry read: 32 of codes, 8 of rope
-constexpr int kSTasks = (kSKT * kSPieces + 255) / 256;  // per thread, per tile
+constexpr int kSThreads = 512;  // 8 waves: 4 head blocks x 2 column halves
+constexpr int kSTasks = (kSKT * kSPieces + kSThreads - 1) / kSThreads;  // per thread, per tile
+static_assert(kSE == 512 + 16 + 128, "entry layout: codes, scales, rope");
 constexpr float kSRescale = 8.f;
 
 // 8 e4m3 codes times a scale, as 8 bf16 values (round to nearest even)
@@ -48,18 +51,19 @@ __device__ __forceinline__ u32x4_t fp8x8_scaled_bf16(uint32_t lo, uint32_t hi, f
                  pack_bf16x2(c[0] * s, c[1] * s), pack_bf16x2(d[0] * s, d[1] * s)};
 }
 
-__global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
+__global__ void __launch_bounds__(kSThreads, 2) sparse_fp8_decode(SparseParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* ring = (MLA_LDS char*)smem_raw;
   MLA_LDS int32_t* slots = (MLA_LDS int32_t*)(ring + 2 * kSSlot);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hb = w >> 1, half = w & 1;  // head block of 16, output columns 256 half .. + 255
   const int bi = blockIdx.x;  // query token b * Sq + i
   const int b = bi / p.q_len, qi = bi - b * p.q_len;
-  const int h = (int)blockIdx.y * 64 + 16 * w + li;  // this lane's head
+  const int h = (int)blockIdx.y * 64 + 16 * hb + li;  // this lane's head
   const bool hok = h < p.n_heads;
   // a wave past the last head only helps load the tiles (wave-uniform)
-  const bool wave_heads = (int)blockIdx.y * 64 + 16 * w < p.n_heads;
+  const bool wave_heads = (int)blockIdx.y * 64 + 16 * hb < p.n_heads;
 
   // this workgroup's part of the slot list, invalid entries as -1
   const int split = (int)blockIdx.z;
@@ -67,7 +71,7 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
   const int jend = p.topk - jbeg < p.split_len ? p.topk : jbeg + p.split_len;
   const int nkeys = jend > jbeg ? jend - jbeg : 0;
   const int32_t* idx = p.idx + (int64_t)b * p.i_s0 + (int64_t)qi * p.i_s1 + jbeg;
-  for (int j = tid; j < nkeys; j += 256) {
+  for (int j = tid; j < nkeys; j += kSThreads) {
     const int32_t s = idx[j];
     slots[j] = (s >= 0 && (int64_t)s < p.num_slots) ? s : -1;
   }
@@ -95,7 +99,7 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
     nokey = 0;
 #pragma unroll
     for (int n = 0; n < kSTasks; ++n) {
-      const int id = tid + 256 * n;
+      const int id = tid + kSThreads * n;
       if (id >= kSKT * kSPieces) break;
       const int r = id / kSPieces, c = id - r * kSPieces;
       const int j = t * kSKT + r;
@@ -115,7 +119,7 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
     MLA_LDS char* kb = ring + slot * kSSlot;
 #pragma unroll
     for (int n = 0; n < kSTasks; ++n) {
-      const int id = tid + 256 * n;
+      const int id = tid + kSThreads * n;
       if (id >= kSKT * kSPieces) break;
       const int r = id / kSPieces, c = id - r * kSPieces;
       MLA_LDS char* row = kb + r * kSP;
@@ -136,7 +140,7 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
     }
   };
 
-  constexpr int DB = 512 / 16;
+  constexpr int DB = 256 / 16;  // this wave's 16 output column blocks
   f32x4_t o[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -201,7 +205,7 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
     }
     // P^T slots 8 g + i: keys 4 g + i (i < 4) and 16 + 4 g + (i - 4)
     const i16x8_t pb = __builtin_bit_cast(i16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-    const MLA_LDS char* vrow0 = kb + (4 * g + (li >> 2)) * kSP + 8 * (li & 3);
+    const MLA_LDS char* vrow0 = kb + (4 * g + (li >> 2)) * kSP + 512 * half + 8 * (li & 3);
     const MLA_LDS char* vrow1 = vrow0 + 16 * kSP;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -228,24 +232,24 @@ __global__ void __launch_bounds__(256) sparse_fp8_decode(SparseParams p) {
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (p.nsplit > 1) {  // normalised partial and its lse, merged by sparse_merge
     const int64_t r = ((int64_t)bi * p.nsplit + split) * p.n_heads + h;
-    float* po = p.part_o + r * 512 + 4 * g;
+    float* po = p.part_o + r * 512 + 256 * half + 4 * g;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
       *(f32x4_t*)(po + 16 * db) = f32x4_t{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
                                           o[db][3] * inv};
-    if (g == 0)
+    if (g == 0 && half == 0)
       p.part_lse[r] = l > 0.f ? (m + __log2f(l)) * 0.69314718055994530942f : -__builtin_inff();
     return;
   }
   uint16_t* orow = (uint16_t*)p.out + (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 +
-                   (int64_t)h * p.o_s2 + 4 * g;
+                   (int64_t)h * p.o_s2 + 256 * half + 4 * g;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const u32x2_t v = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
                        pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
     *(u32x2_t*)(orow + 16 * db) = v;
   }
-  if (p.lse && g == 0)
+  if (p.lse && g == 0 && half == 0)
     p.lse[(int64_t)b * p.l_s0 + (int64_t)qi * p.l_s1 + (int64_t)h * p.l_s2] =
         l > 0.f ? (m + __log2f(l)) * 0.69314718055994530942f : -__builtin_inff();
 }
@@ -320,7 +324,7 @@ hipError_t launch_sparse(const SparseParams& p, hipStream_t s) {
   }
   dim3 grid((unsigned)((int64_t)p.batch * p.q_len), (unsigned)((p.n_heads + 63) / 64),
             (unsigned)p.nsplit);
-  hipLaunchKernelGGL(sparse_fp8_decode, grid, dim3(256), lds, s, p);
+  hipLaunchKernelGGL(sparse_fp8_decode, grid, dim3(kSThreads), lds, s, p);
   if (p.nsplit > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
