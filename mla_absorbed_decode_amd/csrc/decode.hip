@@ -1416,7 +1416,9 @@ __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
 }
 
 // ------------------------------------------ merge + W_UV un-projection, fused
-// For one head h and 16 query tokens: merge each token's row of head h from
+// For one head h, 16 query tokens and a group of 32 W_UV columns (the column
+// groups of a head spread the call over 4x the workgroups; each group merges
+// the same rows, the first writes o_lat and lse): merge each token's row of head h from
 // its split partials (one wave per token; unsplit rows are read back from
 // o_lat), keep the 16 merged rows in LDS as bf16 (the values written to
 // o_lat), then out[token, h, :] = o_lat row . W_UV[h] with 16x16x32 MFMAs,
@@ -1436,15 +1438,19 @@ __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupPara
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   __shared__ int sh_scan[256];
   MLA_LDS char* wslab = (MLA_LDS char*)smem_raw;           // [kKvRank][V] bf16, dense
-  MLA_LDS char* atile = wslab + kKvRank * v.V * 2;          // [16][kVupAPitch]
+  MLA_LDS char* atile = wslab + kKvRank * (v.V / (int)gridDim.z) * 2;  // [16][kVupAPitch]
   const int h = blockIdx.y, tok0 = blockIdx.x * kVupTok;
+  // columns [col0, col0 + VW) of W_UV[h]: the workgroups of a (token group,
+  // head) split the un-projection's columns and each merges the same rows
+  const int VW = v.V / (int)gridDim.z, col0 = (int)blockIdx.z * VW;
+  const bool first = blockIdx.z == 0;  // writes o_lat and lse
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = p.batch * p.q_len;
-  // W_UV[h] -> LDS: chunk q (16 bytes) of the dense [L][V] slab, 64 per load
+  // W_UV[h][:, col0 : col0 + VW] -> LDS: chunk q (16 bytes) of the dense [L][VW] slab, 64 per load
   {
-    const char* W = (const char*)v.w + (int64_t)h * v.w_sh * 2;
-    const int cpr = v.V / 8;  // 16-byte chunks per row
+    const char* W = (const char*)v.w + (int64_t)h * v.w_sh * 2 + (int64_t)col0 * 2;
+    const int cpr = VW / 8;  // 16-byte chunks per row
     const int ninst = kKvRank * cpr / 64;
     for (int inst = wave; inst < ninst; inst += 16) {
       const int q = inst * 64 + lane, r = q / cpr, cp = q % cpr;
@@ -1469,8 +1475,8 @@ __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupPara
     if (merge_row(p, sh_scan, u, row, acc0, acc1, lse2)) {
       packed = u32x4_t{pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
                        pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
-      *(u32x4_t*)orow = packed;
-      if (c0 == 0 && p.lse)
+      if (first) *(u32x4_t*)orow = packed;
+      if (first && c0 == 0 && p.lse)
         p.lse[(int64_t)b * p.l_s0 + (int64_t)qi * p.l_s1 + (int64_t)h * p.l_s2] =
             lse2 == kNegInf ? kNegInf : lse2 * kLn2;
     } else {
@@ -1480,11 +1486,11 @@ __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupPara
   *(MLA_LDS u32x4_t*)(atile + wave * kVupAPitch + c0 * 2) = packed;
   wait_vmcnt<0>();  // this wave's part of the W_UV slab has landed
   __syncthreads();
-  // out tile: waves 0 .. V/16 - 1 take 16 columns each, all 16 tokens
-  if (wave < v.V / 16) {
+  // out tile: waves 0 .. VW/16 - 1 take 16 columns each, all 16 tokens
+  if (wave < VW / 16) {
     const int n0 = wave * 16;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const int row_bytes = v.V * 2, cmask = v.V / 8 - 1;
+    const int row_bytes = VW * 2, cmask = VW / 8 - 1;
 #pragma unroll 4
     for (int ks = 0; ks < kKvRank / 32; ++ks) {
       const i16x8_t av = *(const MLA_LDS i16x8_t*)(atile + li * kVupAPitch + (ks * 32 + 8 * g) * 2);
@@ -1505,7 +1511,7 @@ __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupPara
       if (tt < T) {
         const int b = tt / p.q_len, qi = tt - b * p.q_len;
         ((uint16_t*)v.out)[(int64_t)b * v.o_s0 + (int64_t)qi * v.o_s1 + (int64_t)h * v.o_s2 +
-                           n0 + li] = f32_to_bf16(acc[j]);
+                           col0 + n0 + li] = f32_to_bf16(acc[j]);
       }
     }
   }
@@ -1577,7 +1583,6 @@ hipError_t launch_decode_vup(const DecodePlan& plan, DecodeParams p, const VupPa
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  const size_t smem = (size_t)kKvRank * v.V * 2 + (size_t)kVupTok * kVupAPitch;
   static bool attr_set = false;
   if (!attr_set) {
     e = hipFuncSetAttribute((const void*)decode_merge_vup,
@@ -1587,8 +1592,11 @@ hipError_t launch_decode_vup(const DecodePlan& plan, DecodeParams p, const VupPa
     attr_set = true;
   }
   const int64_t T = (int64_t)p.batch * p.q_len;
-  dim3 grid((unsigned)((T + kVupTok - 1) / kVupTok), (unsigned)p.n_heads);
-  hipLaunchKernelGGL(decode_merge_vup, grid, dim3(1024), smem, s, p, v);
+  // split W_UV's columns into groups of 32 (16 for V = 16) over workgroups
+  const int csplit = v.V >= 32 ? v.V / 32 : 1;
+  const size_t smem_w = (size_t)kKvRank * (v.V / csplit) * 2 + (size_t)kVupTok * kVupAPitch;
+  dim3 grid((unsigned)((T + kVupTok - 1) / kVupTok), (unsigned)p.n_heads, (unsigned)csplit);
+  hipLaunchKernelGGL(decode_merge_vup, grid, dim3(1024), smem_w, s, p, v);
   return hipGetLastError();
 }
 
