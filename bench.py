@@ -248,24 +248,36 @@ def cpu_baseline(case: mi.DecodeCase, step: Step, budget_s: float = 10.0):
     q_pe = f64(step.q_pe.float().cpu().numpy())
     pool = f64(case.pool)
     bt, sl = case.block_table, case.seqlens
-    reps, t_used = 0, 0.0
-    while t_used < budget_s and reps < 100:
-        t0 = time.perf_counter()
-        q_lat = oracle.fold_q(q_nope, w_uk_t)
-        q = np.concatenate([q_lat, q_pe], axis=2)[:, None]
-        o_lat, _ = oracle.attend_paged(q, pool, bt, sl, case.scale, True, case.dims.kv_rank)
-        oracle.v_up(o_lat[:, 0], w_uv)
-        t_used += time.perf_counter() - t0
-        reps += 1
+
+    def run(budget, max_reps):
+        reps, t_used = 0, 0.0
+        while t_used < budget and reps < max_reps:
+            t0 = time.perf_counter()
+            q_lat = oracle.fold_q(q_nope, w_uk_t)
+            q = np.concatenate([q_lat, q_pe], axis=2)[:, None]
+            o_lat, _ = oracle.attend_paged(q, pool, bt, sl, case.scale, True, case.dims.kv_rank)
+            oracle.v_up(o_lat[:, 0], w_uv)
+            t_used += time.perf_counter() - t0
+            reps += 1
+        return reps, t_used
+
+    cores = oracle.num_threads()
+    reps, t_used = run(budget_s, 100)
     kv_bytes = int(sl.astype(np.int64).sum()) * case.dims.entry * 2
+    # the same work on one thread (one repetition, or more within a few seconds)
+    oracle.set_num_threads(1)
+    reps1, t1 = run(3.0, 10)
+    oracle.set_num_threads(cores)
     return {
         "value": round(reps * kv_bytes / t_used / 1e9, 4),
         "unit": "GB/s",
-        "cores": oracle.num_threads(),
+        "cores": cores,
+        "value_1_thread": round(reps1 * kv_bytes / t1 / 1e9, 4),
         "kind": "oracle",
         "sample": f"full V2-Lite batch (64 sequences, {int(sl.sum())} latent rows) x {reps} "
-                  f"repetitions in {t_used:.1f} s: fold, paged attention, un-projection in fp64 "
-                  "(the 64-row cache write is omitted)",
+                  f"repetitions in {t_used:.1f} s on {cores} threads, x {reps1} in {t1:.1f} s on "
+                  "one: fold, paged attention, un-projection in fp64 (the 64-row cache write is "
+                  "omitted)",
         "cpu": platform.processor() or platform.machine(),
     }
 

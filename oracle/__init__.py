@@ -61,6 +61,8 @@ def _load():
         )
         u8p = ctypes.POINTER(ctypes.c_uint8)
         lib.mla_oracle_num_threads.restype = c_int
+        lib.mla_oracle_set_num_threads.argtypes = [c_int]
+        lib.mla_oracle_set_num_threads.restype = None
         lib.mla_oracle_bmm.argtypes = [i64] * 4 + [dp, i64, i64, i64] * 3
         lib.mla_oracle_bmm.restype = None
         lib.mla_oracle_attend_seq.argtypes = [i64] * 5 + [dp, ip64, dp, dbl, c_int, dp, dp, dp]
@@ -121,6 +123,11 @@ def _i32p(a: np.ndarray):
 def num_threads() -> int:
     """OpenMP threads the oracle runs on (honours OMP_NUM_THREADS)."""
     return int(_load().mla_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the following oracle calls."""
+    _load().mla_oracle_set_num_threads(int(n))
 
 
 def bmm_strided(a_buf, a_view, b_buf, b_view, shape):

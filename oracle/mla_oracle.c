@@ -57,6 +57,15 @@ int mla_oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the following calls (the benchmark also times one thread). */
+void mla_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ---------------------------------------------------------------------------
  * Batched matmul, straight from the definition of torch.bmm that [P1]'s
  * double-precision reference (RefBmm) checks against:
