@@ -742,9 +742,21 @@ __device__ __forceinline__ void store_row(const DecodeParams& p, int b, int unit
   if (r >= rows_seq) return;
   const int c0 = 16 * dc0 + 4 * g;
   if (slot >= 0) {
-    float* dst = p.part_o + ((int64_t)slot * p.rows_per_unit + local_row) * kKvRank + c0;
+    // split partials: f32 rows for f32 inputs, bf16 rows (the normalised
+    // partial rounded once) for bf16 inputs, half the split traffic
+    const int64_t off = ((int64_t)slot * p.rows_per_unit + local_row) * kKvRank + c0;
+    if constexpr (C::F32) {
+      float* dst = p.part_o + off;
 #pragma unroll
-    for (int d = 0; d < C::DW; ++d) *(f32x4_t*)(dst + 16 * d) = o[d] * inv;
+      for (int d = 0; d < C::DW; ++d) *(f32x4_t*)(dst + 16 * d) = o[d] * inv;
+    } else {
+      uint16_t* dst = (uint16_t*)p.part_o + off;
+#pragma unroll
+      for (int d = 0; d < C::DW; ++d) {
+        const f32x4_t v = o[d] * inv;
+        *(u32x2_t*)(dst + 16 * d) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+    }
     if (write_lse && g == 0) p.part_lse[(int64_t)slot * p.rows_per_unit + local_row] = lse2;
     return;
   }
@@ -1306,6 +1318,8 @@ decode_partial(DecodeParams p) {
 // 8 columns c0 .. c0 + 7. Returns false when the unit was not split (its only
 // workgroup wrote the row itself); else the merged row (acc0, acc1) and its
 // log2-domain lse (-inf for a unit with no keys, whose row is zero).
+// PART_F32: the split partials are f32 rows (f32 inputs), else bf16 rows.
+template <bool PART_F32>
 __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_scan, int u, int row,
                                           f32x4_t& acc0, f32x4_t& acc1, float& lse2) {
   const int lane = threadIdx.x & 63, c0 = lane * 8;
@@ -1321,8 +1335,22 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
     const int n = last - first + 1;
     const int64_t srow = p.rows_per_unit;
     const float* lp = p.part_lse + (int64_t)(first + u) * srow + row;
-    const float* op = p.part_o + ((int64_t)(first + u) * srow + row) * kKvRank + c0;
+    const int64_t obase = ((int64_t)(first + u) * srow + row) * kKvRank + c0;
     const int64_t ostride = srow * kKvRank;
+    // columns c0 .. c0 + 7 of split row k (k < cnt) as two f32x4
+    auto load_part = [&](int64_t k, f32x4_t& lo, f32x4_t& hi) {
+      if constexpr (PART_F32) {
+        const float* src = p.part_o + obase + k * ostride;
+        lo = *(const f32x4_t*)src;
+        hi = *(const f32x4_t*)(src + 4);
+      } else {
+        const u32x4_t w = *(const u32x4_t*)((const uint16_t*)p.part_o + obase + k * ostride);
+        lo = f32x4_t{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
+                     __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
+        hi = f32x4_t{__builtin_bit_cast(float, w[2] << 16), __builtin_bit_cast(float, w[2] & 0xffff0000u),
+                     __builtin_bit_cast(float, w[3] << 16), __builtin_bit_cast(float, w[3] & 0xffff0000u)};
+      }
+    };
     constexpr int BATCH = 8;
     float M = kNegInf, Lt = 0.f;
     for (int w0 = 0; w0 < n; w0 += 64) {
@@ -1333,9 +1361,7 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
 #pragma unroll
       for (int k = 0; k < BATCH; ++k) {
         const bool in = k < cnt;
-        const float* src = op + (int64_t)(w0 + (in ? k : 0)) * ostride;
-        x0[k] = *(const f32x4_t*)src;
-        x1[k] = *(const f32x4_t*)(src + 4);
+        load_part(w0 + (in ? k : 0), x0[k], x1[k]);
       }
       if (w0 == 0) {
         M = ls;
@@ -1360,9 +1386,7 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
 #pragma unroll
           for (int k = 0; k < BATCH; ++k) {
             const bool in = k0 + k < cnt;
-            const float* src = op + (int64_t)(w0 + (in ? k0 + k : 0)) * ostride;
-            x0[k] = *(const f32x4_t*)src;
-            x1[k] = *(const f32x4_t*)(src + 4);
+            load_part(w0 + (in ? k0 + k : 0), x0[k], x1[k]);
           }
         }
 #pragma unroll
@@ -1398,7 +1422,7 @@ __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   if (r >= p.q_len * p.n_heads) return;
   f32x4_t acc0, acc1;
   float lse2;
-  if (!merge_row(p, sh_scan, u, row, acc0, acc1, lse2)) return;
+  if (!merge_row<F32>(p, sh_scan, u, row, acc0, acc1, lse2)) return;
   const int qi = fdiv(r, p.div_nh), qh = r - qi * p.n_heads;
   const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)qh * p.o_s2 + c0;
   if constexpr (F32) {
@@ -1472,7 +1496,7 @@ __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupPara
     float lse2;
     const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)h * p.o_s2 + c0;
     uint16_t* orow = (uint16_t*)p.out + ooff;
-    if (merge_row(p, sh_scan, u, row, acc0, acc1, lse2)) {
+    if (merge_row<false>(p, sh_scan, u, row, acc0, acc1, lse2)) {
       packed = u32x4_t{pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
                        pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
       if (first) *(u32x4_t*)orow = packed;
