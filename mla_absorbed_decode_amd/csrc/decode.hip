@@ -1319,7 +1319,8 @@ decode_partial(DecodeParams p) {
 // workgroup wrote the row itself); else the merged row (acc0, acc1) and its
 // log2-domain lse (-inf for a unit with no keys, whose row is zero).
 // PART_F32: the split partials are f32 rows (f32 inputs), else bf16 rows.
-template <bool PART_F32>
+// BATCH: partial rows read per round trip (8 or, for bf16 rows, 16).
+template <bool PART_F32, int BATCH = 8>
 __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_scan, int u, int row,
                                           f32x4_t& acc0, f32x4_t& acc1, float& lse2) {
   const int lane = threadIdx.x & 63, c0 = lane * 8;
@@ -1337,31 +1338,42 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
     const float* lp = p.part_lse + (int64_t)(first + u) * srow + row;
     const int64_t obase = ((int64_t)(first + u) * srow + row) * kKvRank + c0;
     const int64_t ostride = srow * kKvRank;
-    // columns c0 .. c0 + 7 of split row k (k < cnt) as two f32x4
-    auto load_part = [&](int64_t k, f32x4_t& lo, f32x4_t& hi) {
+    // split row k's columns c0 .. c0 + 7, as loaded: two f32x4 for f32
+    // partials, one u32x4 of bf16 pairs otherwise (widened when summed)
+    using Raw = std::conditional_t<PART_F32, f32x4_t[2], u32x4_t>;
+    auto load_part = [&](int64_t k, Raw& x) {
       if constexpr (PART_F32) {
         const float* src = p.part_o + obase + k * ostride;
-        lo = *(const f32x4_t*)src;
-        hi = *(const f32x4_t*)(src + 4);
+        x[0] = *(const f32x4_t*)src;
+        x[1] = *(const f32x4_t*)(src + 4);
       } else {
-        const u32x4_t w = *(const u32x4_t*)((const uint16_t*)p.part_o + obase + k * ostride);
-        lo = f32x4_t{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
-                     __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
-        hi = f32x4_t{__builtin_bit_cast(float, w[2] << 16), __builtin_bit_cast(float, w[2] & 0xffff0000u),
-                     __builtin_bit_cast(float, w[3] << 16), __builtin_bit_cast(float, w[3] & 0xffff0000u)};
+        x = *(const u32x4_t*)((const uint16_t*)p.part_o + obase + k * ostride);
       }
     };
-    constexpr int BATCH = 8;
+    auto add_part = [&](float wk, const Raw& x) {
+      if constexpr (PART_F32) {
+        acc0 += wk * x[0];
+        acc1 += wk * x[1];
+      } else {
+        const f32x4_t lo{__builtin_bit_cast(float, x[0] << 16), __builtin_bit_cast(float, x[0] & 0xffff0000u),
+                         __builtin_bit_cast(float, x[1] << 16), __builtin_bit_cast(float, x[1] & 0xffff0000u)};
+        const f32x4_t hi{__builtin_bit_cast(float, x[2] << 16), __builtin_bit_cast(float, x[2] & 0xffff0000u),
+                         __builtin_bit_cast(float, x[3] << 16), __builtin_bit_cast(float, x[3] & 0xffff0000u)};
+        acc0 += wk * lo;
+        acc1 += wk * hi;
+      }
+    };
+    static_assert(BATCH == 8 || (BATCH == 16 && !PART_F32), "8 rows, or 16 bf16 rows");
     float M = kNegInf, Lt = 0.f;
     for (int w0 = 0; w0 < n; w0 += 64) {
       // this lane's split lse, and the first BATCH partial rows, in one round trip
       const int cnt = n - w0 < 64 ? n - w0 : 64;
       const float ls = lane < cnt ? lp[(int64_t)(w0 + lane) * srow] : kNegInf;
-      f32x4_t x0[BATCH], x1[BATCH];
+      Raw x[BATCH];
 #pragma unroll
       for (int k = 0; k < BATCH; ++k) {
         const bool in = k < cnt;
-        load_part(w0 + (in ? k : 0), x0[k], x1[k]);
+        load_part(w0 + (in ? k : 0), x[k]);
       }
       if (w0 == 0) {
         M = ls;
@@ -1386,16 +1398,13 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
 #pragma unroll
           for (int k = 0; k < BATCH; ++k) {
             const bool in = k0 + k < cnt;
-            load_part(w0 + (in ? k0 + k : 0), x0[k], x1[k]);
+            load_part(w0 + (in ? k0 + k : 0), x[k]);
           }
         }
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
           const float wk = __shfl(a, k0 + k);  // weight of split w0 + k0 + k
-          if (k0 + k < cnt) {
-            acc0 += wk * x0[k];
-            acc1 += wk * x1[k];
-          }
+          if (k0 + k < cnt) add_part(wk, x[k]);
         }
       }
     }
@@ -1407,7 +1416,9 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
   return true;
 }
 
-template <bool F32>
+// BATCH 16 (bf16 partials) halves the round trips of units split many ways;
+// with few splits per unit its larger register file costs more than it saves.
+template <bool F32, int BATCH>
 __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   __shared__ int sh_scan[256];
   plan_units(p, sh_scan);
@@ -1422,7 +1433,7 @@ __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   if (r >= p.q_len * p.n_heads) return;
   f32x4_t acc0, acc1;
   float lse2;
-  if (!merge_row<F32>(p, sh_scan, u, row, acc0, acc1, lse2)) return;
+  if (!merge_row<F32, BATCH>(p, sh_scan, u, row, acc0, acc1, lse2)) return;
   const int qi = fdiv(r, p.div_nh), qh = r - qi * p.n_heads;
   const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)qh * p.o_s2 + c0;
   if constexpr (F32) {
@@ -1580,7 +1591,11 @@ hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStre
   hipError_t e = launch_partial<C>(plan, p, s);
   if (e != hipSuccess || !plan.split) return e;
   const int groups = (plan.rows_per_unit + 3) / 4;
-  hipLaunchKernelGGL(decode_merge<C::F32>, dim3(plan.num_units * groups), dim3(256), 0, s, p);
+  // units split about 8 ways or more on average: the 16-row batch
+  if (!C::F32 && plan.grid >= 8 * plan.num_units)
+    hipLaunchKernelGGL((decode_merge<false, 16>), dim3(plan.num_units * groups), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_merge<C::F32, 8>), dim3(plan.num_units * groups), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
