@@ -296,10 +296,11 @@ __global__ void __launch_bounds__(256) sparse_merge(SparseParams p) {
 }  // namespace
 
 size_t plan_sparse(int64_t tokens, int64_t n_heads, int64_t topk, int* split_len, int* nsplit) {
-  // aim for at least 512 workgroups (two per CU), splits of whole 32-entry tiles
+  // aim for at least 256 workgroups, one per CU (a workgroup's 8 waves need over
+  // 128 registers each, so one fills a CU), splits of whole 32-entry tiles
   const int64_t tiles = (topk + kSKT - 1) / kSKT;
   const int64_t base = tokens * ((n_heads + 63) / 64);
-  int64_t want = base > 0 ? (512 + base - 1) / base : 1;
+  int64_t want = base > 0 ? (256 + base - 1) / base : 1;
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
   const int64_t per = (tiles + want - 1) / want;  // tiles per split
