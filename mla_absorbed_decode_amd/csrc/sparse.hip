@@ -54,7 +54,7 @@ __device__ __forceinline__ u32x4_t fp8x8_scaled_bf16(uint32_t lo, uint32_t hi, f
 __global__ void __launch_bounds__(kSThreads, 2) sparse_fp8_decode(SparseParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* ring = (MLA_LDS char*)smem_raw;
-  MLA_LDS int32_t* slots = (MLA_LDS int32_t*)(ring + 2 * kSSlot);
+  MLA_LDS int32_t* slots = (MLA_LDS int32_t*)(ring + 2 * kSSlot + kSThreads * 2 * 16);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hb = w >> 1, half = w & 1;  // head block of 16, output columns 256 half .. + 255
@@ -76,16 +76,20 @@ __global__ void __launch_bounds__(kSThreads, 2) sparse_fp8_decode(SparseParams p
     slots[j] = (s >= 0 && (int64_t)s < p.num_slots) ? s : -1;
   }
 
-  // the head's query row as the B operand: lane holds q[h][32 kk + 8 g .. + 7]
-  constexpr int KK = 576 / 32;
-  i16x8_t qreg[KK];
+  // the two waves of a head block split the score contraction: wave half
+  // takes k-steps KH half .. KH half + KH - 1. The head's query row as the B
+  // operand: lane holds q[h][32 (KH half + kk) + 8 g .. + 7]
+  constexpr int KH = 576 / 32 / 2;
+  i16x8_t qreg[KH];
   {
     const uint16_t* qrow = (const uint16_t*)p.q + (int64_t)b * p.q_s0 + (int64_t)qi * p.q_s1 +
-                           (int64_t)(hok ? h : 0) * p.q_s2 + 8 * g;
+                           (int64_t)(hok ? h : 0) * p.q_s2 + 32 * KH * half + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int kk = 0; kk < KH; ++kk)
       qreg[kk] = hok ? *(const i16x8_t*)(qrow + 32 * kk) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   }
+  // partial scores of every wave, [wave][lane][kh] as f32x4
+  MLA_LDS f32x4_t* xs = (MLA_LDS f32x4_t*)(ring + 2 * kSSlot);
   __syncthreads();  // the slot list is in LDS
 
   const int ntiles = (nkeys + kSKT - 1) / kSKT;
@@ -158,17 +162,25 @@ __global__ void __launch_bounds__(kSThreads, 2) sparse_fp8_decode(SparseParams p
     if (t + 2 < ntiles) load_tile(t + 2, raw2[SET], rsc2[SET], nokey2[SET]);
     const MLA_LDS char* kb = ring + SET * kSSlot;
     const int j0 = t * kSKT;
-    if (wave_heads) {
-    // S^T[key 16 kh + 4 g + jj][head li]
+    // S^T[key 16 kh + 4 g + jj][head li]: this wave's half of the k-steps,
+    // then the other wave's half through LDS (both waves add the same two
+    // partials, so they hold the same scores)
     f32x4_t s[2];
+    if (wave_heads) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      s[kh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const MLA_LDS char* krow = kb + (16 * kh + li) * kSP + 16 * g;
+      for (int kh = 0; kh < 2; ++kh) {
+        s[kh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const MLA_LDS char* krow = kb + (16 * kh + li) * kSP + 64 * KH * half + 16 * g;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        s[kh] = mfma_16x16x32(*(const MLA_LDS i16x8_t*)(krow + 64 * kk), qreg[kk], s[kh]);
+        for (int kk = 0; kk < KH; ++kk)
+          s[kh] = mfma_16x16x32(*(const MLA_LDS i16x8_t*)(krow + 64 * kk), qreg[kk], s[kh]);
+        xs[(w * 64 + lane) * 2 + kh] = s[kh];
+      }
     }
+    __syncthreads();
+    if (wave_heads) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) s[kh] += xs[((w ^ 1) * 64 + lane) * 2 + kh];
     float x[2][4];
     float tmax = -__builtin_inff();
 #pragma unroll
@@ -310,7 +322,11 @@ size_t plan_sparse(int64_t tokens, int64_t n_heads, int64_t topk, int* split_len
   return (size_t)tokens * *nsplit * n_heads * (512 + 1) * sizeof(float);
 }
 
-size_t sparse_lds_bytes(int topk) { return 2 * (size_t)kSSlot + 4 * (size_t)(topk > 0 ? topk : 1); }
+// two ring slots, the partial-score exchange, the slot list
+constexpr int kSXs = kSThreads * 2 * 16;
+size_t sparse_lds_bytes(int topk) {
+  return 2 * (size_t)kSSlot + kSXs + 4 * (size_t)(topk > 0 ? topk : 1);
+}
 
 hipError_t launch_sparse(const SparseParams& p, hipStream_t s) {
   if (p.batch == 0 || p.q_len == 0 || p.n_heads == 0) return hipSuccess;
@@ -319,9 +335,9 @@ hipError_t launch_sparse(const SparseParams& p, hipStream_t s) {
   if (lds > attr) {
     const hipError_t e = hipFuncSetAttribute((const void*)sparse_fp8_decode,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)(2 * kSSlot + 4 * kSparseMaxTopk));
+                                             (int)(2 * kSSlot + kSXs + 4 * kSparseMaxTopk));
     if (e != hipSuccess) return e;
-    attr = 2 * kSSlot + 4 * kSparseMaxTopk;
+    attr = 2 * kSSlot + kSXs + 4 * kSparseMaxTopk;
   }
   dim3 grid((unsigned)((int64_t)p.batch * p.q_len), (unsigned)((p.n_heads + 63) / 64),
             (unsigned)p.nsplit);
