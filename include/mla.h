@@ -438,8 +438,8 @@ int mla_sparse_decode_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
  * needs for `tokens` = B * Sq query tokens of n_heads heads and top-k lists
  * (0 when the call runs unsplit; then workspace may be NULL). When the tokens
  * and head groups alone would leave the chip idle, each slot list is split
- * over several workgroups, whose f32 partials and lse the workspace holds
- * until the merge. Caller-owned, 16-byte aligned, needs no initialisation,
+ * over several workgroups, whose partial rows (normalised, rounded to bf16)
+ * and f32 lse the workspace holds until the merge. Caller-owned, 16-byte aligned, needs no initialisation,
  * carries nothing between calls.
  */
 int mla_sparse_workspace_size(int64_t tokens, int64_t n_heads, int64_t topk, size_t* bytes);

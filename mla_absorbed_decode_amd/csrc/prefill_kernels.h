@@ -63,8 +63,9 @@ struct SparseParams {
   float scale_log2;                              // softmax scale * log2(e)
   // split of each slot list over nsplit workgroups of split_len entries (a
   // multiple of 32); with nsplit > 1 each writes its normalised partial
-  // output part_o [token][split][N][512] and part_lse [token][split][N]
-  // (natural log), and a merge kernel combines them
+  // output, rounded to bf16, as rows of 512 in the first half of part_o
+  // ([token][split][N] rows; the region is sized for f32) and part_lse
+  // [token][split][N] (natural log), and a merge kernel combines them
   int split_len, nsplit;
   float* part_o;
   float* part_lse;

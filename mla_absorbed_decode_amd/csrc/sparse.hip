@@ -242,13 +242,13 @@ __global__ void __launch_bounds__(kSThreads, 2) sparse_fp8_decode(SparseParams p
   l += __shfl_xor(l, 32);
   if (!hok) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (p.nsplit > 1) {  // normalised partial and its lse, merged by sparse_merge
+  if (p.nsplit > 1) {  // normalised partial (rounded to bf16) and its lse, merged by sparse_merge
     const int64_t r = ((int64_t)bi * p.nsplit + split) * p.n_heads + h;
-    float* po = p.part_o + r * 512 + 256 * half + 4 * g;
+    uint16_t* po = (uint16_t*)p.part_o + r * 512 + 256 * half + 4 * g;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      *(f32x4_t*)(po + 16 * db) = f32x4_t{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
-                                          o[db][3] * inv};
+      *(u32x2_t*)(po + 16 * db) = u32x2_t{pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
+                                          pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
     if (g == 0 && half == 0)
       p.part_lse[r] = l > 0.f ? (m + __log2f(l)) * 0.69314718055994530942f : -__builtin_inff();
     return;
@@ -275,21 +275,37 @@ __global__ void __launch_bounds__(256) sparse_merge(SparseParams p) {
   if (h >= p.n_heads) return;
   const int b = bi / p.q_len, qi = bi - b * p.q_len;
   const int64_t r0 = (int64_t)bi * p.nsplit * p.n_heads + h;
-  float mx = -__builtin_inff();
-  for (int s = 0; s < p.nsplit; ++s) mx = fmaxf(mx, p.part_lse[r0 + (int64_t)s * p.n_heads]);
+  // four splits' lse values and bf16 rows per round trip, combined in split
+  // order with a running maximum (the sum rescaled when it rises)
+  float mx = -__builtin_inff(), sum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float sum = 0.f;
-  if (mx != -__builtin_inff()) {
-    for (int s = 0; s < p.nsplit; ++s) {
-      const int64_t r = r0 + (int64_t)s * p.n_heads;
-      const float wgt = __expf(p.part_lse[r] - mx);
-      sum += wgt;
-      const f32x4_t a = *(const f32x4_t*)(p.part_o + r * 512 + 8 * lane);
-      const f32x4_t c = *(const f32x4_t*)(p.part_o + r * 512 + 8 * lane + 4);
+  for (int s0 = 0; s0 < p.nsplit; s0 += 4) {
+    float ls[4];
+    u32x4_t x[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[k] += wgt * a[k];
-        acc[4 + k] += wgt * c[k];
+    for (int k = 0; k < 4; ++k) {
+      const int64_t r = r0 + (int64_t)(s0 + k < p.nsplit ? s0 + k : s0) * p.n_heads;
+      ls[k] = s0 + k < p.nsplit ? p.part_lse[r] : -__builtin_inff();
+      x[k] = *(const u32x4_t*)((const uint16_t*)p.part_o + r * 512 + 8 * lane);
+    }
+    const float gm = fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3]));
+    if (gm > mx) {
+      const float c = mx == -__builtin_inff() ? 0.f : __expf(mx - gm);
+      sum *= c;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= c;
+      mx = gm;
+    }
+    if (mx == -__builtin_inff()) continue;  // no split so far holds a key
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (ls[k] == -__builtin_inff()) continue;  // past the splits, or a split with no key
+      const float wgt = __expf(ls[k] - mx);
+      sum += wgt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wgt * __builtin_bit_cast(float, x[k][i] << 16);
+        acc[2 * i + 1] += wgt * __builtin_bit_cast(float, x[k][i] & 0xffff0000u);
       }
     }
   }
