@@ -629,6 +629,9 @@ int mla_sparse_decode_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
   p.q = q->data; p.q_s0 = q->stride[0]; p.q_s1 = q->stride[1]; p.q_s2 = q->stride[2];
   p.kv = (const uint8_t*)kv_cache->data; p.kv_s0 = kv_cache->stride[0]; p.kv_s1 = kv_cache->stride[1];
   p.num_slots = NB * PG; p.page = (int)PG;
+  p.page_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if (((int64_t)1 << sh) == PG) p.page_shift = sh;
   p.idx = (const int32_t*)indices->data; p.i_s0 = indices->stride[0]; p.i_s1 = indices->stride[1];
   p.topk = (int)K;
   p.out = out->data; p.o_s0 = out->stride[0]; p.o_s1 = out->stride[1]; p.o_s2 = out->stride[2];

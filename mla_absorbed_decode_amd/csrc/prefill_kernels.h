@@ -55,6 +55,7 @@ struct SparseParams {
   const void* q;     int64_t q_s0, q_s1, q_s2;   // [B, Sq, N, 576] bf16
   const uint8_t* kv; int64_t kv_s0, kv_s1;       // [NB, PG, 656] bytes (strides in bytes)
   int64_t num_slots; int page;                   // NB * PG, PG
+  int page_shift;                                // log2(PG) when PG is a power of two, else -1
   const int32_t* idx; int64_t i_s0, i_s1;        // [B, Sq, topk]
   int topk;
   void* out;         int64_t o_s0, o_s1, o_s2;   // [B, Sq, N, 512] bf16

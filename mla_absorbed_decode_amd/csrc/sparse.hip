@@ -112,7 +112,8 @@ __global__ void __launch_bounds__(kSThreads, 2) sparse_fp8_decode(SparseParams p
         s = 0;
         nokey |= 1u << n;
       }
-      const int blk = s / p.page, off = s - blk * p.page;
+      const int blk = p.page_shift >= 0 ? s >> p.page_shift : s / p.page;
+      const int off = s - blk * p.page;
       const uint8_t* e = p.kv + (int64_t)blk * p.kv_s0 + (int64_t)off * p.kv_s1;
       raw[n] = *(const u32x4_t*)(e + (c < 32 ? 16 * c : 528 + 16 * (c - 32)));
       rsc[n] = c < 32 ? *(const float*)(e + 512 + 4 * (c >> 3)) : 1.f;
@@ -198,14 +199,15 @@ __global__ void __launch_bounds__(kSThreads, 2) sparse_fp8_decode(SparseParams p
     const bool move = tmax > m + kSRescale;
     const float mnew = move ? tmax : m;
     const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
-    const float alpha = move ? exp2f(m - muse) : 1.f;
+    const float alpha = move ? __builtin_amdgcn_exp2f(m - muse) : 1.f;
     m = mnew;
     float psum = 0.f;
     uint32_t pk[4];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const float p0 = exp2f(x[kh][0] - muse), p1 = exp2f(x[kh][1] - muse);
-      const float p2 = exp2f(x[kh][2] - muse), p3 = exp2f(x[kh][3] - muse);
+      // the hardware exp2: arguments stay below 8 (the lazy maximum), -inf gives 0
+      const float p0 = __builtin_amdgcn_exp2f(x[kh][0] - muse), p1 = __builtin_amdgcn_exp2f(x[kh][1] - muse);
+      const float p2 = __builtin_amdgcn_exp2f(x[kh][2] - muse), p3 = __builtin_amdgcn_exp2f(x[kh][3] - muse);
       psum += (p0 + p1) + (p2 + p3);
       pk[2 * kh] = pack_bf16x2(p0, p1);
       pk[2 * kh + 1] = pack_bf16x2(p2, p3);
