@@ -186,6 +186,16 @@ struct MhaShape {
 // stay below 2^8, well inside bf16 and f32 range.
 constexpr float kRescale = 8.f;
 
+// 2^x in the attention softmax (arguments below 8, the lazy maximum; -inf
+// gives 0). The hardware instruction alone leaves the narrower instances
+// (192/128: 154 -> 125 registers, a fourth wave per SIMD) 11-28 % faster;
+// the 256-wide one measured 10 % slower with it and keeps exp2f.
+template <int DK>
+__device__ __forceinline__ float softmax_exp2(float x) {
+  if constexpr (DK >= 256) return exp2f(x);
+  else return __builtin_amdgcn_exp2f(x);
+}
+
 template <int DK, int DV>
 __global__ void __launch_bounds__((MhaShape<DK, DV>::THREADS), 2) mha_fwd(MhaParams p) {
   using Sh = MhaShape<DK, DV>;
@@ -355,15 +365,17 @@ __global__ void __launch_bounds__((MhaShape<DK, DV>::THREADS), 2) mha_fwd(MhaPar
         const bool move = tmax > m[qb] + kRescale;
         const float mnew = move ? tmax : m[qb];
         const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
-        alpha[qb] = move ? exp2f(m[qb] - muse) : 1.f;
+        alpha[qb] = move ? softmax_exp2<DK>(m[qb] - muse) : 1.f;
         rescale |= move;
         m[qb] = mnew;
         float psum = 0.f;
         uint32_t pk[4];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-          const float p0 = exp2f(x[kh][0] - muse), p1 = exp2f(x[kh][1] - muse);
-          const float p2 = exp2f(x[kh][2] - muse), p3 = exp2f(x[kh][3] - muse);
+          const float p0 = softmax_exp2<DK>(x[kh][0] - muse);
+          const float p1 = softmax_exp2<DK>(x[kh][1] - muse);
+          const float p2 = softmax_exp2<DK>(x[kh][2] - muse);
+          const float p3 = softmax_exp2<DK>(x[kh][3] - muse);
           psum += (p0 + p1) + (p2 + p3);
           pk[2 * kh] = pack_bf16x2(p0, p1);
           pk[2 * kh + 1] = pack_bf16x2(p2, p3);
