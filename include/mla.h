@@ -267,22 +267,6 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
                       size_t workspace_bytes, mla_stream stream);
 
 /*
- * mla_decode_attend_v_up -- mla_decode_attend followed by the W_UV
- * un-projection of its output, with the split merge and the un-projection in
- * one kernel where the plan splits ([P3] dense decode returning (out, lse);
- * [P2] gate 1, mla_attn_absorbed then mla_decompress_v). o_lat, lse and the
- * workspace are as for mla_decode_attend (o_lat is required: it receives the
- * latent output as usual); then
- *   out[b, i, h, 0:V] = sum_l o_lat[b, i, h, l] * w_uv[h, l, 0:V]
- *   w_uv  [N, L, V]    q's dtype, any strides (inner 1)
- *   out   [B, Sq, N, V] q's dtype, any strides (inner 1)
- * out equals mla_v_up on o_lat bit for bit. The fused kernel takes bf16, a
- * split plan, V = 16, 32, 64 or 128 and 16-byte aligned w_uv rows; other
- * calls run the two kernels one after the other (then, for Sq > 1, o_lat and
- * out must keep one token stride: stride[0] == Sq * stride[1], else
- * MLA_ERR_UNSUPPORTED before anything is launched).
- */
-/*
  * mla_decode_attend_fp8 -- mla_decode_attend over an fp8 latent cache ([P3]
  * test_flashmla_dense_fp8_decode_unified_slot_view: flash_mla_with_kvcache_fp8
  * with a bf16 query, a float8_e4m3fn paged cache, descale_q and descale_k).
@@ -311,6 +295,22 @@ int mla_decode_attend_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
                           const mla_tensor* lse, void* workspace, size_t workspace_bytes,
                           mla_stream stream);
 
+/*
+ * mla_decode_attend_v_up -- mla_decode_attend followed by the W_UV
+ * un-projection of its output, with the split merge and the un-projection in
+ * one kernel where the plan splits ([P3] dense decode returning (out, lse);
+ * [P2] gate 1, mla_attn_absorbed then mla_decompress_v). o_lat, lse and the
+ * workspace are as for mla_decode_attend (o_lat is required: it receives the
+ * latent output as usual); then
+ *   out[b, i, h, 0:V] = sum_l o_lat[b, i, h, l] * w_uv[h, l, 0:V]
+ *   w_uv  [N, L, V]    q's dtype, any strides (inner 1)
+ *   out   [B, Sq, N, V] q's dtype, any strides (inner 1)
+ * out equals mla_v_up on o_lat bit for bit. The fused kernel takes bf16, a
+ * split plan, V = 16, 32, 64 or 128 and 16-byte aligned w_uv rows; other
+ * calls run the two kernels one after the other (then, for Sq > 1, o_lat and
+ * out must keep one token stride: stride[0] == Sq * stride[1], else
+ * MLA_ERR_UNSUPPORTED before anything is launched).
+ */
 int mla_decode_attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,
                            const mla_tensor* block_table, const mla_tensor* seqlens,
                            int64_t max_seqlen, float softmax_scale, int32_t causal,

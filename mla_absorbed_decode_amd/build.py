@@ -1,4 +1,5 @@
-"""Compile libmla.so for gfx950 with hipcc (in-tree, no JIT cache).
+"""Compile libmla.so (and the measurement probes, libmla_probe.so) for gfx950
+with hipcc (in-tree, no JIT cache).
 
     python -m mla_absorbed_decode_amd.build          # or: python mla_absorbed_decode_amd/build.py
 
@@ -20,8 +21,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmla.so")
+PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
 
 SOURCES = ["mla_abi.cpp", "cache_write.hip", "bmm.hip", "decode.hip", "rope.hip", "prefill.hip", "sparse.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -47,18 +50,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

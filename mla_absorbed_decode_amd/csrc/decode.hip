@@ -23,11 +23,14 @@
 // Inside a workgroup
 // ------------------
 // Keys are staged through LDS in tiles of TT tokens with direct global->LDS
-// 16-byte loads, NSLOT tiles deep; every wave loads a quarter of every tile and
-// one barrier per tile publishes it. The four waves split the unit's rows (WR)
-// and the 512 output columns (WC): WR x WC = 4. With few heads (the HBM-bound
-// decode) WC = 4, so each wave keeps a 16-row x 128-column accumulator and the
-// 16 x TT score block is recomputed by each wave; with many rows WR = 4 and
+// 16-byte loads, NSLOT tiles deep; four waves each load a quarter of every
+// tile and one barrier per tile publishes it. The compute waves split the
+// unit's rows (WR row tiles of 16) and the 512 output columns (WC groups):
+// with few heads (the HBM-bound decode) four compute waves of 16 rows x 128
+// columns fed by four dedicated loader waves; with 32 or 64 rows per unit
+// eight waves (two per SIMD, so one wave's LDS waits hide behind the other's
+// MFMAs) of 16 rows x 128 or 256 columns. The waves that share rows split the
+// score contraction by k-step and add their partial scores through LDS, so
 // nothing is recomputed. Per tile a wave computes
 //   S^T[token, row]  = sum_e K[token, e] * Q[row, e]        (MFMA, bf16 -> f32)
 //   online softmax per row (exp2 domain, lazy rescale when the max grows by
@@ -127,6 +130,13 @@ __device__ __forceinline__ int lane_value(int x, int src) {
   return __builtin_amdgcn_readlane(x, src);
 }
 
+// Lane src's value of x for a wave-uniform src in [0, 64): v_readlane, a few
+// cycles, where __shfl would be an LDS permute round trip per call. Indices
+// past 63 wrap (their weights are never used).
+__device__ __forceinline__ float lane_weight(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src & 63));
+}
+
 __device__ void plan_units(const DecodeParams& p, int* sh) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -165,6 +175,7 @@ struct SegLds {
   uint64_t part[4];
   SegHdr hdr;
   uint32_t xs_ctr;  // compute-wave rendezvous of the split score contraction (loader layouts)
+  uint32_t xs_gaveup;  // set by a compute wave whose rendezvous wait gave up (follows xs_ctr)
 };
 // LDS besides the tile ring and score exchange: the workgroup's plan and the
 // staged block table
@@ -371,7 +382,8 @@ struct Cfg {
   static constexpr int PITCH = E * ES;             // bytes per staged row
   static constexpr int CH = PITCH / 16;            // 16-byte chunks per row
   static constexpr int NW = WR * WC;               // compute waves
-  static constexpr int LW = NP > 0 ? NP : NW;       // loader waves
+  // loader waves: the dedicated ones, else the first four compute waves
+  static constexpr int LW = NP > 0 ? NP : (NW < 4 ? NW : 4);
   static constexpr int NT = 64 * (NW + NP);
   static constexpr int ROWS_W = 16 * RT;
   static constexpr int RTILE = ROWS_W * WR;        // rows per unit
@@ -415,7 +427,7 @@ struct Cfg {
   // the same keys and the default policy lets them hit in the caches
   // (measured on the 128-head decode: non-temporal reads cost 7 %).
   static constexpr bool STREAM = !F32 && RTILE <= 32;
-  static_assert(NW == 4, "four compute waves per workgroup");
+  static_assert(NW == 4 || (NW == 8 && NP == 0), "four compute waves, or eight that load too");
   static_assert(NP == 0 || NP == 4, "no loader waves, or four");
   static_assert(!XS || NP == 0 || WR == 1, "with loader waves the exchange spans all compute waves");
   static_assert(!QT || (RTILE <= TT && QI * 64 == RTILE * CH && QI <= LPT), "query tile fits a slot");
@@ -447,7 +459,7 @@ __device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, MLA_LDS f
                                              int j0, const QReg& qreg, WaveState<C>& st,
                                              float scale_log2, int wr, int wc, int dc0,
                                              const Hook& hook, MLA_LDS uint32_t* xs_ctr,
-                                             int& xs_seq) {
+                                             int& xs_seq, int& xs_bad, int rendezvous_polls) {
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   f32x4_t s[C::SUB][C::RT];
 
@@ -502,15 +514,23 @@ __device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, MLA_LDS f
       // meet on a counter: each adds 1 once its partials are stored, then waits
       // until all NW have added for this tile. Every compute wave makes the same
       // sequence of tile_compute calls between the same workgroup barriers, so
-      // the count is reached; the wait is bounded all the same.
+      // the count is reached; the wait is bounded all the same (DecodeParams::rendezvous_polls,
+      // 2^22 by default: seconds), and a wave that gives up marks its segments' outputs NaN
+      // (xs_bad) rather than use partial scores that may not have landed.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       if (lane == 0)
         __hip_atomic_fetch_add(xs_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       const uint32_t target = (uint32_t)C::NW * (uint32_t)(xs_seq + 1);
-      for (int it = 0; it < (1 << 22); ++it) {
+      for (int it = 0; it < rendezvous_polls; ++it) {
         if (__hip_atomic_load(xs_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target)
           break;
         __builtin_amdgcn_s_sleep(1);
+      }
+      if (__hip_atomic_load(xs_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        // tell the other compute waves: every wave that writes part of these
+        // rows then marks them, so a row is NaN as a whole, lse included
+        xs_bad = 1;
+        __hip_atomic_store(xs_ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       ++xs_seq;
@@ -857,7 +877,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
                                               MLA_LDS char* ring, MLA_LDS f32x4_t* xchg) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const bool loader = C::NP == 0 || wave >= C::NW;
+  const bool loader = C::NP == 0 ? wave < C::LW : wave >= C::NW;
   const bool compute = C::NP == 0 || wave < C::NW;
   const int lwave = C::NP == 0 ? wave : wave - C::NW;  // index among the loader waves
   const int g = lane >> 4, li = lane & 15;
@@ -951,7 +971,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
   };
   // global->LDS reads n of this wave's share (n * 3 / LPW == stage) of tile t
   auto issue_part = [&](const NextTile& t, int stage) {
-    if (!t.live) return;
+    if (!t.live || !loader) return;
     MLA_LDS char* dst = ring + t.slot * C::TILE_BYTES;
     if (C::QT && t.query) {
       // query row i of the unit at row i of the slot, staged like a key row;
@@ -1116,6 +1136,9 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     scale_log2 = p.scale_log2 * (*p.descale_q * *p.descale_k);
     vscale = *p.descale_k;
   }
+  int xs_bad = 0;  // set if a rendezvous wait gave up: the outputs written after it are NaN
+  // the rendezvous counter; the word after it is the workgroup's give-up flag
+  MLA_LDS uint32_t* xs_ctr = (MLA_LDS uint32_t*)const_cast<uint32_t*>(&tab->xs_ctr);
   using QV = typename std::conditional<C::F32, f32x4_t, i16x8_t>::type;
   // this wave's k-steps of the query rows: kg = wc + WC*kk (all of them when WC == 1)
   QV qreg[C::RT][C::KW];
@@ -1190,8 +1213,12 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
 #pragma unroll
     for (int rt = 0; rt < C::RT; ++rt) {
       const float lt = wave_sum16(st.l[rt]);
-      const float inv = lt > 0.f ? vscale / lt : 0.f;
-      const float lse2 = lt > 0.f ? st.m[rt] + fast_log2(lt) : kNegInf;
+      if (C::XS && C::NP > 0 &&
+          __hip_atomic_load(xs_ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
+        xs_bad = 1;
+      const float nan = __builtin_nanf("");
+      const float inv = xs_bad ? nan : (lt > 0.f ? vscale / lt : 0.f);
+      const float lse2 = xs_bad ? nan : (lt > 0.f ? st.m[rt] + fast_log2(lt) : kNegInf);
       store_row<C>(p, cs.b, unit_row0, wrow0 + 16 * rt + li, cs.slot, st.o[rt], inv, lse2, dc0,
                    wc == 0);
     }
@@ -1211,8 +1238,9 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
       }
   }
   if (compute) {
-    // retire the query loads (with no loader waves they are older than every tile read in flight)
-    if constexpr (C::NP == 0) {
+    // retire the query loads: in a wave that also loads tiles they are older
+    // than every tile read in flight; a wave with no tile reads waits for all
+    if (C::NP == 0 && loader) {
       const int pro = nsteps < C::NSLOT - 1 ? nsteps : C::NSLOT - 1;
       if (pro <= 0) wait_vmcnt<0>();
       else if (pro == 1) wait_vmcnt<C::LPW>();
@@ -1224,7 +1252,6 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     settle_q();
   }
   int xs_seq = 0;  // tile_compute calls so far (the split-contraction rendezvous count)
-  MLA_LDS uint32_t* xs_ctr = (MLA_LDS uint32_t*)const_cast<uint32_t*>(&tab->xs_ctr);
   if constexpr (C::NP > 0) {
     // ---- separate roles: each runs its own loop (one barrier per stream item)
     if (loader && C::KV8) {
@@ -1250,7 +1277,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
         continue;
       }
       tile_compute<C>(slot, xchg, cs.t_lo + ck * C::TT, qreg, st, scale_log2, wr, wc, dc0,
-                      [](int) {}, xs_ctr, xs_seq);
+                      [](int) {}, xs_ctr, xs_seq, xs_bad, p.rendezvous_polls);
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
         cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
@@ -1274,10 +1301,11 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
         wait_tile(k);
       }
       __syncthreads();
-      const NextTile nt = k + C::NSLOT - 1 < nsteps ? prep_next(k + C::NSLOT - 1) : NextTile{};
+      const NextTile nt =
+          loader && k + C::NSLOT - 1 < nsteps ? prep_next(k + C::NSLOT - 1) : NextTile{};
       tile_compute<C>(ring + (k % C::NSLOT) * C::TILE_BYTES, xchg, cs.t_lo + ck * C::TT, qreg, st,
                       scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); },
-                      xs_ctr, xs_seq);
+                      xs_ctr, xs_seq, xs_bad, p.rendezvous_polls);
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
         cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
@@ -1300,7 +1328,10 @@ decode_partial(DecodeParams p) {
   __shared__ int sh_blk[kBlkCache];
   MLA_LDS char* ring = (MLA_LDS char*)smem_raw;
   MLA_LDS f32x4_t* xchg = (MLA_LDS f32x4_t*)(smem_raw + C::RING_BYTES);
-  if (threadIdx.x == 0) tab.xs_ctr = 0u;  // rendezvous counter; the plan's barrier publishes it
+  if (threadIdx.x == 0) {  // rendezvous counter and give-up flag; the plan's barrier publishes them
+    tab.xs_ctr = 0u;
+    tab.xs_gaveup = 0u;
+  }
   plan_workgroup<C>(p, &tab, sh_blk);
   // a workgroup whose chunk holds no keys (split mode) has nothing to write;
   // without split an empty unit still writes its zero rows
@@ -1319,7 +1350,7 @@ decode_partial(DecodeParams p) {
 // workgroup wrote the row itself); else the merged row (acc0, acc1) and its
 // log2-domain lse (-inf for a unit with no keys, whose row is zero).
 // PART_F32: the split partials are f32 rows (f32 inputs), else bf16 rows.
-// BATCH: partial rows read per round trip (8 or, for bf16 rows, 16).
+// BATCH: partial rows read per round trip.
 template <bool PART_F32, int BATCH = 8>
 __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_scan, int u, int row,
                                           f32x4_t& acc0, f32x4_t& acc1, float& lse2) {
@@ -1363,7 +1394,7 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
         acc1 += wk * hi;
       }
     };
-    static_assert(BATCH == 8 || (BATCH == 16 && !PART_F32), "8 rows, or 16 bf16 rows");
+    static_assert(BATCH == 8, "8 partial rows per round trip");
     float M = kNegInf, Lt = 0.f;
     for (int w0 = 0; w0 < n; w0 += 64) {
       // this lane's split lse, and the first BATCH partial rows, in one round trip
@@ -1403,7 +1434,7 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
         }
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
-          const float wk = __shfl(a, k0 + k);  // weight of split w0 + k0 + k
+          const float wk = lane_weight(a, k0 + k);  // weight of split w0 + k0 + k
           if (k0 + k < cnt) add_part(wk, x[k]);
         }
       }
@@ -1411,13 +1442,100 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
     const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
     acc0 *= inv;
     acc1 *= inv;
-    lse2 = Lt > 0.f ? M + fast_log2(Lt) : kNegInf;
+    // no key: lse -inf; a NaN split (a wave that gave up) makes the row and its lse NaN
+    lse2 = Lt > 0.f ? M + fast_log2(Lt) : (Lt == 0.f ? kNegInf : Lt);
   }
   return true;
 }
 
-// BATCH 16 (bf16 partials) halves the round trips of units split many ways;
-// with few splits per unit its larger register file costs more than it saves.
+// Merge of bf16 partials for plans that split units many ways (the 128-head
+// decode: about 32 splits per unit). One wave per (unit, row, half of the 512
+// columns), 4 columns per lane, so the rows of a call spread over twice the
+// waves of decode_merge; every split's lse and the first kWideBatch partial
+// row pieces are requested in one round trip after the plan. Splits are
+// summed in split order with decode_merge's weights and reductions, so the
+// result is the same bit for bit.
+constexpr int kWideBatch = 32;
+__global__ void __launch_bounds__(256) decode_merge_wide(DecodeParams p) {
+  __shared__ int sh_scan[256];
+  plan_units(p, sh_scan);
+  const int lane = threadIdx.x & 63;
+  const int item = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const int half = item & 1, ur = item >> 1;
+  const int u = ur / p.rows_per_unit, row = ur - u * p.rows_per_unit;
+  if (u >= p.num_units) return;
+  const int b = fdiv(u, p.div_rt);
+  const int r = (u - b * p.row_tiles) * p.rows_per_unit + row;
+  if (r >= p.q_len * p.n_heads) return;
+  const int total = sh_scan[p.num_units - 1];
+  const int chunk = total > 0 ? ceil_div(total, p.grid) : 1;
+  const int end = sh_scan[u], start = u > 0 ? sh_scan[u - 1] : 0;
+  const int qi = fdiv(r, p.div_nh), qh = r - qi * p.n_heads;
+  const int c0 = half * (kKvRank / 2) + lane * 4;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float lse2 = kNegInf;
+  if (end > start) {
+    const int first = (start + p.alpha) / chunk, last = (end - 1) / chunk;
+    if (first == last) return;  // written directly by its only workgroup
+    const int n = last - first + 1;
+    const int64_t srow = p.rows_per_unit;
+    const float* lp = p.part_lse + (int64_t)(first + u) * srow + row;
+    const uint16_t* ob = (const uint16_t*)p.part_o + ((int64_t)(first + u) * srow + row) * kKvRank + c0;
+    const int64_t ostride = srow * kKvRank;
+    auto add_part = [&](float wk, u32x2_t x) {
+      const f32x4_t v{__builtin_bit_cast(float, x[0] << 16), __builtin_bit_cast(float, x[0] & 0xffff0000u),
+                      __builtin_bit_cast(float, x[1] << 16), __builtin_bit_cast(float, x[1] & 0xffff0000u)};
+      acc += wk * v;
+    };
+    float M = kNegInf, Lt = 0.f;
+    u32x2_t x[kWideBatch];
+    for (int w0 = 0; w0 < n; w0 += 64) {
+      const int cnt = n - w0 < 64 ? n - w0 : 64;
+      // this lane's split lse and the first kWideBatch partial pieces, one round trip
+      const float ls = lane < cnt ? lp[(int64_t)(w0 + lane) * srow] : kNegInf;
+#pragma unroll
+      for (int k = 0; k < kWideBatch; ++k)
+        x[k] = *(const u32x2_t*)(ob + (int64_t)(w0 + (k < cnt ? k : 0)) * ostride);
+      if (w0 == 0) {
+        M = ls;
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        for (int w1 = 64; w1 < n; w1 += 64) {
+          const float l2 = w1 + lane < n ? lp[(int64_t)(w1 + lane) * srow] : kNegInf;
+          float m2 = l2;
+          for (int off = 32; off >= 1; off >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, off));
+          M = fmaxf(M, m2);
+        }
+      }
+      const float a = ls == kNegInf ? 0.f : fast_exp2(ls - M);  // this lane's split weight
+      float lsum = a;
+      for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+      Lt += lsum;
+      for (int k0 = 0; k0 < cnt; k0 += kWideBatch) {
+        if (k0 > 0) {
+#pragma unroll
+          for (int k = 0; k < kWideBatch; ++k)
+            x[k] = *(const u32x2_t*)(ob + (int64_t)(w0 + (k0 + k < cnt ? k0 + k : 0)) * ostride);
+        }
+#pragma unroll
+        for (int k = 0; k < kWideBatch; ++k) {
+          const float wk = lane_weight(a, k0 + k);  // weight of split w0 + k0 + k
+          if (k0 + k < cnt) add_part(wk, x[k]);
+        }
+      }
+    }
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    acc *= inv;
+    // no key: lse -inf; a NaN split (a wave that gave up) makes the row and its lse NaN
+    lse2 = Lt > 0.f ? M + fast_log2(Lt) : (Lt == 0.f ? kNegInf : Lt);
+  }
+  const int64_t ooff = (int64_t)b * p.o_s0 + (int64_t)qi * p.o_s1 + (int64_t)qh * p.o_s2 + c0;
+  *(u32x2_t*)((uint16_t*)p.out + ooff) = u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  if (half == 0 && lane == 0 && p.lse)
+    p.lse[(int64_t)b * p.l_s0 + (int64_t)qi * p.l_s1 + (int64_t)qh * p.l_s2] =
+        lse2 == kNegInf ? kNegInf : lse2 * kLn2;
+}
+
+// Plans with few splits per unit (units split many ways take decode_merge_wide).
 template <bool F32, int BATCH>
 __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   __shared__ int sh_scan[256];
@@ -1556,10 +1674,12 @@ __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupPara
 //                      R   WR WC RT TT NSLOT F32    XS     NP
 using Cols64  = Cfg<64, 1, 4, 1, 32, 4, false, true,  4>;  // <= 16 rows: columns split over waves
 using Cols0   = Cfg<0,  1, 4, 1, 32, 4, false, true,  4>;
-using Mixed64 = Cfg<64, 2, 2, 1, 32, 4, false, true,  0>;  // <= 32 rows
-using Mixed0  = Cfg<0,  2, 2, 1, 32, 4, false, true,  0>;
-using Rows64  = Cfg<64, 4, 1, 1, 32, 4, false, false, 0>;  // many rows: rows split over waves
-using Rows0   = Cfg<0,  4, 1, 1, 32, 4, false, false, 0>;
+// 32 rows: eight waves, two 16-row tiles x four 128-column quarters
+using Mixed64 = Cfg<64, 2, 4, 1, 32, 3, false, true,  0>;
+using Mixed0  = Cfg<0,  2, 4, 1, 32, 3, false, true,  0>;
+// 64 rows: eight waves, four 16-row tiles x two 256-column halves
+using Rows64  = Cfg<64, 4, 2, 1, 32, 3, false, true,  0>;
+using Rows0   = Cfg<0,  4, 2, 1, 32, 3, false, true,  0>;
 using ColsF64 = Cfg<64, 1, 4, 1, 16, 4, true,  true,  0>;  // f32
 using ColsF0  = Cfg<0,  1, 4, 1, 16, 4, true,  true,  0>;
 using Cols64F8 = Cfg<64, 1, 4, 1, 32, 2, false, true,  4, true>;  // fp8 cache, any row count
@@ -1592,9 +1712,11 @@ hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStre
   if (e != hipSuccess || !plan.split) return e;
   const int groups = (plan.rows_per_unit + 3) / 4;
   // units split about 8 ways or more on average: the 16-row batch
-  if (!C::F32 && plan.grid >= 8 * plan.num_units)
-    hipLaunchKernelGGL((decode_merge<false, 16>), dim3(plan.num_units * groups), dim3(256), 0, s, p);
-  else
+  if (!C::F32 && plan.grid >= 8 * plan.num_units) {
+    // many splits per unit: two waves per row, every split in one round trip
+    const int64_t waves = (int64_t)plan.num_units * plan.rows_per_unit * 2;
+    hipLaunchKernelGGL(decode_merge_wide, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
+  } else
     hipLaunchKernelGGL((decode_merge<C::F32, 8>), dim3(plan.num_units * groups), dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -1653,7 +1775,10 @@ int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int
   } else if (rows <= 16) {
     variant = rope ? kCols64 : kCols0;
     rtile = Cols64::RTILE;
-  } else if (rows <= 32) {
+  } else if (rows <= 32 || batch * ((rows + Rows64::RTILE - 1) / Rows64::RTILE) < 64) {
+    // 32-row units also where 64-row units would be too few to fill the GPU
+    // without splitting each many ways (the 128-head decode of a few
+    // sequences): their split partials are half as many bytes per key range
     variant = rope ? kMixed64 : kMixed0;
     rtile = Mixed64::RTILE;
   } else {
@@ -1679,8 +1804,9 @@ int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int
     if (g > wb_bound) g = wb_bound;
     plan->grid = (int)g;
     const int64_t slots = g + units;
-    // partials [slots][rtile][L] f32, then lse [slots][rtile] f32
-    plan->workspace_bytes = (size_t)(slots * rtile * (kKvRank + 1) * 4);
+    // partials [slots][rtile][L] (f32 for f32 inputs, bf16 otherwise), then
+    // lse [slots][rtile] f32
+    plan->workspace_bytes = (size_t)(slots * rtile * ((int64_t)kKvRank * (is_f32 ? 4 : 2) + 4));
   } else {
     plan->split = 0;
     plan->grid = (int)units;

@@ -9,6 +9,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "mla.h"
@@ -321,6 +322,19 @@ int mla_decode_workspace_size(int64_t batch, int64_t q_len, int64_t n_heads, int
   return MLA_OK;
 }
 
+// Polls of the decode kernels' bounded LDS rendezvous before a wave gives up
+// and writes NaN: 2^22 (seconds of waiting), or MLA_RENDEZVOUS_POLLS when it
+// is set to a non-negative integer (tests force the give-up path with 0).
+static int rendezvous_polls() {
+  const char* e = getenv("MLA_RENDEZVOUS_POLLS");
+  if (e && *e) {
+    char* end = nullptr;
+    const long v = strtol(e, &end, 10);
+    if (end && *end == 0 && v >= 0 && v <= (1L << 30)) return (int)v;
+  }
+  return 1 << 22;
+}
+
 // Validate an attention call and fill its plan and launch parameters (nothing
 // is launched). *empty is set when the call has nothing to do.
 static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
@@ -397,7 +411,9 @@ static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   if (plan.split) {
     const int64_t slots = (int64_t)plan.grid + plan.num_units;
     p.part_o = (float*)workspace;
-    p.part_lse = (float*)((char*)workspace + (size_t)slots * plan.rows_per_unit * mla::kKvRank * 4);
+    // partial rows are f32 for f32 inputs, bf16 otherwise
+    const size_t pes = dt == MLA_F32 ? 4 : 2;
+    p.part_lse = (float*)((char*)workspace + (size_t)slots * plan.rows_per_unit * mla::kKvRank * pes);
   }
   p.wb = plan.wb;
   p.alpha = plan.alpha;
@@ -413,6 +429,7 @@ static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   p.grid = plan.grid;
   p.descale_q = descale_q;
   p.descale_k = descale_k;
+  p.rendezvous_polls = rendezvous_polls();
   *plan_out = plan;
   *params_out = p;
   return MLA_OK;

@@ -100,7 +100,7 @@ struct DecodeParams {
   int causal;
   void* out; int64_t o_s0, o_s1, o_s2;              // out [B, Sq, N, L]
   float* lse; int64_t l_s0, l_s1, l_s2;             // lse [B, Sq, N] or NULL
-  float* part_o;          // split partials [slots][rows_per_unit][L]
+  float* part_o;          // split partials [slots][rows_per_unit][L]: f32 rows for f32 inputs, else bf16
   float* part_lse;        // [slots][rows_per_unit] (log2 domain)
   int rows_per_unit;      // rows of (query, head) per unit
   int row_tiles;          // units per sequence
@@ -116,6 +116,9 @@ struct DecodeParams {
   // for a bf16 / f32 cache.
   const float* descale_q;
   const float* descale_k;
+  // polls of the compute waves' LDS rendezvous before a wave gives up and
+  // marks its outputs NaN (the few-head layouts)
+  int rendezvous_polls;
 };
 
 // The W_UV un-projection fused into the split merge: out[b, i, h, 0:V] =

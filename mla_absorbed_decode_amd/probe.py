@@ -1,0 +1,87 @@
+"""Measured peaks of the GPU the benchmark runs on (libmla_probe.so, see
+include/mla_probe.h): the dense bf16 MFMA rate and the HBM copy rate.
+
+These are measurement tools for the benchmark, not part of the attention
+path. Each function enqueues its probe kernel on the current stream, times it
+with HIP events on that stream, and returns the rate.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_probe.so")
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(f"{lib_path} is not built; run `python -m mla_absorbed_decode_amd.build`")
+        lib = ctypes.CDLL(lib_path)
+        lib.mla_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.POINTER(ctypes.c_int),
+                                            ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+        lib.mla_probe_mfma_bf16.restype = ctypes.c_int
+        lib.mla_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+        lib.mla_probe_copy.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _timed(fn, reps: int) -> float:
+    """Median ms of `reps` launches of fn() on the current stream."""
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        fn()
+        t1.record(stream)
+        t1.synchronize()
+        times.append(t0.elapsed_time(t1))
+    times.sort()
+    return times[len(times) // 2]
+
+
+def mfma_bf16_tflops(shape: int = 0, waves_per_simd: int = 1, iters: int = 20000,
+                     reps: int = 5) -> float:
+    """Dense bf16 MFMA TFLOP/s over the whole GPU (shape 0: 16x16x32, 1: 32x32x16)."""
+    lib = load()
+    dev = torch.device("cuda:0")
+    sink = torch.empty(1024 * 256 * waves_per_simd, dtype=torch.float32, device=dev)
+    wgs, flops = ctypes.c_int(0), ctypes.c_double(0.0)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        rc = lib.mla_probe_mfma_bf16(sink.data_ptr(), shape, iters, waves_per_simd,
+                                     ctypes.byref(wgs), ctypes.byref(flops), stream)
+        if rc:
+            raise RuntimeError(f"mla_probe_mfma_bf16 failed ({rc})")
+
+    run()
+    ms = _timed(run, reps)
+    return flops.value / (ms * 1e-3) / 1e12
+
+
+def copy_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """HBM GB/s of a device copy of nbytes (read + write counted)."""
+    lib = load()
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        rc = lib.mla_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream)
+        if rc:
+            raise RuntimeError(f"mla_probe_copy failed ({rc})")
+
+    run()
+    ms = _timed(run, reps)
+    return 2 * nbytes / (ms * 1e-3) / 1e9

@@ -247,3 +247,25 @@ def test_workspace_reused_across_calls():
         assert_close(to_np(out), want, "bf16", f"workspace reuse call {i}")
         outs.append(out)
     assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+
+
+def test_rendezvous_give_up_marks_rows_nan(monkeypatch):
+    # The few-head layout's compute waves meet on a bounded LDS counter wait.
+    # With the bound forced to zero polls a wave that arrives before the others
+    # gives up at once: every output row must then be either the right value or
+    # NaN (with a NaN lse), never a silently wrong value.
+    monkeypatch.setenv("MLA_RENDEZVOUS_POLLS", "0")
+    c = mi.decode_case(30, V2, "bf16", [700, 1500, 64, 300, 2222])
+    say("[decode] rendezvous forced to give up (0 polls)")
+    out, lse = run_decode(c)
+    want_o, want_l = oracle_of(c)
+    o, l = to_np(out), to_np(lse)
+    bad = np.isnan(o).any(axis=-1)
+    assert np.array_equal(bad, np.isnan(o).all(axis=-1)), "partly NaN rows"
+    assert np.array_equal(bad, np.isnan(l)), "NaN rows and NaN lse differ"
+    if (~bad).any():
+        assert_close(o[~bad], want_o[~bad], "bf16", "rows that completed")
+        assert_lse_close(l[~bad], want_l[~bad], "rows that completed")
+    monkeypatch.delenv("MLA_RENDEZVOUS_POLLS")
+    out2, _ = run_decode(c)  # the default bound again: a normal, finite result
+    assert_close(to_np(out2), want_o, "bf16", "after the forced give-up")
