@@ -267,6 +267,30 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
                       size_t workspace_bytes, mla_stream stream);
 
 /*
+ * mla_decode_attend_noalloc -- mla_decode_attend for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same validation, plan, kernels and results, bit for bit.
+ * Instead of a caller's workspace the call uses a scratch array of
+ * MLA_NOALLOC_SCRATCH_BYTES bytes held in device memory by the library on
+ * every GPU it runs on, from its load until the process ends. The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * its first call on a device looks the array's address up once.
+ * Errors: as mla_decode_attend; MLA_ERR_WORKSPACE when the call's plan needs
+ * more than MLA_NOALLOC_SCRATCH_BYTES (mla_decode_workspace_size tells), before
+ * anything is launched; MLA_ERR_HIP if the address lookup fails.
+ * Every call on one GPU shares that GPU's array and leaves the last call's
+ * contents in it: calls that overlap in time on one GPU (concurrent streams,
+ * host threads) race and must not be issued; calls in order on one stream
+ * are safe.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mla_decode_attend_noalloc(const mla_tensor* q, const mla_tensor* kv_cache,
+                              const mla_tensor* block_table, const mla_tensor* seqlens,
+                              int64_t max_seqlen, float softmax_scale, int32_t causal,
+                              const mla_tensor* out, const mla_tensor* lse, mla_stream stream);
+
+/*
  * mla_decode_attend_fp8 -- mla_decode_attend over an fp8 latent cache ([P3]
  * test_flashmla_dense_fp8_decode_unified_slot_view: flash_mla_with_kvcache_fp8
  * with a bf16 query, a float8_e4m3fn paged cache, descale_q and descale_k).

@@ -47,6 +47,7 @@ __all__ = [
     "mla_concat_and_cache_rope",
     "mla_absorb_q_and_cache",
     "mla_decode_attend_v_up",
+    "mla_decode_attend_noalloc",
     "mla_status_str",
     "lib_path",
     "load",
@@ -109,6 +110,7 @@ def load() -> ctypes.CDLL:
         lib.mla_concat_and_cache_rope.argtypes = [P, P, P, P, dbl, P, vp]
         lib.mla_absorb_q_and_cache.argtypes = [P, P, P, P, P, P, P, P, P, dbl, vp]
         lib.mla_decode_attend_v_up.argtypes = [P, P, P, P, i64, f32, i32, P, P, P, P, vp, sz, vp]
+        lib.mla_decode_attend_noalloc.argtypes = [P, P, P, P, i64, f32, i32, P, P, vp]
         lib.mla_concat_and_cache_fp8.argtypes = [P, P, P, P, vp, vp]
         lib.mla_decode_attend_fp8.argtypes = [P, P, P, P, i64, f32, i32, vp, vp, P, P, vp, sz, vp]
         lib.mla_decompress_kv.argtypes = [P, P, P, P, P, P, vp]
@@ -120,6 +122,7 @@ def load() -> ctypes.CDLL:
                    "mla_decode_attend", "mla_v_up", "mla_rope_interleaved", "mla_absorb_q_rope",
                    "mla_concat_and_cache_rope", "mla_absorb_q_and_cache",
                    "mla_decode_attend_v_up", "mla_decompress_kv", "mla_prefill_attend",
+                   "mla_decode_attend_noalloc",
                    "mla_sparse_decode_fp8", "mla_sparse_workspace_size"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_status_str.argtypes = [ctypes.c_int]
@@ -282,6 +285,21 @@ def mla_decode_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_sca
                                  int(bool(causal)), _ref(desc(out)), _ref(desc(lse)),
                                  workspace.data_ptr(), workspace.numel(), _stream(out)),
            "mla_decode_attend")
+    return out
+
+
+def mla_decode_attend_noalloc(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
+                              causal, out, lse=None):
+    """mla_decode_attend without a workspace: the library's own device scratch
+    serves as one, and nothing is allocated (for callers that cannot allocate).
+    Calls that overlap in time on one GPU must not be issued (they share it)."""
+    _device_check(q, kv_cache, block_table, seqlens, out, lse)
+    lib = load()
+    _check(lib.mla_decode_attend_noalloc(_ref(desc(q)), _ref(desc(kv_cache)),
+                                         _ref(desc(block_table)), _ref(desc(seqlens)),
+                                         int(max_seqlen), float(softmax_scale), int(bool(causal)),
+                                         _ref(desc(out)), _ref(desc(lse)), _stream(out)),
+           "mla_decode_attend_noalloc")
     return out
 
 

@@ -12,6 +12,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "mla.h"
 #include "mla_kernels.h"
 #include "prefill_kernels.h"
@@ -448,6 +450,51 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   if (rc || empty) return rc;
   const int64_t R = q->shape[3] - out->shape[3];
   return launched(mla::launch_decode(plan, p, R, q->dtype == MLA_F32, (hipStream_t)stream));
+}
+
+// ---------------------------------------------- decode without allocation
+// The scratch of mla_decode_attend_noalloc: a file-scope device array that
+// each GPU holds from the library's load until the process ends. In host code
+// the name `scratch` is only a host-side stand-in for the symbol; the device
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is passed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // per device: the address of its copy of `scratch`
+
+// The current device's scratch address (looked up on the first call on it).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MLA_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return MLA_OK;
+}
+}  // namespace
+
+int mla_decode_attend_noalloc(const mla_tensor* q, const mla_tensor* kv_cache,
+                              const mla_tensor* block_table, const mla_tensor* seqlens,
+                              int64_t max_seqlen, float softmax_scale, int32_t causal,
+                              const mla_tensor* out, const mla_tensor* lse, mla_stream stream) {
+  void* ws = nullptr;
+  int rc = scratch_address(&ws);
+  if (rc) return rc;
+  // the same validation, plan and kernels as mla_decode_attend, with the
+  // device's scratch as the workspace; a plan needing more than the scratch
+  // is rejected (MLA_ERR_WORKSPACE) before anything is launched. The decode
+  // workspace needs no initialisation, so nothing is cleared.
+  return mla_decode_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal,
+                           out, lse, ws, (size_t)MLA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int mla_decode_attend_fp8(const mla_tensor* q, const mla_tensor* kv_cache,

@@ -53,7 +53,7 @@ def test_library_exports_every_declared_symbol(lib):
                           "mla_absorb_q_and_cache", "mla_decode_attend_v_up",
                           "mla_concat_and_cache_fp8", "mla_decode_attend_fp8",
                           "mla_decompress_kv", "mla_prefill_attend", "mla_sparse_decode_fp8",
-                          "mla_sparse_workspace_size"}
+                          "mla_sparse_workspace_size", "mla_decode_attend_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
