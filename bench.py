@@ -25,7 +25,16 @@ value = latent-KV bytes the step must read (sum of seqlens x 576 x 2 B) per
 second of step time. The roofline object covers the attention call (its
 partial and merge kernels): a graph holding only that call, once per cache
 copy, is replayed for K calls right after the steps and timed with HIP events
-on the stream it runs on.
+on the stream it runs on; its fractions are of the published HBM peak and of
+the read rate measured on this GPU (measured_peaks, libmla_probe.so).
+
+The other objects of the line: v2lite_warm (the attention call over one
+cache copy, labelled warm), v3_decode (128 heads, cold over enough copies of
+the rows each call reads; warm and permuted-table runs beside it), fp8_cache,
+rope, sparse_fp8, nope_prefill (bf16 and fp32), cache_write (200 rows into a
+3-layer unified slot), tiny_fp32 (the 64-token fp32 prefill and 32 decode
+steps) and cpu_baseline (the fp64 oracle on the host: the V2-Lite step, and
+the V3 and NoPE attention calls).
 """
 from __future__ import annotations
 
@@ -49,6 +58,7 @@ import mla_inputs as mi  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_MATRIX_PEAK_TFLOPS = 157.3
 LLC_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 # the sources the attention kernels are compiled from
@@ -208,6 +218,32 @@ def time_steps(step: Step, steps: int, warmup: int):
     return total_ms, wall, attn_ms
 
 
+def measured_peaks() -> dict:
+    """The GPU's own peaks, measured by the probes of libmla_probe.so: dense
+    bf16 MFMA (v_mfma_f32_16x16x32_bf16, eight independent chains per wave),
+    an HBM read stream and an HBM copy (1 GiB each, non-temporal 16-byte
+    accesses). The best of a few launch shapes is kept."""
+    from mla_absorbed_decode_amd import probe
+
+    mfma = max(probe.mfma_bf16_tflops(0, w) for w in (2, 4))
+    read = max(probe.read_gbs(1 << 30, w) for w in (1, 2, 4))
+    copy = probe.copy_gbs(1 << 30)
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(read, 1),
+            "hbm_copy_gbs": round(copy, 1),
+            "how": "libmla_probe.so: bf16 16x16x32 MFMA chains (2 or 4 waves/SIMD), "
+                   "1 GiB non-temporal read stream (1, 2 or 4 workgroups/CU) and copy; best kept"}
+
+
+def attention_warm_ms(step: Step, steps: int, warmup: int) -> float:
+    """ms per attention call over ONE cache copy, replayed back to back: its
+    163 MB of latent rows are partly resident in the 256 MB last-level cache
+    (a warm figure, reported apart from the cold headline)."""
+    graphs = capture(lambda _: [step.attend(0) for _ in range(4)], 1)
+    if warmup:
+        replay(graphs, 0, warmup)
+    return replay(graphs, 0, steps) / (4 * steps)
+
+
 def attention_bytes(case: mi.DecodeCase) -> int:
     """Algorithmic bytes of one attention call: every visible latent row once,
     plus q, out and lse."""
@@ -278,22 +314,91 @@ def cpu_baseline(case: mi.DecodeCase, step: Step, budget_s: float = 10.0):
                   f"repetitions in {t_used:.1f} s on {cores} threads, x {reps1} in {t1:.1f} s on "
                   "one: fold, paged attention, un-projection in fp64 (the 64-row cache write is "
                   "omitted)",
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
     }
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _oracle_timed(fn, budget_s: float):
+    """Best of up to 3 runs of fn within budget_s, or one run if it takes longer
+    than 30 s. Returns (seconds, runs)."""
+    best, runs, used = float("inf"), 0, 0.0
+    while runs < 3:
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        best, runs, used = min(best, dt), runs + 1, used + dt
+        if dt > 30.0 or used > budget_s:
+            break
+    return best, runs
+
+
+def cpu_baseline_more(budget_s: float = 20.0) -> dict:
+    """The oracle's absorbed attention alone on the V3 decode batch and on the
+    NoPE prefill (the call timed, its inputs prepared beforehand)."""
+    import oracle
+
+    cores = oracle.num_threads()
+    res = {}
+    c = mi.v3_decode(seed=0, neighbour_fill=0.0)
+    f64 = lambda x: np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    q, pool = f64(c.q), f64(c.pool)
+    sec, runs = _oracle_timed(lambda: oracle.attend_paged(q, pool, c.block_table, c.seqlens,
+                                                          c.scale, True, c.dims.kv_rank), budget_s)
+    kv = int(c.seqlens.astype(np.int64).sum()) * c.dims.entry * 2
+    res["v3_decode"] = {"value": round(kv / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
+                        "gflops": round(attention_flops(c) / sec / 1e9, 2),
+                        "seconds": round(sec, 3), "runs": runs,
+                        "sample": "the whole V3 batch (4 x 4096 keys, 128 heads): paged "
+                                  "absorbed attention in fp64"}
+    n = mi.nope_prefill(0, mi.BF16)
+    d, t = n["dims"], n["t"]
+    q_lat = oracle.fold_q(f64(n["q_nope"]), f64(n["w_uk_t"]))[None]
+    kvp = f64(n["c_kv"]).reshape(t // n["page"], n["page"], d.kv_rank)
+    bt = np.arange(t // n["page"], dtype=np.int32)[None]
+    sl = np.array([t], dtype=np.int32)
+    sec, runs = _oracle_timed(lambda: oracle.attend_paged(q_lat, kvp, bt, sl, n["scale"], True,
+                                                          d.kv_rank), budget_s)
+    pairs = d.n_head * t * (t + 1) // 2
+    res["nope_prefill"] = {"value": round(pairs * 2 * (2 * d.kv_rank) / sec / 1e9, 2),
+                           "unit": "GFLOP/s", "cores": cores, "seconds": round(sec, 3),
+                           "runs": runs,
+                           "sample": "absorbed attention of the NoPE prefill (64 heads, 2048 "
+                                     "causal queries over 2048 latent rows) in fp64"}
+    return res
+
+
 def v3_secondary(dev, steps: int, warmup: int, eager: bool = False):
-    """128-head V3 decode (B=4 x 4096, block-major view): attention call only
-    (eager: every call launched from the host, for counter collection)."""
+    """128-head V3 decode (B=4 x 4096, block-major view): attention call only.
+    Cold: the calls rotate over enough copies of the 3-layer allocation that
+    the latent rows they read (sum(seqlens) x 1152 B per call) exceed twice
+    the last-level cache; also with a permuted block table (cold), and warm
+    (one copy, its rows LLC-resident). eager: every call launched from the
+    host, for counter collection."""
     c = mi.v3_decode(seed=0, neighbour_fill=0.0)
     d = c.dims
     bf = torch.bfloat16
     q = torch.from_numpy(c.q).to(bf).to(dev)
-    copies = max(1, math.ceil(2 * LLC_BYTES / (c.pool.nbytes // 2 * 3)))
+    kv_read = int(c.seqlens.astype(np.int64).sum()) * d.entry * 2
+    copies = math.ceil(2 * LLC_BYTES / kv_read) + 1
     unis = [torch.from_numpy(c.unified()).to(bf).to(dev)]
     unis += [unis[0].clone() for _ in range(copies - 1)]
     views = [u[:, 1] for u in unis]
     bt = torch.from_numpy(c.block_table).to(dev)
+    # the same pool read through a permuted block table (pages in random order)
+    perm = mi.stream(0, 77).permutation(c.num_blocks)
+    bt_perm = torch.from_numpy(perm[c.block_table].astype(np.int32)).to(dev)
     sl = torch.from_numpy(c.seqlens).to(dev)
     out = torch.empty(c.batch, 1, d.n_head, d.kv_rank, dtype=bf, device=dev)
     lse = torch.empty(c.batch, 1, d.n_head, dtype=torch.float32, device=dev)
@@ -317,12 +422,27 @@ def v3_secondary(dev, steps: int, warmup: int, eager: bool = False):
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / steps
         return _v3_line(c, ms)
-    graphs = capture(run, len(views))
-    whole = capture(lambda _: [run(k) for k in range(len(views))], 1)[0]
-    if warmup:
-        replay_steps(whole, graphs, warmup)
-    ms = replay_steps(whole, graphs, steps) / steps
-    return _v3_line(c, ms)
+
+    def timed(fn, n):
+        graphs = capture(fn, n)
+        whole = capture(lambda _: [fn(k) for k in range(n)], 1)[0]
+        if warmup:
+            replay_steps(whole, graphs, warmup)
+        return replay_steps(whole, graphs, steps) / steps
+
+    ms = timed(run, len(views))
+    line = _v3_line(c, ms)
+    line["cache_copies"] = copies
+    line["kv_bytes_rotated"] = copies * kv_read
+    warm_ms = timed(lambda i: run(0), 4)
+    line["warm_attention_us"] = round(warm_ms * 1e3, 2)
+    line["warm_label"] = "one cache copy reused: its 18.9 MB of latent rows stay in the LLC"
+    runp = lambda i: mla.mla_decode_attend(q, views[i % len(views)], bt_perm, sl, c.max_seqlen,
+                                           c.scale, True, out, lse, workspace=ws)
+    runp(0)
+    torch.cuda.synchronize()
+    line["permuted_table_attention_us"] = round(timed(runp, len(views)) * 1e3, 2)
+    return line
 
 
 def _v3_line(c, ms):
@@ -475,6 +595,44 @@ def prefill_secondary(dev, steps: int, warmup: int):
     res["decompress_kv_tflops"] = round(tf(2 * fold, res["decompress_kv_us"]), 1)
     res["absorbed_route_us"] = round(res["fold_us"] + res["absorbed_attend_us"] + res["v_up_us"], 2)
     res["naive_route_us"] = round(res["decompress_kv_us"] + res["naive_attend_us"], 2)
+    # the same absorbed route in fp32 (fp32 inputs, fp32 MFMA; the naive
+    # attention kernel takes bf16 only)
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+    c32 = mi.nope_prefill(0, mi.F32)
+    qn32, ckv32, wk32, wv32 = f32(c32["q_nope"]), f32(c32["c_kv"]), f32(c32["w_uk_t"]), f32(c32["w_uv"])
+    cache32 = ckv32.view(nb, page, L)
+    q32 = torch.empty(1, t, N, L, dtype=torch.float32, device=dev)
+    o32 = torch.empty(1, t, N, L, dtype=torch.float32, device=dev)
+    out32 = torch.empty(t, N, V, dtype=torch.float32, device=dev)
+    ws32 = torch.empty(max(1, mla.mla_decode_workspace_size(1, t, N, L, t, page, torch.float32)),
+                       dtype=torch.uint8, device=dev)
+    k32 = torch.empty(t, N, P, dtype=torch.float32, device=dev)
+    v32 = torch.empty(t, N, V, dtype=torch.float32, device=dev)
+    calls32 = {
+        "fold_us": lambda: mla.mla_absorb_q(qn32, wk32, None, q32[0]),
+        "absorbed_attend_us": lambda: mla.mla_decode_attend(q32, cache32, bt, sl, t, scale, True,
+                                                            o32, None, workspace=ws32),
+        "v_up_us": lambda: mla.mla_v_up(o32[0], wv32, out32),
+        "decompress_kv_us": lambda: mla.mla_decompress_kv(ckv32, None, wk32, wv32, k32, v32),
+    }
+    r32 = {}
+    for name, fn in calls32.items():
+        fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        reps = 3
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        r32[name] = round(t0.elapsed_time(t1) / reps * 1e3, 2)
+    r32["absorbed_attend_tflops"] = round(tf(abs_att, r32["absorbed_attend_us"]), 1)
+    r32["absorbed_attend_frac_of_fp32_matrix_peak"] = round(
+        r32["absorbed_attend_tflops"] / FP32_MATRIX_PEAK_TFLOPS, 4)
+    r32["absorbed_route_us"] = round(r32["fold_us"] + r32["absorbed_attend_us"] + r32["v_up_us"], 2)
+    res["fp32"] = r32
     res["algorithmic_gflop"] = {"absorbed_attend": round(abs_att / 1e9, 1),
                                 "naive_attend": round(nai_att / 1e9, 1),
                                 "fold": round(fold / 1e9, 1), "v_up": round(fold / 1e9, 1),
@@ -525,6 +683,91 @@ def sparse_secondary(dev, steps: int, warmup: int):
     res["workload"] = ("sparse fp8 decode, 656-byte entries (512 e4m3 + 4 f32 scales + 64 bf16 "
                        "rope), 64-entry pages, N(0,0.1^2) values, scales 1; graphs of 4 calls "
                        "on one pool (warm: the pools fit the last-level cache)")
+    return res
+
+
+def cache_write_secondary(dev, steps: int, warmup: int):
+    """The latent cache write config: 200 bf16 [c_kv | k_pe] rows (N(0,1))
+    through a random-permutation slot map into the middle layer of a 3-layer
+    block-major unified slot [32, 3 x 64 x 576]. Graphs of 20 calls."""
+    c = mi.cache_write_case(0)
+    bf = torch.bfloat16
+    kv_c = torch.from_numpy(c["kv_c"]).to(bf).to(dev)
+    k_pe = torch.from_numpy(c["k_pe"]).to(bf).to(dev)
+    slots = torch.from_numpy(c["slots"]).to(dev)
+    buf = torch.zeros(c["buf_shape"], dtype=bf, device=dev)
+    view = buf.view(c["num_blocks"], c["n_layers"], c["page"], c["entry"])[:, c["layer"]]
+    reps = 20
+    fn = lambda i: [mla.mla_concat_and_cache(kv_c, k_pe, slots, view) for _ in range(reps)]
+    fn(0)
+    graphs = capture(fn, 1)
+    if warmup:
+        replay(graphs, 0, warmup)
+    us = replay(graphs, 0, steps) / (steps * reps) * 1e3
+    nbytes = 2 * len(c["slots"]) * c["entry"] * 2  # each row read once and written once
+    return {"workload": "cache write: 200 tokens x (512 + 64) bf16 into the middle layer of a "
+                        "3-layer block-major unified slot [32, 3 x 64 x 576], random slots",
+            "us": round(us, 2), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "bound": "latency (230 KB read + 230 KB written per call)"}
+
+
+def tiny_fp32_secondary(dev, steps: int, warmup: int):
+    """The tiny fp32 config (16 heads, d_nope 128, rope 64, v 128, rank 512,
+    one 64-token page): the causal prefill of 64 tokens (fold, cache write,
+    attention, un-projection), and the 32 decode steps of the stepwise gate
+    (each writes row t, folds token t, attends over t + 1 keys and
+    un-projects) as one graph."""
+    c = mi.tiny_prefill_decode(0)
+    d, T = c["dims"], c["t"]
+    f = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+    q_nope, q_pe, c_kv, k_pe = f(c["q_nope"]), f(c["q_pe"]), f(c["c_kv"]), f(c["k_pe"])
+    w_uk_t, w_uv = f(c["w_uk_t"]), f(c["w_uv"])
+    cache = torch.zeros(1, T, d.entry, dtype=torch.float32, device=dev)
+    bt = torch.zeros(1, 1, dtype=torch.int32, device=dev)
+    slots = torch.arange(T, dtype=torch.int64, device=dev)
+    q = torch.empty(1, T, d.n_head, d.entry, dtype=torch.float32, device=dev)
+    o_lat = torch.empty(1, T, d.n_head, d.kv_rank, dtype=torch.float32, device=dev)
+    out = torch.empty(T, d.n_head, d.d_v, dtype=torch.float32, device=dev)
+    sl_full = torch.tensor([T], dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, mla.mla_decode_workspace_size(1, T, d.n_head, d.kv_rank, T, T,
+                                                          torch.float32)),
+                     dtype=torch.uint8, device=dev)
+    ws1 = torch.empty(max(1, mla.mla_decode_workspace_size(1, 1, d.n_head, d.kv_rank, T, T,
+                                                           torch.float32)),
+                      dtype=torch.uint8, device=dev)
+
+    def prefill(_):
+        mla.mla_absorb_q(q_nope, w_uk_t, q_pe, q[0])
+        mla.mla_concat_and_cache(c_kv, k_pe, slots, cache)
+        mla.mla_decode_attend(q, cache, bt, sl_full, T, c["scale"], True, o_lat, None,
+                              workspace=ws)
+        mla.mla_v_up(o_lat[0], w_uv, out)
+
+    first = T // 2
+    sls = [torch.tensor([t + 1], dtype=torch.int32, device=dev) for t in range(first, T)]
+    q1 = torch.empty(1, 1, d.n_head, d.entry, dtype=torch.float32, device=dev)
+    o1 = torch.empty(1, 1, d.n_head, d.kv_rank, dtype=torch.float32, device=dev)
+    out1 = torch.empty(1, d.n_head, d.d_v, dtype=torch.float32, device=dev)
+
+    def decode(_):
+        for k, t in enumerate(range(first, T)):
+            mla.mla_concat_and_cache(c_kv[t:t + 1], k_pe[t:t + 1], slots[t:t + 1], cache)
+            mla.mla_absorb_q(q_nope[t:t + 1], w_uk_t, q_pe[t:t + 1], q1[:, 0])
+            mla.mla_decode_attend(q1, cache, bt, sls[k], T, c["scale"], True, o1, None,
+                                  workspace=ws1)
+            mla.mla_v_up(o1[:, 0], w_uv, out1)
+
+    res = {"workload": "tiny fp32: 16 heads, d_nope 128, d_rope 64, d_v 128, rank 512, "
+                       "t_q = t_kv = 64 causal, one page; then 32 decode steps"}
+    for name, fn in (("prefill_us", prefill), ("decode_32_steps_us", decode)):
+        fn(0)
+        graphs = capture(fn, 1)
+        if warmup:
+            replay(graphs, 0, warmup)
+        res[name] = round(replay(graphs, 0, steps) / steps * 1e3, 2)
+    pairs = d.n_head * T * (T + 1) // 2
+    res["prefill_attention_pairs"] = pairs
+    res["decode_step_us"] = round(res["decode_32_steps_us"] / (T - first), 2)
     return res
 
 
@@ -600,6 +843,10 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from the host instead of replaying graphs "
                          "(for counter collection)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA / HBM peaks (libmla_probe.so)")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the cache-write and tiny fp32 lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy three times (reference for "
                          "scaling HBM byte counters)")
@@ -668,9 +915,25 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "roofline": roof,
     }
+    if not args.eager:
+        warm_ms = attention_warm_ms(step, max(10, args.steps // 2), args.warmup)
+        line["v2lite_warm"] = {
+            "attention_us": round(warm_ms * 1e3, 2),
+            "gbs": round(a_bytes / (warm_ms * 1e-3) / 1e9, 1),
+            "label": "warm: one cache copy replayed back to back (its latent rows partly "
+                     "LLC-resident); the headline and roofline are cold"}
+    peaks = None
+    if not args.no_peaks:
+        peaks = measured_peaks()
+        line["measured_peaks"] = peaks
+        roof["peak_measured"] = peaks["hbm_read_gbs"]
+        roof["frac_measured"] = round(achieved / peaks["hbm_read_gbs"], 4)
     if not args.no_v3:
         line["v3_decode"] = v3_secondary(dev, max(10, args.steps // 2), args.warmup,
                                          eager=args.eager)
+        if peaks:
+            line["v3_decode"]["mfma_frac_measured"] = round(
+                line["v3_decode"]["tflops"] / peaks["mfma_bf16_tflops"], 4)
     if not args.no_fp8:
         line["fp8_cache"] = fp8_secondary(step, dev, max(10, args.steps // 2), args.warmup,
                                           eager=args.eager)
@@ -680,8 +943,12 @@ def main():
         line["sparse_fp8"] = sparse_secondary(dev, max(5, args.steps // 5), min(args.warmup, 3))
     if not args.no_prefill:
         line["nope_prefill"] = prefill_secondary(dev, max(5, args.steps // 10), min(args.warmup, 3))
+    if not args.no_small:
+        line["cache_write"] = cache_write_secondary(dev, max(10, args.steps // 2), args.warmup)
+        line["tiny_fp32"] = tiny_fp32_secondary(dev, max(10, args.steps // 2), args.warmup)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(case, step)
+        line["cpu_baseline"].update(cpu_baseline_more())
     print(json.dumps(line), flush=True)
 
 

@@ -2,8 +2,8 @@
  * attention interface in mla.h).
  *
  * The benchmark quotes each kernel against the published MI355X peaks and
- * also against the peaks these two probes measure on the GPU it runs on: the
- * dense bf16 matrix-core rate and the HBM copy rate. Both enqueue one kernel
+ * also against the peaks these probes measure on the GPU it runs on: the
+ * dense bf16 matrix-core rate and the HBM copy and read rates. Each enqueues one kernel
  * on `stream` and return at once; the caller times them (HIP events) and
  * owns every buffer. Return value: 0 on success, -1 for a NULL pointer, -5
  * for an argument outside the supported range, -7 for a HIP error.
@@ -13,6 +13,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -33,6 +34,14 @@ int mla_probe_mfma_bf16(float* sink, int shape, int iters, int waves_per_simd, i
  * from src to dst with 16-byte non-temporal loads and stores, 8 workgroups
  * of 256 threads per compute unit. The HBM traffic is 2 * bytes. */
 int mla_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+/* HBM read rate: a grid of workgroups_per_cu (1..32) workgroups of 256
+ * threads per compute unit reads `bytes` (a multiple of 16; src 16-byte
+ * aligned) with 16-byte non-temporal loads, eight in flight per thread, and
+ * writes one word per thread to sink (at least cus * workgroups_per_cu * 256
+ * words). The HBM traffic is `bytes`. */
+int mla_probe_read(uint32_t* sink, const void* src, size_t bytes, int workgroups_per_cu,
+                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

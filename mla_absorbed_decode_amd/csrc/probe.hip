@@ -1,5 +1,5 @@
-// probe.hip -- the two machine measurements the benchmark divides by: the bf16
-// matrix-core rate and the HBM copy rate of the GPU it runs on. They are not
+// probe.hip -- the machine measurements the benchmark divides by: the bf16
+// matrix-core rate and the HBM copy and read rates of the GPU it runs on. They are not
 // part of the attention path; they give the measured peaks that the
 // benchmark's roofline fractions are also quoted against, next to the
 // published ones.
@@ -77,6 +77,25 @@ __global__ void __launch_bounds__(256) copy16_kernel(u32x4_t* __restrict__ dst,
   for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Grid-stride read of 16-byte words with non-temporal loads, UNROLL in flight
+// per thread; one xor of everything read per thread goes to sink.
+template <int UNROLL>
+__global__ void __launch_bounds__(256) read16_kernel(uint32_t* __restrict__ sink,
+                                                     const u32x4_t* __restrict__ src, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (; i + (UNROLL - 1) * stride < n; i += UNROLL * stride) {
+    u32x4_t v[UNROLL];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) v[k] = __builtin_nontemporal_load(src + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) acc ^= v[k];
+  }
+  for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 int cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -120,6 +139,19 @@ int mla_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream)
   if (grid > need) grid = need;
   hipLaunchKernelGGL(copy16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (u32x4_t*)dst,
                      (const u32x4_t*)src, n);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int mla_probe_read(uint32_t* sink, const void* src, size_t bytes, int workgroups_per_cu,
+                   hipStream_t stream) {
+  if (!sink || !src) return -1;
+  if (bytes % 16 || (uintptr_t)src % 16 || workgroups_per_cu < 1 || workgroups_per_cu > 32)
+    return -5;
+  const int cus = cu_count();
+  if (cus <= 0) return -7;
+  const int64_t n = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(read16_kernel<8>, dim3((unsigned)(cus * workgroups_per_cu)), dim3(256), 0,
+                     stream, sink, (const u32x4_t*)src, n);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -1,5 +1,5 @@
 """Measured peaks of the GPU the benchmark runs on (libmla_probe.so, see
-include/mla_probe.h): the dense bf16 MFMA rate and the HBM copy rate.
+include/mla_probe.h): the dense bf16 MFMA rate and the HBM copy and read rates.
 
 These are measurement tools for the benchmark, not part of the attention
 path. Each function enqueues its probe kernel on the current stream, times it
@@ -29,6 +29,9 @@ def load() -> ctypes.CDLL:
         lib.mla_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]
         lib.mla_probe_copy.restype = ctypes.c_int
+        lib.mla_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_int, ctypes.c_void_p]
+        lib.mla_probe_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -85,3 +88,21 @@ def copy_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
     run()
     ms = _timed(run, reps)
     return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def read_gbs(nbytes: int = 1 << 30, workgroups_per_cu: int = 8, reps: int = 5) -> float:
+    """HBM GB/s of a read-only stream over nbytes."""
+    lib = load()
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(1024 * 256 * workgroups_per_cu, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        rc = lib.mla_probe_read(sink.data_ptr(), src.data_ptr(), nbytes, workgroups_per_cu, stream)
+        if rc:
+            raise RuntimeError(f"mla_probe_read failed ({rc})")
+
+    run()
+    ms = _timed(run, reps)
+    return nbytes / (ms * 1e-3) / 1e9
