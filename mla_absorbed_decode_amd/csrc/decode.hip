@@ -202,20 +202,29 @@ __device__ __forceinline__ void stage_segment(const DecodeParams& p, StageRefs& 
     st.idx[k] = in ? base + e : st.idx[k];
   }
 }
-// Read the first n stage entries (all in one round trip) into sh_blk, clamped
-// to [0, num_blocks) so every tile read stays inside the cache. n is
+// Read the first n stage entries (all in one round trip) into registers. n is
 // wave-uniform; n > 0 implies a non-empty block table.
-__device__ __forceinline__ void stage_read(const DecodeParams& p, const StageRefs& st, int n,
-                                           int* sh_blk) {
-  const int lane = threadIdx.x & 63;
-  int v[kStagePer];
+__device__ __forceinline__ void stage_fetch(const DecodeParams& p, const StageRefs& st, int n,
+                                            int* v) {
 #pragma unroll
   for (int k = 0; k < kStagePer; ++k)
     if (64 * k < n) v[k] = p.block_table[st.idx[k]];
+}
+// The fetched entries into sh_blk, clamped to [0, num_blocks) so every tile
+// read stays inside the cache.
+__device__ __forceinline__ void stage_store(const DecodeParams& p, int n, const int* v,
+                                            int* sh_blk) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int k = 0; k < kStagePer; ++k)
     if (64 * k < n)
       sh_blk[64 * k + lane] = v[k] < 0 ? 0 : (v[k] >= p.num_blocks ? (int)p.num_blocks - 1 : v[k]);
+}
+__device__ __forceinline__ void stage_read(const DecodeParams& p, const StageRefs& st, int n,
+                                           int* sh_blk) {
+  int v[kStagePer];
+  stage_fetch(p, st, n, v);
+  stage_store(p, n, v, sh_blk);
 }
 
 // Build the workgroup's SegLds and stage its block-table entries in one pass
@@ -236,10 +245,15 @@ __device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk) 
     if (!p.split) {
       const int u = p.num_units - 1 - (int)blockIdx.x;  // heaviest row tiles first
       const int b = fdiv(u, p.div_rt);
+      // the first entries of the sequence's block-table row, read in the same
+      // round trip as its length (the ones past its pages are not used)
+      const int nb_max = p.max_blocks < kBlkCache ? p.max_blocks : kBlkCache;
+      stage_segment(p, st, b, 0, 0, nb_max);
+      int v[kStagePer];
+      stage_fetch(p, st, nb_max, v);
       const int n = unit_kvlen(p, u);
       const int np = n > 0 ? page_of(p, n - 1) + 1 : 0;
-      stage_segment(p, st, b, 0, 0, np);
-      stage_read(p, st, np < kBlkCache ? np : kBlkCache, sh_blk);
+      stage_store(p, np < kBlkCache ? np : kBlkCache, v, sh_blk);
       if (lane == 0) {
         tab->kv[0] = n;
         tab->sl[0] = seq_len(p, b);
@@ -1592,11 +1606,23 @@ __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupPara
   __shared__ int sh_scan[256];
   MLA_LDS char* wslab = (MLA_LDS char*)smem_raw;           // [kKvRank][V] bf16, dense
   MLA_LDS char* atile = wslab + kKvRank * (v.V / (int)gridDim.z) * 2;  // [16][kVupAPitch]
-  const int h = blockIdx.y, tok0 = blockIdx.x * kVupTok;
+  // (token group, head, column group) of this workgroup. Workgroup i runs on
+  // XCD i % 8: when the (head, column group) slabs divide evenly over the 8
+  // XCDs, all token groups of one slab go to one XCD, so its W_UV columns are
+  // read from HBM once and then found in that XCD's L2.
+  const int ntg = (int)gridDim.x, nslab = (int)(gridDim.y * gridDim.z);
+  int tg = (int)blockIdx.x, slab = (int)(blockIdx.y + gridDim.y * blockIdx.z);
+  if (nslab % 8 == 0) {
+    const int lin = (int)blockIdx.x + ntg * slab, k = lin / 8;
+    slab = lin % 8 + 8 * (k / ntg);
+    tg = k % ntg;
+  }
+  const int h = slab % (int)gridDim.y, cg = slab / (int)gridDim.y;
+  const int tok0 = tg * kVupTok;
   // columns [col0, col0 + VW) of W_UV[h]: the workgroups of a (token group,
   // head) split the un-projection's columns and each merges the same rows
-  const int VW = v.V / (int)gridDim.z, col0 = (int)blockIdx.z * VW;
-  const bool first = blockIdx.z == 0;  // writes o_lat and lse
+  const int VW = v.V / (int)gridDim.z, col0 = cg * VW;
+  const bool first = cg == 0;  // writes o_lat and lse
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = p.batch * p.q_len;

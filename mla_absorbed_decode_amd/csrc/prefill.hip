@@ -121,6 +121,79 @@ __global__ void __launch_bounds__(256) bmm_nt_big(BmmNtParams p) {
   copy_rope_broadcast<uint16_t>(p, g.t0, h, kGT);
 }
 
+// f32 operands (16-byte aligned rows, K a multiple of 16): v_mfma_f32_16x16x4f32
+// with both operands read along k straight from global memory. Each wave owns a
+// 32 x 32 output tile (two row tiles x two column tiles). For a 16-wide k block
+// lane (li, g) loads a[t][k0 + 4g .. + 3] and w[n][k0 + 4g .. + 3] as float4;
+// MFMA c (c = 0..3) takes component c of both, i.e. k = k0 + 4g + c over the
+// four lane groups, so the four MFMAs cover the block. The next block's
+// operands are loaded while the current one is multiplied.
+__global__ void __launch_bounds__(256) bmm_nt_f32(BmmNtParams p) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+  const int64_t t0 = (int64_t)blockIdx.y * kNtM + (w >> 1) * 32;
+  const int64_t n0 = (int64_t)blockIdx.x * kNtN + (w & 1) * 32;
+  const int h = blockIdx.z;
+  const float* A = (const float*)p.a + (int64_t)h * p.a_sh;
+  const float* W = (const float*)p.w + (int64_t)h * p.w_sh;
+  // rows past T or N read row 0 (valid memory); their outputs are not stored
+  const float* ap[2];
+  const float* wp[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t t = t0 + 16 * i + li, n = n0 + 16 * i + li;
+    ap[i] = A + (t < p.T ? t : 0) * p.a_st + 4 * g;
+    wp[i] = W + (n < p.N ? n : 0) * p.w_sn + 4 * g;
+  }
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t ab[2][2], wb[2][2];
+  auto load = [&](int64_t k0, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ab[buf][i] = *(const f32x4_t*)(ap[i] + k0);
+      wb[buf][i] = *(const f32x4_t*)(wp[i] + k0);
+    }
+  };
+  load(0, 0);
+  const int64_t nk = p.K / 16;
+  for (int64_t kb = 0; kb < nk; ++kb) {
+    const int cur = (int)(kb & 1);
+    if (kb + 1 < nk) load((kb + 1) * 16, cur ^ 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = mfma_16x16x4f32(ab[cur][i][c], wb[cur][j][c], acc[i][j]);
+  }
+  // lane holds out[t0 + 16 i + 4 g + r][n0 + 16 j + li], r = 0..3
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = n0 + 16 * j + li;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 16 * i + 4 * g + r;
+        if (t < p.T) ((float*)p.out)[t * p.o_st + (int64_t)h * p.o_sh + n] = acc[i][j][r];
+      }
+    }
+  if (blockIdx.x == 0 && (w & 1) == 0 && p.R > 0) {
+    // the rope rows of this wave's 32 tokens, copied bit for bit behind every head's N columns
+    for (int e = lane; e < 32 * (int)p.R; e += 64) {
+      const int64_t t = t0 + e / p.R, r = e % p.R;
+      if (t < p.T)
+        ((uint32_t*)p.out)[t * p.o_st + (int64_t)h * p.o_sh + p.N + r] =
+            ((const uint32_t*)p.pe)[t * p.pe_st + r];
+    }
+  }
+}
+
 // Any size or alignment, bf16 or f32: one thread per output element, f32
 // accumulation in k order.
 template <bool F32>
@@ -466,6 +539,9 @@ hipError_t launch_bmm_nt(const BmmNtParams& p, hipStream_t s) {
   } else if (!p.is_f32 && aligned && p.K % kNtK == 0 && p.K > 0 && p.N > 0) {
     dim3 grid((unsigned)((p.N + kNtN - 1) / kNtN), (unsigned)((p.T + kNtM - 1) / kNtM), (unsigned)p.H);
     hipLaunchKernelGGL(bmm_nt_bf16, grid, dim3(256), 0, s, p);
+  } else if (p.is_f32 && aligned && p.K % 16 == 0 && p.K > 0 && p.N > 0 && p.T <= INT32_MAX) {
+    dim3 grid((unsigned)((p.N + kNtN - 1) / kNtN), (unsigned)((p.T + kNtM - 1) / kNtM), (unsigned)p.H);
+    hipLaunchKernelGGL(bmm_nt_f32, grid, dim3(256), 0, s, p);
   } else {
     const int64_t total = p.T * p.H * (p.N + p.R);
     const unsigned blocks = (unsigned)((total + 255) / 256);

@@ -69,7 +69,8 @@ def test_decompress_kv_matches_oracle(S, N, P, R, V):
 
 def test_decompress_kv_strided_views_and_f32():
     """Outputs written through non-contiguous views (a head-major buffer and a
-    padded one) leave the padding untouched; f32 takes the plain kernel."""
+    padded one) leave the padding untouched; f32 takes the f32 MFMA kernel, and
+    a latent view that is not 16-byte aligned the plain one."""
     mla = _mla()
     S, N, P, R, V, L = 70, 4, 64, 64, 64, 512
     dims = mi.Dims(n_head=N, d_nope=P, d_rope=R, d_v=V, kv_rank=L)
@@ -91,6 +92,15 @@ def test_decompress_kv_strided_views_and_f32():
         assert_close(to_np(v_out), vw, dt, "v")
         assert np.array_equal(to_np(k_out[:, :, P:]), np.broadcast_to(k_pe[:, None, :], (S, N, R)))
         assert torch.isnan(kbuf[:, :, P + R:]).all() and torch.isnan(vbuf[:, :, V:]).all()
+        # the latent rows one element into a padded buffer: 4-byte alignment only
+        c_odd = to_dev(np.concatenate([np.zeros((S, 1), np.float32), c_kv,
+                                       np.zeros((S, 7), np.float32)], 1), dt)[:, 1:L + 1]
+        k2 = _poisoned((S, N, P + R), tdt)
+        v2 = _poisoned((S, N, V), tdt)
+        mla.mla_decompress_kv(c_odd, to_dev(k_pe, dt), to_dev(w_uk_t, dt), to_dev(w_uv, dt), k2, v2)
+        torch.cuda.synchronize()
+        assert_close(to_np(k2[:, :, :P]), kw[:, :, :P], dt, "k_nope, unaligned latent rows")
+        assert_close(to_np(v2), vw, dt, "v, unaligned latent rows")
 
 
 # ---------------------------------------------------------------- attention
