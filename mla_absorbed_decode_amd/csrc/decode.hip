@@ -380,8 +380,8 @@ __device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk) 
 // dedicated loader waves (0: the compute waves load); KV8: an fp8 (e4m3) cache
 // whose loader waves widen each row to bf16 on its way into LDS, so the LDS
 // tile and the compute are the bf16 ones. KV8 reads every stream item (key
-// tile or query tile) global->LDS into one of three staging slots, three
-// items ahead; at its step each loader lane widens (or, for query rows,
+// tile or query tile) global->LDS into one of NS8 staging slots, NS8 items
+// ahead; at its step each loader lane widens (or, for query rows,
 // copies) the bytes it read itself into the NSLOT-deep bf16 ring.
 template <int R_, int WR_, int WC_, int RT_, int TT_, int NSLOT_, bool F32_, bool XS_, int NP_,
           bool KV8_ = false>
@@ -418,11 +418,10 @@ struct Cfg {
   // bf16 (RTILE rows of 2E), P8 / QI 1 KB reads, L8 of them per loader wave
   static constexpr int P8 = KV8 ? TT * E / 1024 : 0;
   static constexpr int STAGE_SLOT = KV8 ? (TT * E > RTILE * E * 2 ? TT * E : RTILE * E * 2) : 0;
-  // staging depth: items read ahead of the one being landed (4 when the LDS
-  // holds them: more bytes in flight per CU against the memory latency)
-  static constexpr int NS8 =
-      KV8 ? (NSLOT * TILE_BYTES + XCHG_BYTES + 4 * STAGE_SLOT + kStaticLdsAlloc <= 160 * 1024 ? 4 : 3)
-          : 1;
+  // staging depth: items read ahead of the one being landed. Two: with more
+  // bytes in flight per CU the stream gets slower on MI355X (the V2-Lite fp8
+  // call measured 40.1 us with two, 40.7-40.8 with three, 41.0-41.4 with four)
+  static constexpr int NS8 = KV8 ? 2 : 1;
   static constexpr int STAGE_BYTES = KV8 ? NS8 * STAGE_SLOT : 0;
   static constexpr int SMEM_BYTES = RING_BYTES + XCHG_BYTES + STAGE_BYTES;
   // With loader waves the query rows of every segment but the first travel
@@ -457,6 +456,20 @@ struct Cfg {
                          P8 <= 64 && QI <= 64),
                 "fp8: bf16 compute, loader waves, whole 1 KB staging reads");
 };
+
+// vmcnt <= n * STEP for a wave-uniform n >= 0 (n above MAXN counts as MAXN).
+template <int MAXN, int STEP>
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<MAXN * STEP>();
+      return;
+    }
+    wait_vmcnt_n<MAXN - 1, STEP>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
 
 // Everything a wave carries through one segment.
 template <class C>
@@ -1122,11 +1135,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     for (int k = 0; k < C::NS8 && k < nsteps; ++k) issue(k);
     for (int k = 0; k < nsteps; ++k) {
       // item k's reads are older than those of the (at most NS8 - 1) items after it
-      const int ahead = nsteps - 1 - k;
-      if (ahead <= 0) wait_vmcnt<0>();
-      else if (ahead == 1) wait_vmcnt<C::L8>();
-      else if (ahead == 2 || C::NS8 == 3) wait_vmcnt<2 * C::L8>();
-      else wait_vmcnt<(C::NS8 >= 4 ? 3 : 2) * C::L8>();
+      wait_vmcnt_n<C::NS8 - 1, C::L8>(nsteps - 1 - k);
       static_assert(C::NS8 * C::L8 < 64, "vmcnt range");
       kv8_land(k, (qmask >> (k % C::NS8)) & 1u);
       __syncthreads();
@@ -1135,13 +1144,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
   };
 
   // wait until this loader wave's reads of tile k have landed
-  auto wait_tile = [&](int k) {
-    int ahead = nsteps - 1 - k;
-    ahead = ahead < C::NSLOT - 2 ? ahead : C::NSLOT - 2;
-    if (ahead <= 0) wait_vmcnt<0>();
-    else if (ahead == 1) wait_vmcnt<C::LPW>();
-    else wait_vmcnt<(C::NSLOT >= 4 ? 2 * C::LPW : 0)>();
-  };
+  auto wait_tile = [&](int k) { wait_vmcnt_n<C::NSLOT - 2, C::LPW>(nsteps - 1 - k); };
 
   // ---- compute walker state
   // fp8: the scores take q * descale_q and keys * descale_k, the values * descale_k
@@ -1698,8 +1701,11 @@ __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupPara
 
 // ------------------------------------------------------------- variants
 //                      R   WR WC RT TT NSLOT F32    XS     NP
-using Cols64  = Cfg<64, 1, 4, 1, 32, 4, false, true,  4>;  // <= 16 rows: columns split over waves
-using Cols0   = Cfg<0,  1, 4, 1, 32, 4, false, true,  4>;
+// <= 16 rows: columns split over waves. Three ring slots (two tiles in flight
+// per CU) stream faster than four here: the V2-Lite attention call measured
+// 38.6 us against 39.5 us (and 44.9 us with two slots).
+using Cols64  = Cfg<64, 1, 4, 1, 32, 3, false, true,  4>;
+using Cols0   = Cfg<0,  1, 4, 1, 32, 3, false, true,  4>;
 // 32 rows: eight waves, two 16-row tiles x four 128-column quarters
 using Mixed64 = Cfg<64, 2, 4, 1, 32, 3, false, true,  0>;
 using Mixed0  = Cfg<0,  2, 4, 1, 32, 3, false, true,  0>;
