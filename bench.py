@@ -640,6 +640,54 @@ def prefill_secondary(dev, steps: int, warmup: int):
     return res
 
 
+def skewed_secondary(dev, steps: int, warmup: int):
+    """A ragged V2-Lite decode batch with more units than workgroups: 300
+    sequences of 16 heads, 299 of U[128, 1024] tokens and one of 32768, 64-token
+    pages. The split-KV plan spreads the long sequence's keys over the grid
+    like everyone else's. Cold: the calls rotate over enough copies of the
+    pool that the rows they read exceed twice the last-level cache."""
+    rng = mi.stream(0, 90)
+    seqlens = rng.integers(128, 1025, size=300).astype(np.int32)
+    seqlens[150] = 32768
+    c = mi.decode_case(0, mi.V2_LITE, mi.BF16, seqlens, tail_fill=0.0)
+    d = c.dims
+    bf = torch.bfloat16
+    q = torch.from_numpy(c.q).to(bf).to(dev)
+    kv_read = int(c.seqlens.astype(np.int64).sum()) * d.entry * 2
+    copies = math.ceil(2 * LLC_BYTES / kv_read) + 1
+    pools = [torch.from_numpy(c.pool).to(bf).to(dev)]
+    pools += [pools[0].clone() for _ in range(copies - 1)]
+    bt = torch.from_numpy(c.block_table).to(dev)
+    sl = torch.from_numpy(c.seqlens).to(dev)
+    out = torch.empty(c.batch, 1, d.n_head, d.kv_rank, dtype=bf, device=dev)
+    lse = torch.empty(c.batch, 1, d.n_head, dtype=torch.float32, device=dev)
+    nbytes = mla.mla_decode_workspace_size(c.batch, 1, d.n_head, d.kv_rank, c.max_seqlen,
+                                           c.page, bf)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    run = lambda i: mla.mla_decode_attend(q, pools[i % copies], bt, sl, c.max_seqlen, c.scale,
+                                          True, out, lse, workspace=ws)
+    for i in range(copies):
+        run(i)
+    torch.cuda.synchronize()
+    graphs = capture(run, copies)
+    whole = capture(lambda _: [run(k) for k in range(copies)], 1)[0]
+    if warmup:
+        replay_steps(whole, graphs, warmup)
+    ms = replay_steps(whole, graphs, steps) / steps
+    byts = attention_bytes(c)
+    return {
+        "workload": "V2-Lite decode bf16, 300 sequences: 299 of U[128,1024] tokens and one of "
+                    "32768, 64-token pages, N(0,0.1^2); split-KV over 256 workgroups",
+        "sum_seqlens": int(c.seqlens.sum()),
+        "units": c.batch,
+        "workspace_bytes": nbytes,
+        "cache_copies": copies,
+        "attention_us": round(ms * 1e3, 2),
+        "gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def sparse_secondary(dev, steps: int, warmup: int):
     """Sparse fp8 decode over 656-byte entries: the sparse-decode page's shape
     (batch 2 x 128 heads, top-128 over 32 blocks of 64 entries) and a longer
@@ -837,6 +885,8 @@ def main():
     ap.add_argument("--no-v3", action="store_true", help="skip the 128-head secondary line")
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding line")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache line")
+    ap.add_argument("--no-skewed", action="store_true",
+                    help="skip the 300-sequence ragged decode line")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse fp8 decode line")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the NoPE prefill line (absorbed and naive routes)")
@@ -934,6 +984,8 @@ def main():
         if peaks:
             line["v3_decode"]["mfma_frac_measured"] = round(
                 line["v3_decode"]["tflops"] / peaks["mfma_bf16_tflops"], 4)
+    if not args.no_skewed:
+        line["skewed_300"] = skewed_secondary(dev, max(10, args.steps // 2), args.warmup)
     if not args.no_fp8:
         line["fp8_cache"] = fp8_secondary(step, dev, max(10, args.steps // 2), args.warmup,
                                           eager=args.eager)

@@ -92,13 +92,16 @@ __device__ __forceinline__ int row_limit(const DecodeParams& p, int s, int qi) {
 }
 
 // Keys a unit needs: the most any of its rows sees.
-__device__ __forceinline__ int unit_kvlen(const DecodeParams& p, int u) {
+// (the same for a sequence length s already read)
+__device__ __forceinline__ int unit_kvlen_s(const DecodeParams& p, int u, int s) {
   const int b = fdiv(u, p.div_rt), rt = u - b * p.row_tiles;
-  const int s = seq_len(p, b);
   const int rows = p.q_len * p.n_heads;
   int r_last = (rt + 1) * p.rows_per_unit;
   r_last = (r_last > rows ? rows : r_last) - 1;
   return row_limit(p, s, p.q_len == 1 ? 0 : fdiv(r_last, p.div_nh));
+}
+__device__ __forceinline__ int unit_kvlen(const DecodeParams& p, int u) {
+  return unit_kvlen_s(p, u, seq_len(p, fdiv(u, p.div_rt)));
 }
 
 // Split plan: unit u occupies plan positions [scan[u-1], scan[u]) where scan
@@ -109,8 +112,8 @@ __device__ __forceinline__ int unit_kvlen(const DecodeParams& p, int u) {
 // chunks of ceil(total / grid), one per workgroup.
 //
 // The merge's copy of the plan: every unit's scan value, computed by wave 0
-// with register shuffles (up to 256 units, four per lane) and published in
-// sh[0..255] with one barrier.
+// with register shuffles (up to kSplitUnits units, kUPL per lane) and
+// published in sh[0 .. kSplitUnits) with one barrier.
 // Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no
 // LDS round trips): shifts by 1, 2, 4 and 8 within each row of 16 lanes, then
 // lane 15 of rows 0 and 2 added to rows 1 and 3, then lane 31 to rows 2 and 3.
@@ -125,7 +128,9 @@ __device__ __forceinline__ int wave_scan_incl(int x) {
   return x;
 }
 
-// Lane src's value of x, src wave-uniform.
+// a wave-uniform value, held in a scalar register
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ int lane_value(int x, int src) {
   return __builtin_amdgcn_readlane(x, src);
 }
@@ -137,20 +142,37 @@ __device__ __forceinline__ float lane_weight(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src & 63));
 }
 
+constexpr int kUPL = kSplitUnits / 64;  // units per lane of the planning wave
+
+// A[k] for a wave-uniform k < N, as a chain of selects (no dynamic register indexing).
+template <class T, int N>
+__device__ __forceinline__ T pick(const T (&a)[N], int k) {
+  T r = a[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j)
+    if (j == k) r = a[j];
+  return r;
+}
+
 __device__ void plan_units(const DecodeParams& p, int* sh) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int v[4], run = 0;
+    const int per = (p.num_units + 63) >> 6;  // units per lane, at most kUPL
+    int v[kUPL], run = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int u = lane * 4 + k;
+    for (int k = 0; k < kUPL; ++k) {
+      if (k >= per) break;
+      const int u = lane * per + k;
       const int n = u < p.num_units ? unit_kvlen(p, u) : 0;
       run += n > 0 ? ceil_div(n, p.wb) + p.alpha : 0;
       v[k] = run;
     }
     const int excl = wave_scan_incl(run) - run;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sh[lane * 4 + k] = excl + v[k];
+    for (int k = 0; k < kUPL; ++k) {
+      if (k >= per) break;
+      if (lane * per + k < kSplitUnits) sh[lane * per + k] = excl + v[k];
+    }
   }
   __syncthreads();
 }
@@ -168,11 +190,11 @@ struct SegHdr {
 // and bit masks of the units in range and of those whose keys reach other
 // workgroups too (written as partials for the merge).
 struct SegLds {
-  int kv[256];
-  int sl[256];
-  int poff[256];
-  uint64_t live[4];
-  uint64_t part[4];
+  int kv[kSplitUnits];
+  int sl[kSplitUnits];
+  int poff[kSplitUnits];
+  uint64_t live[kUPL];
+  uint64_t part[kUPL];
   SegHdr hdr;
   uint32_t xs_ctr;  // compute-wave rendezvous of the split score contraction (loader layouts)
   uint32_t xs_gaveup;  // set by a compute wave whose rendezvous wait gave up (follows xs_ctr)
@@ -180,7 +202,7 @@ struct SegLds {
 // LDS besides the tile ring and score exchange: the workgroup's plan and the
 // staged block table
 constexpr int kStaticLds = (int)sizeof(SegLds) + kBlkCache * 4;
-// the static LDS as allocated (the compiler reports 8 KB for these kernels)
+// the static LDS, rounded up to whole 4 KB for the budget check
 constexpr int kStaticLdsAlloc = (kStaticLds + 4095) / 4096 * 4096;
 
 // Block-table entries staged in LDS: entry e of the stage is read by lane
@@ -229,14 +251,15 @@ __device__ __forceinline__ void stage_read(const DecodeParams& p, const StageRef
 
 // Build the workgroup's SegLds and stage its block-table entries in one pass
 // of wave 0, then one barrier. In split mode lane l holds units l, l + 64,
-// l + 128, l + 192, so that a ballot over the lanes is one 64-unit word of a
-// mask; every unit's cost, plan positions, overlap with this workgroup's
+// l + 128, ... (kUPL of them), so that a ballot over the lanes is one 64-unit
+// word of a mask; every unit's cost, plan positions, overlap with this workgroup's
 // chunk, key range, tiles and pages are computed side by side rather than
 // walked unit by unit. Without split the workgroup's one unit is the whole
 // table. The stage holds the first kBlkCache pages of the segments in stream
 // order; the loader reads any beyond that from global memory.
 template <class C>
-__device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk) {
+__device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk,
+                               MLA_LDS int* scratch) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     StageRefs st;
@@ -258,90 +281,91 @@ __device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk) 
         tab->kv[0] = n;
         tab->sl[0] = seq_len(p, b);
         tab->poff[0] = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          tab->live[w] = w == 0 ? 1ull : 0ull;
-          tab->part[w] = 0ull;
-        }
+        tab->live[0] = 1ull;  // the one unit, whole in this workgroup
+        tab->part[0] = 0ull;
         tab->hdr.u0 = tab->hdr.u1 = u;
         tab->hdr.tlo0 = 0;
         tab->hdr.thi1 = n;
         tab->hdr.nsteps = n > 0 ? ceil_div(n, C::TT) : 0;
       }
     } else {
-      int n[4], sl[4], cost[4], incl[4];
+      // Per-unit values go to LDS as they are computed -- tab's tables, and
+      // scratch tables in the tile ring, which no tile has reached yet -- so
+      // the pass keeps no register array per unit. Lane l handles units l,
+      // l + 64, ...; each lane reads back only what it wrote itself, except
+      // for the wave-uniform reads of the staging loop (one wave, so LDS
+      // order is program order).
+      MLA_LDS int* t_incl = scratch;
+      MLA_LDS int* t_cost = scratch + kSplitUnits;
+      MLA_LDS int* t_tlo = scratch + 2 * kSplitUnits;
+      MLA_LDS int* t_thi = scratch + 3 * kSplitUnits;
+      MLA_LDS int* t_pages = scratch + 4 * kSplitUnits;
+      const int nk = (p.num_units + 63) >> 6;  // units per lane, at most kUPL
+      int slv[kUPL];  // the lane's sequence lengths, all read in one round trip
+#pragma unroll
+      for (int k = 0; k < kUPL; ++k) {
+        if (k >= nk) break;
+        const int u = lane + 64 * k;
+        slv[k] = u < p.num_units ? seq_len(p, fdiv(u, p.div_rt)) : 0;
+      }
       int run = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kUPL; ++k) {
+        if (k >= nk) break;
         const int u = lane + 64 * k;
-        n[k] = u < p.num_units ? unit_kvlen(p, u) : 0;
-        sl[k] = u < p.num_units ? seq_len(p, fdiv(u, p.div_rt)) : 0;
-        cost[k] = n[k] > 0 ? ceil_div(n[k], C::TT) + p.alpha : 0;  // work blocks are tiles
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int x = wave_scan_incl(cost[k]);
-        incl[k] = x + run;
+        const int n = u < p.num_units ? unit_kvlen_s(p, u, slv[k]) : 0;
+        const int cost = n > 0 ? ceil_div(n, C::TT) + p.alpha : 0;  // work blocks are tiles
+        const int x = wave_scan_incl(cost);
+        t_incl[u] = x + run;
+        t_cost[u] = cost;
+        tab->kv[u] = n;
+        tab->sl[u] = slv[k];
         run += lane_value(x, 63);
       }
       const int total = run;
       const int chunk = total > 0 ? ceil_div(total, p.grid) : 1;
       const int w0 = (int)blockIdx.x * chunk;
       const int w1 = w0 + chunk < total ? w0 + chunk : total;
-      uint64_t live[4], part[4];
-      int tlo[4], thi[4], pages[4];
+      int u0 = kSplitUnits, u1 = -1, steps = 0, prun = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int first = incl[k] - cost[k] + p.alpha, end = incl[k];
+      for (int k = 0; k < kUPL; ++k) {
+        if (k >= nk) break;
+        const int u = lane + 64 * k;
+        const int n = tab->kv[u], cost = t_cost[u], incl = t_incl[u];
+        const int first = incl - cost + p.alpha, end = incl;
         const int lo = w0 > first ? w0 : first, hi = w1 < end ? w1 : end;
-        const bool in = cost[k] > 0 && lo < hi;
-        tlo[k] = (lo - first) * C::TT;
-        thi[k] = (hi - first) * C::TT < n[k] ? (hi - first) * C::TT : n[k];
-        pages[k] = in ? page_of(p, thi[k] - 1) - page_of(p, tlo[k]) + 1 : 0;
-        live[k] = __ballot(in);
+        const bool in = cost > 0 && lo < hi;
+        const int tlo = (lo - first) * C::TT;
+        const int thi = (hi - first) * C::TT < n ? (hi - first) * C::TT : n;
+        const int pages = in ? page_of(p, thi - 1) - page_of(p, tlo) + 1 : 0;
+        const uint64_t live = __ballot(in);
         // whole in this workgroup only if it starts and ends inside its chunk
-        part[k] = __ballot(in && !(first >= w0 && end <= w0 + chunk));
-      }
-      int u0 = 256, u1 = -1;
-#pragma unroll
-      for (int k = 3; k >= 0; --k)
-        if (live[k]) u0 = 64 * k + __builtin_ctzll(live[k]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (live[k]) u1 = 64 * k + 63 - __builtin_clzll(live[k]);
-      int steps = 0, prun = 0, poff[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const bool in = (live[k] >> lane) & 1;
-        const int nt = in ? ceil_div(thi[k] - tlo[k], C::TT) : 0;
-        steps += nt + (C::QT && in && lane + 64 * k != u0 ? 1 : 0);
-        const int x = wave_scan_incl(pages[k]);
-        poff[k] = x - pages[k] + prun;
+        const uint64_t part = __ballot(in && !(first >= w0 && end <= w0 + chunk));
+        if (live && u0 == kSplitUnits) u0 = 64 * k + __builtin_ctzll(live);
+        if (live) u1 = 64 * k + 63 - __builtin_clzll(live);
+        steps += (in ? ceil_div(thi - tlo, C::TT) : 0) + (C::QT && in && u != u0 ? 1 : 0);
+        const int x = wave_scan_incl(pages);
+        tab->poff[u] = x - pages + prun;
         prun += lane_value(x, 63);
+        t_tlo[u] = tlo;
+        t_thi[u] = thi;
+        t_pages[u] = pages;
+        if (lane == 0) {
+          tab->live[k] = live;
+          tab->part[k] = part;
+        }
       }
-      // key range ends of the first and last units, from the lanes holding them
-      int a = 0, z = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (k == (u0 >> 6)) a = tlo[k];
-        if (k == (u1 >> 6)) z = thi[k];
-      }
-      a = lane_value(a, u0 & 63);
-      z = lane_value(z, u1 & 63);
+      // key range ends of the first and last units
+      const int a = u0 <= u1 ? t_tlo[u0] : 0, z = u0 <= u1 ? t_thi[u1] : 0;
       steps = lane_value(wave_scan_incl(steps), 63);
-      // stage the pages of every unit in range, in unit order: one pass per
-      // segment, the unit's values read from the lane holding it
+      // stage the pages of every unit in range, in unit order: one pass per segment
       for (int u = u0; u <= u1;) {
-        const int k = u >> 6, src = u & 63;
-        const int tl = k == 0 ? tlo[0] : k == 1 ? tlo[1] : k == 2 ? tlo[2] : tlo[3];
-        const int po = k == 0 ? poff[0] : k == 1 ? poff[1] : k == 2 ? poff[2] : poff[3];
-        const int np = k == 0 ? pages[0] : k == 1 ? pages[1] : k == 2 ? pages[2] : pages[3];
-        stage_segment(p, st, fdiv(u, p.div_rt), page_of(p, lane_value(tl, src)),
-                      lane_value(po, src), lane_value(np, src));
+        stage_segment(p, st, fdiv(u, p.div_rt), page_of(p, uni(t_tlo[u])), uni(tab->poff[u]),
+                      uni(t_pages[u]));
         // next unit in range
-        int nu = 256;
-        for (int w = (u + 1) >> 6; w < 4; ++w) {
-          const uint64_t lw = w == 0 ? live[0] : w == 1 ? live[1] : w == 2 ? live[2] : live[3];
+        int nu = kSplitUnits;
+        for (int w = (u + 1) >> 6; w < nk; ++w) {
+          const uint64_t lw = tab->live[w];
           const uint64_t m = w == ((u + 1) >> 6) ? lw & (~0ull << ((u + 1) & 63)) : lw;
           if (m) {
             nu = 64 * w + __builtin_ctzll(m);
@@ -351,18 +375,7 @@ __device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk) 
         u = nu;
       }
       stage_read(p, st, prun < kBlkCache ? prun : kBlkCache, sh_blk);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        tab->kv[lane + 64 * k] = n[k];
-        tab->sl[lane + 64 * k] = sl[k];
-        tab->poff[lane + 64 * k] = poff[k];
-      }
       if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          tab->live[k] = live[k];
-          tab->part[k] = part[k];
-        }
         tab->hdr.u0 = u0;
         tab->hdr.u1 = u1;
         tab->hdr.tlo0 = a;
@@ -452,6 +465,7 @@ struct Cfg {
   static_assert(NSLOT >= 2 && NSLOT <= 4, "ring depth");
   static_assert(KSTEPS % KB == 0 && DW % PB == 0, "batching");
   static_assert(SMEM_BYTES + kStaticLdsAlloc <= 160 * 1024, "LDS budget");
+  static_assert(RING_BYTES >= 5 * kSplitUnits * 4, "the split plan's tables fit in the ring");
   static_assert(!KV8 || (!F32 && NP > 0 && TT * E % 1024 == 0 && L8 * NP >= P8 && L8 * NP >= QI &&
                          P8 <= 64 && QI <= 64),
                 "fp8: bf16 compute, loader waves, whole 1 KB staging reads");
@@ -839,8 +853,6 @@ struct Seg {
   int poff;    // staged block-table position of the segment's first page
 };
 
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
 __device__ __forceinline__ SegHdr read_hdr(const SegLds* tab) {
   SegHdr h;
   h.u0 = uni(tab->hdr.u0);
@@ -857,7 +869,7 @@ template <class C>
 __device__ __forceinline__ Seg seg_of(const DecodeParams& p, const SegLds* tab, const SegHdr& h,
                                       int u) {
   const bool valid = u <= h.u1 && u < p.num_units;
-  const int i = p.split ? (u < 256 ? u : 255) : 0;
+  const int i = p.split ? (u < kSplitUnits ? u : kSplitUnits - 1) : 0;
   const int n = uni(tab->kv[i]), s = uni(tab->sl[i]), po = uni(tab->poff[i]);
   const int pw = uni((int)(tab->part[i >> 6] >> (i & 63)));
   Seg sg;
@@ -880,7 +892,7 @@ __device__ __forceinline__ int seg_pages(const DecodeParams& p, const Seg& sg) {
 // The next unit in the workgroup's range after u, or num_units.
 __device__ __forceinline__ int next_live(const DecodeParams& p, const SegLds* tab, int u) {
   if (!p.split) return p.num_units;
-  for (int i = u + 1; i < 256; i = (i | 63) + 1) {
+  for (int i = u + 1; i < p.num_units; i = (i | 63) + 1) {
     const uint64_t w = tab->live[i >> 6] >> (i & 63);
     const uint32_t lo = (uint32_t)uni((int)(uint32_t)w), hi = (uint32_t)uni((int)(uint32_t)(w >> 32));
     const uint64_t ws = ((uint64_t)hi << 32) | lo;
@@ -1349,7 +1361,7 @@ decode_partial(DecodeParams p) {
     tab.xs_ctr = 0u;
     tab.xs_gaveup = 0u;
   }
-  plan_workgroup<C>(p, &tab, sh_blk);
+  plan_workgroup<C>(p, &tab, sh_blk, (MLA_LDS int*)ring);
   // a workgroup whose chunk holds no keys (split mode) has nothing to write;
   // without split an empty unit still writes its zero rows
   if (p.split && tab.hdr.u0 > tab.hdr.u1) return;
@@ -1474,7 +1486,7 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
 // result is the same bit for bit.
 constexpr int kWideBatch = 32;
 __global__ void __launch_bounds__(256) decode_merge_wide(DecodeParams p) {
-  __shared__ int sh_scan[256];
+  __shared__ int sh_scan[kSplitUnits];
   plan_units(p, sh_scan);
   const int lane = threadIdx.x & 63;
   const int item = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
@@ -1555,7 +1567,7 @@ __global__ void __launch_bounds__(256) decode_merge_wide(DecodeParams p) {
 // Plans with few splits per unit (units split many ways take decode_merge_wide).
 template <bool F32, int BATCH>
 __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
-  __shared__ int sh_scan[256];
+  __shared__ int sh_scan[kSplitUnits];
   plan_units(p, sh_scan);
   const int groups = (p.rows_per_unit + 3) / 4;
   const int u = blockIdx.x / groups;
@@ -1606,7 +1618,7 @@ __device__ __forceinline__ int vswz(int r) { return 2 * (((r >> 1) & 1) | (((r >
 
 __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupParams v) {
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
-  __shared__ int sh_scan[256];
+  __shared__ int sh_scan[kSplitUnits];
   MLA_LDS char* wslab = (MLA_LDS char*)smem_raw;           // [kKvRank][V] bf16, dense
   MLA_LDS char* atile = wslab + kKvRank * (v.V / (int)gridDim.z) * 2;  // [16][kVupAPitch]
   // (token group, head, column group) of this workgroup. Workgroup i runs on
@@ -1712,8 +1724,8 @@ using Mixed0  = Cfg<0,  2, 4, 1, 32, 3, false, true,  0>;
 // 64 rows: eight waves, four 16-row tiles x two 256-column halves
 using Rows64  = Cfg<64, 4, 2, 1, 32, 3, false, true,  0>;
 using Rows0   = Cfg<0,  4, 2, 1, 32, 3, false, true,  0>;
-using ColsF64 = Cfg<64, 1, 4, 1, 16, 4, true,  true,  0>;  // f32
-using ColsF0  = Cfg<0,  1, 4, 1, 16, 4, true,  true,  0>;
+using ColsF64 = Cfg<64, 1, 4, 1, 16, 3, true,  true,  0>;  // f32
+using ColsF0  = Cfg<0,  1, 4, 1, 16, 3, true,  true,  0>;
 using Cols64F8 = Cfg<64, 1, 4, 1, 32, 2, false, true,  4, true>;  // fp8 cache, any row count
 using Cols0F8  = Cfg<0,  1, 4, 1, 32, 2, false, true,  4, true>;
 

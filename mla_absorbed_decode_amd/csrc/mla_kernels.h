@@ -10,8 +10,7 @@
 namespace mla {
 
 constexpr int kKvRank = 512;     // latent width L the attention kernels implement
-constexpr int kSplitUnits = 256; // fewer (sequence, row-tile) units than this => split KV
-constexpr int kMaxUnitsSplit = 1024;
+constexpr int kSplitUnits = 1024; // fewer (sequence, row-tile) units than this => split KV
 
 // ------------------------------------------------------------ rotary embedding
 // Interleaved rotation of the rope part: pair (2i, 2i+1) of token t's vector

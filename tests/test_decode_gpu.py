@@ -133,22 +133,61 @@ def test_non_causal_multi_query():
     check(c, "non-causal 3 queries")
 
 
-def test_prefill_many_units_no_split():
-    # 300 queries x 64 heads = 300 units of 64 rows: one workgroup per unit
+def test_prefill_many_units_split():
+    # 300 queries x 64 heads = 300 units of 64 rows, split over 256 workgroups
     c = mi.decode_case(10, NOPE, "bf16", [300], q_len=300, dist="uniform", std=1.0,
                        scale=1.0 / 16)
     check(c, "NoPE prefill 300 x 64 heads")
 
 
+def test_prefill_many_units_no_split():
+    # 1100 queries x 64 heads = 1100 units of 64 rows, past the 1024 units a
+    # split plan holds: one workgroup per unit
+    c = mi.decode_case(10, NOPE, "bf16", [1100], q_len=1100, dist="uniform", std=1.0,
+                       scale=1.0 / 16)
+    check(c, "NoPE prefill 1100 x 64 heads")
+
+
 def test_long_sequence_past_the_staged_block_table():
-    # 256 sequences (one unit each, no split): the long one has 1250 pages of 16
-    # tokens, more than the 1024 block-table entries a workgroup stages, so its
-    # last pages come through the loader's direct block-table reads
+    # 1100 sequences (one unit each, no split): the long one has 1250 pages of
+    # 16 tokens, more than the 1024 block-table entries a workgroup stages, so
+    # its last pages come through the loader's direct block-table reads
     rng = mi.stream(19, 0)
-    seqlens = rng.integers(1, 41, size=256).astype(np.int32)
-    seqlens[77] = 20_000
+    seqlens = rng.integers(1, 41, size=1100).astype(np.int32)
+    seqlens[777] = 20_000
     c = mi.decode_case(19, V2, "bf16", seqlens, page=16)
-    check(c, "256 sequences, one of 1250 pages")
+    check(c, "1100 sequences, one of 1250 pages")
+
+
+def test_split_300_sequences_one_long():
+    # 300 units (more than the 256 workgroups of a split grid): short
+    # sequences and one of 8000 tokens, whose keys spread over many workgroups
+    rng = mi.stream(23, 0)
+    seqlens = rng.integers(0, 200, size=300).astype(np.int32)
+    seqlens[123] = 8000
+    c = mi.decode_case(23, V2, "bf16", seqlens)
+    check(c, "300 sequences, one of 8000 tokens")
+
+
+def test_split_1023_units_page16():
+    # the largest split plan (16 units per planning lane, every bit of the
+    # live/partial masks in use), empty sequences among them, pages of 16
+    rng = mi.stream(24, 0)
+    seqlens = rng.integers(0, 60, size=1023).astype(np.int32)
+    seqlens[::97] = 0
+    seqlens[1000] = 3000
+    seqlens[5] = 2000
+    c = mi.decode_case(24, V2, "bf16", seqlens, page=16)
+    check(c, "1023 sequences, pages of 16")
+
+
+def test_split_many_heads_two_units_per_sequence():
+    # 128 heads over 64-row units: 2 units per sequence, 800 units in a split plan
+    rng = mi.stream(25, 0)
+    seqlens = rng.integers(1, 120, size=400).astype(np.int32)
+    seqlens[0] = 3000
+    c = mi.decode_case(25, V3, "bf16", seqlens)
+    check(c, "400 sequences x 128 heads")
 
 
 # -------------------------------------------------------------------- fp32
