@@ -1012,7 +1012,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
   auto issue_part = [&](const NextTile& t, int stage) {
     if (!t.live || !loader) return;
     MLA_LDS char* dst = ring + t.slot * C::TILE_BYTES;
-    if (C::QT && t.query) {
+    if (t.query) {
       // query row i of the unit at row i of the slot, staged like a key row;
       // reads past QI repeat one (same bytes to the same place), so every
       // loader wave sends LPW reads for every tile
@@ -1191,8 +1191,8 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     }
   };
   // folded query rows of the segment's unit -> registers (B operand layout),
-  // loaded asynchronously from global memory (no query tiles); rows past the
-  // end load row 0 and are zeroed by settle_q
+  // loaded from global memory ahead of the tile reads (no query tiles); rows
+  // past the end load row 0 and are zeroed by settle_q
   auto load_q = [&]() {
     const int unit_row0 = (cs.u - cs.b * p.row_tiles) * p.rows_per_unit;
 #pragma unroll
@@ -1206,7 +1206,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
         // with a split contraction a k-step past the row end (uneven split)
         // reloads the wave's first one, never used
         const int kg = !C::XS ? kk : (wc + C::WC * kk < C::KSTEPS ? wc + C::WC * kk : wc);
-        load_16_async(qreg[rt][kk], qp + 64 * kg);
+        load_16(qreg[rt][kk], qp + 64 * kg);
       }
     }
   };
@@ -1232,10 +1232,8 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
 #pragma unroll
     for (int rt = 0; rt < C::RT; ++rt)
 #pragma unroll
-      for (int kk = 0; kk < C::KW; ++kk) {
-        settle(qreg[rt][kk]);
+      for (int kk = 0; kk < C::KW; ++kk)
         if (!qvalid[rt]) qreg[rt][kk] = QV{};
-      }
   };
   auto end_seg = [&]() {
     const int unit_row0 = (cs.u - cs.b * p.row_tiles) * p.rows_per_unit;
@@ -1253,10 +1251,26 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     }
   };
 
-  if (compute) {
-    begin_state();
-    load_q();  // ahead of the first tiles' reads
+  // The first segment's query rows. Where every wave computes and the unit's
+  // rows fit in a tile (QD), the loader waves read them like a query tile into
+  // ring slot NSLOT - 1, which the first tile reads leave free, so the wait
+  // for them retires nothing younger; otherwise they are read into registers
+  // ahead of the first tiles.
+  constexpr bool QD = C::NP == 0 && C::RTILE <= C::TT && !C::KV8;
+  if (compute) begin_state();
+  if constexpr (QD) {
+    NextTile qt;
+    qt.live = true;
+    qt.query = true;
+    qt.slot = C::NSLOT - 1;
+    qt.qb = cs.b;
+    qt.qrow0 = (cs.u - cs.b * p.row_tiles) * p.rows_per_unit;
+#pragma unroll
+    for (int st3 = 0; st3 < 3; ++st3) issue_part(qt, st3);
+  } else if (compute) {
+    load_q();
   }
+  // prologue: the first NSLOT - 1 tiles
   if (loader && !C::KV8) {
 #pragma unroll
     for (int k = 0; k < C::NSLOT - 1; ++k)
@@ -1266,18 +1280,15 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
         for (int st3 = 0; st3 < 3; ++st3) issue_part(t, st3);
       }
   }
-  if (compute) {
-    // retire the query loads: in a wave that also loads tiles they are older
-    // than every tile read in flight; a wave with no tile reads waits for all
-    if (C::NP == 0 && loader) {
-      const int pro = nsteps < C::NSLOT - 1 ? nsteps : C::NSLOT - 1;
-      if (pro <= 0) wait_vmcnt<0>();
-      else if (pro == 1) wait_vmcnt<C::LPW>();
-      else if (pro == 2) wait_vmcnt<(C::NSLOT >= 3 ? 2 * C::LPW : 0)>();
-      else wait_vmcnt<(C::NSLOT >= 4 ? 3 * C::LPW : 0)>();
-    } else {
-      wait_vmcnt<0>();
-    }
+  if constexpr (QD) {
+    // the query reads are older than the prologue's tile reads
+    const int pro = nsteps < C::NSLOT - 1 ? nsteps : C::NSLOT - 1;
+    if (loader) wait_vmcnt_n<C::NSLOT - 1, C::LPW>(pro);
+    __syncthreads();
+    read_q_tile(ring + (C::NSLOT - 1) * C::TILE_BYTES);
+  } else if (compute) {
+    // the compiler's wait for the query loads also retires the tile reads
+    wait_vmcnt<0>();
     settle_q();
   }
   int xs_seq = 0;  // tile_compute calls so far (the split-contraction rendezvous count)
@@ -1322,7 +1333,10 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     bool q_pending = false;
     for (int k = 0; k < nsteps; ++k) {
       if (q_pending) {
-        // query rows of a new segment were loaded after every tile read in flight
+        // a new segment's query rows: read and waited for here, on this path
+        // only, so no other path has query loads in flight (the wait also
+        // retires the tile reads)
+        load_q();
         wait_vmcnt<0>();
         settle_q();
         q_pending = false;
@@ -1340,7 +1354,6 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
         cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
         ck = 0;
         begin_state();
-        load_q();
         q_pending = true;
       }
     }

@@ -167,19 +167,13 @@ __device__ __forceinline__ void load_lds_16_sbase(uint64_t sbase, uint32_t voff,
                  : "memory", "m0");
 }
 
-// 16-byte global load issued as inline assembly (not modelled by the compiler's
-// wait insertion, like load_lds_16). The result must not be used before a
-// wait_vmcnt<> that retires it followed by settle() on the destination.
+// 16-byte global load into registers, as an ordinary load: the compiler
+// places the wait before the first use. Its wait does not see the LDS DMA
+// reads above (they are inline assembly), so it may retire those too.
 template <class T>
-__device__ __forceinline__ void load_16_async(T& dst, const void* gptr) {
+__device__ __forceinline__ void load_16(T& dst, const void* gptr) {
   static_assert(sizeof(T) == 16, "16-byte register");
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(gptr) : "memory");
-}
-// Tell the compiler a register is (re)defined here: its uses stay after this
-// point. Placed after the wait that retires an asynchronous load into it.
-template <class T>
-__device__ __forceinline__ void settle(T& x) {
-  asm volatile("" : "+v"(x));
+  dst = *(const T*)gptr;
 }
 
 // Reductions over lanes {l, l^16, l^32, l^48} with gfx950's permlane swaps:
