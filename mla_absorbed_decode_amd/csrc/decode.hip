@@ -1115,25 +1115,31 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
       }
       return;
     }
-    // piece c of row r holds bf16 chunks 2c and 2c + 1 of the row; all the
-    // lane's staged pieces are read before any ring write
-    constexpr int PR = C::E / 16;
-    u32x4_t v8[C::L8 > 0 ? C::L8 : 1];
+    // The staged bytes are the tile's e4m3 rows back to back. Each 1 KB read
+    // (all 64 lanes of one instruction of this wave) lands as two halves:
+    // lane j widens bytes 8j .. 8j + 7 of a half into one 16-byte bf16 chunk,
+    // so the 64 lanes of a ring write cover consecutive chunks (no bank
+    // conflicts). All of the lane's staged bytes are read before any ring write.
+    constexpr int CR = C::E / 8;  // bf16 chunks of a row
+    u32x2_t v8[C::L8 > 0 ? C::L8 : 1][2];
+    const MLA_LDS char* stg0 = stage + (k % C::NS8) * C::STAGE_SLOT;
 #pragma unroll
     for (int n = 0; n < C::L8; ++n) {
       const int d = (lwave + n * C::LW) % (C::P8 > 0 ? C::P8 : 1);
-      v8[n] = *(const MLA_LDS u32x4_t*)(stg + d * 1024);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        v8[n][h] = *(const MLA_LDS u32x2_t*)(stg0 + d * 1024 + h * 512 + lane * 8);
     }
 #pragma unroll
     for (int n = 0; n < C::L8; ++n) {
       const int d = (lwave + n * C::LW) % (C::P8 > 0 ? C::P8 : 1);
-      const int idx = d * 64 + lane;
-      const int r = idx / PR, c = idx % PR;
-      const u32x4_t v = v8[n];
-      const int sw = lds_swz(r & 15);
-      MLA_LDS char* row = dst + r * C::PITCH;
-      *(MLA_LDS u32x4_t*)(row + (((2 * c) ^ sw) << 4)) = fp8x8_to_bf16x8(u32x2_t{v[0], v[1]});
-      *(MLA_LDS u32x4_t*)(row + (((2 * c + 1) ^ sw) << 4)) = fp8x8_to_bf16x8(u32x2_t{v[2], v[3]});
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ci = d * 128 + h * 64 + lane;  // chunk of the tile
+        const int r = ci / CR, c = ci % CR;
+        *(MLA_LDS u32x4_t*)(dst + r * C::PITCH + ((c ^ lds_swz(r & 15)) << 4)) =
+            fp8x8_to_bf16x8(v8[n][h]);
+      }
     }
   };
   auto kv8_loader = [&]() {
