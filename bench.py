@@ -688,6 +688,68 @@ def skewed_secondary(dev, steps: int, warmup: int):
     }
 
 
+def _attend_graph_us(c: mi.DecodeCase, dev, steps: int, warmup: int) -> float:
+    """Attention call time (us) of case c over rotated cache copies (cold)."""
+    d = c.dims
+    bf = torch.bfloat16
+    q = torch.from_numpy(np.ascontiguousarray(c.q)).to(bf).to(dev)
+    kv_read = int(c.seqlens.astype(np.int64).sum()) * d.entry * 2
+    copies = max(2, math.ceil(2 * LLC_BYTES / kv_read) + 1)
+    pools = [torch.from_numpy(c.pool).to(bf).to(dev)]
+    pools += [pools[0].clone() for _ in range(copies - 1)]
+    bt = torch.from_numpy(c.block_table).to(dev)
+    sl = torch.from_numpy(c.seqlens).to(dev)
+    out = torch.empty(c.batch, 1, d.n_head, d.kv_rank, dtype=bf, device=dev)
+    lse = torch.empty(c.batch, 1, d.n_head, dtype=torch.float32, device=dev)
+    nbytes = mla.mla_decode_workspace_size(c.batch, 1, d.n_head, d.kv_rank, c.max_seqlen,
+                                           c.page, bf)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    run = lambda i: mla.mla_decode_attend(q, pools[i % copies], bt, sl, c.max_seqlen, c.scale,
+                                          True, out, lse, workspace=ws)
+    for i in range(copies):
+        run(i)
+    torch.cuda.synchronize()
+    graphs = capture(run, copies)
+    whole = capture(lambda _: [run(k) for k in range(copies)], 1)[0]
+    if warmup:
+        replay_steps(whole, graphs, warmup)
+    return replay_steps(whole, graphs, steps) / steps * 1e3
+
+
+def _fit(xs, ys):
+    """Least-squares line y = a + b x: (a, b)."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+    return my - b * mx, b
+
+
+def sweep_secondary(dev, steps: int, warmup: int):
+    """Attention time against the work of a call, for the fixed cost (the
+    intercept of a straight-line fit) and the streaming rate (its slope):
+    V2-Lite sequences (16 heads, seqlens U[512,4096]) at batch 16..128, and
+    the 128-head geometry (batch 4) at seqlen 1024..8192."""
+    res = {"v2lite_batch": [], "v3_seqlen": []}
+    for B in (16, 32, 64, 128):
+        seqlens = mi.stream(0, 5).integers(512, 4097, size=B).astype(np.int32)
+        c = mi.decode_case(0, mi.V2_LITE, mi.BF16, seqlens, tail_fill=0.0)
+        us = _attend_graph_us(c, dev, steps, warmup)
+        res["v2lite_batch"].append({"batch": B, "kv_mb": round(attention_bytes(c) / 1e6, 2),
+                                    "attention_us": round(us, 2)})
+    for S in (1024, 2048, 4096, 8192):
+        c = mi.decode_case(0, mi.V3, mi.BF16, [S] * 4, tail_fill=0.0)
+        us = _attend_graph_us(c, dev, steps, warmup)
+        res["v3_seqlen"].append({"seqlen": S, "kv_mb": round(attention_bytes(c) / 1e6, 2),
+                                 "attention_us": round(us, 2)})
+    for key in ("v2lite_batch", "v3_seqlen"):
+        a, b = _fit([r["kv_mb"] for r in res[key]], [r["attention_us"] for r in res[key]])
+        res[key + "_fit"] = {"intercept_us": round(a, 2), "us_per_mb": round(b, 4),
+                             "slope_gbs": round(1e3 / b, 1) if b > 0 else None}
+    res["workload"] = ("attention calls (bf16, 64-token pages, rotated cache copies): V2-Lite "
+                       "geometry over batch, 128-head geometry over seqlen")
+    return res
+
+
 def sparse_secondary(dev, steps: int, warmup: int):
     """Sparse fp8 decode over 656-byte entries: the sparse-decode page's shape
     (batch 2 x 128 heads, top-128 over 32 blocks of 64 entries) and a longer
@@ -887,6 +949,9 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache line")
     ap.add_argument("--no-skewed", action="store_true",
                     help="skip the 300-sequence ragged decode line")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the attention call over batch (V2-Lite) and seqlen "
+                         "(128 heads): fixed cost and streaming rate")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse fp8 decode line")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the NoPE prefill line (absorbed and naive routes)")
@@ -986,6 +1051,8 @@ def main():
                 line["v3_decode"]["tflops"] / peaks["mfma_bf16_tflops"], 4)
     if not args.no_skewed:
         line["skewed_300"] = skewed_secondary(dev, max(10, args.steps // 2), args.warmup)
+    if args.sweep:
+        line["sweep"] = sweep_secondary(dev, max(10, args.steps // 2), args.warmup)
     if not args.no_fp8:
         line["fp8_cache"] = fp8_secondary(step, dev, max(10, args.steps // 2), args.warmup,
                                           eager=args.eager)
