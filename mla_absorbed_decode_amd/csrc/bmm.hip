@@ -37,9 +37,11 @@ __device__ __forceinline__ int wswz(int r) { return 2 * (r & 3); }  // bf16 weig
 // the workgroups of one (token tile, head): 16-byte pieces when the rows allow
 // it, all of a thread's loads issued before its stores.
 template <class T>
-__device__ __forceinline__ void copy_rope(const BmmParams& p, int t0, int h) {
+// (wx: this workgroup's column tile; the gridDim.x column tiles of a row tile
+// share the copy)
+__device__ __forceinline__ void copy_rope(const BmmParams& p, int t0, int h, int wx) {
   const int nt = (int)(p.T - t0 < kTM ? p.T - t0 : kTM);
-  const int nwg = (int)gridDim.x, tid = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int nwg = (int)gridDim.x, tid = (int)(wx * blockDim.x + threadIdx.x);
   const int stride = nwg * (int)blockDim.x;
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte piece
   if (p.rope.pos) {
@@ -188,7 +190,7 @@ __global__ void __launch_bounds__(256) bmm_bf16_mfma(BmmParams p) {
         ((uint16_t*)p.out)[(int64_t)tt * p.o_st + (int64_t)h * p.o_sh + n] = f32_to_bf16(acc[nt][j]);
     }
   }
-  if (p.R > 0) copy_rope<uint16_t>(p, t0, h);
+  if (p.R > 0) copy_rope<uint16_t>(p, t0, h, (int)blockIdx.x);
 }
 
 // Prefill-sized token counts (bf16): 128 x 128 output tiles of the shared
@@ -196,17 +198,18 @@ __global__ void __launch_bounds__(256) bmm_bf16_mfma(BmmParams p) {
 // as in bmm_bf16_mfma.
 __global__ void __launch_bounds__(256) bmm_bf16_big(BmmParams p) {
   __shared__ __attribute__((aligned(16))) char lds_raw[kGLds];
-  const int h = blockIdx.z;
+  int nt, tt, h;
+  gemm_tile_coords(nt, tt, h);
   GemmTileArgs g;
   g.a = (const uint16_t*)p.a + (int64_t)h * p.a_sh; g.a_st = p.a_st;
   g.w = (const uint16_t*)p.w + (int64_t)h * p.w_sh; g.w_s1 = p.w_sk;
   g.out = (uint16_t*)p.out + (int64_t)h * p.o_sh; g.o_st = p.o_st;
   g.T = (int)p.T; g.K = (int)p.K; g.N = (int)p.N;
-  g.t0 = blockIdx.y * kGT; g.n0 = blockIdx.x * kGT;
+  g.t0 = tt * kGT; g.n0 = nt * kGT;
   gemm_tile_128<false>(g, (MLA_LDS char*)lds_raw);
   if (p.R > 0) {
-    copy_rope<uint16_t>(p, g.t0, h);
-    if (g.t0 + kTM < p.T) copy_rope<uint16_t>(p, g.t0 + kTM, h);
+    copy_rope<uint16_t>(p, g.t0, h, nt);
+    if (g.t0 + kTM < p.T) copy_rope<uint16_t>(p, g.t0 + kTM, h, nt);
   }
 }
 
@@ -269,7 +272,7 @@ __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
       if (tt < p.T) ((float*)p.out)[(int64_t)tt * p.o_st + (int64_t)h * p.o_sh + n] = acc[nt][j];
     }
   }
-  if (p.R > 0) copy_rope<uint32_t>(p, t0, h);
+  if (p.R > 0) copy_rope<uint32_t>(p, t0, h, (int)blockIdx.x);
 }
 
 // Any sizes: one thread per output element, fp32 accumulation in k order.
@@ -321,7 +324,9 @@ hipError_t launch_bmm(const BmmParams& p, hipStream_t s) {
   if (mfma_ok && p.is_f32) {
     dim3 grid((unsigned)((p.N + kTN - 1) / kTN), (unsigned)((p.T + kTM - 1) / kTM), hz);
     hipLaunchKernelGGL(bmm_f32_mfma, grid, dim3(256), 0, s, p);
-  } else if (mfma_ok && !p.with_cw && p.T >= kBigT && p.K <= INT32_MAX && p.T <= INT32_MAX) {
+  } else if (mfma_ok && !p.with_cw && p.T >= kBigT && p.K <= INT32_MAX && p.T <= INT32_MAX &&
+             (uintptr_t)p.out % 16 == 0 && p.o_st * es % 16 == 0 && p.o_sh * es % 16 == 0) {
+    // (the 128 x 128 tile writes 16-byte pieces of out rows)
     dim3 grid((unsigned)((p.N + kGT - 1) / kGT), (unsigned)((p.T + kGT - 1) / kGT), (unsigned)p.H);
     hipLaunchKernelGGL(bmm_bf16_big, grid, dim3(256), 0, s, p);
   } else if (mfma_ok) {

@@ -29,6 +29,7 @@ constexpr int kGSlotA = kGT * kGAP;
 constexpr int kGSlotB = kGT * kGAP > kGK * kGBP ? kGT * kGAP : kGK * kGBP;
 constexpr int kGSlot = kGSlotA + kGSlotB;
 constexpr int kGLds = 2 * kGSlot;
+constexpr int kGOP = kGT * 2 + 16;  // output tile row pitch in LDS (bf16 row + 16 bytes)
 
 struct GemmTileArgs {
   const uint16_t* a; int64_t a_st;  // row t of head h at a + t * a_st (head offset applied)
@@ -37,6 +38,21 @@ struct GemmTileArgs {
   int T, K, N;                      // N >= 16, a multiple of 8; K a multiple of 32
   int t0, n0;                       // tile origin
 };
+
+// The (column tile, row tile, head) of this workgroup for a grid of
+// (column tiles, row tiles, heads). Workgroup i runs on XCD i % 8; when the
+// grid divides evenly, XCD x takes the x-th eighth of the tiles in
+// column-fastest order, so the column tiles that share rows of `a`, and the
+// tiles of one head's weight, run on one XCD and meet in its L2.
+__device__ __forceinline__ void gemm_tile_coords(int& nt, int& tt, int& h) {
+  const int gx = (int)gridDim.x, gy = (int)gridDim.y;
+  const int total = gx * gy * (int)gridDim.z;
+  int lin = (int)blockIdx.x + gx * ((int)blockIdx.y + gy * (int)blockIdx.z);
+  if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+  nt = lin % gx;
+  tt = (lin / gx) % gy;
+  h = lin / (gx * gy);
+}
 
 template <bool NT>
 __device__ __forceinline__ void gemm_tile_128(const GemmTileArgs& g, MLA_LDS char* lds) {
@@ -123,19 +139,28 @@ __device__ __forceinline__ void gemm_tile_128(const GemmTileArgs& g, MLA_LDS cha
     if (more) store((ks + 1) & 1);
     __syncthreads();
   }
-  // lane holds out[t0 + 64 wr + 16 i + 4 gq + jj][n0 + 64 wc + 16 j + li]
+  // The tile goes out through LDS (free after the last barrier): lane holds
+  // out[64 wr + 16 i + 4 gq + jj][64 wc + 16 j + li] of the tile; it is
+  // stored as bf16 rows of kGOP bytes, then every thread writes 16-byte pieces
+  // of whole rows, so each row's 256 bytes leave in full lines.
+  static_assert(kGT * kGOP <= kGLds, "output tile fits the ring");
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = g.n0 + 64 * wc + 16 * j + li;
-      if (n >= g.N) continue;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int t = g.t0 + 64 * wr + 16 * i + 4 * gq + jj;
-        if (t < g.T) g.out[(int64_t)t * g.o_st + n] = f32_to_bf16(acc[i][j][jj]);
-      }
-    }
+      for (int jj = 0; jj < 4; ++jj)
+        *(MLA_LDS uint16_t*)(lds + (64 * wr + 16 * i + 4 * gq + jj) * kGOP +
+                             2 * (64 * wc + 16 * j + li)) = f32_to_bf16(acc[i][j][jj]);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kGT * kGT / 8 / 256; ++i) {
+    const int idx = tid + 256 * i;
+    const int r = idx >> 4, c = idx & 15;  // row, 8-column piece
+    const int t = g.t0 + r, n = g.n0 + 8 * c;
+    if (t < g.T && n < g.N)  // N is a multiple of 8: a piece is all in or all out
+      *(u32x4_t*)(g.out + (int64_t)t * g.o_st + n) = *(const MLA_LDS u32x4_t*)(lds + r * kGOP + 16 * c);
+  }
 }
 
 }  // namespace mla

@@ -43,8 +43,8 @@ constexpr int kNtM = 64, kNtN = 64, kNtK = 32;
 // first column tile.
 template <class T>
 __device__ __forceinline__ void copy_rope_broadcast(const BmmNtParams& p, int t0, int h,
-                                                    int rows = kNtM) {
-  if (p.R == 0 || blockIdx.x != 0) return;
+                                                    int rows = kNtM, int wx = -1) {
+  if (p.R == 0 || (wx < 0 ? (int)blockIdx.x : wx) != 0) return;
   const int nt = (int)(p.T - t0 < rows ? p.T - t0 : rows);
   const int R = (int)p.R;
   for (int e = threadIdx.x; e < nt * R; e += blockDim.x) {
@@ -110,15 +110,16 @@ __global__ void __launch_bounds__(256) bmm_nt_bf16(BmmNtParams p) {
 // tile (gemm_tile.h), then the rope rows of the tile's 128 tokens.
 __global__ void __launch_bounds__(256) bmm_nt_big(BmmNtParams p) {
   __shared__ __attribute__((aligned(16))) char lds_raw[kGLds];
-  const int h = blockIdx.z;
+  int nt, tt, h;
+  gemm_tile_coords(nt, tt, h);
   GemmTileArgs g;
   g.a = (const uint16_t*)p.a + (int64_t)h * p.a_sh; g.a_st = p.a_st;
   g.w = (const uint16_t*)p.w + (int64_t)h * p.w_sh; g.w_s1 = p.w_sn;
   g.out = (uint16_t*)p.out + (int64_t)h * p.o_sh; g.o_st = p.o_st;
   g.T = (int)p.T; g.K = (int)p.K; g.N = (int)p.N;
-  g.t0 = blockIdx.y * kGT; g.n0 = blockIdx.x * kGT;
+  g.t0 = tt * kGT; g.n0 = nt * kGT;
   gemm_tile_128<true>(g, (MLA_LDS char*)lds_raw);
-  copy_rope_broadcast<uint16_t>(p, g.t0, h, kGT);
+  copy_rope_broadcast<uint16_t>(p, g.t0, h, kGT, nt);
 }
 
 // f32 operands (16-byte aligned rows, K a multiple of 16): v_mfma_f32_16x16x4f32
@@ -532,8 +533,11 @@ hipError_t launch_bmm_nt(const BmmNtParams& p, hipStream_t s) {
   const bool aligned = ((uintptr_t)p.a % 16 == 0) && ((uintptr_t)p.w % 16 == 0) &&
                        (p.a_st * es % 16 == 0) && (p.a_sh * es % 16 == 0) &&
                        (p.w_sh * es % 16 == 0) && (p.w_sn * es % 16 == 0);
-  if (!p.is_f32 && aligned && p.K % kNtK == 0 && p.K > 0 && p.N > 0 && p.T >= kBigT &&
-      p.T <= INT32_MAX && p.K <= INT32_MAX) {
+  // the 128 x 128 tile also writes 16-byte pieces of out rows
+  const bool out_aligned = ((uintptr_t)p.out % 16 == 0) && (p.o_st * es % 16 == 0) &&
+                           (p.o_sh * es % 16 == 0) && p.N % 8 == 0;
+  if (!p.is_f32 && aligned && out_aligned && p.K % kNtK == 0 && p.K > 0 && p.N > 0 &&
+      p.T >= kBigT && p.T <= INT32_MAX && p.K <= INT32_MAX) {
     dim3 grid((unsigned)((p.N + kGT - 1) / kGT), (unsigned)((p.T + kGT - 1) / kGT), (unsigned)p.H);
     hipLaunchKernelGGL(bmm_nt_big, grid, dim3(256), 0, s, p);
   } else if (!p.is_f32 && aligned && p.K % kNtK == 0 && p.K > 0 && p.N > 0) {
