@@ -263,6 +263,17 @@ def test_v3_full_config_block_major():
     assert torch.equal(out_c.view(torch.int16), out_v.view(torch.int16))
 
 
+def test_v3_full_config_permuted_block_table():
+    # the same geometry with the pages in random pool order (a permuted block
+    # table), element by element against the oracle, and bit-identical between
+    # the block-major view and a contiguous copy
+    c = mi.v3_decode(seed=1, permute=True)
+    assert not np.array_equal(np.sort(c.block_table.ravel()), c.block_table.ravel())
+    out_v, _ = check(c, "V3 decode B=4 x 4096 permuted pages, block-major view", block_major=True)
+    out_c, _ = run_decode(c, block_major=False)
+    assert torch.equal(out_c.view(torch.int16), out_v.view(torch.int16))
+
+
 def test_workspace_reused_across_calls():
     # one uninitialised workspace serves a sequence of calls of different plans
     import mla_absorbed_decode_amd as mla

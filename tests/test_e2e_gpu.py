@@ -101,9 +101,11 @@ def test_nope_prefill_full_size_sampled(dtype):
     mla.mla_v_up(o_lat[0], w_uv, out)
     torch.cuda.synchronize()
 
-    # sampled queries: first, last, and a seeded spread; every head of each
+    # sampled queries, every head of each: the first two, the last, every 16th
+    # from 5 (every tile of 32 queries and every 128-row block is hit) and a
+    # seeded spread
     rng = np.random.default_rng(5)
-    qs = np.unique(np.concatenate([[0, 1, T - 1], rng.integers(0, T, 9)]))
+    qs = np.unique(np.concatenate([[0, 1, T - 1], np.arange(5, T, 16), rng.integers(0, T, 9)]))
     q_dev = to_np(q[0])[qs]          # [nq, N, L] as the device stored it
     o_dev = to_np(o_lat[0])[qs]
     # stage 1: the fold of the sampled rows

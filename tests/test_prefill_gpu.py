@@ -212,7 +212,7 @@ def test_naive_prefill_meets_both_oracles(t_q, t_kv):
 def test_naive_prefill_nope_full_size_sampled():
     """The NoPE prefill workload (64 heads x 256, rank 512, t = 2048 causal,
     U[-1,1] activations, U[+-1/sqrt(512)] weights) through the naive route at
-    full size; sampled query rows of two heads against the oracle, and
+    full size; sampled query rows of four heads against the oracle, and
     sampled decompressed rows."""
     mla = _mla()
     c = mi.nope_prefill(0, mi.BF16)
@@ -230,8 +230,9 @@ def test_naive_prefill_nope_full_size_sampled():
                            lse)
     torch.cuda.synchronize()
     assert not torch.isnan(out).any() and not torch.isnan(k_out).any()
-    heads = [0, N - 1]
-    rows = np.array([0, 1, 63, 64, 700, 1500, t - 1])
+    heads = [0, 17, 40, N - 1]
+    # tile edges, the last row, and every 64th row from 3 (every 128-row block)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 700, 1500, t - 1], np.arange(3, t, 64)]))
     kw, vw = oracle.decompress_kv(c["c_kv"][rows], None, c["w_uk_t"][heads], c["w_uv"][heads])
     assert_close(to_np(k_out[rows][:, heads]), kw, "bf16", "k rows")
     assert_close(to_np(v_out[rows][:, heads]), vw, "bf16", "v rows")
