@@ -142,7 +142,8 @@ __device__ __forceinline__ void gemm_tile_128(const GemmTileArgs& g, MLA_LDS cha
   // The tile goes out through LDS (free after the last barrier): lane holds
   // out[64 wr + 16 i + 4 gq + jj][64 wc + 16 j + li] of the tile; it is
   // stored as bf16 rows of kGOP bytes, then every thread writes 16-byte pieces
-  // of whole rows, so each row's 256 bytes leave in full lines.
+  // of whole rows, so each row's 256 bytes leave in full lines (non-temporal:
+  // the product is read by a later kernel, not by this one).
   static_assert(kGT * kGOP <= kGLds, "output tile fits the ring");
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -159,7 +160,8 @@ __device__ __forceinline__ void gemm_tile_128(const GemmTileArgs& g, MLA_LDS cha
     const int r = idx >> 4, c = idx & 15;  // row, 8-column piece
     const int t = g.t0 + r, n = g.n0 + 8 * c;
     if (t < g.T && n < g.N)  // N is a multiple of 8: a piece is all in or all out
-      *(u32x4_t*)(g.out + (int64_t)t * g.o_st + n) = *(const MLA_LDS u32x4_t*)(lds + r * kGOP + 16 * c);
+      __builtin_nontemporal_store(*(const MLA_LDS u32x4_t*)(lds + r * kGOP + 16 * c),
+                                  (u32x4_t*)(g.out + (int64_t)t * g.o_st + n));
   }
 }
 
