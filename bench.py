@@ -9,23 +9,28 @@ workload (16 heads, kv_rank 512 + rope 64, batch 64, seqlens uniform on
   1+2. mla_absorb_q_and_cache, one launch:
        q fold   q_nope [64,16,128] x W_UK_T [16,128,512] -> q[..., :512], q_pe -> q[..., 512:]
        cache    each sequence's newest [c_kv | k_pe] row into its page
-  3+4. mla_decode_attend_v_up: split-KV attention over the paged latent cache, then
-       the log-sum-exp merge and o_lat [64,16,512] x W_UV [16,512,128] in one kernel
+  3+4. mla_decode_attend_v_up_planned: split-KV attention over the paged latent cache,
+       then the log-sum-exp merge and o_lat [64,16,512] x W_UV [16,512,128] in one kernel
+
+The split plan (each attention workgroup's share of the keys) depends only on
+the block table, seqlens and sizes, which every layer of a token step shares:
+one mla_decode_plan launch heads each graph of layer calls and its time is
+counted (--no-plan: every call plans for itself, as mla_decode_attend does).
 
 Inputs are resident in HBM before timing. The latent cache is held in enough
 copies (rotated per step) that the step's working set exceeds twice the
-256 MB last-level cache, so the cache read is an HBM read. The steps over the
-cache copies, one after another, are captured in one HIP graph, the way a
-serving decode loop captures every layer of a token's step in one graph
-(each copy stands for one layer's cache); single-step graphs cover a
-remainder. W warm-up steps, then K timed steps between device
+256 MB last-level cache, so the cache read is an HBM read. A token step's
+layer calls (27, DeepSeek-V2-Lite's depth; call k reads copy k mod copies)
+are captured in one HIP graph, the way a serving decode loop captures a
+token's step in one graph; a second graph holds the calls a count leaves
+over. W warm-up steps, then exactly K timed steps between device
 synchronisations; one JSON line is printed.
 
 value = latent-KV bytes the step must read (sum of seqlens x 576 x 2 B) per
 second of step time. The roofline object covers the attention call (its
-partial and merge kernels): a graph holding only that call, once per cache
-copy, is replayed for K calls right after the steps and timed with HIP events
-on the stream it runs on; its fractions are of the published HBM peak and of
+partial and merge kernels, and its share of the step's plan): graphs of that
+call alone, laid out as the steps', are replayed for K calls right after the
+steps and timed with HIP events on the stream they run on; its fractions are of the published HBM peak and of
 the read rate measured on this GPU (measured_peaks, libmla_probe.so).
 
 The other objects of the line: v2lite_warm (the attention call over one
@@ -75,6 +80,34 @@ def src_sha(paths) -> str:
     return h.hexdigest()[:16]
 
 
+# One split plan per token step (mla_decode_plan), read by every layer's
+# attention call; --no-plan makes every call plan for itself.
+USE_PLAN = True
+
+
+class Plan:
+    """The split plan of attention calls over one block table and seqlens: one
+    mla_decode_plan launch serves every layer's call of a token step."""
+
+    def __init__(self, q, cache, bt, sl, max_seqlen):
+        self.args = (q, cache, bt, sl, max_seqlen)
+        n = mla.mla_decode_plan_size(q.shape[0], q.shape[1], q.shape[2], 512, max_seqlen,
+                                     cache.shape[1], q.dtype) if USE_PLAN else 0
+        self.buf = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+    def launch(self):
+        if self.buf is not None:
+            q, cache, bt, sl, max_seqlen = self.args
+            mla.mla_decode_plan(q, cache, bt, sl, max_seqlen, True, self.buf)
+
+
+def plan_label(layers: int) -> str:
+    if not USE_PLAN:
+        return "none: every call plans its split in its own kernels"
+    return (f"one mla_decode_plan launch per token step of {layers} layer calls, its time "
+            "included (a timed count's last part step reuses the plan made before it)")
+
+
 class Step:
     """Device-resident inputs of one decode step and the four calls."""
 
@@ -108,11 +141,13 @@ class Step:
         nbytes = mla.mla_decode_workspace_size(B, 1, N, d.kv_rank, case.max_seqlen, case.page, bf)
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         self.max_seqlen = case.max_seqlen
+        self.plan = Plan(self.q, self.caches[0], self.bt, self.seqlens, self.max_seqlen)
 
     def attend(self, i: int):
         c = self.caches[i % len(self.caches)]
-        mla.mla_decode_attend(self.q, c, self.bt, self.seqlens, self.max_seqlen, self.case.scale,
-                              True, self.o_lat, self.lse, workspace=self.ws)
+        mla.mla_decode_attend_planned(self.q, c, self.bt, self.seqlens, self.max_seqlen,
+                                      self.case.scale, True, self.o_lat, self.plan.buf, self.lse,
+                                      workspace=self.ws)
 
     def run(self, i: int):
         c = self.caches[i % len(self.caches)]
@@ -120,10 +155,10 @@ class Step:
         mla.mla_absorb_q_and_cache(self.q_nope, self.w_uk_t, self.q_pe, self.q[:, 0],
                                    self.kv_new, self.pe_new, self.slots, c)
         # attention, then the split merge fused with the W_UV un-projection
-        mla.mla_decode_attend_v_up(self.q, c, self.bt, self.seqlens, self.max_seqlen,
-                                   self.case.scale, True, self.w_uv, self.o_lat,
-                                   self.out.view(self.case.batch, 1, self.case.dims.n_head, -1),
-                                   self.lse, workspace=self.ws)
+        mla.mla_decode_attend_v_up_planned(
+            self.q, c, self.bt, self.seqlens, self.max_seqlen, self.case.scale, True, self.w_uv,
+            self.o_lat, self.out.view(self.case.batch, 1, self.case.dims.n_head, -1),
+            self.plan.buf, self.lse, workspace=self.ws)
 
 
 def capture(fn, n: int):
@@ -151,15 +186,80 @@ def replay(graphs, first: int, count: int):
     return t0.elapsed_time(t1)
 
 
+# Attention calls per token step: the decoder layers of DeepSeek-V2-Lite (27)
+# and DeepSeek-V3 (61), from the models' published configurations. A token
+# step computes its split plan once and every layer's call reads it.
+V2_LITE_LAYERS = 27
+V3_LAYERS = 61
+
+
+class Rotation:
+    """Graphs of calls fn(0), fn(1), ..., call k reading cache copy k % n: one
+    graph of `per` calls (the smallest multiple of n that is at least `layers`:
+    one token step's attention calls) led by head() (the step's one split plan),
+    and, captured before any timing, a graph of the calls a count leaves over
+    (they read the plan already made: the same step's tables)."""
+
+    def __init__(self, fn, n: int, layers: int, head=None):
+        self.fn, self.head = fn, head
+        self.per = n * math.ceil(max(layers, 1) / n)
+
+        def every(_):
+            if head:
+                head()
+            for k in range(self.per):
+                fn(k)
+
+        self.whole = capture(every, 1)[0]
+        self.tails = {}
+
+    def prepare(self, count: int):
+        r = count % self.per
+        if r and r not in self.tails:
+            self.tails[r] = capture(lambda _: [self.fn(k) for k in range(r)], 1)[0]
+
+    def replay(self, count: int) -> float:
+        """Replay exactly `count` calls between two events; returns ms."""
+        self.prepare(count)
+        tail = self.tails.get(count % self.per)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(count // self.per):
+            self.whole.replay()
+        if tail is not None:
+            tail.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    def whole_calls(self, count: int) -> int:
+        """count rounded up to whole token steps."""
+        return self.per * max(1, math.ceil(count / self.per))
+
+
+def time_calls(fn, n: int, layers: int, steps: int, warmup: int, head=None) -> float:
+    """ms per call of fn over n rotated cache copies, timed over whole token
+    steps of graphs (at least `steps` calls)."""
+    rot = Rotation(fn, n, layers, head)
+    if warmup:
+        rot.replay(rot.whole_calls(warmup))
+    count = rot.whole_calls(steps)
+    return rot.replay(count) / count
+
+
 def time_steps_eager(step: Step, steps: int, warmup: int):
-    """As time_steps, every call launched from the host."""
+    """As time_steps, every call launched from the host (a plan per step)."""
     for i in range(warmup):
+        step.plan.launch()
         step.run(i)
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record()
     for i in range(warmup, warmup + steps):
+        step.plan.launch()
         step.run(i)
     t1.record()
     torch.cuda.synchronize()
@@ -167,6 +267,7 @@ def time_steps_eager(step: Step, steps: int, warmup: int):
     total_ms = t0.elapsed_time(t1)
     t0.record()
     for i in range(warmup, warmup + steps):
+        step.plan.launch()
         step.attend(i)
     t1.record()
     torch.cuda.synchronize()
@@ -182,39 +283,25 @@ def copy_calibration(dev):
     torch.cuda.synchronize()
 
 
-def replay_steps(whole, singles, count: int):
-    """Replay `count` steps: whole graphs of len(singles) steps each, then
-    single-step graphs for the remainder, between two events; returns ms."""
-    n = len(singles)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(count // n):
-        whole.replay()
-    for i in range(count % n):
-        singles[i].replay()
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1)
-
-
 def time_steps(step: Step, steps: int, warmup: int):
-    """(ms for `steps` whole steps, host seconds for them, ms per attention call)."""
+    """(ms for exactly `steps` steps, host seconds for them, ms per attention call)."""
     n = len(step.caches)
+    step.plan.launch()
     for i in range(n):  # eager pass: one-time kernel attributes are set outside capture
         step.run(i)
+        step.attend(i)
     torch.cuda.synchronize()
-    step_graphs = capture(step.run, n)
-    attn_graphs = capture(step.attend, n)
-    all_steps = capture(lambda _: [step.run(k) for k in range(n)], 1)[0]
-    all_attn = capture(lambda _: [step.attend(k) for k in range(n)], 1)[0]
+    rot = Rotation(step.run, n, V2_LITE_LAYERS, step.plan.launch)
     if warmup:
-        replay_steps(all_steps, step_graphs, warmup)
+        rot.replay(warmup)
+    rot.prepare(steps)
     wall0 = time.perf_counter()
-    total_ms = replay_steps(all_steps, step_graphs, steps)
+    total_ms = rot.replay(steps)
     wall = time.perf_counter() - wall0
-    attn_ms = replay_steps(all_attn, attn_graphs, steps) / steps
+    attn = Rotation(step.attend, n, V2_LITE_LAYERS, step.plan.launch)
+    if warmup:
+        attn.replay(warmup)
+    attn_ms = attn.replay(steps) / steps
     return total_ms, wall, attn_ms
 
 
@@ -238,10 +325,8 @@ def attention_warm_ms(step: Step, steps: int, warmup: int) -> float:
     """ms per attention call over ONE cache copy, replayed back to back: its
     163 MB of latent rows are partly resident in the 256 MB last-level cache
     (a warm figure, reported apart from the cold headline)."""
-    graphs = capture(lambda _: [step.attend(0) for _ in range(4)], 1)
-    if warmup:
-        replay(graphs, 0, warmup)
-    return replay(graphs, 0, steps) / (4 * steps)
+    return time_calls(lambda i: step.attend(0), 1, V2_LITE_LAYERS, steps, warmup,
+                      step.plan.launch)
 
 
 def attention_bytes(case: mi.DecodeCase) -> int:
@@ -405,8 +490,10 @@ def v3_secondary(dev, steps: int, warmup: int, eager: bool = False):
     nbytes = mla.mla_decode_workspace_size(c.batch, 1, d.n_head, d.kv_rank, c.max_seqlen,
                                            c.page, bf)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    run = lambda i: mla.mla_decode_attend(q, views[i % len(views)], bt, sl, c.max_seqlen,
-                                          c.scale, True, out, lse, workspace=ws)
+    plan = Plan(q, views[0], bt, sl, c.max_seqlen)
+    run = lambda i: mla.mla_decode_attend_planned(q, views[i % len(views)], bt, sl, c.max_seqlen,
+                                                  c.scale, True, out, plan.buf, lse, workspace=ws)
+    plan.launch()
     for i in range(len(views)):
         run(i)
     torch.cuda.synchronize()
@@ -414,34 +501,34 @@ def v3_secondary(dev, steps: int, warmup: int, eager: bool = False):
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         for i in range(warmup):
+            plan.launch()
             run(i)
         t0.record()
         for i in range(steps):
+            plan.launch()
             run(i)
         t1.record()
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / steps
         return _v3_line(c, ms)
 
-    def timed(fn, n):
-        graphs = capture(fn, n)
-        whole = capture(lambda _: [fn(k) for k in range(n)], 1)[0]
-        if warmup:
-            replay_steps(whole, graphs, warmup)
-        return replay_steps(whole, graphs, steps) / steps
-
-    ms = timed(run, len(views))
+    ms = time_calls(run, len(views), V3_LAYERS, steps, warmup, plan.launch)
     line = _v3_line(c, ms)
     line["cache_copies"] = copies
     line["kv_bytes_rotated"] = copies * kv_read
-    warm_ms = timed(lambda i: run(0), 4)
+    line["split_plan"] = plan_label(V3_LAYERS)
+    warm_ms = time_calls(lambda i: run(0), 1, V3_LAYERS, steps, warmup, plan.launch)
     line["warm_attention_us"] = round(warm_ms * 1e3, 2)
     line["warm_label"] = "one cache copy reused: its 18.9 MB of latent rows stay in the LLC"
-    runp = lambda i: mla.mla_decode_attend(q, views[i % len(views)], bt_perm, sl, c.max_seqlen,
-                                           c.scale, True, out, lse, workspace=ws)
+    plan_p = Plan(q, views[0], bt_perm, sl, c.max_seqlen)
+    runp = lambda i: mla.mla_decode_attend_planned(q, views[i % len(views)], bt_perm, sl,
+                                                   c.max_seqlen, c.scale, True, out, plan_p.buf,
+                                                   lse, workspace=ws)
+    plan_p.launch()
     runp(0)
     torch.cuda.synchronize()
-    line["permuted_table_attention_us"] = round(timed(runp, len(views)) * 1e3, 2)
+    line["permuted_table_attention_us"] = round(
+        time_calls(runp, len(views), V3_LAYERS, steps, warmup, plan_p.launch) * 1e3, 2)
     return line
 
 
@@ -509,13 +596,8 @@ def fp8_secondary(step: Step, dev, steps: int, warmup: int, eager: bool = False)
             res_ms.append(t0.elapsed_time(t1) / steps)
         attn_ms, step_ms = res_ms
     else:
-        def timed(fn):
-            graphs = capture(fn, copies)
-            whole = capture(lambda _: [fn(k) for k in range(copies)], 1)[0]
-            if warmup:
-                replay_steps(whole, graphs, warmup)
-            return replay_steps(whole, graphs, steps) / steps
-        attn_ms, step_ms = timed(attend), timed(run)
+        attn_ms = time_calls(attend, copies, V2_LITE_LAYERS, steps, warmup)
+        step_ms = time_calls(run, copies, V2_LITE_LAYERS, steps, warmup)
     rows = B * N
     a_bytes = touched + rows * (d.entry * 2 + d.kv_rank * 2 + 4)
     gbs = a_bytes / (attn_ms * 1e-3) / 1e9
@@ -664,16 +746,14 @@ def skewed_secondary(dev, steps: int, warmup: int):
     nbytes = mla.mla_decode_workspace_size(c.batch, 1, d.n_head, d.kv_rank, c.max_seqlen,
                                            c.page, bf)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    run = lambda i: mla.mla_decode_attend(q, pools[i % copies], bt, sl, c.max_seqlen, c.scale,
-                                          True, out, lse, workspace=ws)
+    plan = Plan(q, pools[0], bt, sl, c.max_seqlen)
+    run = lambda i: mla.mla_decode_attend_planned(q, pools[i % copies], bt, sl, c.max_seqlen,
+                                                  c.scale, True, out, plan.buf, lse, workspace=ws)
+    plan.launch()
     for i in range(copies):
         run(i)
     torch.cuda.synchronize()
-    graphs = capture(run, copies)
-    whole = capture(lambda _: [run(k) for k in range(copies)], 1)[0]
-    if warmup:
-        replay_steps(whole, graphs, warmup)
-    ms = replay_steps(whole, graphs, steps) / steps
+    ms = time_calls(run, copies, V2_LITE_LAYERS, steps, warmup, plan.launch)
     byts = attention_bytes(c)
     return {
         "workload": "V2-Lite decode bf16, 300 sequences: 299 of U[128,1024] tokens and one of "
@@ -682,13 +762,14 @@ def skewed_secondary(dev, steps: int, warmup: int):
         "units": c.batch,
         "workspace_bytes": nbytes,
         "cache_copies": copies,
+        "split_plan": plan_label(V2_LITE_LAYERS),
         "attention_us": round(ms * 1e3, 2),
         "gbs": round(byts / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
 
 
-def _attend_graph_us(c: mi.DecodeCase, dev, steps: int, warmup: int) -> float:
+def _attend_graph_us(c: mi.DecodeCase, dev, steps: int, warmup: int, layers: int) -> float:
     """Attention call time (us) of case c over rotated cache copies (cold)."""
     d = c.dims
     bf = torch.bfloat16
@@ -704,16 +785,14 @@ def _attend_graph_us(c: mi.DecodeCase, dev, steps: int, warmup: int) -> float:
     nbytes = mla.mla_decode_workspace_size(c.batch, 1, d.n_head, d.kv_rank, c.max_seqlen,
                                            c.page, bf)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    run = lambda i: mla.mla_decode_attend(q, pools[i % copies], bt, sl, c.max_seqlen, c.scale,
-                                          True, out, lse, workspace=ws)
+    plan = Plan(q, pools[0], bt, sl, c.max_seqlen)
+    run = lambda i: mla.mla_decode_attend_planned(q, pools[i % copies], bt, sl, c.max_seqlen,
+                                                  c.scale, True, out, plan.buf, lse, workspace=ws)
+    plan.launch()
     for i in range(copies):
         run(i)
     torch.cuda.synchronize()
-    graphs = capture(run, copies)
-    whole = capture(lambda _: [run(k) for k in range(copies)], 1)[0]
-    if warmup:
-        replay_steps(whole, graphs, warmup)
-    return replay_steps(whole, graphs, steps) / steps * 1e3
+    return time_calls(run, copies, layers, steps, warmup, plan.launch) * 1e3
 
 
 def _fit(xs, ys):
@@ -733,12 +812,12 @@ def sweep_secondary(dev, steps: int, warmup: int):
     for B in (16, 32, 64, 128):
         seqlens = mi.stream(0, 5).integers(512, 4097, size=B).astype(np.int32)
         c = mi.decode_case(0, mi.V2_LITE, mi.BF16, seqlens, tail_fill=0.0)
-        us = _attend_graph_us(c, dev, steps, warmup)
+        us = _attend_graph_us(c, dev, steps, warmup, V2_LITE_LAYERS)
         res["v2lite_batch"].append({"batch": B, "kv_mb": round(attention_bytes(c) / 1e6, 2),
                                     "attention_us": round(us, 2)})
     for S in (1024, 2048, 4096, 8192):
         c = mi.decode_case(0, mi.V3, mi.BF16, [S] * 4, tail_fill=0.0)
-        us = _attend_graph_us(c, dev, steps, warmup)
+        us = _attend_graph_us(c, dev, steps, warmup, V3_LAYERS)
         res["v3_seqlen"].append({"seqlen": S, "kv_mb": round(attention_bytes(c) / 1e6, 2),
                                  "attention_us": round(us, 2)})
     for key in ("v2lite_batch", "v3_seqlen"):
@@ -962,10 +1041,14 @@ def main():
                     help="skip the measured MFMA / HBM peaks (libmla_probe.so)")
     ap.add_argument("--no-small", action="store_true",
                     help="skip the cache-write and tiny fp32 lines")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="no shared split plan: every attention call plans for itself")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy three times (reference for "
                          "scaling HBM byte counters)")
     args = ap.parse_args()
+    global USE_PLAN
+    USE_PLAN = not args.no_plan
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this implementation runs on a single MI355X and has "
               "no multi-GPU path; run with --gpus 1", file=sys.stderr)
@@ -995,7 +1078,8 @@ def main():
     achieved = a_bytes / (attn_avg_ms * 1e-3) / 1e9
     roof = {
         "bound": "hbm",
-        "kernel": "mla_decode_attend (decode_partial + decode_merge)",
+        "kernel": "mla_decode_attend_planned (decode_partial + decode_merge; one decode_plan "
+                  "per graph of calls)",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
@@ -1028,6 +1112,7 @@ def main():
         },
         "query_heads_tokens_per_s": round(pairs / (ms_per_step * 1e-3), 1),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "split_plan": plan_label(V2_LITE_LAYERS),
         "roofline": roof,
     }
     if not args.eager:

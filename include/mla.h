@@ -343,6 +343,52 @@ int mla_decode_attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,
                            mla_stream stream);
 
 /*
+ * mla_decode_plan -- the split plan of a decode call, computed once for
+ * several calls ([P3] dense decode tests: the tile-scheduler metadata and
+ * split count are computed once from cache_seqlens and passed to every layer's
+ * decode call). Without a plan every workgroup of an attention call plans its
+ * own share (two dependent global round trips: sequence lengths, then block
+ * table); with one it reads its share in one. The plan depends on q's sizes,
+ * the cache's page size and page count, block_table, seqlens (their values),
+ * max_seqlen and causal -- not on q's, the cache's or the output's values, so
+ * one plan serves every layer of a decode step.
+ *   q, kv_cache, block_table, seqlens, max_seqlen, causal: as the attention
+ *     calls it serves (only sizes and the two int32 tables are read)
+ *   plan, plan_bytes: device buffer of at least mla_decode_plan_size() bytes,
+ *     16-byte aligned, caller-owned; written on `stream`
+ * Nothing is launched when the call would not split (mla_decode_plan_size
+ * gives 0; the planned calls then ignore the plan). Errors: as
+ * mla_decode_attend; MLA_ERR_WORKSPACE for a missing or short plan buffer.
+ *
+ * mla_decode_attend_planned, mla_decode_attend_v_up_planned -- the calls
+ * above reading a plan from mla_decode_plan instead of planning. Results are
+ * bit-identical to the unplanned calls. The plan must come from mla_decode_plan
+ * with the same sizes and with block_table and seqlens unchanged since; a plan
+ * made for other sizes (its header says which) is ignored and the call plans
+ * itself. A plan for other table contents gives unspecified rows (the plan's
+ * indices stay within the sizes its header names). plan may be NULL (the
+ * unplanned call). Only bf16 and f32 caches take a plan.
+ */
+int mla_decode_plan_size(int64_t batch, int64_t q_len, int64_t n_heads, int64_t kv_rank,
+                         int64_t max_seqlen, int64_t page, int32_t dtype, size_t* bytes);
+int mla_decode_plan(const mla_tensor* q, const mla_tensor* kv_cache, const mla_tensor* block_table,
+                    const mla_tensor* seqlens, int64_t max_seqlen, int32_t causal, void* plan,
+                    size_t plan_bytes, mla_stream stream);
+int mla_decode_attend_planned(const mla_tensor* q, const mla_tensor* kv_cache,
+                              const mla_tensor* block_table, const mla_tensor* seqlens,
+                              int64_t max_seqlen, float softmax_scale, int32_t causal,
+                              const mla_tensor* out, const mla_tensor* lse, void* workspace,
+                              size_t workspace_bytes, const void* plan, size_t plan_bytes,
+                              mla_stream stream);
+int mla_decode_attend_v_up_planned(const mla_tensor* q, const mla_tensor* kv_cache,
+                                   const mla_tensor* block_table, const mla_tensor* seqlens,
+                                   int64_t max_seqlen, float softmax_scale, int32_t causal,
+                                   const mla_tensor* w_uv, const mla_tensor* o_lat,
+                                   const mla_tensor* out, const mla_tensor* lse, void* workspace,
+                                   size_t workspace_bytes, const void* plan, size_t plan_bytes,
+                                   mla_stream stream);
+
+/*
  * mla_v_up -- un-project the latent attention output through W_UV ([P1] the
  * `_v_up_proj` bmm writing into a transposed [B, N, V] view; [P2]
  * `mla_decompress_v`).

@@ -48,6 +48,10 @@ __all__ = [
     "mla_absorb_q_and_cache",
     "mla_decode_attend_v_up",
     "mla_decode_attend_noalloc",
+    "mla_decode_plan_size",
+    "mla_decode_plan",
+    "mla_decode_attend_planned",
+    "mla_decode_attend_v_up_planned",
     "mla_status_str",
     "lib_path",
     "load",
@@ -111,6 +115,13 @@ def load() -> ctypes.CDLL:
         lib.mla_absorb_q_and_cache.argtypes = [P, P, P, P, P, P, P, P, P, dbl, vp]
         lib.mla_decode_attend_v_up.argtypes = [P, P, P, P, i64, f32, i32, P, P, P, P, vp, sz, vp]
         lib.mla_decode_attend_noalloc.argtypes = [P, P, P, P, i64, f32, i32, P, P, vp]
+        lib.mla_decode_plan_size.argtypes = [i64, i64, i64, i64, i64, i64, i32,
+                                             ctypes.POINTER(sz)]
+        lib.mla_decode_plan.argtypes = [P, P, P, P, i64, i32, vp, sz, vp]
+        lib.mla_decode_attend_planned.argtypes = [P, P, P, P, i64, f32, i32, P, P, vp, sz, vp, sz,
+                                                  vp]
+        lib.mla_decode_attend_v_up_planned.argtypes = [P, P, P, P, i64, f32, i32, P, P, P, P, vp,
+                                                       sz, vp, sz, vp]
         lib.mla_concat_and_cache_fp8.argtypes = [P, P, P, P, vp, vp]
         lib.mla_decode_attend_fp8.argtypes = [P, P, P, P, i64, f32, i32, vp, vp, P, P, vp, sz, vp]
         lib.mla_decompress_kv.argtypes = [P, P, P, P, P, P, vp]
@@ -122,7 +133,8 @@ def load() -> ctypes.CDLL:
                    "mla_decode_attend", "mla_v_up", "mla_rope_interleaved", "mla_absorb_q_rope",
                    "mla_concat_and_cache_rope", "mla_absorb_q_and_cache",
                    "mla_decode_attend_v_up", "mla_decompress_kv", "mla_prefill_attend",
-                   "mla_decode_attend_noalloc",
+                   "mla_decode_attend_noalloc", "mla_decode_plan_size", "mla_decode_plan",
+                   "mla_decode_attend_planned", "mla_decode_attend_v_up_planned",
                    "mla_sparse_decode_fp8", "mla_sparse_workspace_size"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.mla_status_str.argtypes = [ctypes.c_int]
@@ -341,6 +353,76 @@ def mla_decode_attend_v_up(q, kv_cache, block_table, seqlens, max_seqlen, softma
                                       _ref(desc(o_lat)), _ref(desc(out)), _ref(desc(lse)),
                                       workspace.data_ptr(), workspace.numel(), _stream(out)),
            "mla_decode_attend_v_up")
+    return out
+
+
+def mla_decode_plan_size(batch, q_len, n_heads, kv_rank, max_seqlen, page, dtype) -> int:
+    """Bytes of the split plan mla_decode_plan writes (0: such calls do not split)."""
+    out = ctypes.c_size_t(0)
+    _check(load().mla_decode_plan_size(int(batch), int(q_len), int(n_heads), int(kv_rank),
+                                       int(max_seqlen), int(page), _DTYPES[dtype],
+                                       ctypes.byref(out)), "mla_decode_plan_size")
+    return int(out.value)
+
+
+def mla_decode_plan(q, kv_cache, block_table, seqlens, max_seqlen, causal, plan=None):
+    """The split plan of attention calls with q's sizes over this block_table and
+    seqlens, written once for several calls (one per layer). ``plan`` (uint8 device
+    tensor of at least mla_decode_plan_size() bytes) is allocated here when not given;
+    returns it, or None when such calls do not split."""
+    _device_check(q, kv_cache, block_table, seqlens, plan)
+    lib = load()
+    if plan is None:
+        nbytes = mla_decode_plan_size(q.shape[0], q.shape[1], q.shape[2], 512, max_seqlen,
+                                      kv_cache.shape[1], q.dtype)
+        if nbytes == 0:
+            return None
+        plan = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check(lib.mla_decode_plan(_ref(desc(q)), _ref(desc(kv_cache)), _ref(desc(block_table)),
+                               _ref(desc(seqlens)), int(max_seqlen), int(bool(causal)),
+                               plan.data_ptr(), plan.numel(), _stream(q)), "mla_decode_plan")
+    return plan
+
+
+def _plan_args(plan):
+    return (0, 0) if plan is None else (plan.data_ptr(), plan.numel())
+
+
+def mla_decode_attend_planned(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal,
+                              out, plan, lse=None, workspace=None):
+    """mla_decode_attend reading the split plan from mla_decode_plan (None: plan here)."""
+    _device_check(q, kv_cache, block_table, seqlens, out, lse, workspace, plan)
+    lib = load()
+    if workspace is None:
+        nbytes = mla_decode_workspace_size(q.shape[0], q.shape[1], q.shape[2], out.shape[3],
+                                           max_seqlen, kv_cache.shape[1], q.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.mla_decode_attend_planned(_ref(desc(q)), _ref(desc(kv_cache)),
+                                         _ref(desc(block_table)), _ref(desc(seqlens)),
+                                         int(max_seqlen), float(softmax_scale), int(bool(causal)),
+                                         _ref(desc(out)), _ref(desc(lse)), workspace.data_ptr(),
+                                         workspace.numel(), *_plan_args(plan), _stream(out)),
+           "mla_decode_attend_planned")
+    return out
+
+
+def mla_decode_attend_v_up_planned(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
+                                   causal, w_uv, o_lat, out, plan, lse=None, workspace=None):
+    """mla_decode_attend_v_up reading the split plan from mla_decode_plan."""
+    _device_check(q, kv_cache, block_table, seqlens, w_uv, o_lat, out, lse, workspace, plan)
+    lib = load()
+    if workspace is None:
+        nbytes = mla_decode_workspace_size(q.shape[0], q.shape[1], q.shape[2], o_lat.shape[3],
+                                           max_seqlen, kv_cache.shape[1], q.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.mla_decode_attend_v_up_planned(_ref(desc(q)), _ref(desc(kv_cache)),
+                                              _ref(desc(block_table)), _ref(desc(seqlens)),
+                                              int(max_seqlen), float(softmax_scale),
+                                              int(bool(causal)), _ref(desc(w_uv)),
+                                              _ref(desc(o_lat)), _ref(desc(out)), _ref(desc(lse)),
+                                              workspace.data_ptr(), workspace.numel(),
+                                              *_plan_args(plan), _stream(out)),
+           "mla_decode_attend_v_up_planned")
     return out
 
 

@@ -196,6 +196,9 @@ struct SegLds {
   uint64_t live[kUPL];
   uint64_t part[kUPL];
   SegHdr hdr;
+  int ubase;    // the per-unit tables and masks hold units ubase, ubase + 1, ...
+  int ncache;   // leading stream pages staged in sh_blk (the rest come from the block table)
+  int nstaged;  // of those, the ones the segments use
   uint32_t xs_ctr;  // compute-wave rendezvous of the split score contraction (loader layouts)
   uint32_t xs_gaveup;  // set by a compute wave whose rendezvous wait gave up (follows xs_ctr)
 };
@@ -283,6 +286,9 @@ __device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk,
         tab->poff[0] = 0;
         tab->live[0] = 1ull;  // the one unit, whole in this workgroup
         tab->part[0] = 0ull;
+        tab->ubase = 0;
+        tab->ncache = kBlkCache;
+        tab->nstaged = np < kBlkCache ? np : kBlkCache;
         tab->hdr.u0 = tab->hdr.u1 = u;
         tab->hdr.tlo0 = 0;
         tab->hdr.thi1 = n;
@@ -376,6 +382,9 @@ __device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk,
       }
       stage_read(p, st, prun < kBlkCache ? prun : kBlkCache, sh_blk);
       if (lane == 0) {
+        tab->ubase = 0;
+        tab->ncache = kBlkCache;
+        tab->nstaged = prun < kBlkCache ? prun : kBlkCache;
         tab->hdr.u0 = u0;
         tab->hdr.u1 = u1;
         tab->hdr.tlo0 = a;
@@ -385,6 +394,98 @@ __device__ void plan_workgroup(const DecodeParams& p, SegLds* tab, int* sh_blk,
     }
   }
   __syncthreads();
+}
+
+// ------------------------------------------------ a plan shared by calls
+// The call's sizes a plan is tied to: 16 header ints after the magic check.
+__device__ __forceinline__ int plan_field(const DecodeParams& p, int i) {
+  switch (i) {
+    case 0: return kPlanMagic;
+    case 1: return p.variant;
+    case 2: return p.grid;
+    case 3: return p.num_units;
+    case 4: return p.batch;
+    case 5: return p.q_len;
+    case 6: return p.n_heads;
+    case 7: return p.page;
+    case 8: return p.wb;
+    case 9: return p.alpha;
+    case 10: return p.causal;
+    case 11: return p.max_blocks;
+    case 12: return (int)p.num_blocks;
+    case 13: return p.seq_cap;
+    case 14: return p.rows_per_unit;
+    default: return p.row_tiles;
+  }
+}
+
+// Read the merge's copy of the plan (the inclusive cost scan) into sh from
+// p.plan; false (nothing read) when the plan's header is not this call's.
+// Every thread of the workgroup takes part.
+__device__ bool load_scan(const DecodeParams& p, int* sh) {
+  __shared__ int ok;
+  if (threadIdx.x == 0) ok = 1;
+  __syncthreads();
+  if (threadIdx.x < 16 && p.plan[threadIdx.x] != plan_field(p, threadIdx.x)) ok = 0;
+  for (int u = threadIdx.x; u < p.num_units; u += blockDim.x) sh[u] = p.plan[kPlanHdrInts + u];
+  __syncthreads();
+  return ok != 0;
+}
+
+// This workgroup's part of a plan computed beforehand: the descriptor and the
+// header in one round trip (through scratch LDS), then the per-unit tables,
+// masks and staged block ids, as plan_workgroup leaves them (tables indexed
+// from the first unit in range). False (nothing written) when the header is
+// not this call's or the descriptor holds too many units.
+template <class C>
+__device__ bool load_plan(const DecodeParams& p, SegLds* tab, int* sh_blk, MLA_LDS int* scratch) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int* d = p.plan + kPlanHdrInts + kSplitUnits + (int64_t)blockIdx.x * kDescInts;
+  for (int i = t; i < kDescInts / 4; i += C::NT) {
+    const u32x4_t v = ((const u32x4_t*)d)[i];
+    *(MLA_LDS u32x4_t*)(scratch + 4 * i) = v;
+  }
+  if (t < 16) scratch[kDescInts + t] = (int)(p.plan[t] != plan_field(p, t));
+  __syncthreads();
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bad |= scratch[kDescInts + i];
+  const int n = scratch[5];
+  const int npg = scratch[6] < 0 ? 0 : (scratch[6] < kDescPages ? scratch[6] : kDescPages);
+  // the same values in every thread; the fallback plan overwrites scratch
+  // only after every wave has read them
+  if (bad || n < 0 || n > kDescUnits) {
+    __syncthreads();
+    return false;
+  }
+#pragma unroll
+  for (int wd = wave; wd < kUPL; wd += C::NW + C::NP) {
+    const int i = 64 * wd + lane;
+    const int fl = i < n ? scratch[8 + 4 * i + 3] : 0;
+    if (i < n) {
+      tab->kv[i] = scratch[8 + 4 * i];
+      tab->sl[i] = scratch[8 + 4 * i + 1];
+      tab->poff[i] = scratch[8 + 4 * i + 2];
+    }
+    const uint64_t live = __ballot(fl & 1), part = __ballot(fl & 2);
+    if (lane == 0) {
+      tab->live[wd] = live;
+      tab->part[wd] = part;
+    }
+  }
+  for (int i = t; i < npg; i += C::NT) sh_blk[i] = scratch[kDescPageOff + i];
+  if (t == 0) {
+    tab->hdr.u0 = scratch[0];
+    tab->hdr.u1 = scratch[1];
+    tab->hdr.tlo0 = scratch[2];
+    tab->hdr.thi1 = scratch[3];
+    tab->hdr.nsteps = scratch[4];
+    tab->ubase = scratch[0];
+    tab->ncache = npg;
+    tab->nstaged = npg;
+  }
+  __syncthreads();
+  return true;
 }
 
 // R: rope width; WR x WC compute waves split the unit's rows and the 512
@@ -869,7 +970,8 @@ template <class C>
 __device__ __forceinline__ Seg seg_of(const DecodeParams& p, const SegLds* tab, const SegHdr& h,
                                       int u) {
   const bool valid = u <= h.u1 && u < p.num_units;
-  const int i = p.split ? (u < kSplitUnits ? u : kSplitUnits - 1) : 0;
+  int i = p.split ? u - uni(tab->ubase) : 0;  // table index
+  i = i < 0 ? 0 : (i < kSplitUnits ? i : kSplitUnits - 1);
   const int n = uni(tab->kv[i]), s = uni(tab->sl[i]), po = uni(tab->poff[i]);
   const int pw = uni((int)(tab->part[i >> 6] >> (i & 63)));
   Seg sg;
@@ -892,11 +994,13 @@ __device__ __forceinline__ int seg_pages(const DecodeParams& p, const Seg& sg) {
 // The next unit in the workgroup's range after u, or num_units.
 __device__ __forceinline__ int next_live(const DecodeParams& p, const SegLds* tab, int u) {
   if (!p.split) return p.num_units;
-  for (int i = u + 1; i < p.num_units; i = (i | 63) + 1) {
+  const int base = uni(tab->ubase);
+  const int iend = p.num_units - base < kSplitUnits ? p.num_units - base : kSplitUnits;
+  for (int i = u + 1 - base; i < iend; i = (i | 63) + 1) {
     const uint64_t w = tab->live[i >> 6] >> (i & 63);
     const uint32_t lo = (uint32_t)uni((int)(uint32_t)w), hi = (uint32_t)uni((int)(uint32_t)(w >> 32));
     const uint64_t ws = ((uint64_t)hi << 32) | lo;
-    if (ws) return i + __builtin_ctzll(ws);
+    if (ws) return base + i + __builtin_ctzll(ws);
   }
   return p.num_units;
 }
@@ -950,10 +1054,11 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
   int lk = 0;         // tile within ls
   bool lq = true;     // ls's query tile sent (the first segment has none)
   // cache block of page pg of segment ls (staged entry, or a global read past the stage)
+  const int ncache = uni(tab->ncache);
   auto block_of = [&](int pg) -> int {
     const int ti = ls.poff + pg - page_of(p, ls.t_lo);
     int blk;
-    if (ti < kBlkCache) {
+    if (ti < ncache) {
       blk = sh_blk[ti];
     } else {
       blk = load_scalar_i32(p.block_table, (int64_t)ls.b * p.bt_s0 + pg);
@@ -1380,11 +1485,57 @@ decode_partial(DecodeParams p) {
     tab.xs_ctr = 0u;
     tab.xs_gaveup = 0u;
   }
-  plan_workgroup<C>(p, &tab, sh_blk, (MLA_LDS int*)ring);
+  if (!(p.plan && p.split && load_plan<C>(p, &tab, sh_blk, (MLA_LDS int*)ring)))
+    plan_workgroup<C>(p, &tab, sh_blk, (MLA_LDS int*)ring);
   // a workgroup whose chunk holds no keys (split mode) has nothing to write;
   // without split an empty unit still writes its zero rows
   if (p.split && tab.hdr.u0 > tab.hdr.u1) return;
   process_range<C>(p, &tab, sh_blk, ring, xchg);
+}
+
+// The split plan of a call, computed once into p.plan for the calls that
+// share its sequence lengths, block table and sizes (one layer's attention
+// after another): one 64-thread workgroup per attention workgroup runs that
+// workgroup's plan pass and writes its descriptor; workgroup 0 also writes the
+// merge's cost scan and the header, last.
+template <class C>
+__global__ void __launch_bounds__(64) decode_plan(DecodeParams p) {
+  __shared__ SegLds tab;
+  __shared__ int sh_blk[kBlkCache];
+  __shared__ int scratch[5 * kSplitUnits];
+  plan_workgroup<C>(p, &tab, sh_blk, (MLA_LDS int*)scratch);
+  const int lane = threadIdx.x;
+  int* d = p.plan + kPlanHdrInts + kSplitUnits + (int64_t)blockIdx.x * kDescInts;
+  const int u0 = tab.hdr.u0, u1 = tab.hdr.u1;
+  const int n = u1 >= u0 ? u1 - u0 + 1 : 0;
+  const int npg = tab.nstaged < kDescPages ? tab.nstaged : kDescPages;
+  const bool fits = n <= kDescUnits;
+  if (lane == 0) {
+    d[0] = u0;
+    d[1] = u1;
+    d[2] = tab.hdr.tlo0;
+    d[3] = tab.hdr.thi1;
+    d[4] = tab.hdr.nsteps;
+    d[5] = fits ? n : -1;
+    d[6] = npg;
+    d[7] = 0;
+  }
+  if (fits) {
+    for (int i = lane; i < n; i += 64) {
+      const int u = u0 + i;  // tables indexed by unit (ubase 0)
+      d[8 + 4 * i] = tab.kv[u];
+      d[8 + 4 * i + 1] = tab.sl[u];
+      d[8 + 4 * i + 2] = tab.poff[u];
+      d[8 + 4 * i + 3] = (int)((tab.live[u >> 6] >> (u & 63)) & 1u) |
+                         ((int)((tab.part[u >> 6] >> (u & 63)) & 1u) << 1);
+    }
+  }
+  for (int i = lane; i < npg; i += 64) d[kDescPageOff + i] = sh_blk[i];
+  if (blockIdx.x == 0) {
+    plan_units(p, scratch);
+    for (int u = lane; u < p.num_units; u += 64) p.plan[kPlanHdrInts + u] = scratch[u];
+    if (lane < 16) p.plan[lane] = plan_field(p, lane);
+  }
 }
 
 // ------------------------------------------------------------------- merge
@@ -1506,7 +1657,7 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
 constexpr int kWideBatch = 32;
 __global__ void __launch_bounds__(256) decode_merge_wide(DecodeParams p) {
   __shared__ int sh_scan[kSplitUnits];
-  plan_units(p, sh_scan);
+  if (!(p.plan && load_scan(p, sh_scan))) plan_units(p, sh_scan);
   const int lane = threadIdx.x & 63;
   const int item = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
   const int half = item & 1, ur = item >> 1;
@@ -1587,7 +1738,7 @@ __global__ void __launch_bounds__(256) decode_merge_wide(DecodeParams p) {
 template <bool F32, int BATCH>
 __global__ void __launch_bounds__(256) decode_merge(DecodeParams p) {
   __shared__ int sh_scan[kSplitUnits];
-  plan_units(p, sh_scan);
+  if (!(p.plan && load_scan(p, sh_scan))) plan_units(p, sh_scan);
   const int groups = (p.rows_per_unit + 3) / 4;
   const int u = blockIdx.x / groups;
   const int lane = threadIdx.x & 63;
@@ -1671,7 +1822,7 @@ __global__ void __launch_bounds__(1024) decode_merge_vup(DecodeParams p, VupPara
       load_lds_16(W + (int64_t)r * v.w_sk * 2 + c * 16, wslab + inst * 1024);
     }
   }
-  plan_units(p, sh_scan);
+  if (!(p.plan && load_scan(p, sh_scan))) plan_units(p, sh_scan);
   // merge: wave w takes token tok0 + w
   const int t = tok0 + wave;
   const int c0 = lane * 8;
@@ -1876,6 +2027,25 @@ int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int
     plan->workspace_bytes = 0;
   }
   return 0;
+}
+
+hipError_t launch_decode_plan(const DecodePlan& plan, DecodeParams p, hipStream_t s) {
+  if (!plan.split || !p.plan) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)plan.grid), block(64);
+  switch (plan.variant) {
+    case kCols64: hipLaunchKernelGGL(decode_plan<Cols64>, grid, block, 0, s, p); break;
+    case kCols0: hipLaunchKernelGGL(decode_plan<Cols0>, grid, block, 0, s, p); break;
+    case kMixed64: hipLaunchKernelGGL(decode_plan<Mixed64>, grid, block, 0, s, p); break;
+    case kMixed0: hipLaunchKernelGGL(decode_plan<Mixed0>, grid, block, 0, s, p); break;
+    case kRows64: hipLaunchKernelGGL(decode_plan<Rows64>, grid, block, 0, s, p); break;
+    case kRows0: hipLaunchKernelGGL(decode_plan<Rows0>, grid, block, 0, s, p); break;
+    case kColsF64: hipLaunchKernelGGL(decode_plan<ColsF64>, grid, block, 0, s, p); break;
+    case kColsF0: hipLaunchKernelGGL(decode_plan<ColsF0>, grid, block, 0, s, p); break;
+    case kCols64F8: hipLaunchKernelGGL(decode_plan<Cols64F8>, grid, block, 0, s, p); break;
+    case kCols0F8: hipLaunchKernelGGL(decode_plan<Cols0F8>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodePlan& plan, DecodeParams p, int64_t rope, int is_f32,

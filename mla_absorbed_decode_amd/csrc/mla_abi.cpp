@@ -345,7 +345,9 @@ static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
                         const mla_tensor* out, const mla_tensor* lse, void* workspace,
                         size_t workspace_bytes, mla::DecodePlan* plan_out,
                         mla::DecodeParams* params_out, int* empty,
-                        const float* descale_q = nullptr, const float* descale_k = nullptr) {
+                        const float* descale_q = nullptr, const float* descale_k = nullptr,
+                        const void* plan_buf = nullptr, size_t plan_bytes = 0,
+                        bool plan_only = false) {
   int rc;
   *empty = 0;
   if ((rc = check_desc(q, 4)) || (rc = check_desc(kv_cache, 3)) ||
@@ -383,11 +385,15 @@ static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   mla::DecodePlan plan;
   if (mla::plan_decode(B, Sq, N, R, max_seqlen, dt == MLA_F32, &plan, kv8))
     return MLA_ERR_UNSUPPORTED;
-  if (plan.workspace_bytes > 0) {
+  if (plan.workspace_bytes > 0 && !plan_only) {
     if (!workspace) return MLA_ERR_WORKSPACE;
     if (workspace_bytes < plan.workspace_bytes) return MLA_ERR_WORKSPACE;
     if ((uintptr_t)workspace % 16) return MLA_ERR_WORKSPACE;
   }
+  // a plan buffer is used by split calls only (an unsplit call plans in one round trip)
+  const bool use_plan = plan_buf != nullptr && plan.split;
+  if (use_plan && (plan_bytes < mla::plan_bytes_for(plan.grid) || (uintptr_t)plan_buf % 16))
+    return MLA_ERR_WORKSPACE;
   if (NB == 0) {
     // an empty pool can only serve empty sequences; the kernel never reads it
   }
@@ -432,6 +438,8 @@ static int build_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   p.descale_q = descale_q;
   p.descale_k = descale_k;
   p.rendezvous_polls = rendezvous_polls();
+  p.variant = plan.variant;
+  p.plan = use_plan ? (int*)const_cast<void*>(plan_buf) : nullptr;
   *plan_out = plan;
   *params_out = p;
   return MLA_OK;
@@ -450,6 +458,59 @@ int mla_decode_attend(const mla_tensor* q, const mla_tensor* kv_cache,
   if (rc || empty) return rc;
   const int64_t R = q->shape[3] - out->shape[3];
   return launched(mla::launch_decode(plan, p, R, q->dtype == MLA_F32, (hipStream_t)stream));
+}
+
+// ---------------------------------------------- one plan for several calls
+int mla_decode_plan_size(int64_t batch, int64_t q_len, int64_t n_heads, int64_t kv_rank,
+                         int64_t max_seqlen, int64_t page, int32_t dtype, size_t* bytes) {
+  if (!bytes) return MLA_ERR_NULL;
+  if (batch < 0 || q_len < 0 || n_heads < 0 || max_seqlen < 0 || page <= 0) return MLA_ERR_SHAPE;
+  if (!is_value_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (kv_rank != mla::kKvRank || page % 16) return MLA_ERR_UNSUPPORTED;
+  *bytes = 0;
+  if (batch == 0 || q_len == 0 || n_heads == 0) return MLA_OK;
+  mla::DecodePlan plan;
+  if (mla::plan_decode(batch, q_len, n_heads, 64, max_seqlen, dtype == MLA_F32, &plan))
+    return MLA_ERR_UNSUPPORTED;
+  *bytes = plan.split ? mla::plan_bytes_for(plan.grid) : 0;
+  return MLA_OK;
+}
+
+int mla_decode_plan(const mla_tensor* q, const mla_tensor* kv_cache, const mla_tensor* block_table,
+                    const mla_tensor* seqlens, int64_t max_seqlen, int32_t causal, void* plan,
+                    size_t plan_bytes, mla_stream stream) {
+  int rc;
+  if ((rc = check_desc(q, 4))) return rc;
+  // the output's shape and layout as the attention call sees it: [B, Sq, N, L]
+  // (only its sizes are used here)
+  mla_tensor out = *q;
+  out.shape[3] = mla::kKvRank;
+  mla::DecodePlan pl;
+  mla::DecodeParams p;
+  int empty;
+  if ((rc = build_attend(q, kv_cache, block_table, seqlens, max_seqlen, 1.f, causal, &out, nullptr,
+                         nullptr, 0, &pl, &p, &empty, nullptr, nullptr, plan, plan_bytes, true)))
+    return rc;
+  if (empty || !pl.split) return MLA_OK;  // nothing to plan
+  if (!plan) return MLA_ERR_WORKSPACE;
+  return launched(mla::launch_decode_plan(pl, p, (hipStream_t)stream));
+}
+
+int mla_decode_attend_planned(const mla_tensor* q, const mla_tensor* kv_cache,
+                              const mla_tensor* block_table, const mla_tensor* seqlens,
+                              int64_t max_seqlen, float softmax_scale, int32_t causal,
+                              const mla_tensor* out, const mla_tensor* lse, void* workspace,
+                              size_t workspace_bytes, const void* plan, size_t plan_bytes,
+                              mla_stream stream) {
+  mla::DecodePlan pl;
+  mla::DecodeParams p;
+  int empty;
+  const int rc = build_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal,
+                              out, lse, workspace, workspace_bytes, &pl, &p, &empty, nullptr,
+                              nullptr, plan, plan_bytes);
+  if (rc || empty) return rc;
+  const int64_t R = q->shape[3] - out->shape[3];
+  return launched(mla::launch_decode(pl, p, R, q->dtype == MLA_F32, (hipStream_t)stream));
 }
 
 // ---------------------------------------------- decode without allocation
@@ -515,17 +576,18 @@ int mla_decode_attend_fp8(const mla_tensor* q, const mla_tensor* kv_cache,
   return launched(mla::launch_decode(plan, p, R, 0, (hipStream_t)stream));
 }
 
-int mla_decode_attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,
-                           const mla_tensor* block_table, const mla_tensor* seqlens,
-                           int64_t max_seqlen, float softmax_scale, int32_t causal,
-                           const mla_tensor* w_uv, const mla_tensor* o_lat, const mla_tensor* out,
-                           const mla_tensor* lse, void* workspace, size_t workspace_bytes,
-                           mla_stream stream) {
+static int attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,
+                       const mla_tensor* block_table, const mla_tensor* seqlens,
+                       int64_t max_seqlen, float softmax_scale, int32_t causal,
+                       const mla_tensor* w_uv, const mla_tensor* o_lat, const mla_tensor* out,
+                       const mla_tensor* lse, void* workspace, size_t workspace_bytes,
+                       const void* plan_buf, size_t plan_bytes, mla_stream stream) {
   mla::DecodePlan plan;
   mla::DecodeParams p;
   int empty, rc;
   if ((rc = build_attend(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal,
-                         o_lat, lse, workspace, workspace_bytes, &plan, &p, &empty)))
+                         o_lat, lse, workspace, workspace_bytes, &plan, &p, &empty, nullptr,
+                         nullptr, plan_buf, plan_bytes)))
     return rc;
   // the un-projection's arguments: o_lat [B, Sq, N, L] seen as [B*Sq, N, L] tokens
   if ((rc = check_desc(w_uv, 3)) || (rc = check_desc(out, 4))) return rc;
@@ -561,6 +623,27 @@ int mla_decode_attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,
   b.T = B * Sq; b.H = N; b.K = L; b.N = V; b.R = 0;
   b.is_f32 = dt == MLA_F32;
   return launched(mla::launch_bmm(b, (hipStream_t)stream));
+}
+
+int mla_decode_attend_v_up(const mla_tensor* q, const mla_tensor* kv_cache,
+                           const mla_tensor* block_table, const mla_tensor* seqlens,
+                           int64_t max_seqlen, float softmax_scale, int32_t causal,
+                           const mla_tensor* w_uv, const mla_tensor* o_lat, const mla_tensor* out,
+                           const mla_tensor* lse, void* workspace, size_t workspace_bytes,
+                           mla_stream stream) {
+  return attend_v_up(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal, w_uv,
+                     o_lat, out, lse, workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+int mla_decode_attend_v_up_planned(const mla_tensor* q, const mla_tensor* kv_cache,
+                                   const mla_tensor* block_table, const mla_tensor* seqlens,
+                                   int64_t max_seqlen, float softmax_scale, int32_t causal,
+                                   const mla_tensor* w_uv, const mla_tensor* o_lat,
+                                   const mla_tensor* out, const mla_tensor* lse, void* workspace,
+                                   size_t workspace_bytes, const void* plan, size_t plan_bytes,
+                                   mla_stream stream) {
+  return attend_v_up(q, kv_cache, block_table, seqlens, max_seqlen, softmax_scale, causal, w_uv,
+                     o_lat, out, lse, workspace, workspace_bytes, plan, plan_bytes, stream);
 }
 
 int mla_decompress_kv(const mla_tensor* kv_c, const mla_tensor* k_pe, const mla_tensor* w_uk_t,

@@ -118,7 +118,29 @@ struct DecodeParams {
   // polls of the compute waves' LDS rendezvous before a wave gives up and
   // marks its outputs NaN (the few-head layouts)
   int rendezvous_polls;
+  // a split plan computed once (decode_plan) for several calls: NULL = every
+  // workgroup plans for itself. The plan kernel writes it; the attention and
+  // merge kernels read it and plan for themselves when its header does not
+  // match their call.
+  int* plan;
+  int variant;            // kernel variant of the call (checked against the plan)
 };
+
+// Plan buffer: kPlanHdrInts header ints, the merge's inclusive cost scan
+// (kSplitUnits ints), then one descriptor of kDescInts ints per workgroup:
+// [u0, u1, tlo0, thi1, nsteps, units stored (-1: too many, plan in the kernel),
+// pages stored, 0], kDescUnits entries [visible keys, sequence length, first
+// staged page, live | part << 1], then kDescPages staged block ids.
+constexpr int kPlanMagic = 0x4d4c4150;
+constexpr int kPlanHdrInts = 64;
+constexpr int kDescInts = 1024;
+constexpr int kDescUnits = 96;
+constexpr int kDescPageOff = 8 + 4 * kDescUnits;
+constexpr int kDescPages = 512;
+static_assert(kDescPageOff + kDescPages <= kDescInts, "descriptor layout");
+constexpr size_t plan_bytes_for(int grid) {
+  return ((size_t)kPlanHdrInts + kSplitUnits + (size_t)grid * kDescInts) * 4;
+}
 
 // The W_UV un-projection fused into the split merge: out[b, i, h, 0:V] =
 // o_lat[b, i, h, :] . W_UV[h] (o_lat is DecodeParams::out).
@@ -143,6 +165,8 @@ struct DecodePlan {
 // kv8: an fp8 cache (bf16 queries); its layout takes units of 16 rows.
 int plan_decode(int64_t batch, int64_t q_len, int64_t n_heads, int64_t rope, int64_t max_seqlen,
                 int is_f32, DecodePlan* plan, int kv8 = 0);
+// Compute the split plan of a call into p.plan (a split plan only).
+hipError_t launch_decode_plan(const DecodePlan& plan, DecodeParams p, hipStream_t s);
 hipError_t launch_decode(const DecodePlan& plan, DecodeParams p, int64_t rope, int is_f32,
                          hipStream_t s);
 // The same with the merge and the W_UV un-projection in one kernel; only for a

@@ -53,7 +53,9 @@ def test_library_exports_every_declared_symbol(lib):
                           "mla_absorb_q_and_cache", "mla_decode_attend_v_up",
                           "mla_concat_and_cache_fp8", "mla_decode_attend_fp8",
                           "mla_decompress_kv", "mla_prefill_attend", "mla_sparse_decode_fp8",
-                          "mla_sparse_workspace_size", "mla_decode_attend_noalloc"}
+                          "mla_sparse_workspace_size", "mla_decode_attend_noalloc",
+                          "mla_decode_plan_size", "mla_decode_plan", "mla_decode_attend_planned",
+                          "mla_decode_attend_v_up_planned"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -265,6 +267,43 @@ def test_decode_v_up_validation(lib):
                                       ctypes.c_float(0.04), 1, R(T([N, 512, 128], F32)), R(o2),
                                       R(T([B, 2, N, 128], F32)), None, ctypes.c_void_p(FAKE),
                                       ctypes.c_size_t(1 << 30), None) == UNSUP
+
+
+def test_decode_plan_validation(lib):
+    B, N = 2, 16
+    q, kv, bt, sl = T([B, 1, N, 576]), T([8, 64, 576]), T([B, 4], I32), T([B], I32)
+    out, lse = T([B, 1, N, 512]), T([B, 1, N], F32)
+    n = ctypes.c_size_t(0)
+    assert lib.mla_decode_plan_size(B, 1, N, 512, 128, 64, BF16, ctypes.byref(n)) == OK
+    need = n.value
+    assert need > 0                                            # few units: a split plan
+    assert lib.mla_decode_plan_size(1, 2048, 64, 512, 2048, 64, BF16, ctypes.byref(n)) == OK
+    assert n.value == 0                                        # no split, nothing to plan
+    assert lib.mla_decode_plan_size(B, 1, N, 256, 128, 64, BF16, ctypes.byref(n)) == UNSUP
+    assert lib.mla_decode_plan_size(B, 1, N, 512, 128, 64, I32, ctypes.byref(n)) == DTYPE
+    assert lib.mla_decode_plan_size(B, 1, N, 512, 128, 64, BF16, None) == NULL
+    plan = lambda q_=q, p=FAKE, nb=need: lib.mla_decode_plan(
+        R(q_), R(kv), R(bt), R(sl), 128, 1, ctypes.c_void_p(p), ctypes.c_size_t(nb), None)
+    assert plan(p=0) == WS                                     # a split call needs the buffer
+    assert plan(nb=need - 1) == WS
+    assert plan(p=FAKE + 4) == WS
+    assert plan(q_=T([B, 1, N, 544])) == SHAPE                 # q and cache widths differ
+    assert plan(q_=None) == NULL
+    rc, wneed = ws_size(lib, B, 1, N, 512, 128, 64)
+    att = lambda p, nb: lib.mla_decode_attend_planned(
+        R(q), R(kv), R(bt), R(sl), 128, ctypes.c_float(0.04), 1, R(out), R(lse),
+        ctypes.c_void_p(FAKE), ctypes.c_size_t(wneed), ctypes.c_void_p(p), ctypes.c_size_t(nb),
+        None)
+    assert att(FAKE, need - 1) == WS                           # short plan
+    assert att(FAKE + 8, need) == WS                           # misaligned plan
+    assert lib.mla_decode_attend_planned(R(q), R(kv), R(bt), R(sl), 128, ctypes.c_float(0.04), 1,
+                                         R(out), R(lse), None, 0, ctypes.c_void_p(FAKE),
+                                         ctypes.c_size_t(need), None) == WS   # workspace still due
+    w, o_lat, out2 = T([N, 512, 128]), T([B, 1, N, 512]), T([B, 1, N, 128])
+    assert lib.mla_decode_attend_v_up_planned(
+        R(q), R(kv), R(bt), R(sl), 128, ctypes.c_float(0.04), 1, R(w), R(o_lat), R(out2), R(lse),
+        ctypes.c_void_p(FAKE), ctypes.c_size_t(wneed), ctypes.c_void_p(FAKE),
+        ctypes.c_size_t(need - 1), None) == WS
 
 
 # ------------------------------------------------------------------- fp8
