@@ -12,6 +12,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -72,6 +73,12 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, flo
 // (i = 0..7) and receives D[4*(l/16)+j][l%16] (j = 0..3).
 __device__ __forceinline__ f32x4_t mfma_16x16x32(i16x8_t a, i16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+// 32x32x16 bf16 -> f32. Lane l holds A[l%32][8*(l/32)+i], B[8*(l/32)+i][l%32]
+// (i = 0..7) and receives D[8*(r/4) + 4*(l/32) + r%4][l%32] (r = 0..15).
+__device__ __forceinline__ f32x16_t mfma_32x32x16(i16x8_t a, i16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 // 16x16x16 bf16 -> f32. Lane l holds A[l%16][4*(l/16)+i], B[4*(l/16)+i][l%16]
