@@ -42,6 +42,7 @@ struct MhaParams {
   int dk, dv;
   int causal;
   float scale_log2;                     // softmax scale * log2(e)
+  int pair_tiles;                       // set by launch_mha: a workgroup takes two query tiles
 };
 hipError_t launch_mha(const MhaParams& p, hipStream_t s);
 bool mha_supported(int dk, int dv);

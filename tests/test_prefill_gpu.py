@@ -143,6 +143,23 @@ def test_prefill_attend_varlen_matches_oracle(DK, DV, N, causal):
     assert_lse_close(to_np(lse), want_lse, "lse")
 
 
+@pytest.mark.parametrize("DK,DV", [(192, 128), (256, 256)])
+def test_prefill_attend_paired_query_tiles(DK, DV):
+    # enough heads x sequences that a causal call pairs its query tiles (the
+    # longest with the shortest, one workgroup for both): three 128-row tiles
+    # (an odd count: the middle one alone), sequences of other lengths, a
+    # chunked-prefill suffix and a sequence of one query
+    lens_q, lens_k = [300, 129, 1, 257], [300, 200, 5, 300]
+    N = 32
+    say(f"prefill_attend paired tiles DK={DK} DV={DV} N={N} lens_q={lens_q} lens_k={lens_k}")
+    q, k, v, cu_q, cu_k = _mha_inputs(7, N, DK, DV, lens_q, lens_k)
+    scale = DK ** -0.5
+    want, want_lse = oracle.mha_varlen(q, k, v, cu_q, cu_k, scale, True)
+    out, lse = _run_mha(q, k, v, cu_q, cu_k, scale, True)
+    assert_close(to_np(out), want, "bf16", "out")
+    assert_lse_close(to_np(lse), want_lse, "lse")
+
+
 def test_prefill_attend_queries_without_keys():
     """More queries than keys: the first queries of the suffix see nothing
     (out 0, lse -inf); a sequence with no keys at all likewise."""
