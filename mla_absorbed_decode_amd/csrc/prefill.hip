@@ -282,7 +282,7 @@ __device__ __forceinline__ float softmax_exp2(float x) {
 template <int DK, int DV>
 __global__ void __launch_bounds__((MhaShape<DK, DV>::THREADS), 2) mha_fwd(MhaParams p) {
   using Sh = MhaShape<DK, DV>;
-  constexpr int QB = Sh::QB, NW = Sh::NW, THREADS = Sh::THREADS, QT = Sh::QT;
+  constexpr int QB = Sh::QB, THREADS = Sh::THREADS, QT = Sh::QT;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
@@ -563,7 +563,7 @@ struct Mha32Shape {
 template <int DK, int DV>
 __global__ void __launch_bounds__((Mha32Shape<DK, DV>::THREADS), 2) mha_fwd32(MhaParams p) {
   using Sh = Mha32Shape<DK, DV>;
-  constexpr int NW = Sh::NW, THREADS = Sh::THREADS, QT = Sh::QT;
+  constexpr int THREADS = Sh::THREADS, QT = Sh::QT;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
