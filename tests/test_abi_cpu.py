@@ -289,6 +289,9 @@ def test_decode_plan_validation(lib):
     assert plan(p=FAKE + 4) == WS
     assert plan(q_=T([B, 1, N, 544])) == SHAPE                 # q and cache widths differ
     assert plan(q_=None) == NULL
+    # an fp8 cache plans in its own call (mla_decode_attend_fp8 takes no plan)
+    assert lib.mla_decode_plan(R(q), R(T([8, 64, 576], FP8)), R(bt), R(sl), 128, 1,
+                               ctypes.c_void_p(FAKE), ctypes.c_size_t(need), None) == DTYPE
     rc, wneed = ws_size(lib, B, 1, N, 512, 128, 64)
     att = lambda p, nb: lib.mla_decode_attend_planned(
         R(q), R(kv), R(bt), R(sl), 128, ctypes.c_float(0.04), 1, R(out), R(lse),

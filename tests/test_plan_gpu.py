@@ -255,8 +255,11 @@ def _v_up_case(c, w_seed):
     return w_uv_np
 
 
-@pytest.mark.parametrize("name", ["V2-Lite B=64", "V3 B=4 x 4096", "300 sequences one of 8000"])
+@pytest.mark.parametrize("name", ["V2-Lite B=64", "V3 B=4 x 4096", "300 sequences one of 8000",
+                                  "fp32", "16 heads x 2 queries"])
 def test_planned_v_up_bit_identical(name):
+    # the fused merge + un-projection where it applies; f32 and two-query calls take the
+    # attention call and then the separate un-projection
     c = CASES[name]()
     say(f"[plan] attend + v_up planned: {name}")
     q, cache, bt, sl = _inputs(c)
