@@ -548,11 +548,11 @@ struct Cfg {
   static constexpr int KB = F32 ? (KSTEPS % 6 == 0 ? 6 : 4) : (SUB == 1 ? (KSTEPS % 6 == 0 ? 6 : 4)
                                                 : (KSTEPS % 3 == 0 ? 3 : 4));
   static constexpr int PB = 4;
-  // Latent rows that only one unit reads stream with the non-temporal policy.
-  // The bf16 layouts of at most 32 rows are only planned when a unit holds
-  // every row of its sequence; with more rows the sequence's other units read
-  // the same keys and the default policy lets them hit in the caches
-  // (measured on the 128-head decode: non-temporal reads cost 7 %).
+  // Latent rows stream with the non-temporal policy in the bf16 layouts of at
+  // most 32 rows: on the 128-head decode's 32-row units (four units of a
+  // sequence read the same keys) 28.1 us against 28.6 us with the default
+  // policy. The 64-row layout keeps the default policy, which lets a
+  // sequence's other units hit in the caches (non-temporal reads cost it 7 %).
   static constexpr bool STREAM = !F32 && RTILE <= 32;
   static_assert(NW == 4 || (NW == 8 && NP == 0), "four compute waves, or eight that load too");
   static_assert(NP == 0 || NP == 4, "no loader waves, or four");
@@ -1657,13 +1657,15 @@ __device__ __forceinline__ bool merge_row(const DecodeParams& p, const int* sh_s
 }
 
 // Merge of bf16 partials for plans that split units many ways (the 128-head
-// decode: about 32 splits per unit). One wave per (unit, row, half of the 512
-// columns), 4 columns per lane, so the rows of a call spread over twice the
-// waves of decode_merge; every split's lse and the first kWideBatch partial
-// row pieces are requested in one round trip after the plan. Splits are
-// summed in split order with decode_merge's weights and reductions, so the
-// result is the same bit for bit.
-constexpr int kWideBatch = 32;
+// decode of 4 sequences: 16 splits per unit). One wave per (unit, row, half of
+// the 512 columns), 4 columns per lane, so the rows of a call spread over
+// twice the waves of decode_merge; every split's lse and the first BATCH
+// partial row pieces are requested in one round trip after the plan (BATCH
+// near the split count: a batch past it re-reads the first split, which
+// measured 1.6 us slower at 16 splits with 32). Splits are summed in split
+// order with decode_merge's weights and reductions, so the result is the same
+// bit for bit.
+template <int kWideBatch>
 __global__ void __launch_bounds__(256) decode_merge_wide(DecodeParams p) {
   __shared__ int sh_scan[kSplitUnits];
   if (!(p.plan && load_scan(p, sh_scan))) plan_units(p, sh_scan);
@@ -1938,7 +1940,12 @@ hipError_t launch_variant(const DecodePlan& plan, const DecodeParams& p, hipStre
   if (!C::F32 && plan.grid >= 8 * plan.num_units) {
     // many splits per unit: two waves per row, every split in one round trip
     const int64_t waves = (int64_t)plan.num_units * plan.rows_per_unit * 2;
-    hipLaunchKernelGGL(decode_merge_wide, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    // splits per unit: about grid / units (plus one where a chunk boundary falls inside)
+    if (plan.grid <= 16 * plan.num_units)
+      hipLaunchKernelGGL(decode_merge_wide<16>, grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(decode_merge_wide<32>, grid, dim3(256), 0, s, p);
   } else
     hipLaunchKernelGGL((decode_merge<C::F32, 8>), dim3(plan.num_units * groups), dim3(256), 0, s, p);
   return hipGetLastError();

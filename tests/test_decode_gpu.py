@@ -274,6 +274,14 @@ def test_v3_full_config_permuted_block_table():
     assert torch.equal(out_c.view(torch.int16), out_v.view(torch.int16))
 
 
+@pytest.mark.parametrize("seqlens", [[4096, 3000], [5000]])
+def test_many_splits_per_unit(seqlens):
+    # 128 heads over one or two sequences: 4 or 8 units of 32 rows split 64 or
+    # 32 ways over the grid, past the 16 splits the merge reads in one batch
+    c = mi.decode_case(26, V3, "bf16", seqlens)
+    check(c, f"128 heads, {len(seqlens)} sequences, many splits per unit")
+
+
 def test_workspace_reused_across_calls():
     # one uninitialised workspace serves a sequence of calls of different plans
     import mla_absorbed_decode_amd as mla
