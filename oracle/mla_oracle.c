@@ -25,7 +25,7 @@
  * W_UK_T is [n_head, d_nope, kv_rank] and W_UV is [n_head, kv_rank, d_v] ([P1]
  * header comment on the V2-Lite shapes).
  *
- * Readings of points the pages leave open (each also listed in the design doc):
+ * Readings of points the pages leave open:
  *   - query i of t_q sits at absolute position t_kv - t_q + i (queries are a
  *     suffix of the cache, [P2] gate 1 "chunked" shape and gate 2); causal means
  *     it sees keys 0..pos, otherwise all t_kv keys.
