@@ -2057,9 +2057,7 @@ hipError_t launch_decode_plan(const DecodePlan& plan, DecodeParams p, hipStream_
     case kRows0: hipLaunchKernelGGL(decode_plan<Rows0>, grid, block, 0, s, p); break;
     case kColsF64: hipLaunchKernelGGL(decode_plan<ColsF64>, grid, block, 0, s, p); break;
     case kColsF0: hipLaunchKernelGGL(decode_plan<ColsF0>, grid, block, 0, s, p); break;
-    case kCols64F8: hipLaunchKernelGGL(decode_plan<Cols64F8>, grid, block, 0, s, p); break;
-    case kCols0F8: hipLaunchKernelGGL(decode_plan<Cols0F8>, grid, block, 0, s, p); break;
-    default: return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;  // fp8 calls plan for themselves
   }
   return hipGetLastError();
 }
