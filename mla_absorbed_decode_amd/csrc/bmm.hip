@@ -215,18 +215,25 @@ __global__ void __launch_bounds__(256) bmm_bf16_big(BmmParams p) {
 
 __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
   if (cache_write_slot(p)) return;
-  __shared__ __attribute__((aligned(16))) float wt[2][kKB * kTN];
+  // kDepth k-blocks of 32 rows in flight: block kb's weight tile and activation
+  // tile are requested kDepth - 1 blocks before they are used, so a long
+  // contraction (the un-projection, K = 512: 16 blocks) waits for about one round
+  // trip rather than one per block. Both tiles travel global -> LDS, so every
+  // wait below is explicit and counts exactly these loads.
+  constexpr int kDepth = 4;
+  constexpr int kOps = 4;  // 16-byte loads per thread per block: two of W, two of A
+  __shared__ __attribute__((aligned(16))) float wt[kDepth][kKB * kTN];  // [k][n]
+  __shared__ __attribute__((aligned(16))) float at[kDepth][kTM * kKB];  // [t][k], swizzled
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
   const int n0 = blockIdx.x * kTN, t0 = blockIdx.y * kTM, h = blockIdx.z;
   const float* W = (const float*)p.w + (int64_t)h * p.w_sh;
-  const int t = t0 + 16 * w + li;
-  const bool tvalid = t < p.T;
-  const float* arow = (const float*)p.a + (int64_t)(tvalid ? t : 0) * p.a_st + (int64_t)h * p.a_sh + 4 * g;
   const int nk = (int)(p.K / kKB);
   f32x4_t acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // the 32 x 64 float tile is 512 16-byte chunks: two per thread, slot = threadIdx.x + 256 * i
+  // A tile: row r (token t0 + r) holds 8 chunks of 4 floats; chunk c sits at
+  // position c ^ ((r >> 1) & 7), so the 16 rows one read touches fall in distinct
+  // banks. Thread slot q = threadIdx.x + 256 i loads position q % 8 of row q / 8.
   auto issue = [&](int kb, int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -237,30 +244,65 @@ __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
       load_lds_16(W + (int64_t)(kb * kKB + r) * p.w_sk + col,
                   (MLA_LDS char*)&wt[buf][0] + (i * 256 + w * 64) * 16);
     }
-  };
-  f32x4_t a0 = tvalid ? *(const f32x4_t*)arow : f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f32x4_t a1 = tvalid ? *(const f32x4_t*)(arow + 16) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-  issue(0, 0);
-  for (int kb = 0; kb < nk; ++kb) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    const f32x4_t c0 = a0, c1 = a1;
-    if (kb + 1 < nk) {
-      const float* an = arow + (kb + 1) * kKB;
-      a0 = tvalid ? *(const f32x4_t*)an : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      a1 = tvalid ? *(const f32x4_t*)(an + 16) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      issue(kb + 1, (kb + 1) & 1);
-    }
-    const MLA_LDS float* tile = (const MLA_LDS float*)wt[kb & 1];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int i = 0; i < 2; ++i) {
+      const int slot = threadIdx.x + 256 * i;
+      const int r = slot >> 3, pos = slot & 7, c = pos ^ ((r >> 1) & 7);
+      int tr = t0 + r;
+      if (tr >= p.T) tr = (int)p.T - 1;  // rows past T repeat the last one; never stored
+      load_lds_16((const float*)p.a + (int64_t)tr * p.a_st + (int64_t)h * p.a_sh + kb * kKB + 4 * c,
+                  (MLA_LDS char*)&at[buf][0] + (i * 256 + w * 64) * 16);
+    }
+  };
+  for (int kb = 0; kb < kDepth - 1 && kb < nk; ++kb) issue(kb, kb);
+  // A tile of at most 16 tokens (a decode step): every wave takes rows 0..15, each
+  // for one 16-column group, so a wave's MFMA chain per block is a quarter as long.
+  // The condition is uniform over the workgroup.
+  const bool narrow = p.T - t0 <= 16;
+  const int r = narrow ? li : 16 * w + li;  // this lane's A row
+  for (int kb = 0; kb < nk; ++kb) {
+    // blocks kb + 1 .. min(kb + kDepth - 2, nk - 1) may stay in flight
+    const int ahead = nk - 1 - kb < kDepth - 2 ? nk - 1 - kb : kDepth - 2;
+    wait_vmcnt_n<kDepth - 2, kOps>(ahead);
+    __syncthreads();  // block kb has landed for every wave; block kb - 1's buffers are free
+    if (kb + kDepth - 1 < nk) issue(kb + kDepth - 1, (kb + kDepth - 1) % kDepth);
+    const int buf = kb % kDepth;
+    const MLA_LDS float* tile = (const MLA_LDS float*)wt[buf];
+    const MLA_LDS float* arow = (const MLA_LDS float*)at[buf] + r * kKB;
+    // k = 4g + x (chunk g) and 16 + 4g + x (chunk 4 + g)
+    const f32x4_t c0 = *(const MLA_LDS f32x4_t*)(arow + 4 * (g ^ ((r >> 1) & 7)));
+    const f32x4_t c1 = *(const MLA_LDS f32x4_t*)(arow + 4 * ((4 + g) ^ ((r >> 1) & 7)));
+    if (narrow) {
+      // four independent chains (one per x), summed after the loop
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        // k = 4g + x (first half) and 16 + 4g + x (second half)
-        acc[nt] = mfma_16x16x4f32(c0[x], tile[(4 * g + x) * kTN + 16 * nt + li], acc[nt]);
-        acc[nt] = mfma_16x16x4f32(c1[x], tile[(16 + 4 * g + x) * kTN + 16 * nt + li], acc[nt]);
+        acc[x] = mfma_16x16x4f32(c0[x], tile[(4 * g + x) * kTN + 16 * w + li], acc[x]);
+        acc[x] = mfma_16x16x4f32(c1[x], tile[(16 + 4 * g + x) * kTN + 16 * w + li], acc[x]);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          acc[nt] = mfma_16x16x4f32(c0[x], tile[(4 * g + x) * kTN + 16 * nt + li], acc[nt]);
+          acc[nt] = mfma_16x16x4f32(c1[x], tile[(16 + 4 * g + x) * kTN + 16 * nt + li], acc[nt]);
+        }
       }
     }
+  }
+  if (narrow) {
+    const int n = n0 + 16 * w + li;
+    if (n < p.N) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tt = t0 + 4 * g + j;
+        if (tt < p.T)
+          ((float*)p.out)[(int64_t)tt * p.o_st + (int64_t)h * p.o_sh + n] =
+              (acc[0][j] + acc[1][j]) + (acc[2][j] + acc[3][j]);
+      }
+    }
+    if (p.R > 0) copy_rope<uint32_t>(p, t0, h, (int)blockIdx.x);
+    return;
   }
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {

@@ -572,20 +572,6 @@ struct Cfg {
                 "fp8: bf16 compute, loader waves, whole 1 KB staging reads");
 };
 
-// vmcnt <= n * STEP for a wave-uniform n >= 0 (n above MAXN counts as MAXN).
-template <int MAXN, int STEP>
-__device__ __forceinline__ void wait_vmcnt_n(int n) {
-  if constexpr (MAXN > 0) {
-    if (n >= MAXN) {
-      wait_vmcnt<MAXN * STEP>();
-      return;
-    }
-    wait_vmcnt_n<MAXN - 1, STEP>(n);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
 // Everything a wave carries through one segment.
 template <class C>
 struct WaveState {

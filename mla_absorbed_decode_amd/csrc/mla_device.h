@@ -125,6 +125,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// vmcnt <= n * STEP for a wave-uniform n >= 0 (n above MAXN counts as MAXN).
+template <int MAXN, int STEP>
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<MAXN * STEP>();
+      return;
+    }
+    wait_vmcnt_n<MAXN - 1, STEP>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 // Global -> LDS 16-byte load: each lane's 16 bytes land at lds_base + 16*lane
 // (lds_base must be wave-uniform; it goes to M0). Issued as inline assembly so
 // the compiler's wait insertion does not model it: callers wait for these
