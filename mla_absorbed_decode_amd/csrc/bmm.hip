@@ -317,6 +317,60 @@ __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
   if (p.R > 0) copy_rope<uint32_t>(p, t0, h, (int)blockIdx.x);
 }
 
+// f32, a whole call of at most 16 tokens (a decode step): one workgroup per
+// (16-column group, head), so the un-projection (N = 128) spreads over 8
+// workgroups per head rather than 2. Wave w of the eight takes k-blocks w, w + 8,
+// ... of 32 rows (two for K = 512, so all its loads are in flight together) with
+// its operands loaded straight from global memory; the waves' partial tiles are
+// summed through LDS in wave order.
+constexpr int kNarrowWaves = 8;
+
+__global__ void __launch_bounds__(64 * kNarrowWaves) bmm_f32_narrow(BmmParams p) {
+  if (cache_write_slot(p)) return;
+  __shared__ f32x4_t part[kNarrowWaves - 1][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+  const int n = blockIdx.x * 16 + li, h = blockIdx.z;  // N % 16 == 0 here, so n < N
+  const int tr = li < p.T ? li : (int)p.T - 1;  // rows past T repeat the last one; never stored
+  const float* arow = (const float*)p.a + (int64_t)tr * p.a_st + (int64_t)h * p.a_sh + 4 * g;
+  const float* wcol = (const float*)p.w + (int64_t)h * p.w_sh + (int64_t)(4 * g) * p.w_sk + n;
+  const int nk = (int)(p.K / kKB);
+  f32x4_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int kb = w; kb < nk; kb += kNarrowWaves) {
+    // this lane's A values at k = 4g + x and 16 + 4g + x of the block, and the
+    // matching W rows of column n
+    const f32x4_t c0 = *(const f32x4_t*)(arow + kb * kKB);
+    const f32x4_t c1 = *(const f32x4_t*)(arow + kb * kKB + 16);
+    const float* wk = wcol + (int64_t)kb * kKB * p.w_sk;
+    float b0[4], b1[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      b0[x] = wk[x * p.w_sk];
+      b1[x] = wk[(16 + x) * p.w_sk];
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      acc[x] = mfma_16x16x4f32(c0[x], b0[x], acc[x]);
+      acc[x] = mfma_16x16x4f32(c1[x], b1[x], acc[x]);
+    }
+  }
+  f32x4_t sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  if (w > 0) part[w - 1][lane] = sum;
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int i = 0; i < kNarrowWaves - 1; ++i) sum += part[i][lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tt = 4 * g + j;  // D row of this lane's j-th value
+      if (tt < p.T) ((float*)p.out)[(int64_t)tt * p.o_st + (int64_t)h * p.o_sh + n] = sum[j];
+    }
+  }
+  if (p.R > 0) copy_rope<uint32_t>(p, 0, h, (int)blockIdx.x);
+}
+
 // Any sizes: one thread per output element, fp32 accumulation in k order.
 template <bool F32>
 __global__ void __launch_bounds__(256) bmm_plain(BmmParams p) {
@@ -363,7 +417,10 @@ hipError_t launch_bmm(const BmmParams& p, hipStream_t s) {
       (p.a_sh * es % 16 == 0) && (p.w_sh * es % 16 == 0) && (p.w_sk * es % 16 == 0);
   const bool mfma_ok = aligned && p.K % kKB == 0 && p.N % 16 == 0 && p.N >= 16;
   const unsigned hz = (unsigned)p.H + (p.with_cw ? 1u : 0u);  // head slots (+ the cache write)
-  if (mfma_ok && p.is_f32) {
+  if (mfma_ok && p.is_f32 && p.T <= 16) {
+    dim3 grid((unsigned)(p.N / 16), 1, hz);
+    hipLaunchKernelGGL(bmm_f32_narrow, grid, dim3(64 * kNarrowWaves), 0, s, p);
+  } else if (mfma_ok && p.is_f32) {
     dim3 grid((unsigned)((p.N + kTN - 1) / kTN), (unsigned)((p.T + kTM - 1) / kTM), hz);
     hipLaunchKernelGGL(bmm_f32_mfma, grid, dim3(256), 0, s, p);
   } else if (mfma_ok && !p.with_cw && p.T >= kBigT && p.K <= INT32_MAX && p.T <= INT32_MAX &&

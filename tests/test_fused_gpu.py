@@ -21,7 +21,7 @@ def bits(t):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("rope", [False, True])
-@pytest.mark.parametrize("T", [64, 200])
+@pytest.mark.parametrize("T", [9, 64, 200])
 def test_fused_equals_two_calls(dtype, rope, T):
     d = mi.V2_LITE
     td = torch.bfloat16 if dtype == "bf16" else torch.float32
