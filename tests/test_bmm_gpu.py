@@ -117,10 +117,12 @@ def test_odd_sizes(shape):
     assert np.all(np.abs(got - ref) <= 5e-3 * np.maximum(1.0, np.abs(ref)))
 
 
-# T <= 16 per 64-token tile takes the narrow layout (each wave one 16-column group):
-# a whole tile of 1, 3 or 16 tokens, and the 6-token tail of T = 70
+# 16 heads: calls of at most 16 tokens take the split-K kernel; the others take
+# 64 x 64 tiles, whose tiles of at most 16 tokens (the 6-token tail of T = 70,
+# the 16-token one of T = 272) use the narrow layout (each wave one 16-column group)
 @pytest.mark.parametrize("T,K,N", [(64, 128, 512), (64, 512, 128), (3, 256, 512), (70, 512, 256),
-                                   (1, 512, 128), (16, 128, 512), (70, 512, 80), (17, 256, 96)])
+                                   (1, 512, 128), (16, 128, 512), (70, 512, 80), (17, 256, 96),
+                                   (300, 256, 512), (272, 128, 256)])
 def test_fp32_folds(T, K, N):
     H = 16
     a = rand((T, H, K), 5, torch.float32).to(dev())
