@@ -213,7 +213,13 @@ __global__ void __launch_bounds__(256) bmm_bf16_big(BmmParams p) {
   }
 }
 
-__global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
+// NWV = 4: wave w computes rows 16w .. 16w + 15 of the 64 x 64 tile, all 64
+// columns. NWV = 16 (grids too small to fill the chip): wave w computes the
+// 16 x 16 block (rows 16 (w % 4), columns 16 (w / 4)) with four independent
+// chains, a quarter of the MFMA chain per wave; the tiles are loaded the same way.
+template <int NWV>
+__global__ void __launch_bounds__(64 * NWV) bmm_f32_mfma(BmmParams p) {
+  static_assert(NWV == 4 || NWV == 16, "four or sixteen waves");
   if (cache_write_slot(p)) return;
   // kDepth k-blocks of 32 rows in flight: block kb's weight tile and activation
   // tile are requested kDepth - 1 blocks before they are used, so a long
@@ -221,13 +227,17 @@ __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
   // trip rather than one per block. Both tiles travel global -> LDS, so every
   // wait below is explicit and counts exactly these loads.
   constexpr int kDepth = 4;
-  constexpr int kOps = 4;  // 16-byte loads per thread per block: two of W, two of A
+  // 16-byte loads per loading thread per tile: the 512 chunks of a tile over
+  // 256 threads (two each) or over the first 512 of 1024 (one each)
+  constexpr int NLD = NWV == 4 ? 2 : 1;
+  constexpr int kOps = 2 * NLD;  // per block: W and A
   __shared__ __attribute__((aligned(16))) float wt[kDepth][kKB * kTN];  // [k][n]
   __shared__ __attribute__((aligned(16))) float at[kDepth][kTM * kKB];  // [t][k], swizzled
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
   const int n0 = blockIdx.x * kTN, t0 = blockIdx.y * kTM, h = blockIdx.z;
   const float* W = (const float*)p.w + (int64_t)h * p.w_sh;
   const int nk = (int)(p.K / kKB);
+  const bool loads = threadIdx.x < 512;
   f32x4_t acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -235,37 +245,42 @@ __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
   // position c ^ ((r >> 1) & 7), so the 16 rows one read touches fall in distinct
   // banks. Thread slot q = threadIdx.x + 256 i loads position q % 8 of row q / 8.
   auto issue = [&](int kb, int buf) {
+    if (!loads) return;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NLD; ++i) {
       const int slot = threadIdx.x + 256 * i;
       const int r = slot >> 4, c = slot & 15;
       int col = n0 + 4 * c;
       if (col + 4 > p.N) col = (int)p.N - 4;
       load_lds_16(W + (int64_t)(kb * kKB + r) * p.w_sk + col,
-                  (MLA_LDS char*)&wt[buf][0] + (i * 256 + w * 64) * 16);
+                  (MLA_LDS char*)&wt[buf][0] + (slot - lane) * 16);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NLD; ++i) {
       const int slot = threadIdx.x + 256 * i;
       const int r = slot >> 3, pos = slot & 7, c = pos ^ ((r >> 1) & 7);
       int tr = t0 + r;
       if (tr >= p.T) tr = (int)p.T - 1;  // rows past T repeat the last one; never stored
       load_lds_16((const float*)p.a + (int64_t)tr * p.a_st + (int64_t)h * p.a_sh + kb * kKB + 4 * c,
-                  (MLA_LDS char*)&at[buf][0] + (i * 256 + w * 64) * 16);
+                  (MLA_LDS char*)&at[buf][0] + (slot - lane) * 16);
     }
   };
   for (int kb = 0; kb < kDepth - 1 && kb < nk; ++kb) issue(kb, kb);
-  // A tile of at most 16 tokens (a decode step): every wave takes rows 0..15, each
-  // for one 16-column group, so a wave's MFMA chain per block is a quarter as long.
-  // The condition is uniform over the workgroup.
-  const bool narrow = p.T - t0 <= 16;
-  const int r = narrow ? li : 16 * w + li;  // this lane's A row
+  // NWV = 4 and a tile of at most 16 tokens (the tail of a call): every wave
+  // takes rows 0..15, each for one 16-column group, as NWV = 16 does.
+  // Both conditions are uniform over the workgroup.
+  const bool narrow = NWV == 16 || p.T - t0 <= 16;
+  const int wr = NWV == 16 ? (w & 3) : (narrow ? 0 : w);  // 16-row group
+  const int wq = NWV == 16 ? (w >> 2) : w;                // 16-column group when narrow
+  const bool busy = t0 + 16 * wr < p.T;  // wave-uniform: its rows hold tokens
+  const int r = 16 * wr + li;            // this lane's A row
   for (int kb = 0; kb < nk; ++kb) {
     // blocks kb + 1 .. min(kb + kDepth - 2, nk - 1) may stay in flight
     const int ahead = nk - 1 - kb < kDepth - 2 ? nk - 1 - kb : kDepth - 2;
     wait_vmcnt_n<kDepth - 2, kOps>(ahead);
     __syncthreads();  // block kb has landed for every wave; block kb - 1's buffers are free
     if (kb + kDepth - 1 < nk) issue(kb + kDepth - 1, (kb + kDepth - 1) % kDepth);
+    if (!busy) continue;
     const int buf = kb % kDepth;
     const MLA_LDS float* tile = (const MLA_LDS float*)wt[buf];
     const MLA_LDS float* arow = (const MLA_LDS float*)at[buf] + r * kKB;
@@ -276,8 +291,8 @@ __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
       // four independent chains (one per x), summed after the loop
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        acc[x] = mfma_16x16x4f32(c0[x], tile[(4 * g + x) * kTN + 16 * w + li], acc[x]);
-        acc[x] = mfma_16x16x4f32(c1[x], tile[(16 + 4 * g + x) * kTN + 16 * w + li], acc[x]);
+        acc[x] = mfma_16x16x4f32(c0[x], tile[(4 * g + x) * kTN + 16 * wq + li], acc[x]);
+        acc[x] = mfma_16x16x4f32(c1[x], tile[(16 + 4 * g + x) * kTN + 16 * wq + li], acc[x]);
       }
     } else {
 #pragma unroll
@@ -291,11 +306,11 @@ __global__ void __launch_bounds__(256) bmm_f32_mfma(BmmParams p) {
     }
   }
   if (narrow) {
-    const int n = n0 + 16 * w + li;
-    if (n < p.N) {
+    const int n = n0 + 16 * wq + li;
+    if (busy && n < p.N) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int tt = t0 + 4 * g + j;
+        const int tt = t0 + 16 * wr + 4 * g + j;
         if (tt < p.T)
           ((float*)p.out)[(int64_t)tt * p.o_st + (int64_t)h * p.o_sh + n] =
               (acc[0][j] + acc[1][j]) + (acc[2][j] + acc[3][j]);
@@ -422,7 +437,11 @@ hipError_t launch_bmm(const BmmParams& p, hipStream_t s) {
     hipLaunchKernelGGL(bmm_f32_narrow, grid, dim3(64 * kNarrowWaves), 0, s, p);
   } else if (mfma_ok && p.is_f32) {
     dim3 grid((unsigned)((p.N + kTN - 1) / kTN), (unsigned)((p.T + kTM - 1) / kTM), hz);
-    hipLaunchKernelGGL(bmm_f32_mfma, grid, dim3(256), 0, s, p);
+    // a grid that leaves most of the chip idle takes sixteen waves per tile
+    if ((int64_t)grid.x * grid.y * p.H < 256)
+      hipLaunchKernelGGL(bmm_f32_mfma<16>, grid, dim3(1024), 0, s, p);
+    else
+      hipLaunchKernelGGL(bmm_f32_mfma<4>, grid, dim3(256), 0, s, p);
   } else if (mfma_ok && !p.with_cw && p.T >= kBigT && p.K <= INT32_MAX && p.T <= INT32_MAX &&
              (uintptr_t)p.out % 16 == 0 && p.o_st * es % 16 == 0 && p.o_sh * es % 16 == 0) {
     // (the 128 x 128 tile writes 16-byte pieces of out rows)
