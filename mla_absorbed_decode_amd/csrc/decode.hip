@@ -526,7 +526,10 @@ struct Cfg {
   // wc takes k-steps wc, wc + WC, wc + 2 WC, ... (at most KW of them) and the
   // partial scores are summed through LDS in wave order.
   static constexpr int KW = XS ? (KSTEPS + WC - 1) / WC : KSTEPS;
-  static constexpr int XCHG_BYTES = XS ? NW * SUB * RT * 64 * 16 : 0;  // partial score blocks
+  // partial score blocks; the layouts without loader waves alternate between two
+  // copies (their one barrier per tile sits at the exchange)
+  static constexpr int XCHG_HALF = XS ? NW * SUB * RT * 64 : 0;  // f32x4 per copy
+  static constexpr int XCHG_BYTES = XCHG_HALF * 16 * (NP == 0 ? 2 : 1);
   static constexpr int RING_BYTES = NSLOT * TILE_BYTES;
   // KV8 staging: a key tile as e4m3 bytes (TT rows of E) or a query tile as
   // bf16 (RTILE rows of 2E), P8 / QI 1 KB reads, L8 of them per loader wave
@@ -582,11 +585,15 @@ struct WaveState {
 };
 
 // ---------------------------------------------------------------- one tile
-template <class C, class QReg, class Hook>
+// hook(stage): the caller's work at three points of the tile (tile reads to
+// issue); mid(): without loader waves, the workgroup barrier between storing
+// the partial scores and reading them back.
+template <class C, class QReg, class Hook, class Mid>
 __device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, MLA_LDS f32x4_t* xchg,
                                              int j0, const QReg& qreg, WaveState<C>& st,
                                              float scale_log2, int wr, int wc, int dc0,
-                                             const Hook& hook, MLA_LDS uint32_t* xs_ctr,
+                                             const Hook& hook, const Mid& mid,
+                                             MLA_LDS uint32_t* xs_ctr,
                                              int& xs_seq, int& xs_bad, int rendezvous_polls) {
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   f32x4_t s[C::SUB][C::RT];
@@ -663,7 +670,7 @@ __device__ __forceinline__ void tile_compute(const MLA_LDS char* tile, MLA_LDS f
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       ++xs_seq;
     } else {
-      __syncthreads();
+      mid();
     }
     const MLA_LDS f32x4_t* grp = xchg + wr * C::WC * (C::SUB * C::RT * 64) + lane;
     f32x4_t part[C::WC][C::SUB][C::RT];
@@ -1423,7 +1430,7 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
         continue;
       }
       tile_compute<C>(slot, xchg, cs.t_lo + ck * C::TT, qreg, st, scale_log2, wr, wc, dc0,
-                      [](int) {}, xs_ctr, xs_seq, xs_bad, p.rendezvous_polls);
+                      [](int) {}, []() {}, xs_ctr, xs_seq, xs_bad, p.rendezvous_polls);
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
         cs = seg_of<C>(p, tab, h, next_live(p, tab, cs.u));
@@ -1435,8 +1442,18 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
     end_seg();
     }
   } else {
-    // ---- every wave loads and computes
+    // ---- every wave loads and computes. One workgroup barrier per tile, at the
+    // score exchange of tile k: it publishes the partial scores (stored in the
+    // copy k % 2 of the exchange), makes tile k + 1 visible (each loader wave
+    // first waits for its reads of it, the only ones in flight) and frees the
+    // slot of tile k - 1, into which tile k + NSLOT - 1 is then read. Tile 0 is
+    // waited for before the loop.
+    static_assert(C::XS, "the barrier sits at the score exchange");
     bool q_pending = false;
+    if (nsteps > 0) {
+      wait_tile(0);
+      __syncthreads();
+    }
     for (int k = 0; k < nsteps; ++k) {
       if (q_pending) {
         // a new segment's query rows: read and waited for here, on this path
@@ -1446,14 +1463,19 @@ __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLd
         wait_vmcnt<0>();
         settle_q();
         q_pending = false;
-      } else {
-        wait_tile(k);
       }
-      __syncthreads();
       const NextTile nt =
           loader && k + C::NSLOT - 1 < nsteps ? prep_next(k + C::NSLOT - 1) : NextTile{};
-      tile_compute<C>(ring + (k % C::NSLOT) * C::TILE_BYTES, xchg, cs.t_lo + ck * C::TT, qreg, st,
-                      scale_log2, wr, wc, dc0, [&](int stage) { issue_part(nt, stage); },
+      tile_compute<C>(ring + (k % C::NSLOT) * C::TILE_BYTES, xchg + (k & 1) * C::XCHG_HALF,
+                      cs.t_lo + ck * C::TT, qreg, st, scale_log2, wr, wc, dc0,
+                      [&](int stage) {
+                        if (stage > 0) issue_part(nt, stage);
+                      },
+                      [&]() {
+                        wait_vmcnt<0>();
+                        __syncthreads();
+                        issue_part(nt, 0);
+                      },
                       xs_ctr, xs_seq, xs_bad, p.rendezvous_polls);
       if (++ck == cs.ntiles && k + 1 < nsteps) {
         end_seg();
