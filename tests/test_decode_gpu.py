@@ -109,6 +109,18 @@ def test_many_heads_ragged(rope):
     check(c, f"128 heads ragged rope={rope}")
 
 
+@pytest.mark.parametrize("nseq", [24, 48])
+def test_many_heads_many_tiny_sequences(nseq):
+    # 128 heads over many sequences of 1 to 100 keys: the split plan gives most
+    # workgroups several units, so their tile loops cross segment boundaries
+    # (a new unit's query rows read between two tiles). 24 sequences take
+    # 32-row units, 48 take 64-row units.
+    d = mi.Dims(n_head=128, d_nope=128, d_rope=64, d_v=128, kv_rank=512)
+    lens = [[1, 2, 3, 31, 32, 33, 64, 65, 100][i % 9] for i in range(nseq)]
+    c = mi.decode_case(40 + nseq, d, "bf16", lens)
+    check(c, f"128 heads x {nseq} tiny sequences")
+
+
 def test_many_heads_page16_tiles_span_pages():
     c = mi.decode_case(6, V3, "bf16", [300, 129], page=16)
     check(c, "128 heads page 16")
