@@ -315,10 +315,16 @@ def measured_peaks() -> dict:
     mfma = max(probe.mfma_bf16_tflops(0, w) for w in (2, 4))
     read = max(probe.read_gbs(1 << 30, w) for w in (1, 2, 4))
     copy = probe.copy_gbs(1 << 30)
+    # the V2-Lite call's bytes read alone: 256 workgroups x 17 tiles of 36 KB
+    tile_us, tile_gbs = probe.tile_stream_us(256, 17)
     return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(read, 1),
             "hbm_copy_gbs": round(copy, 1),
+            "tile_stream_us": round(tile_us, 2), "tile_stream_gbs": round(tile_gbs, 1),
             "how": "libmla_probe.so: bf16 16x16x32 MFMA chains (2 or 4 waves/SIMD), "
-                   "1 GiB non-temporal read stream (1, 2 or 4 workgroups/CU) and copy; best kept"}
+                   "1 GiB non-temporal read stream (1, 2 or 4 workgroups/CU) and copy; best kept; "
+                   "tile_stream: 256 workgroups x 17 tiles of 36 KB from random 72 KB pages "
+                   "through a three-slot LDS ring, the few-head decode's load schedule with "
+                   "no arithmetic"}
 
 
 def attention_warm_ms(step: Step, steps: int, warmup: int) -> float:

@@ -3,7 +3,8 @@
  *
  * The benchmark quotes each kernel against the published MI355X peaks and
  * also against the peaks these probes measure on the GPU it runs on: the
- * dense bf16 matrix-core rate and the HBM copy and read rates. Each enqueues one kernel
+ * dense bf16 matrix-core rate and the HBM copy and read rates, and the cost of
+ * the few-head decode's tile stream alone. Each enqueues one kernel
  * on `stream` and return at once; the caller times them (HIP events) and
  * owns every buffer. Return value: 0 on success, -1 for a NULL pointer, -5
  * for an argument outside the supported range, -7 for a HIP error.
@@ -42,6 +43,21 @@ int mla_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream)
  * words). The HBM traffic is `bytes`. */
 int mla_probe_read(uint32_t* sink, const void* src, size_t bytes, int workgroups_per_cu,
                    hipStream_t stream);
+
+/* The few-head decode's tile stream with no arithmetic: what reading the
+ * attention call's latent rows in the partial kernel's partition costs.
+ * `workgroups` (1..65535) workgroups of 256 threads; workgroup w reads tiles
+ * w * T .. w * T + T - 1 (T = tiles_per_workgroup >= 1) of 36,864 bytes (32
+ * rows of 576 bf16), tile t being half t % 2 of page page_perm[t / 2] of src,
+ * whose pages are 73,728 bytes. The reads go global -> LDS with 16-byte
+ * non-temporal loads into a three-slot ring, two tiles in flight, one
+ * workgroup barrier per tile, as the partial kernel issues them. The caller
+ * owns and sizes every buffer: page_perm (device) holds
+ * ceil(workgroups * T / 2) page indices, each below the page count of src
+ * (16-byte aligned); sink (device) takes one word per workgroup. The HBM
+ * traffic is workgroups * T * 36,864 bytes. */
+int mla_probe_tile_stream(uint32_t* sink, const void* src, const int32_t* page_perm,
+                          int tiles_per_workgroup, int workgroups, hipStream_t stream);
 
 #ifdef __cplusplus
 }

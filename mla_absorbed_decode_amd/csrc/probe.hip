@@ -2,10 +2,12 @@
 // matrix-core rate and the HBM copy and read rates of the GPU it runs on. They are not
 // part of the attention path; they give the measured peaks that the
 // benchmark's roofline fractions are also quoted against, next to the
-// published ones.
+// published ones. A fourth probe streams tiles with the few-head decode's load
+// schedule and no arithmetic: what reading the call's bytes alone costs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mla_device.h"
 #include "mla_probe.h"
 
 namespace {
@@ -96,6 +98,46 @@ __global__ void __launch_bounds__(256) read16_kernel(uint32_t* __restrict__ sink
   sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// The few-head decode's load schedule without its arithmetic: workgroup w
+// reads tiles w * T .. w * T + T - 1 of kTileBytes each, tile t being half t % 2
+// of page page_perm[t / 2] (2 * kTileBytes per page), global -> LDS with
+// non-temporal 16-byte loads into a three-slot ring; four waves issue (nine
+// 1 KB reads each per tile), two tiles in flight, one barrier per tile.
+constexpr int kTileBytes = 32 * 1152;         // 32 latent rows of 576 bf16
+constexpr int kTileReads = kTileBytes / 1024;  // 1 KB wave reads per tile
+constexpr int kTileSlots = 3;
+
+__global__ void __launch_bounds__(256) tile_stream_kernel(uint32_t* __restrict__ sink,
+                                                          const char* __restrict__ base,
+                                                          const int32_t* __restrict__ page_perm,
+                                                          int tiles_per_workgroup) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  MLA_LDS char* ring = (MLA_LDS char*)smem;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int kPerWave = kTileReads / 4;
+  static_assert(kPerWave * 4 == kTileReads, "tile reads split over four waves");
+  const int T = tiles_per_workgroup;
+  const int64_t t0 = (int64_t)blockIdx.x * T;
+  auto issue = [&](int i) {
+    const int64_t t = t0 + i;
+    const char* a = base + (int64_t)page_perm[t >> 1] * (2 * kTileBytes) + (t & 1) * kTileBytes;
+    MLA_LDS char* dst = ring + (i % kTileSlots) * kTileBytes;
+#pragma unroll
+    for (int n = 0; n < kPerWave; ++n) {
+      const int piece = w + 4 * n;
+      mla::load_lds_16<true>(a + piece * 1024 + lane * 16, dst + piece * 1024);
+    }
+  };
+  for (int i = 0; i < kTileSlots - 1 && i < T; ++i) issue(i);
+  for (int i = 0; i < T; ++i) {
+    // tile i has landed; tile i + 1 may stay in flight
+    mla::wait_vmcnt_n<kTileSlots - 2, kPerWave>(T - 1 - i);
+    __syncthreads();  // every wave's part of tile i is in LDS; the slot of tile i - 1 is free
+    if (i + kTileSlots - 1 < T) issue(i + kTileSlots - 1);
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = *(const MLA_LDS uint32_t*)ring;
+}
+
 int cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -152,6 +194,25 @@ int mla_probe_read(uint32_t* sink, const void* src, size_t bytes, int workgroups
   const int64_t n = (int64_t)(bytes / 16);
   hipLaunchKernelGGL(read16_kernel<8>, dim3((unsigned)(cus * workgroups_per_cu)), dim3(256), 0,
                      stream, sink, (const u32x4_t*)src, n);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int mla_probe_tile_stream(uint32_t* sink, const void* src, const int32_t* page_perm,
+                          int tiles_per_workgroup, int workgroups, hipStream_t stream) {
+  if (!sink || !src || !page_perm) return -1;
+  if ((uintptr_t)src % 16 || tiles_per_workgroup < 1 || workgroups < 1 || workgroups > 65535)
+    return -5;
+  static bool attr = false;  // the attribute is per function, set once per process
+  if (!attr) {
+    if (hipFuncSetAttribute((const void*)tile_stream_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kTileSlots * kTileBytes) != hipSuccess)
+      return -7;
+    attr = true;
+  }
+  hipLaunchKernelGGL(tile_stream_kernel, dim3((unsigned)workgroups), dim3(256),
+                     kTileSlots * kTileBytes, stream, sink, (const char*)src, page_perm,
+                     tiles_per_workgroup);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -1,5 +1,6 @@
 """Measured peaks of the GPU the benchmark runs on (libmla_probe.so, see
-include/mla_probe.h): the dense bf16 MFMA rate and the HBM copy and read rates.
+include/mla_probe.h): the dense bf16 MFMA rate and the HBM copy and read rates,
+and the time of the few-head decode's tile stream with no arithmetic.
 
 These are measurement tools for the benchmark, not part of the attention
 path. Each function enqueues its probe kernel on the current stream, times it
@@ -32,6 +33,9 @@ def load() -> ctypes.CDLL:
         lib.mla_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_int, ctypes.c_void_p]
         lib.mla_probe_read.restype = ctypes.c_int
+        lib.mla_probe_tile_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.mla_probe_tile_stream.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -106,3 +110,40 @@ def read_gbs(nbytes: int = 1 << 30, workgroups_per_cu: int = 8, reps: int = 5) -
     run()
     ms = _timed(run, reps)
     return nbytes / (ms * 1e-3) / 1e9
+
+
+TILE_BYTES = 32 * 1152   # a 32-row tile of 576 bf16 latent rows
+PAGE_BYTES = 2 * TILE_BYTES
+
+
+def tile_stream_us(workgroups: int = 256, tiles_per_workgroup: int = 17, copies: int = 4,
+                   reps: int = 12, seed: int = 0) -> tuple[float, float]:
+    """Median µs (and GB/s) of reading workgroups * tiles_per_workgroup 36 KB
+    tiles in the few-head decode's partition and load schedule, with no
+    arithmetic: the pages (two tiles each) in a seeded random order, as a
+    shuffled block table gives them. Launches rotate over `copies` buffers so
+    that the reads come from HBM."""
+    import numpy as np
+
+    lib = load()
+    dev = torch.device("cuda:0")
+    tiles = workgroups * tiles_per_workgroup
+    pages = (tiles + 1) // 2
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(pages).astype(np.int32)).to(dev)
+    bufs = [torch.ones(pages * PAGE_BYTES, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    sink = torch.empty(workgroups, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    turn = [0]
+
+    def run():
+        buf = bufs[turn[0] % copies]
+        turn[0] += 1
+        rc = lib.mla_probe_tile_stream(sink.data_ptr(), buf.data_ptr(), perm.data_ptr(),
+                                       tiles_per_workgroup, workgroups, stream)
+        if rc:
+            raise RuntimeError(f"mla_probe_tile_stream failed ({rc})")
+
+    for _ in range(copies):
+        run()
+    ms = _timed(run, reps)
+    return ms * 1e3, tiles * TILE_BYTES / (ms * 1e-3) / 1e9

@@ -60,6 +60,28 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_every_declared_symbol():
+    # libmla_probe.so (the benchmark's measured peaks) against include/mla_probe.h
+    import os
+    import re
+
+    from mla_absorbed_decode_amd import probe
+
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "include", "mla_probe.h")
+    names = re.findall(r"^int\s+(mla_probe_\w+)\s*\(", open(hdr).read(), flags=re.M)
+    assert set(names) == {"mla_probe_mfma_bf16", "mla_probe_copy", "mla_probe_read",
+                          "mla_probe_tile_stream"}
+    plib = probe.load()
+    for n in names:
+        assert hasattr(plib, n), n
+    # argument checks run before any HIP call
+    assert plib.mla_probe_tile_stream(None, None, None, 17, 256, None) == -1
+    assert plib.mla_probe_tile_stream(FAKE, FAKE, FAKE, 0, 256, None) == -5
+    assert plib.mla_probe_tile_stream(FAKE, FAKE + 8, FAKE, 17, 256, None) == -5
+    assert plib.mla_probe_tile_stream(FAKE, FAKE, FAKE, 17, 0, None) == -5
+
+
 def test_status_strings(lib):
     for code, name in mla.STATUS.items():
         assert mla.mla_status_str(code).startswith(name)
