@@ -911,15 +911,17 @@ __device__ __forceinline__ void store_row(const DecodeParams& p, int b, int unit
         const f32x4_t v = o[d] * inv;
         const u32x2_t w = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         // the layouts without loader waves (32 and 64 rows: units that share keys)
-        // write their partials with the non-temporal policy: the 128-head decode
-        // measured 29.4 -> 28.1 us; the few-head layout measured slower with it
-        if constexpr (C::NP == 0) __builtin_nontemporal_store(w, (u32x2_t*)(dst + 16 * d));
+        // and the fp8 layout write their partials with the non-temporal policy:
+        // the 128-head decode measured 29.4 -> 28.1 us, the fp8 call 38.3 -> 37.6
+        // us; the bf16 few-head layout measured slower with it (37.9 -> 41.0 us,
+        // its merge then reading the partials from memory rather than the L2)
+        if constexpr (C::NP == 0 || C::KV8) __builtin_nontemporal_store(w, (u32x2_t*)(dst + 16 * d));
         else *(u32x2_t*)(dst + 16 * d) = w;
       }
     }
     if (write_lse && g == 0) {
       float* lp = p.part_lse + (int64_t)slot * p.rows_per_unit + local_row;
-      if constexpr (C::NP == 0) __builtin_nontemporal_store(lse2, lp);
+      if constexpr (C::NP == 0 || C::KV8) __builtin_nontemporal_store(lse2, lp);
       else *lp = lse2;
     }
     return;
