@@ -1011,14 +1011,16 @@ __device__ __forceinline__ int next_live(const DecodeParams& p, const SegLds* ta
 
 // ------------------------------------------------------ the tile stream
 // All tiles of the workgroup's segments form one stream staged through an LDS
-// ring of NSLOT tiles, with one workgroup barrier per tile: before barrier k
-// tile k has landed and every compute wave is done with tile k-1, whose slot
-// the reads of tile k + NSLOT - 1 then refill. Reads run NSLOT - 1 tiles ahead
-// of the compute, across segment boundaries. At a boundary the compute waves
-// write the finished segment (final output, or a partial for the merge) and
-// load the next segment's query rows. With NP loader waves the compute waves
-// never stall on a full memory queue; without them the compute waves send the
-// next tile's reads in three groups between their own phases.
+// ring of NSLOT tiles, with one workgroup barrier per tile. With NP loader
+// waves the barrier opens tile k: before it tile k has landed and every compute
+// wave is done with tile k-1, whose slot the reads of tile k + NSLOT - 1 then
+// refill, so reads run NSLOT - 1 tiles ahead and the compute waves never stall
+// on a full memory queue. Without loader waves the barrier sits at tile k's
+// score exchange: before it tile k + 1 has landed and every wave is done with
+// tile k - 1, and the waves send the reads of tile k + NSLOT - 1 in three
+// groups between their own phases. Either way the stream runs across segment
+// boundaries; at a boundary the compute waves write the finished segment (final
+// output, or a partial for the merge) and load the next segment's query rows.
 template <class C>
 __device__ __forceinline__ void process_range(const DecodeParams& p, const SegLds* tab, int* sh_blk,
                                               MLA_LDS char* ring, MLA_LDS f32x4_t* xchg) {
