@@ -16,8 +16,9 @@
 // of one tile each. With many units (prefill) each workgroup takes one unit. With few
 // units (decode) the work blocks of all units are laid end to end and cut
 // into `grid` equal chunks, one per workgroup; a unit that lands in more than
-// one chunk is written as normalised fp32 partials plus a log2-domain lse per
-// chunk and merged by decode_merge in chunk order (deterministic). The plan
+// one chunk is written as normalised partial rows (bf16 for bf16 inputs, f32
+// for f32) plus an f32 log2-domain lse per chunk and merged by decode_merge in
+// chunk order (deterministic). The plan
 // depends only on seqlens and sizes, never on strides or pointers.
 //
 // Inside a workgroup
